@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA NF4 + double-quant + LoRA linear on one MI355X.
+
+One step = forward + backward (dX, dA, dB) of the three LLaMA-7B-shaped linears
+4096->4096, 4096->11008, 11008->4096 at M = 4096 tokens, r = 64, alpha = 16, on
+seeded synthetic bf16 inputs already resident in HBM.  The weights are quantized
+(NF4 + 8-bit double quantization) once before timing; quantization throughput is
+reported separately.  The headline value is algorithmic TFLOP/s,
+4MNK + 6Mr(K+N) per linear (no dW is computed).
+
+Also reported: the M = 1 forward weight stream (GB/s) on the 4096->11008 and
+11008->4096 weights (r = 16, alpha = 32), replayed from a HIP graph over more than
+512 MB of distinct weight copies so the bytes come from HBM; the roofline of the
+dominant kernel (the fused NF4 GEMM, timed per launch with HIP events recorded by
+the library on its launch stream); and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NF4+LoRA linear fwd+bwd TFLOP/s at M=4096; weight-stream GB/s at M=1"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its launch stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pool = []
+
+    def pair(self):
+        a, b = ctypes.c_void_p(), ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(a)) or self.lib.hipEventCreate(ctypes.byref(b)):
+            raise RuntimeError("hipEventCreate failed")
+        self.pool.append((a.value, b.value))
+        return a.value, b.value
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), a, b):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for a, b in self.pool:
+            self.lib.hipEventDestroy(a)
+            self.lib.hipEventDestroy(b)
+        self.pool = []
+
+
+def linear_flops(M, K, N, r):
+    return 4 * M * N * K + 6 * M * r * (K + N)
+
+
+def stream_bytes(M, K, N, r):
+    n = N * K
+    return n // 2 + n // 64 + 8 * ((n // 64 + 255) // 256) + 2 * r * (K + N) + 2 * M * K + 2 * M * N
+
+
+def setup_workload2(torch, q, synth, gc):
+    wl = synth.WORKLOADS[2]
+    M = wl.M[0]
+    L = []
+    for i, (K, N) in enumerate(wl.linears):
+        d = synth.workload_linear(2, i)
+        W = gc.dev_weight(d)
+        qw = q.quantize(W)
+        e = dict(K=K, N=N, qw=qw, W=W, X=gc.dev_bf16(d["X"]), A=gc.dev_bf16(d["A"]),
+                 B=gc.dev_bf16(d["B"]), dY=gc.dev_bf16(d["dY"]))
+        e["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        e["U"] = torch.empty((M, wl.r), dtype=torch.bfloat16, device="cuda")
+        e["dX"] = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        e["dA"] = torch.empty((wl.r, K), dtype=torch.bfloat16, device="cuda")
+        e["dB"] = torch.empty((N, wl.r), dtype=torch.bfloat16, device="cuda")
+        e["ws"] = q.workspace(1, M, K, N, wl.r, "cuda")
+        L.append(e)
+    return wl, M, L
+
+
+def run_step(q, wl, L, ev=None, record=None):
+    for e in L:
+        if ev is not None:
+            a, b = ev.pair()
+            q._lib.qlora_time_next_gemm(a, b)
+            record.append((a, b, "fwd", e))
+        q.linear_fwd(e["qw"], e["X"], e["A"], e["B"], wl.alpha, Y=e["Y"], U=e["U"])
+        if ev is not None:
+            a, b = ev.pair()
+            q._lib.qlora_time_next_gemm(a, b)
+            record.append((a, b, "dx", e))
+        q.linear_bwd(e["qw"], e["dY"], e["X"], e["A"], e["B"], wl.alpha, e["U"], dX=e["dX"],
+                     dA=e["dA"], dB=e["dB"], ws=e["ws"])
+
+
+def measure_quantize(torch, q, L, reps=5):
+    t = []
+    elems = 0
+    for e in L:
+        for _ in range(2):
+            q.quantize(e["W"])
+        torch.cuda.synchronize()
+        s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            q.quantize(e["W"])
+        f.record()
+        torch.cuda.synchronize()
+        t.append(s.elapsed_time(f) / reps)
+        elems += e["K"] * e["N"]
+    ms = sum(t)
+    return {"value": round(elems * 2.516 / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "bytes_per_weight": 2.516, "ms_three_weights": round(ms, 4),
+            "frac_of_hbm_peak": round(elems * 2.516 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "what": "bf16 -> NF4 codes + int8 DQ constants, the three workload-2 weights"}
+
+
+def measure_m1(torch, q, synth, gc, ev, min_bytes=600 << 20, calls=200):
+    """M = 1 forward over distinct weight copies, replayed from a HIP graph."""
+    wl = synth.WORKLOADS[3]
+    out = {"per_linear": []}
+    tot_bytes = tot_ms = 0.0
+    for i, (K, N) in enumerate(wl.linears):
+        d = synth.workload_linear(3, i, M=1, parts=("W", "X", "A", "B"))
+        qw0 = q.quantize(gc.dev_weight(d))
+        wbytes = qw0.codes.numel() + qw0.absmax_q.numel() + 8 * qw0.dq_scale.numel()
+        copies = max(2, -(-min_bytes // wbytes))
+        qws = [q.NF4Weight(qw0.codes.clone(), qw0.absmax_q.clone(), qw0.dq_scale.clone(),
+                           qw0.dq_offset.clone(), qw0.n_rows, qw0.n_cols) for _ in range(copies)]
+        X, A, B = gc.dev_bf16(d["X"]), gc.dev_bf16(d["A"]), gc.dev_bf16(d["B"])
+        Y = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+        U = torch.empty((1, wl.r), dtype=torch.bfloat16, device="cuda")
+        for c in range(copies):  # warm up, and make sure every copy works eagerly
+            q.linear_fwd(qws[c], X, A, B, wl.alpha, Y=Y, U=U)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in range(calls):
+                q.linear_fwd(qws[c % copies], X, A, B, wl.alpha, Y=Y, U=U)
+        g.replay()
+        torch.cuda.synchronize()
+        s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        reps = 5
+        for _ in range(reps):
+            g.replay()
+        f.record()
+        torch.cuda.synchronize()
+        ms_call = s.elapsed_time(f) / (reps * calls)
+        # kernel-only time of the GEMV (event hook, eager launches)
+        rec = []
+        for c in range(copies):
+            a, b = ev.pair()
+            q._lib.qlora_time_next_gemm(a, b)
+            q.linear_fwd(qws[c], X, A, B, wl.alpha, Y=Y, U=U)
+        torch.cuda.synchronize()
+        kms = sum(ev.ms(a, b) for a, b in ev.pool[-copies:]) / copies
+        nb = stream_bytes(1, K, N, wl.r)
+        out["per_linear"].append({"K": K, "N": N, "us_per_call": round(ms_call * 1e3, 3),
+                                  "GB/s": round(nb / (ms_call * 1e-3) / 1e9, 1),
+                                  "gemv_kernel_us": round(kms * 1e3, 3),
+                                  "gemv_kernel_GB/s": round(nb / (kms * 1e-3) / 1e9, 1),
+                                  "weight_copies": copies})
+        tot_bytes += nb
+        tot_ms += ms_call
+        del qws
+    out.update({"value": round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                "frac_of_hbm_peak": round(tot_bytes / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "bytes_per_call": "N*K/2 + N*K/64 + 8*groups + 2r(K+N) + 2MK + 2MN",
+                "timing": "HIP graph replay of 200 calls over >512 MB of weight copies"})
+    return out
+
+
+def cpu_baseline(synth, sample_m=1024):
+    """The oracle (float64 numpy) on a bounded sample of the workload: the first
+    linear (4096 -> 4096) with the first `sample_m` tokens: decode of W' from the
+    stored format, forward and backward."""
+    import numpy as np
+    from oracle import linear, nf4
+    wl = synth.WORKLOADS[2]
+    d = synth.workload_linear(2, 0)
+    K, N = wl.linears[0]
+    qw = nf4.quantize_nf4(synth.bf16_bits_to_f32(d["W"]))
+    f = lambda k: synth.bf16_bits_to_f32(d[k]).astype(np.float64)  # noqa: E731
+    X, A, B, dY = f("X")[:sample_m], f("A"), f("B"), f("dY")[:sample_m]
+    t0 = time.perf_counter()
+    Wd = nf4.dequantize_bf16(qw)
+    linear.forward(X, Wd, A, B, wl.alpha, wl.r)
+    linear.backward(dY, X, Wd, A, B, wl.alpha, wl.r)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    fl = linear_flops(sample_m, K, N, wl.r)
+    return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"linear 4096->4096 of the workload, first {sample_m} of 4096 tokens: "
+                      "decode W' + forward + backward in float64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the M=1 and quantize legs")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1 "
+              "(the data-parallel all-reduce of dA/dB is not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_lora_nf4_amd as q
+    import synth
+    from tests import gpu_cases as gc
+
+    print("bench: setting up workload 2 (3 linears, M=4096)", file=sys.stderr, flush=True)
+    wl, M, L = setup_workload2(torch, q, synth, gc)
+    ev = HipEvents()
+    for _ in range(args.warmup):
+        run_step(q, wl, L)
+    torch.cuda.synchronize()
+    rec = []
+    t0 = time.perf_counter()
+    s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        run_step(q, wl, L, ev, rec)
+    f.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = s.elapsed_time(f) / args.steps
+    flops_step = sum(linear_flops(M, e["K"], e["N"], wl.r) for e in L)
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    print(f"bench: {args.steps} steps, {ms_step:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr,
+          flush=True)
+
+    g_fl = g_ms = 0.0
+    per = {}
+    for a, b, kind, e in rec:
+        ms = ev.ms(a, b)
+        fl = 2 * M * e["N"] * e["K"] + 2 * M * wl.r * (e["N"] if kind == "fwd" else e["K"])
+        g_fl += fl
+        g_ms += ms
+        key = f"{kind} {e['K']}->{e['N']}"
+        per.setdefault(key, [0.0, 0.0, 0])
+        per[key][0] += fl
+        per[key][1] += ms
+        per[key][2] += 1
+    achieved = g_fl / (g_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "kernel": "fused NF4-decode GEMM (forward and dX launches)",
+            "per_launch_flops": "fwd 2MNK + 2MNr; dX 2MNK + 2MKr",
+            "avg_launch_us": round(g_ms * 1e3 / max(1, len(rec)), 2),
+            "per_shape": {k: {"TFLOP/s": round(v[0] / (v[1] * 1e-3) / 1e12, 1),
+                              "avg_us": round(v[1] * 1e3 / v[2], 1)} for k, v in per.items()},
+            "step_time_in_gemm": round(g_ms / args.steps / ms_step, 4)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,.02^2) bf16 weights NF4+DQ-quantized; X, dY ~ N(0,1))",
+        "config": {"workload": "LLaMA-7B linears 4096->4096, 4096->11008, 11008->4096; fwd+bwd",
+                   "M": M, "r": wl.r, "alpha": wl.alpha, "block": 64, "dq_group": 256,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    ev.close()
+    if not args.no_extras:
+        print("bench: M=1 weight stream", file=sys.stderr, flush=True)
+        result["weight_stream_m1"] = measure_m1(torch, q, synth, gc, ev)
+        ev.close()
+        result["quantize"] = measure_quantize(torch, q, L)
+    if not args.no_cpu_baseline:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+"""QLoRA linear layer (NF4 weight + double-quantized constants + LoRA) for MI355X.
+
+The compute happens in the HIP library ``libqlora_nf4.so`` (C ABI in
+``include/qlora_nf4.h``).  This module only marshals torch tensors into that ABI:
+torch provides device memory and the current stream.  There is no CPU or PyTorch
+fallback; every call fails loudly if the library is missing or the device is not
+a gfx950.
+
+    qw = quantize(W)                                   # W [N, K] fp32 or bf16, on the GPU
+    Y, U = linear_fwd(qw, X, A, B, alpha)              # Y = X W'^T + (alpha/r) X A^T B^T
+    dX, dA, dB = linear_bwd(qw, dY, X, A, B, alpha, U)
+"""
+
+from dataclasses import dataclass
+
+from . import _lib
+from ._lib import (QLORA_BF16, QLORA_F32, QloraError, qlora_dequantize, qlora_linear_bwd,  # noqa: F401
+                   qlora_linear_fwd, qlora_nf4_codebook, qlora_nf4_sizes, qlora_quantize_nf4,
+                   qlora_workspace_bytes)
+
+__all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "workspace",
+           "QloraError", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
+           "qlora_linear_bwd", "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+@dataclass
+class NF4Weight:
+    """Device arrays of a quantized weight W[n_rows = d_out, n_cols = d_in]."""
+    codes: "object"      # uint8 [n_rows * n_cols / 2]
+    absmax_q: "object"   # int8 [n_blocks]
+    dq_scale: "object"   # float32 [n_groups]
+    dq_offset: "object"  # float32 [n_groups]
+    n_rows: int
+    n_cols: int
+
+    def descriptor(self):
+        return _lib.qlora_nf4_weight(self.codes.data_ptr(), self.absmax_q.data_ptr(),
+                                     self.dq_scale.data_ptr(), self.dq_offset.data_ptr(),
+                                     self.n_rows, self.n_cols)
+
+    @property
+    def shape(self):
+        return (self.n_rows, self.n_cols)
+
+
+def _stream(t):
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize(W, return_absmax=False):
+    """NF4 + double quantization of W [n_rows, n_cols] (fp32 or bf16, on the GPU)."""
+    torch = _torch()
+    if W.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("W must be float32 or bfloat16")
+    _need(W, W.dtype, "W")
+    n_rows, n_cols = W.shape
+    code_bytes, n_blocks, n_groups = qlora_nf4_sizes(n_rows, n_cols)
+    dev = W.device
+    codes = torch.empty(code_bytes, dtype=torch.uint8, device=dev)
+    absmax_q = torch.empty(n_blocks, dtype=torch.int8, device=dev)
+    s = torch.empty(n_groups, dtype=torch.float32, device=dev)
+    o = torch.empty(n_groups, dtype=torch.float32, device=dev)
+    c = torch.empty(n_blocks, dtype=torch.float32, device=dev) if return_absmax else None
+    dt = QLORA_BF16 if W.dtype == torch.bfloat16 else QLORA_F32
+    _lib.check(qlora_quantize_nf4(W.data_ptr(), dt, n_rows, n_cols, codes.data_ptr(),
+                                  absmax_q.data_ptr(), s.data_ptr(), o.data_ptr(), _ptr(c),
+                                  _stream(W)), "qlora_quantize_nf4")
+    qw = NF4Weight(codes, absmax_q, s, o, n_rows, n_cols)
+    return (qw, c) if return_absmax else qw
+
+
+def dequantize(qw, dtype=None, out=None):
+    """W' [n_rows, n_cols]: bf16 (default) or the fp32 product before bf16 rounding."""
+    torch = _torch()
+    dtype = dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty(qw.shape, dtype=dtype, device=qw.codes.device)
+    dt = QLORA_BF16 if dtype == torch.bfloat16 else QLORA_F32
+    _lib.check(qlora_dequantize(qw.descriptor(), out.data_ptr(), dt, _stream(out)), "qlora_dequantize")
+    return out
+
+
+def workspace(op, M, K, N, r, device):
+    """Allocate the caller workspace for op 0 (forward) or 1 (backward)."""
+    torch = _torch()
+    n = qlora_workspace_bytes(op, M, K, N, r)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def linear_fwd(qw, X, A=None, B=None, alpha=16.0, save_u=True, Y=None, U=None, ws=None):
+    """Y = bf16(X W'^T + U_s B^T) with U_s = bf16((alpha/r) X A^T).  Returns (Y, U_s or None)."""
+    torch = _torch()
+    _need(X, torch.bfloat16, "X")
+    M, K = X.shape
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _need(A, torch.bfloat16, "A")
+        _need(B, torch.bfloat16, "B")
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((M, qw.n_rows), dtype=torch.bfloat16, device=dev)
+    if r and save_u and U is None:
+        U = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    if r and not save_u and ws is None:
+        ws = workspace(0, M, K, qw.n_rows, r, dev)
+    _lib.check(qlora_linear_fwd(qw.descriptor(), X.data_ptr(), M, _ptr(A), _ptr(B), r, float(alpha),
+                                Y.data_ptr(), _ptr(U) if save_u else None, _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(X)), "qlora_linear_fwd")
+    return Y, (U if save_u else None)
+
+
+def linear_bwd(qw, dY, X, A=None, B=None, alpha=16.0, U=None, need_dx=True, dX=None, dA=None,
+               dB=None, ws=None):
+    """(dX, dA, dB) of the QLoRA linear; no gradient for the frozen weight."""
+    torch = _torch()
+    _need(dY, torch.bfloat16, "dY")
+    M = dY.shape[0]
+    K, N = qw.n_cols, qw.n_rows
+    r = 0 if A is None else A.shape[0]
+    dev = dY.device
+    if need_dx and dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if r:
+        if dA is None:
+            dA = torch.empty((r, K), dtype=torch.bfloat16, device=dev)
+        if dB is None:
+            dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+        if ws is None:
+            ws = workspace(1, M, K, N, r, dev)
+    _lib.check(qlora_linear_bwd(qw.descriptor(), dY.data_ptr(), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                float(alpha), _ptr(U), _ptr(dX) if need_dx else None, _ptr(dA),
+                                _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dY)),
+               "qlora_linear_bwd")
+    return (dX if need_dx else None), dA, dB

@@ -1,0 +1,138 @@
+"""ctypes binding of ``libqlora_nf4.so``: the C ABI of ``include/qlora_nf4.h``, same names.
+
+Argument marshalling only.  Loading the library needs no GPU; the device entry
+points return ``QLORA_ERR_DEVICE`` when no gfx950 device is present.  There is no
+fallback: if the shared library has not been built, loading raises.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqlora_nf4.so")
+
+QLORA_OK = 0
+QLORA_ERR_NULL = -1
+QLORA_ERR_SHAPE = -2
+QLORA_ERR_RANK = -3
+QLORA_ERR_DTYPE = -4
+QLORA_ERR_WORKSPACE = -5
+QLORA_ERR_ALIGN = -6
+QLORA_ERR_DEVICE = -7
+QLORA_ERR_LAUNCH = -8
+QLORA_F32 = 0
+QLORA_BF16 = 1
+
+EXPORTED = (
+    "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes", "qlora_status_string",
+    "qlora_last_error", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
+    "qlora_linear_bwd", "qlora_time_next_gemm",
+)
+
+
+class qlora_nf4_weight(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("absmax_q", ctypes.c_void_p),
+        ("dq_scale", ctypes.c_void_p),
+        ("dq_offset", ctypes.c_void_p),
+        ("n_rows", ctypes.c_int64),
+        ("n_cols", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load (once) and return the ctypes library with prototypes set."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m bit_quantized_lora_nf4_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I64, I32, SZ, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    W = ctypes.POINTER(qlora_nf4_weight)
+    lib.qlora_nf4_sizes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(I64), ctypes.POINTER(I64)]
+    lib.qlora_nf4_sizes.restype = I32
+    lib.qlora_nf4_codebook.argtypes = [ctypes.POINTER(F32), ctypes.POINTER(F32)]
+    lib.qlora_nf4_codebook.restype = None
+    lib.qlora_workspace_bytes.argtypes = [I32, I64, I64, I64, I32]
+    lib.qlora_workspace_bytes.restype = SZ
+    lib.qlora_status_string.argtypes = [I32]
+    lib.qlora_status_string.restype = ctypes.c_char_p
+    lib.qlora_last_error.argtypes = []
+    lib.qlora_last_error.restype = ctypes.c_char_p
+    lib.qlora_quantize_nf4.argtypes = [P, I32, I64, I64, P, P, P, P, P, P]
+    lib.qlora_quantize_nf4.restype = I32
+    lib.qlora_dequantize.argtypes = [W, P, I32, P]
+    lib.qlora_dequantize.restype = I32
+    lib.qlora_linear_fwd.argtypes = [W, P, I64, P, P, I32, F32, P, P, P, SZ, P]
+    lib.qlora_linear_fwd.restype = I32
+    lib.qlora_linear_bwd.argtypes = [W, P, P, I64, P, P, I32, F32, P, P, P, P, P, SZ, P]
+    lib.qlora_linear_bwd.restype = I32
+    lib.qlora_time_next_gemm.argtypes = [P, P]
+    lib.qlora_time_next_gemm.restype = None
+    _lib = lib
+    return lib
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status, where):
+        lib = load()
+        msg = lib.qlora_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {lib.qlora_status_string(status).decode()} ({status}): {msg}")
+        self.status = status
+
+
+def check(status, where):
+    if status != QLORA_OK:
+        raise QloraError(status, where)
+
+
+# ---- same-name thin wrappers (plain integers / pointers) ------------------------
+
+def qlora_nf4_sizes(n_rows, n_cols):
+    lib = load()
+    cb, nb, ng = ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int64()
+    check(lib.qlora_nf4_sizes(n_rows, n_cols, ctypes.byref(cb), ctypes.byref(nb), ctypes.byref(ng)),
+          "qlora_nf4_sizes")
+    return cb.value, nb.value, ng.value
+
+
+def qlora_nf4_codebook():
+    lib = load()
+    q = (ctypes.c_float * 16)()
+    t = (ctypes.c_float * 15)()
+    lib.qlora_nf4_codebook(q, t)
+    return list(q), list(t)
+
+
+def qlora_workspace_bytes(op, M, K, N, r):
+    return load().qlora_workspace_bytes(op, M, K, N, r)
+
+
+def qlora_quantize_nf4(W, w_dtype, n_rows, n_cols, codes, absmax_q, dq_scale, dq_offset,
+                       absmax_f32, stream):
+    return load().qlora_quantize_nf4(W, w_dtype, n_rows, n_cols, codes, absmax_q, dq_scale,
+                                     dq_offset, absmax_f32, stream)
+
+
+def qlora_dequantize(w, out, out_dtype, stream):
+    return load().qlora_dequantize(ctypes.byref(w), out, out_dtype, stream)
+
+
+def qlora_linear_fwd(w, X, M, A, B, r, alpha, Y, U_saved, workspace, workspace_bytes, stream):
+    return load().qlora_linear_fwd(ctypes.byref(w), X, M, A, B, r, alpha, Y, U_saved, workspace,
+                                   workspace_bytes, stream)
+
+
+def qlora_linear_bwd(w, dY, X, M, A, B, r, alpha, U_saved, dX, dA, dB, workspace,
+                     workspace_bytes, stream):
+    return load().qlora_linear_bwd(ctypes.byref(w), dY, X, M, A, B, r, alpha, U_saved, dX, dA, dB,
+                                   workspace, workspace_bytes, stream)
+
+
+def qlora_time_next_gemm(start_event, stop_event):
+    load().qlora_time_next_gemm(start_event, stop_event)

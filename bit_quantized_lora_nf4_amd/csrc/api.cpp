@@ -1,0 +1,325 @@
+// C ABI of the library: argument checks, workspace layout and kernel dispatch.
+// Every check runs on the host before anything is enqueued; the kernels then run
+// asynchronously on the caller's stream.  No device memory is allocated here.
+
+#include "../../include/qlora_nf4.h"
+#include "qlora_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+
+// Launch through the timing hook: bracket with the armed events, then disarm.
+template <typename F>
+hipError_t timed_launch(hipStream_t st, F launch) {
+  if (!g_ev_start || !g_ev_stop) return launch();
+  hipEvent_t a = g_ev_start, b = g_ev_stop;
+  g_ev_start = g_ev_stop = nullptr;
+  hipError_t e = hipEventRecord(a, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  return hipEventRecord(b, st);
+}
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 40;
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+int check_weight_shape(int64_t n_rows, int64_t n_cols) {
+  if (n_rows < 1 || n_cols < 1 || n_cols % qlora::kBlock != 0)
+    return fail(QLORA_ERR_SHAPE, "weight shape [%lld, %lld]: need n_rows >= 1 and n_cols a positive multiple of 64",
+                (long long)n_rows, (long long)n_cols);
+  if (n_rows > kMaxDim || n_cols > kMaxDim || n_rows > kMaxDim / n_cols)
+    return fail(QLORA_ERR_SHAPE, "weight shape [%lld, %lld] too large", (long long)n_rows,
+                (long long)n_cols);
+  return QLORA_OK;
+}
+
+int check_weight(const qlora_nf4_weight *w) {
+  if (!w) return fail(QLORA_ERR_NULL, "weight descriptor is NULL");
+  int s = check_weight_shape(w->n_rows, w->n_cols);
+  if (s != QLORA_OK) return s;
+  if (!w->codes || !w->absmax_q || !w->dq_scale || !w->dq_offset)
+    return fail(QLORA_ERR_NULL, "weight descriptor has a NULL array");
+  if (!aligned16(w->codes))
+    return fail(QLORA_ERR_ALIGN, "weight codes must be 16-byte aligned");
+  return QLORA_OK;
+}
+
+int check_rank(int r, float alpha) {
+  if (r < 0 || r > QLORA_MAX_RANK) return fail(QLORA_ERR_RANK, "r = %d outside [0, 256]", r);
+  if (r > 0 && !std::isfinite(alpha)) return fail(QLORA_ERR_RANK, "alpha is not finite");
+  return QLORA_OK;
+}
+
+int check_m(int64_t M) {
+  if (M < 1 || M > kMaxDim) return fail(QLORA_ERR_SHAPE, "M = %lld must be >= 1", (long long)M);
+  return QLORA_OK;
+}
+
+// The library runs on gfx950 only; the answer is cached per device ordinal.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(QLORA_ERR_DEVICE, "no HIP device available");
+  }
+  static std::mutex mu;
+  static int known[64] = {0};  // 0 unknown, 1 ok, 2 not gfx950
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 64 && known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(QLORA_ERR_DEVICE, "hipGetDeviceProperties failed on device %d", dev);
+    }
+    known[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+  }
+  if (dev >= 64 || known[dev] != 1)
+    return fail(QLORA_ERR_DEVICE, "device %d is not a gfx950 (MI355X) GPU", dev);
+  return QLORA_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+  if (e != hipSuccess)
+    return fail(QLORA_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return QLORA_OK;
+}
+
+qlora::WeightView view(const qlora_nf4_weight *w) {
+  return qlora::WeightView{w->codes, w->absmax_q, w->dq_scale, w->dq_offset, w->n_rows,
+                           w->n_cols};
+}
+
+// ---- workspace layouts ------------------------------------------------------
+struct FwdLayout {
+  size_t u = 0, total = 0;
+};
+FwdLayout fwd_layout(int64_t M, int r) {
+  FwdLayout L;
+  L.u = 0;
+  L.total = r > 0 ? align_up(size_t(M) * r * 2) : 0;
+  return L;
+}
+
+struct BwdLayout {
+  size_t u, bt, v, at, part, total;
+};
+BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N, int r) {
+  BwdLayout L{};
+  if (r == 0) return L;
+  size_t off = 0;
+  L.u = off;
+  off += align_up(size_t(M) * r * 2);
+  L.bt = off;
+  off += align_up(size_t(N) * r * 2);
+  L.v = off;
+  off += align_up(size_t(M) * r * 2);
+  L.at = off;
+  off += align_up(size_t(K) * r * 2);
+  L.part = off;
+  size_t p1 = qlora::reduce_m_workspace(M, N, r), p2 = qlora::reduce_m_workspace(M, K, r);
+  off += align_up(p1 > p2 ? p1 : p2);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "null pointer";
+    case QLORA_ERR_SHAPE: return "invalid shape";
+    case QLORA_ERR_RANK: return "invalid rank or alpha";
+    case QLORA_ERR_DTYPE: return "unsupported dtype";
+    case QLORA_ERR_WORKSPACE: return "workspace too small";
+    case QLORA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QLORA_ERR_DEVICE: return "no usable gfx950 device";
+    case QLORA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char *qlora_last_error(void) { return g_last_error.c_str(); }
+
+void qlora_time_next_gemm(void *start_event, void *stop_event) {
+  g_ev_start = static_cast<hipEvent_t>(start_event);
+  g_ev_stop = static_cast<hipEvent_t>(stop_event);
+}
+
+int qlora_nf4_sizes(int64_t n_rows, int64_t n_cols, size_t *code_bytes, int64_t *n_blocks,
+                    int64_t *n_groups) {
+  int s = check_weight_shape(n_rows, n_cols);
+  if (s != QLORA_OK) return s;
+  const int64_t n = n_rows * n_cols;
+  const int64_t nb = n / qlora::kBlock;
+  if (code_bytes) *code_bytes = static_cast<size_t>(n / 2);
+  if (n_blocks) *n_blocks = nb;
+  if (n_groups) *n_groups = (nb + qlora::kGroup - 1) / qlora::kGroup;
+  return QLORA_OK;
+}
+
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int r) {
+  if (M < 1 || K < 1 || N < 1 || K % 64 != 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (op == 0) return fwd_layout(M, r).total;
+  if (op == 1) return bwd_layout(M, K, N, r).total;
+  return 0;
+}
+
+int qlora_quantize_nf4(const void *W, int w_dtype, int64_t n_rows, int64_t n_cols, uint8_t *codes,
+                       int8_t *absmax_q, float *dq_scale, float *dq_offset, float *absmax_f32,
+                       void *stream) {
+  int s = check_weight_shape(n_rows, n_cols);
+  if (s != QLORA_OK) return s;
+  if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_DTYPE, "w_dtype %d: expected QLORA_F32 or QLORA_BF16", w_dtype);
+  if (!W || !codes || !absmax_q || !dq_scale || !dq_offset)
+    return fail(QLORA_ERR_NULL, "quantize: NULL input or output");
+  if (!aligned16(W) || !aligned16(codes))
+    return fail(QLORA_ERR_ALIGN, "quantize: W and codes must be 16-byte aligned");
+  if (!qlora::codebook().bucket_ok) return fail(QLORA_ERR_DEVICE, "internal: bucket table");
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  return launched(qlora::launch_quantize(W, w_dtype == QLORA_BF16, n_rows, n_cols, codes, absmax_q,
+                                         dq_scale, dq_offset, absmax_f32,
+                                         static_cast<hipStream_t>(stream)),
+                  "quantize");
+}
+
+int qlora_dequantize(const qlora_nf4_weight *w, void *out, int out_dtype, void *stream) {
+  int s = check_weight(w);
+  if (s != QLORA_OK) return s;
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_DTYPE, "out_dtype %d: expected QLORA_F32 or QLORA_BF16", out_dtype);
+  if (!out) return fail(QLORA_ERR_NULL, "dequantize: out is NULL");
+  if (!aligned16(out)) return fail(QLORA_ERR_ALIGN, "dequantize: out must be 16-byte aligned");
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  return launched(qlora::launch_dequantize(view(w), out, out_dtype == QLORA_BF16,
+                                           static_cast<hipStream_t>(stream)),
+                  "dequantize");
+}
+
+int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
+                     const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  int s = check_weight(w);
+  if (s == QLORA_OK) s = check_m(M);
+  if (s == QLORA_OK) s = check_rank(r, alpha);
+  if (s != QLORA_OK) return s;
+  if (!X || !Y) return fail(QLORA_ERR_NULL, "linear_fwd: X and Y are required");
+  if (r > 0 && (!A || !B)) return fail(QLORA_ERR_NULL, "linear_fwd: A and B are required when r > 0");
+  if (!aligned16(X) || !aligned16(Y) || (r > 0 && (!aligned16(A) || !aligned16(B))) ||
+      (U_saved && !aligned16(U_saved)))
+    return fail(QLORA_ERR_ALIGN, "linear_fwd: tensors must be 16-byte aligned");
+  const int64_t K = w->n_cols;
+  const FwdLayout L = fwd_layout(M, r);
+  const bool need_ws = r > 0 && !U_saved;
+  if (need_ws && (!workspace || workspace_bytes < L.total))
+    return fail(QLORA_ERR_WORKSPACE, "linear_fwd: workspace of %zu bytes needed, %zu given", L.total,
+                workspace_bytes);
+  if (need_ws && !aligned16(workspace))
+    return fail(QLORA_ERR_ALIGN, "linear_fwd: workspace must be 16-byte aligned");
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t *U = nullptr;
+  if (r > 0) {
+    U = U_saved ? U_saved : reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + L.u);
+    s = launched(qlora::launch_lora_down(X, M, K, A, r, alpha / static_cast<float>(r), U, st),
+                 "lora_down");
+    if (s != QLORA_OK) return s;
+  }
+  const qlora::WeightView wv = view(w);
+  if (M <= 16)
+    return launched(timed_launch(st, [&] { return qlora::launch_gemv_fwd(wv, X, M, U, B, r, Y, st); }),
+                    "gemv_fwd");
+  return launched(timed_launch(st, [&] { return qlora::launch_gemm_fwd(wv, X, M, U, B, r, Y, st); }),
+                  "gemm_fwd");
+}
+
+int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16_t *X, int64_t M,
+                     const uint16_t *A, const uint16_t *B, int r, float alpha,
+                     const uint16_t *U_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  int s = check_weight(w);
+  if (s == QLORA_OK) s = check_m(M);
+  if (s == QLORA_OK) s = check_rank(r, alpha);
+  if (s != QLORA_OK) return s;
+  if (!dY) return fail(QLORA_ERR_NULL, "linear_bwd: dY is required");
+  if (r > 0 && (!A || !B || !X || !dA || !dB))
+    return fail(QLORA_ERR_NULL, "linear_bwd: X, A, B, dA and dB are required when r > 0");
+  if (r == 0 && !dX) return fail(QLORA_ERR_NULL, "linear_bwd: nothing to compute (r = 0, dX NULL)");
+  const void *ptrs[] = {dY, X, A, B, U_saved, dX, dA, dB};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(QLORA_ERR_ALIGN, "linear_bwd: tensors must be 16-byte aligned");
+  const int64_t K = w->n_cols, N = w->n_rows;
+  const BwdLayout L = bwd_layout(M, K, N, r);
+  if (r > 0 && (!workspace || workspace_bytes < L.total))
+    return fail(QLORA_ERR_WORKSPACE, "linear_bwd: workspace of %zu bytes needed, %zu given", L.total,
+                workspace_bytes);
+  if (r > 0 && !aligned16(workspace))
+    return fail(QLORA_ERR_ALIGN, "linear_bwd: workspace must be 16-byte aligned");
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const qlora::WeightView wv = view(w);
+  char *ws = static_cast<char *>(workspace);
+  const uint16_t *V = nullptr, *At = nullptr;
+  if (r > 0) {
+    const float scale = alpha / static_cast<float>(r);
+    const uint16_t *U = U_saved;
+    if (!U) {
+      uint16_t *Uw = reinterpret_cast<uint16_t *>(ws + L.u);
+      s = launched(qlora::launch_lora_down(X, M, K, A, r, scale, Uw, st), "lora_down(U)");
+      if (s != QLORA_OK) return s;
+      U = Uw;
+    }
+    uint16_t *Bt = reinterpret_cast<uint16_t *>(ws + L.bt);
+    uint16_t *Vw = reinterpret_cast<uint16_t *>(ws + L.v);
+    uint16_t *Atw = reinterpret_cast<uint16_t *>(ws + L.at);
+    float *part = reinterpret_cast<float *>(ws + L.part);
+    s = launched(qlora::launch_transpose_bf16(B, N, r, Bt, st), "transpose(B)");
+    if (s == QLORA_OK)
+      s = launched(qlora::launch_lora_down(dY, M, N, Bt, r, scale, Vw, st), "lora_down(V)");
+    if (s == QLORA_OK)
+      s = launched(qlora::launch_reduce_m(dY, M, N, U, r, part, dB, false, st), "reduce(dB)");
+    if (s == QLORA_OK)
+      s = launched(qlora::launch_reduce_m(X, M, K, Vw, r, part, dA, true, st), "reduce(dA)");
+    if (s == QLORA_OK && dX)
+      s = launched(qlora::launch_transpose_bf16(A, r, K, Atw, st), "transpose(A)");
+    if (s != QLORA_OK) return s;
+    V = Vw;
+    At = Atw;
+  }
+  if (dX)
+    return launched(timed_launch(st, [&] { return qlora::launch_gemm_dx(wv, dY, M, V, At, r, dX, st); }),
+                    "gemm_dx");
+  return QLORA_OK;
+}
+
+}  // extern "C"

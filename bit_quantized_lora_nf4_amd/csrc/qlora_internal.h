@@ -1,0 +1,71 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qlora {
+
+constexpr int kBlock = 64;     // weights per first-level block
+constexpr int kGroup = 256;    // block constants per double-quantization group
+constexpr int kBuckets = 129;  // quantizer bucket table entries (x in [-1, 1])
+
+struct Codebook {
+  float q[16];                  // NF4 levels, ascending
+  float thr[15];                // decision thresholds
+  float bucket_thr[kBuckets];   // the threshold inside each bucket window (2.0 if none)
+  int bucket_base[kBuckets];    // thresholds below each bucket window
+  bool bucket_ok;               // every window holds at most one threshold
+};
+
+const Codebook &codebook();
+
+// Kernel arguments passed by value (kernarg segment).
+struct QuantTable {
+  float thr[kBuckets];
+  int base[kBuckets];
+};
+struct LevelTable {
+  float q[16];
+};
+
+// Device view of a quantized weight.
+struct WeightView {
+  const uint8_t *codes;
+  const int8_t *absmax_q;
+  const float *dq_scale;
+  const float *dq_offset;
+  int64_t n_rows;  // N = d_out
+  int64_t n_cols;  // K = d_in
+};
+
+// ---- launchers (each returns the HIP error of its launches) -----------------
+hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n_rows, int64_t n_cols,
+                           uint8_t *codes, int8_t *absmax_q, float *dq_scale, float *dq_offset,
+                           float *absmax_f32, hipStream_t stream);
+hipError_t launch_dequantize(const WeightView &w, void *out, bool out_bf16, hipStream_t stream);
+
+// OUT[M, r] (pitch r, bf16) = bf16(scale * IN[M, Kc] . WT[r, Kc]^T);  IN pitch Kc.
+hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, const uint16_t *WT, int r,
+                            float scale, uint16_t *OUT, hipStream_t stream);
+// OUT[C, R] = IN[R, C]^T for bf16 matrices (both dense row-major).
+hipError_t launch_transpose_bf16(const uint16_t *IN, int64_t R, int64_t C, uint16_t *OUT,
+                                 hipStream_t stream);
+// P[s][No][r] fp32 partials of sum over m in split s of IN[m][no] * S[m][j]; then
+// OUT = bf16(sum_s P) written as [No, r] (trans_out = false) or [r, No] (true).
+size_t reduce_m_workspace(int64_t M, int64_t No, int r);
+hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, const uint16_t *S, int r,
+                           float *partials, uint16_t *OUT, bool trans_out, hipStream_t stream);
+
+// Y[M, N] = bf16(X . W'^T + U . Bl^T)  (U [M, r] pitch r, Bl [N, r]); r may be 0.
+hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
+                           const uint16_t *Bl, int r, uint16_t *Y, hipStream_t stream);
+// Small-M forward (M <= 16): same contract as launch_gemm_fwd.
+hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
+                           const uint16_t *Bl, int r, uint16_t *Y, hipStream_t stream);
+// dX[M, K] = bf16(dY . W' + V . At^T)  (V [M, r], At [K, r]); r may be 0.
+hipError_t launch_gemm_dx(const WeightView &w, const uint16_t *dY, int64_t M, const uint16_t *V,
+                          const uint16_t *At, int r, uint16_t *dX, hipStream_t stream);
+
+}  // namespace qlora

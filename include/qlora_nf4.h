@@ -1,0 +1,154 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) QLoRA linear library.
+ *
+ * The library computes the frozen-base QLoRA linear layer
+ *
+ *     Y = X . W'^T + (alpha / r) . (X . A^T) . B^T
+ *
+ * where W' is the bf16 decode of a weight stored as blockwise NF4 codes with
+ * 8-bit double-quantized block constants.  Pages cited below:
+ *   [QLoRA note]  "1. 啥是 QLoRA" (p19e99.github.io/posts/note/qlora)
+ *   [Ch. 11.3]    "11.3 QLoRA：单卡微调大模型" (gheillcoat.github.io)
+ *   [Paper note]  "QLoRA — 让 65B 大模型微调落到单张 48GB GPU 上" (awesome.papernotes.org)
+ *   [Digest]      "QLoRA: 高效微调量化大语言模型" (aipaper.cc)
+ *   [Repro]       "LoRA / QLoRA低秩更新、量化和显存预算" (mhpn.cn)
+ *
+ * Conventions (all entry points):
+ *   - Shapes follow [Repro] "LoRA 的公式和张量形状": the weight is W[N = d_out,
+ *     K = d_in] row-major (K contiguous); A is [r, K], B is [N, r], X is
+ *     [M, K], Y and dY are [M, N].  All matrices are dense row-major.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte
+ *     aligned.  The library never allocates or frees memory and keeps no
+ *     device state; scratch memory comes from the caller's workspace.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Each call checks
+ *     its arguments on the host, then enqueues its kernels asynchronously on
+ *     `stream` and returns.  Kernel faults surface at the caller's next
+ *     synchronisation.  Host code never synchronises.
+ *   - Return value: QLORA_OK (0) or a negative qlora_status; on error nothing
+ *     was enqueued (except QLORA_ERR_LAUNCH, where an earlier kernel of the
+ *     same call may already be queued).  qlora_last_error() gives a
+ *     thread-local message for the last failing call of this thread.
+ *   - Outputs must not alias inputs.  Inputs must be finite.
+ *   - K (= n_cols) must be a multiple of 64; M >= 1; 0 <= r <= 256 (r = 0
+ *     means no adapter: A, B may be NULL).
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = -1,      /* a required pointer is NULL                        */
+  QLORA_ERR_SHAPE = -2,     /* M < 1, n_rows < 1, n_cols % 64 != 0, size overflow */
+  QLORA_ERR_RANK = -3,      /* r outside [0, 256] or alpha not finite             */
+  QLORA_ERR_DTYPE = -4,     /* unsupported dtype enum                             */
+  QLORA_ERR_WORKSPACE = -5, /* workspace smaller than qlora_workspace_bytes()     */
+  QLORA_ERR_ALIGN = -6,     /* a pointer is not 16-byte aligned                   */
+  QLORA_ERR_DEVICE = -7,    /* no usable gfx950 device                            */
+  QLORA_ERR_LAUNCH = -8     /* the HIP runtime refused a kernel launch            */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+enum { QLORA_BLOCK = 64, QLORA_GROUP = 256, QLORA_MAX_RANK = 256 };
+
+/* A quantized weight W[n_rows = d_out, n_cols = d_in] ([Digest] "数学公式与关键细节"
+ * items 1-2; [Ch. 11.3] "核心创新二").  Block b holds the 64 consecutive elements
+ * [64 b, 64 b + 64) of the row-major weight; group g holds blocks [256 g, 256 g + 256).
+ *   codes      [n_rows * n_cols / 2]   byte i = code(2i) | code(2i+1) << 4
+ *   absmax_q   [n_blocks]              int8 double-quantized block constant
+ *   dq_scale   [n_groups]              fp32 group scale s
+ *   dq_offset  [n_groups]              fp32 group offset o
+ * Block constant decode: c' = fma(absmax_q[b], s[g], o[g]) (one rounding).
+ * Weight decode:          W'  = bf16_rne(q[code] * c')   (fp32 product, RN). */
+typedef struct {
+  const uint8_t *codes;
+  const int8_t *absmax_q;
+  const float *dq_scale;
+  const float *dq_offset;
+  int64_t n_rows;
+  int64_t n_cols;
+} qlora_nf4_weight;
+
+/* ---- host-only helpers (no GPU needed) ------------------------------------ */
+
+/* Storage sizes of an n_rows x n_cols weight.  Any output pointer may be NULL.
+ * Returns QLORA_ERR_SHAPE unless n_rows >= 1 and n_cols is a positive multiple of 64. */
+int qlora_nf4_sizes(int64_t n_rows, int64_t n_cols, size_t *code_bytes, int64_t *n_blocks,
+                    int64_t *n_groups);
+
+/* The NF4 codebook q[0..15] (ascending; q[0] = -1, q[7] = 0, q[15] = +1) and the 15
+ * decision thresholds T[j] = largest fp32 <= (q[j] + q[j+1]) / 2, computed by the
+ * library in double precision from N(0,1) quantiles ([QLoRA note] "2. NF4";
+ * [Paper note] "关键设计 1", quantile-midpoint equation; [Digest] item 1, "特点":
+ * exact zero through asymmetric halves).  Either pointer may be NULL. */
+void qlora_nf4_codebook(float q[16], float thresholds[15]);
+
+/* Bytes of caller workspace needed by qlora_linear_fwd (op = 0) or qlora_linear_bwd
+ * (op = 1) for the given shapes; 0 for invalid arguments. */
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int r);
+
+const char *qlora_status_string(int status);
+const char *qlora_last_error(void);
+
+/* Timing hook for measurement tools.  Arms the calling thread so that its next
+ * fused NF4 GEMM launch (the main kernel of qlora_linear_fwd or of the dX part of
+ * qlora_linear_bwd) is bracketed by hipEventRecord(start) and hipEventRecord(stop)
+ * on that call's stream; the hook then disarms itself.  The events are hipEvent_t
+ * handles owned by the caller; passing NULL disarms.  No effect on results. */
+void qlora_time_next_gemm(void *start_event, void *stop_event);
+
+/* ---- device entry points ---------------------------------------------------- */
+
+/* Blockwise NF4 quantization plus double quantization of the block constants
+ * ([QLoRA note] "2. NF4", "3. 双重量化"; [Digest] "数学公式与关键细节" items 1-2).
+ *   W         [n_rows, n_cols] fp32 (w_dtype = QLORA_F32) or bf16 (QLORA_BF16)
+ *   per block: c = max |w|; x = RN(w * RN(1/c)); code = #{j : x > T[j]}
+ *              (ties go to the lower code; a block with c < 2^-126 gets code 7);
+ *   per group: o = RN(min c + max c) * 0.5; h = max |RN(c - o)|; s = RN(h / 127);
+ *              absmax_q = clamp(rint_even(RN(RN(c - o) / s)), -127, 127) (0 if h = 0).
+ * Outputs are the four arrays of qlora_nf4_weight; absmax_f32 (nullable, [n_blocks])
+ * receives the first-level constants c. */
+int qlora_quantize_nf4(const void *W, int w_dtype, int64_t n_rows, int64_t n_cols, uint8_t *codes,
+                       int8_t *absmax_q, float *dq_scale, float *dq_offset, float *absmax_f32,
+                       void *stream);
+
+/* doubleDequant ([Digest] item 3, doubleDequant equation): out[n_rows, n_cols] =
+ * RN(q[code] * c') as fp32 (out_dtype = QLORA_F32) or its bf16 rounding (QLORA_BF16). */
+int qlora_dequantize(const qlora_nf4_weight *w, void *out, int out_dtype, void *stream);
+
+/* Forward ([Paper note] "关键设计 3" equation and qlora_linear listing; [Digest]
+ * "方法步骤与流程" step 3; [Repro] "LoRA 的公式和张量形状", scaling alpha / r):
+ *   U_s = bf16((alpha / r) . X . A^T)                 [M, r]
+ *   Y   = bf16(X . W'^T + U_s . B^T)                  [M, N], fp32 accumulation
+ * X bf16 [M, K]; A bf16 [r, K]; B bf16 [N, r]; Y bf16 [M, N].
+ * U_saved (nullable) receives U_s for the backward.  The decode of W' happens inside
+ * the GEMM; no bf16 copy of the weight is written. */
+int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
+                     const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward ([Digest] "方法步骤与流程" step 4; [QLoRA note] "5. QLoRA 训练方式本身":
+ * gradients flow through W' into the adapter only; no gradient for W):
+ *   V  = bf16((alpha / r) . dY . B)                   [M, r]
+ *   dX = bf16(dY . W' + V . A)                        [M, K]  (skipped if dX == NULL)
+ *   dB = bf16(dY^T . U_s)                             [N, r]
+ *   dA = bf16(V^T . X)                                [r, K]
+ * U_saved is the forward's U_s; if NULL it is recomputed from X and A.
+ * dY bf16 [M, N]; X bf16 [M, K] (needed for dA, and for U_s when U_saved is NULL). */
+int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16_t *X, int64_t M,
+                     const uint16_t *A, const uint16_t *B, int r, float alpha,
+                     const uint16_t *U_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLORA_NF4_H */

@@ -1,0 +1,235 @@
+"""GPU parity of the QLoRA linear forward and backward against the float64 oracle.
+
+Tolerance (stated for the forward, dX, dA and dB): max|G - R| / max|R| <= 2e-2 with
+R the oracle in float64 on the same bf16 operands; the measured error is printed.
+Exact checks: Y(B = 0) == Y(r = 0) bitwise; X = I gives Y = W'^T bitwise (one
+nonzero term per output); B = 0 gives dA == 0; repeated runs are bitwise equal.
+Full-size workloads compare sampled rows (and the whole of dA and dB).
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import linear, nf4
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_lora_nf4_amd as q
+    return q
+
+
+def _oracle_w(d):
+    return nf4.dequantize_bf16(nf4.quantize_nf4(gc.weight_f32(d))).astype(np.float64)
+
+
+def _dev(d, r):
+    X = gc.dev_bf16(d["X"])
+    A = gc.dev_bf16(d["A"]) if r else None
+    B = gc.dev_bf16(d["B"]) if r else None
+    return X, A, B
+
+
+def _check(name, G, R, tol=TOL):
+    e = gc.rel_err(G, R)
+    print(f"  {name}: rel err {e:.3e}", flush=True)
+    assert e <= tol, f"{name}: {e}"
+    return e
+
+
+SMALL = [  # (M, K, N, r)
+    (77, 320, 200, 8),
+    (300, 1088, 520, 16),
+    (257, 256, 257, 64),
+    (33, 64, 1, 4),
+    (600, 640, 96, 0),
+    (300, 128, 300, 24),
+    (5, 192, 77, 3),       # M <= 16: the GEMV path, odd rank
+    (16, 4096, 300, 16),
+    (1, 1024, 1000, 8),
+    (17, 512, 260, 32),    # just above the GEMV bound
+]
+
+
+@pytest.mark.parametrize("M,K,N,r", SMALL)
+def test_forward_backward_small(lib, M, K, N, r):
+    import torch
+    print(f"linear case M={M} K={K} N={N} r={r}", flush=True)
+    alpha = 16.0
+    d = synth.case(M, K, N, r, seed=M * 7 + N)
+    qw = lib.quantize(gc.dev_weight(d))
+    X, A, B = _dev(d, r)
+    Y, U = lib.linear_fwd(qw, X, A, B, alpha)
+    dYt = gc.dev_bf16(d["dY"])
+    dX, dA, dB = lib.linear_bwd(qw, dYt, X, A, B, alpha, U)
+    torch.cuda.synchronize()
+    Wd = _oracle_w(d)
+    Xf, Af, Bf, dYf = (gc.f64(d[k]) for k in ("X", "A", "B", "dY"))
+    _check("Y", gc.host_f32_from_bf16(Y), linear.forward(Xf, Wd, Af, Bf, alpha, r))
+    rdX, rdA, rdB = linear.backward(dYf, Xf, Wd, Af, Bf, alpha, r)
+    _check("dX", gc.host_f32_from_bf16(dX), rdX)
+    if r:
+        _check("U", gc.host_f32_from_bf16(U), linear.lora_down(Xf, Af, alpha, r))
+        _check("dA", gc.host_f32_from_bf16(dA), rdA)
+        _check("dB", gc.host_f32_from_bf16(dB), rdB)
+
+
+@pytest.mark.parametrize("M", [40, 3])
+def test_zero_B_equals_base_bitwise(lib, M):
+    import torch
+    K, N, r, alpha = 512, 384, 16, 16.0
+    d = synth.case(M, K, N, r, seed=99)
+    qw = lib.quantize(gc.dev_weight(d))
+    X, A, _ = _dev(d, r)
+    B0 = torch.zeros((N, r), dtype=torch.bfloat16, device="cuda")
+    Y0, _ = lib.linear_fwd(qw, X, A, B0, alpha)
+    Yb, _ = lib.linear_fwd(qw, X)
+    dYt = gc.dev_bf16(d["dY"])
+    dX0, dA0, dB0 = lib.linear_bwd(qw, dYt, X, A, B0, alpha)
+    dXb, _, _ = lib.linear_bwd(qw, dYt, X)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0.view(torch.int16), Yb.view(torch.int16))
+    assert torch.equal(dX0.view(torch.int16), dXb.view(torch.int16))
+    assert torch.count_nonzero(dA0.float()) == 0
+    assert torch.count_nonzero(dB0.float()) > 0
+
+
+@pytest.mark.parametrize("M,K,N", [(256, 256, 200), (320, 320, 77)])
+def test_identity_input_gives_weight_bitwise(lib, M, K, N):
+    """X = I (M = K): every output is a single product 1 * W'[n, k], so Y = W'^T exactly."""
+    import torch
+    d = synth.case(1, K, N, 0, seed=K, parts=("W",))
+    qw = lib.quantize(gc.dev_weight(d))
+    X = torch.eye(K, dtype=torch.bfloat16, device="cuda")
+    Y, _ = lib.linear_fwd(qw, X)
+    torch.cuda.synchronize()
+    ref = nf4.dequantize_bf16_bits(nf4.quantize_nf4(gc.weight_f32(d))).T
+    assert np.array_equal(gc.host_bits(Y), ref)
+    # the transposed decode of the backward: dY = I (M = N) gives dX = W' exactly
+    dY = torch.eye(N, dtype=torch.bfloat16, device="cuda")
+    dX, _, _ = lib.linear_bwd(qw, dY, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(gc.host_bits(dX), ref.T)
+
+
+def test_deterministic(lib):
+    import torch
+    M, K, N, r = 700, 1024, 640, 64
+    d = synth.case(M, K, N, r, seed=3)
+    qw = lib.quantize(gc.dev_weight(d))
+    X, A, B = _dev(d, r)
+    dYt = gc.dev_bf16(d["dY"])
+    outs = []
+    for _ in range(2):
+        Y, U = lib.linear_fwd(qw, X, A, B, 16.0)
+        g = lib.linear_bwd(qw, dYt, X, A, B, 16.0, U)
+        outs.append([Y.clone(), *[t.clone() for t in g]])
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("with_B", [False, True])
+def test_workload1_full(lib, with_B):
+    """1024 -> 1024, M = 64, r = 8, alpha = 16, fp32 weight; B = 0 then B ~ N(0, 0.01^2)."""
+    import torch
+    wl = synth.WORKLOADS[1]
+    d = synth.workload_linear(1, 0)
+    if not with_B:
+        d["B"] = np.zeros_like(d["B"])
+    qw = lib.quantize(gc.dev_weight(d))
+    X, A, B = _dev(d, wl.r)
+    Y, U = lib.linear_fwd(qw, X, A, B, wl.alpha)
+    dX, dA, dB = lib.linear_bwd(qw, gc.dev_bf16(d["dY"]), X, A, B, wl.alpha, U)
+    torch.cuda.synchronize()
+    Wd = _oracle_w(d)
+    Xf, Af, Bf, dYf = (gc.f64(d[k]) for k in ("X", "A", "B", "dY"))
+    Yr = linear.forward(Xf, Wd, Af, Bf, wl.alpha, wl.r)
+    if not with_B:
+        assert np.array_equal(Yr, linear.base_forward(Xf, Wd))
+    _check("Y", gc.host_f32_from_bf16(Y), Yr)
+    rdX, rdA, rdB = linear.backward(dYf, Xf, Wd, Af, Bf, wl.alpha, wl.r)
+    _check("dX", gc.host_f32_from_bf16(dX), rdX)
+    _check("dA", gc.host_f32_from_bf16(dA), rdA)
+    _check("dB", gc.host_f32_from_bf16(dB), rdB)
+
+
+def _full_linear(lib, number, i, M=None, rows=16, bwd=True):
+    import torch
+    wl = synth.WORKLOADS[number]
+    d = synth.workload_linear(number, i, M=M)
+    M = d["X"].shape[0]
+    K, N = wl.linears[i]
+    print(f"workload {number} linear {i}: M={M} K={K} N={N} r={wl.r}", flush=True)
+    qw = lib.quantize(gc.dev_weight(d))
+    X, A, B = _dev(d, wl.r)
+    Y, U = lib.linear_fwd(qw, X, A, B, wl.alpha)
+    if bwd:
+        dX, dA, dB = lib.linear_bwd(qw, gc.dev_bf16(d["dY"]), X, A, B, wl.alpha, U)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(number * 10 + i)
+    sel = np.sort(rng.choice(M, min(rows, M), replace=False))
+    Wd = _oracle_w(d)
+    Xf, Af, Bf = (gc.f64(d[k]) for k in ("X", "A", "B"))
+    Yh = gc.host_f32_from_bf16(Y)
+    _check("Y rows", Yh[sel], linear.forward(Xf[sel], Wd, Af, Bf, wl.alpha, wl.r))
+    if not bwd:
+        return
+    dYf = gc.f64(d["dY"])
+    scale = wl.alpha / wl.r
+    V = scale * (dYf @ Bf)
+    rdX = dYf[sel] @ Wd + V[sel] @ Af
+    _check("dX rows", gc.host_f32_from_bf16(dX)[sel], rdX)
+    _check("dA", gc.host_f32_from_bf16(dA), V.T @ Xf)
+    _check("dB", gc.host_f32_from_bf16(dB), scale * (dYf.T @ (Xf @ Af.T)))
+
+
+@pytest.mark.parametrize("i", [0, 1, 2])
+def test_workload2_full(lib, i):
+    _full_linear(lib, 2, i)
+
+
+@pytest.mark.parametrize("i", [0, 1])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_workload3_full(lib, i, M):
+    import torch
+    wl = synth.WORKLOADS[3]
+    d = synth.workload_linear(3, i, M=M, parts=("W", "X", "A", "B"))
+    K, N = wl.linears[i]
+    print(f"workload 3 linear {i}: M={M} K={K} N={N}", flush=True)
+    qw = lib.quantize(gc.dev_weight(d))
+    X, A, B = _dev(d, wl.r)
+    Y, _ = lib.linear_fwd(qw, X, A, B, wl.alpha)
+    torch.cuda.synchronize()
+    Xf, Af, Bf = (gc.f64(d[k]) for k in ("X", "A", "B"))
+    _check("Y", gc.host_f32_from_bf16(Y), linear.forward(Xf, _oracle_w(d), Af, Bf, wl.alpha, wl.r))
+
+
+def test_workload4_q_proj(lib):
+    _full_linear(lib, 4, 0, rows=8)
+
+
+def test_workload5_forward_sampled_columns(lib):
+    """Stress weight 8192 x 22016 (K = 22016 -> N = 8192), M = 512, r = 32: sampled
+    output columns against the oracle decode of just those weight rows."""
+    import torch
+    wl = synth.WORKLOADS[5]
+    d = synth.workload_linear(5, 0, parts=("W", "X", "A", "B"))
+    qw = lib.quantize(gc.dev_weight(d))
+    X, A, B = _dev(d, wl.r)
+    Y, _ = lib.linear_fwd(qw, X, A, B, wl.alpha)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(55)
+    cols = np.sort(rng.choice(8192, 24, replace=False))
+    Wrows = gc.oracle_rows(gc.weight_f32(d), cols)
+    Xf, Af, Bf = (gc.f64(d[k]) for k in ("X", "A", "B"))
+    ref = Xf @ Wrows.T + (wl.alpha / wl.r) * (Xf @ Af.T) @ Bf[cols].T
+    _check("Y cols", gc.host_f32_from_bf16(Y)[:, cols], ref)
