@@ -88,6 +88,7 @@ def setup_workload2(torch, q, synth, gc):
         e["dA"] = torch.empty((wl.r, K), dtype=torch.bfloat16, device="cuda")
         e["dB"] = torch.empty((N, wl.r), dtype=torch.bfloat16, device="cuda")
         e["ws"] = q.workspace(1, M, K, N, wl.r, "cuda")
+        e["wsf"] = q.workspace(0, M, K, N, wl.r, "cuda")
         L.append(e)
     return wl, M, L
 
@@ -98,7 +99,7 @@ def run_step(q, wl, L, ev=None, record=None):
             a, b = ev.pair()
             q._lib.qlora_time_next_gemm(a, b)
             record.append((a, b, "fwd", e))
-        q.linear_fwd(e["qw"], e["X"], e["A"], e["B"], wl.alpha, Y=e["Y"], U=e["U"])
+        q.linear_fwd(e["qw"], e["X"], e["A"], e["B"], wl.alpha, Y=e["Y"], U=e["U"], ws=e["wsf"])
         if ev is not None:
             a, b = ev.pair()
             q._lib.qlora_time_next_gemm(a, b)
@@ -144,13 +145,14 @@ def measure_m1(torch, q, synth, gc, ev, min_bytes=600 << 20, calls=200):
         X, A, B = gc.dev_bf16(d["X"]), gc.dev_bf16(d["A"]), gc.dev_bf16(d["B"])
         Y = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
         U = torch.empty((1, wl.r), dtype=torch.bfloat16, device="cuda")
+        wsf = q.workspace(0, 1, K, N, wl.r, "cuda")
         for c in range(copies):  # warm up, and make sure every copy works eagerly
-            q.linear_fwd(qws[c], X, A, B, wl.alpha, Y=Y, U=U)
+            q.linear_fwd(qws[c], X, A, B, wl.alpha, Y=Y, U=U, ws=wsf)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for c in range(calls):
-                q.linear_fwd(qws[c % copies], X, A, B, wl.alpha, Y=Y, U=U)
+                q.linear_fwd(qws[c % copies], X, A, B, wl.alpha, Y=Y, U=U, ws=wsf)
         g.replay()
         torch.cuda.synchronize()
         s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -166,7 +168,7 @@ def measure_m1(torch, q, synth, gc, ev, min_bytes=600 << 20, calls=200):
         for c in range(copies):
             a, b = ev.pair()
             q._lib.qlora_time_next_gemm(a, b)
-            q.linear_fwd(qws[c], X, A, B, wl.alpha, Y=Y, U=U)
+            q.linear_fwd(qws[c], X, A, B, wl.alpha, Y=Y, U=U, ws=wsf)
         torch.cuda.synchronize()
         kms = sum(ev.ms(a, b) for a, b in ev.pool[-copies:]) / copies
         nb = stream_bytes(1, K, N, wl.r)
@@ -185,33 +187,35 @@ def measure_m1(torch, q, synth, gc, ev, min_bytes=600 << 20, calls=200):
     return out
 
 
-def cpu_baseline(synth, sample_m=1024):
-    """The oracle (float64 numpy) on a bounded sample of the workload: the first
-    linear (4096 -> 4096) with the first `sample_m` tokens: decode of W' from the
-    stored format, forward and backward."""
+def cpu_baseline(synth, sample_m=4096):
+    """The oracle (float64 numpy) on a bounded sample of the workload: each of the three
+    linears with the first `sample_m` tokens: decode of W' from the stored format,
+    forward and backward.  The oracle's own quantization of W is not timed."""
     import numpy as np
     from oracle import linear, nf4
     wl = synth.WORKLOADS[2]
-    d = synth.workload_linear(2, 0)
-    K, N = wl.linears[0]
-    qw = nf4.quantize_nf4(synth.bf16_bits_to_f32(d["W"]))
-    f = lambda k: synth.bf16_bits_to_f32(d[k]).astype(np.float64)  # noqa: E731
-    X, A, B, dY = f("X")[:sample_m], f("A"), f("B"), f("dY")[:sample_m]
-    t0 = time.perf_counter()
-    Wd = nf4.dequantize_bf16(qw)
-    linear.forward(X, Wd, A, B, wl.alpha, wl.r)
-    linear.backward(dY, X, Wd, A, B, wl.alpha, wl.r)
-    dt = time.perf_counter() - t0
+    dt = fl = 0.0
+    for i, (K, N) in enumerate(wl.linears):
+        d = synth.workload_linear(2, i)
+        qw = nf4.quantize_nf4(synth.bf16_bits_to_f32(d["W"]))
+        f = lambda k: synth.bf16_bits_to_f32(d[k]).astype(np.float64)  # noqa: E731
+        X, A, B, dY = f("X")[:sample_m], f("A"), f("B"), f("dY")[:sample_m]
+        del d
+        t0 = time.perf_counter()
+        Wd = nf4.dequantize_bf16(qw)
+        linear.forward(X, Wd, A, B, wl.alpha, wl.r)
+        linear.backward(dY, X, Wd, A, B, wl.alpha, wl.r)
+        dt += time.perf_counter() - t0
+        fl += linear_flops(sample_m, K, N, wl.r)
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count()
-    fl = linear_flops(sample_m, K, N, wl.r)
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"linear 4096->4096 of the workload, first {sample_m} of 4096 tokens: "
-                      "decode W' + forward + backward in float64 numpy"}
+            "sample": f"the three linears of the workload with the first {sample_m} of 4096 tokens: "
+                      "decode W' + forward + backward in float64 numpy (quantization untimed)"}
 
 
 def main():

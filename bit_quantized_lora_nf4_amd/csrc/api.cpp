@@ -114,12 +114,18 @@ qlora::WeightView view(const qlora_nf4_weight *w) {
 
 // ---- workspace layouts ------------------------------------------------------
 struct FwdLayout {
-  size_t u = 0, total = 0;
+  size_t u = 0, part = 0, total = 0;
 };
-FwdLayout fwd_layout(int64_t M, int r) {
+// U_s (when the caller does not keep it) then the fp32 partial sums of lora_down.
+FwdLayout fwd_layout(int64_t M, int64_t K, int r, bool need_u) {
   FwdLayout L;
-  L.u = 0;
-  L.total = r > 0 ? align_up(size_t(M) * r * 2) : 0;
+  if (r == 0) return L;
+  size_t off = 0;
+  L.u = off;
+  if (need_u) off += align_up(size_t(M) * r * 2);
+  L.part = off;
+  off += align_up(qlora::lora_down_workspace(M, K, r));
+  L.total = off;
   return L;
 }
 
@@ -139,8 +145,11 @@ BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N, int r) {
   L.at = off;
   off += align_up(size_t(K) * r * 2);
   L.part = off;
-  size_t p1 = qlora::reduce_m_workspace(M, N, r), p2 = qlora::reduce_m_workspace(M, K, r);
-  off += align_up(p1 > p2 ? p1 : p2);
+  size_t p = qlora::reduce_m_workspace(M, N, r);
+  const size_t others[] = {qlora::reduce_m_workspace(M, K, r), qlora::lora_down_workspace(M, K, r),
+                           qlora::lora_down_workspace(M, N, r)};
+  for (size_t o : others) p = o > p ? o : p;
+  off += align_up(p);
   L.total = off;
   return L;
 }
@@ -185,7 +194,7 @@ int qlora_nf4_sizes(int64_t n_rows, int64_t n_cols, size_t *code_bytes, int64_t 
 
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int r) {
   if (M < 1 || K < 1 || N < 1 || K % 64 != 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
-  if (op == 0) return fwd_layout(M, r).total;
+  if (op == 0) return fwd_layout(M, K, r, true).total;
   if (op == 1) return bwd_layout(M, K, N, r).total;
   return 0;
 }
@@ -237,8 +246,8 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, co
       (U_saved && !aligned16(U_saved)))
     return fail(QLORA_ERR_ALIGN, "linear_fwd: tensors must be 16-byte aligned");
   const int64_t K = w->n_cols;
-  const FwdLayout L = fwd_layout(M, r);
-  const bool need_ws = r > 0 && !U_saved;
+  const FwdLayout L = fwd_layout(M, K, r, !U_saved);
+  const bool need_ws = L.total > 0;
   if (need_ws && (!workspace || workspace_bytes < L.total))
     return fail(QLORA_ERR_WORKSPACE, "linear_fwd: workspace of %zu bytes needed, %zu given", L.total,
                 workspace_bytes);
@@ -249,8 +258,10 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint16_t *U = nullptr;
   if (r > 0) {
-    U = U_saved ? U_saved : reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + L.u);
-    s = launched(qlora::launch_lora_down(X, M, K, A, r, alpha / static_cast<float>(r), U, st),
+    char *ws = static_cast<char *>(workspace);
+    U = U_saved ? U_saved : reinterpret_cast<uint16_t *>(ws + L.u);
+    s = launched(qlora::launch_lora_down(X, M, K, A, r, alpha / static_cast<float>(r), U,
+                                         reinterpret_cast<float *>(ws + L.part), st),
                  "lora_down");
     if (s != QLORA_OK) return s;
   }
@@ -295,7 +306,9 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16
     const uint16_t *U = U_saved;
     if (!U) {
       uint16_t *Uw = reinterpret_cast<uint16_t *>(ws + L.u);
-      s = launched(qlora::launch_lora_down(X, M, K, A, r, scale, Uw, st), "lora_down(U)");
+      s = launched(qlora::launch_lora_down(X, M, K, A, r, scale, Uw,
+                                           reinterpret_cast<float *>(ws + L.part), st),
+                   "lora_down(U)");
       if (s != QLORA_OK) return s;
       U = Uw;
     }
@@ -305,7 +318,7 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16
     float *part = reinterpret_cast<float *>(ws + L.part);
     s = launched(qlora::launch_transpose_bf16(B, N, r, Bt, st), "transpose(B)");
     if (s == QLORA_OK)
-      s = launched(qlora::launch_lora_down(dY, M, N, Bt, r, scale, Vw, st), "lora_down(V)");
+      s = launched(qlora::launch_lora_down(dY, M, N, Bt, r, scale, Vw, part, st), "lora_down(V)");
     if (s == QLORA_OK)
       s = launched(qlora::launch_reduce_m(dY, M, N, U, r, part, dB, false, st), "reduce(dB)");
     if (s == QLORA_OK)

@@ -7,9 +7,15 @@
 // ([Paper note] "关键设计 3" equation and listing; [Repro] "LoRA 的公式和张量形状":
 // scaling = lora_alpha / r; [Digest] "方法步骤与流程" step 4: only the adapter
 // receives gradients.)  All products run on the 32x32x16 bf16 MFMA with fp32
-// accumulation.  The reductions over M are split over workgroups; each writes fp32
-// partial sums to caller workspace and a second pass adds the partials in a fixed
-// order, so results are bitwise reproducible (no floating-point atomics).
+// accumulation.  These kernels are HBM-bound (they stream X or dY once), so they
+// are split over many workgroups: each writes fp32 partial sums to caller
+// workspace and a finalize pass adds the partials in a fixed order and rounds to
+// bf16 once, so results are bitwise reproducible (no floating-point atomics).
+//
+// Fast paths need 16-byte aligned rows (row length % 8 == 0, r % 8 == 0) and
+// tensors below 4 GiB (32-bit buffer offsets; out-of-range buffer reads return
+// zero, which handles every tile edge without branches).  Other shapes take the
+// generic kernels at the end of this file.
 
 #include "device_common.h"
 #include "qlora_internal.h"
@@ -18,13 +24,248 @@ namespace qlora {
 namespace {
 
 constexpr int NT = 256;
+constexpr uint64_t k4G = 0xFFFFFFF0ull;
 
+// ---------------------------------------------------------------------------------
+// lora_down: P[ks][m][j] = sum_{k in split ks} IN[m][k] WT[j][k]
+// Workgroup: 64 rows of IN x all RT*32 >= r columns, one K-split; the four waves
+// take consecutive quarters of the split and are summed in LDS (fixed order).
+// MFMA roles: A = WT fragment (rows j), B = IN fragment (columns m), so each lane
+// ends with 4 consecutive j of one m: 16-byte partial stores.
+template <int RT>
+__global__ __launch_bounds__(NT) void lora_down_partial_kernel(
+    const uint16_t *__restrict__ IN, int M, int Kc, const uint16_t *__restrict__ WT, int r, int KR,
+    float *__restrict__ P) {
+  __shared__ f32x16_t red[3][2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * 64;
+  const int ks = blockIdx.y;
+  const int kq = KR / 4;
+  const int wbeg = ks * KR + wave * kq;
+  const int wend = min(Kc, wbeg + kq);
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(IN, static_cast<uint32_t>(uint64_t(M) * Kc * 2));
+  const __amdgpu_buffer_rsrc_t rwt = make_rsrc(WT, static_cast<uint32_t>(uint64_t(r) * Kc * 2));
+  const int kl = (lane >> 5) * 8;
+
+  f32x16_t acc[2][RT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.0f;
+
+  uint32_t in_row[2], wt_row[RT];
+  bool in_ok[2], wt_ok[RT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + i * 32 + (lane & 31);
+    in_ok[i] = row < M;
+    in_row[i] = static_cast<uint32_t>(row) * Kc * 2;
+  }
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int j = t * 32 + (lane & 31);
+    wt_ok[t] = j < r;
+    wt_row[t] = static_cast<uint32_t>(j) * Kc * 2;
+  }
+
+  for (int k = wbeg; k < wend; k += 64) {
+    u32x4_t a[4][RT], b[4][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kk = k + s * 16 + kl;
+      const bool kin = kk < wend;
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        a[s][t] = buf_load16(rwt, (wt_ok[t] && kin) ? wt_row[t] + kk * 2 : kOOB);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        b[s][i] = buf_load16(rin, (in_ok[i] && kin) ? in_row[i] + kk * 2 : kOOB);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[i][t] = mfma32x32x16(a[s][t], b[s][i], acc[i][t]);
+  }
+
+  float *dst = P + static_cast<size_t>(ks) * M * r;
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) red[wave - 1][i][lane] = acc[i][t];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f32x16_t v = acc[i][t];
+        v += red[0][i][lane];
+        v += red[1][i][lane];
+        v += red[2][i][lane];
+        const int m = m0 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int j0 = t * 32 + g * 8 + (lane >> 5) * 4;
+          if (m < M && j0 < r) {
+            f32x4_t o = {v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+            *reinterpret_cast<f32x4_t *>(dst + static_cast<size_t>(m) * r + j0) = o;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// reduce_m: partial sums over a split of rows m of IN[m][no] * S[m][j].
+// Workgroup: 64 columns of IN x all RT*32 >= r columns of S, one M-split.  Each
+// 32-row step is loaded with 16-byte reads and written to LDS transposed as
+// packed (m, m+1) bf16 pairs, so the MFMA reads 8 consecutive m per lane.
+//   JMAJOR = false: P[s][no][j]  (A = S rows j, B = IN columns no)   -> dB [N, r]
+//   JMAJOR = true:  P[s][j][no]  (A = IN rows no, B = S columns j)   -> dA [r, K]
+constexpr int PD = 20;  // dwords per LDS row: 16 m-pairs + 4 padding
+
+template <int RT, bool JMAJOR>
+__global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
+    const uint16_t *__restrict__ IN, int M, int No, const uint16_t *__restrict__ S, int r, int MR,
+    float *__restrict__ P) {
+  __shared__ __attribute__((aligned(16))) uint32_t sIn[64 * PD];
+  __shared__ __attribute__((aligned(16))) uint32_t sS[RT * 32 * PD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb0 = blockIdx.x * 64;
+  const int sp = blockIdx.y;
+  const int mb = sp * MR, me = min(M, mb + MR);
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(IN, static_cast<uint32_t>(uint64_t(M) * No * 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, static_cast<uint32_t>(uint64_t(M) * r * 2));
+
+  // load tasks: (pair p, 8-column chunk c) of IN (128 tasks) then of S (RT*64 tasks)
+  constexpr int NTASK = 128 + RT * 64;
+  constexpr int TPT = (NTASK + NT - 1) / NT;  // tasks per thread
+  u32x4_t ra[TPT], rb[TPT];
+
+  auto issue = [&](int mstep) {
+#pragma unroll
+    for (int q = 0; q < TPT; ++q) {
+      const int task = tid + q * NT;
+      uint32_t oa = kOOB, ob = kOOB;
+      if (task < 128) {
+        const int p = task & 15, c = task >> 4;
+        const int m = mstep + 2 * p, col = nb0 + c * 8;
+        if (col < No) {
+          if (m < me) oa = (static_cast<uint32_t>(m) * No + col) * 2;
+          if (m + 1 < me) ob = (static_cast<uint32_t>(m + 1) * No + col) * 2;
+        }
+        ra[q] = buf_load16(rin, oa);
+        rb[q] = buf_load16(rin, ob);
+      } else if (task < NTASK) {
+        const int t2 = task - 128;
+        const int p = t2 & 15, c = t2 >> 4;
+        const int m = mstep + 2 * p, col = c * 8;
+        if (col < r) {
+          if (m < me) oa = (static_cast<uint32_t>(m) * r + col) * 2;
+          if (m + 1 < me) ob = (static_cast<uint32_t>(m + 1) * r + col) * 2;
+        }
+        ra[q] = buf_load16(rs, oa);
+        rb[q] = buf_load16(rs, ob);
+      }
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int q = 0; q < TPT; ++q) {
+      const int task = tid + q * NT;
+      if (task >= NTASK) continue;
+      const bool is_in = task < 128;
+      const int t2 = is_in ? task : task - 128;
+      const int p = t2 & 15, c = t2 >> 4;
+      uint32_t *base = (is_in ? sIn : sS) + (c * 8) * PD + p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        base[(2 * e) * PD] = pack_lo(ra[q][e], rb[q][e]);
+        base[(2 * e + 1) * PD] = pack_hi(ra[q][e], rb[q][e]);
+      }
+    }
+  };
+
+  // output tiles: 2 (no) x RT (j) tiles of 32x32 spread over the 4 waves
+  constexpr int TILES = 2 * RT;
+  constexpr int TPW = (TILES + 3) / 4;
+  f32x16_t acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[u][e] = 0.0f;
+
+  if (mb < me) issue(mb);
+  for (int ms = mb; ms < me; ms += 32) {
+    __syncthreads();
+    stage();
+    __syncthreads();
+    if (ms + 32 < me) issue(ms + 32);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = wave + 4 * u;
+      if (tile >= TILES) continue;
+      const int nbk = tile & 1, t = tile >> 1;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int doff = kk * 8 + (lane >> 5) * 4;
+        const u32x4_t fin =
+            *reinterpret_cast<const u32x4_t *>(sIn + (nbk * 32 + (lane & 31)) * PD + doff);
+        const u32x4_t fs =
+            *reinterpret_cast<const u32x4_t *>(sS + (t * 32 + (lane & 31)) * PD + doff);
+        acc[u] = JMAJOR ? mfma32x32x16(fin, fs, acc[u]) : mfma32x32x16(fs, fin, acc[u]);
+      }
+    }
+  }
+
+  float *dst = P + static_cast<size_t>(sp) * No * r;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = wave + 4 * u;
+    if (tile >= TILES) continue;
+    const int nbk = tile & 1, t = tile >> 1;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4_t o = {acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
+      const int rq = g * 8 + (lane >> 5) * 4;  // first of 4 consecutive rows
+      if (!JMAJOR) {
+        const int no = nb0 + nbk * 32 + (lane & 31), j0 = t * 32 + rq;
+        if (no < No && j0 < r) *reinterpret_cast<f32x4_t *>(dst + static_cast<size_t>(no) * r + j0) = o;
+      } else {
+        const int j = t * 32 + (lane & 31), no0 = nb0 + nbk * 32 + rq;
+        if (j < r && no0 < No) *reinterpret_cast<f32x4_t *>(dst + static_cast<size_t>(j) * No + no0) = o;
+      }
+    }
+  }
+}
+
+// OUT[i] = bf16(scale * sum_s P[s][i]) for i < count (count % 4 == 0), fixed order.
+__global__ __launch_bounds__(NT) void finalize_kernel(const float *__restrict__ P, int splits,
+                                                      int64_t count, float scale,
+                                                      uint16_t *__restrict__ OUT) {
+  const int64_t n4 = count / 4;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * NT) {
+    f32x4_t s = reinterpret_cast<const f32x4_t *>(P)[i];
+    for (int k = 1; k < splits; ++k) s += reinterpret_cast<const f32x4_t *>(P + k * count)[i];
+    u32x2_t o = {pack_bf16x2(s[0] * scale, s[1] * scale), pack_bf16x2(s[2] * scale, s[3] * scale)};
+    reinterpret_cast<u32x2_t *>(OUT)[i] = o;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Generic kernels (any row length or rank): simple and unvectorized.
 __device__ __forceinline__ u32x4_t load8(const uint16_t *p, int64_t rows, int64_t cols, int64_t row,
-                                         int64_t col, bool vec_ok) {
+                                         int64_t col) {
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (row >= rows || col >= cols) return v;
   const uint16_t *src = p + row * cols + col;
-  if (vec_ok && col + 8 <= cols) return *reinterpret_cast<const u32x4_t *>(src);
   uint16_t t[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) t[e] = (col + e < cols) ? src[e] : uint16_t(0);
@@ -33,16 +274,13 @@ __device__ __forceinline__ u32x4_t load8(const uint16_t *p, int64_t rows, int64_
   return v;
 }
 
-// OUT[M, r] = bf16(scale * IN[M, Kc] . WT[r, Kc]^T).  Each wave owns 32 rows of IN and
-// all RT * 32 >= r output columns; a workgroup covers 128 rows.
+// OUT[M, r] = bf16(scale * IN[M, Kc] . WT[r, Kc]^T); one wave per 32 rows.
 template <int RT>
-__global__ __launch_bounds__(NT) void lora_down_kernel(const uint16_t *__restrict__ IN, int64_t M,
-                                                       int64_t Kc, const uint16_t *__restrict__ WT,
-                                                       int r, float scale,
-                                                       uint16_t *__restrict__ OUT) {
+__global__ __launch_bounds__(NT) void lora_down_generic_kernel(
+    const uint16_t *__restrict__ IN, int64_t M, int64_t Kc, const uint16_t *__restrict__ WT, int r,
+    float scale, uint16_t *__restrict__ OUT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 128 + wave * 32 + (lane & 31);
-  const bool vec = (Kc % 8) == 0;
   f32x16_t acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t)
@@ -50,12 +288,10 @@ __global__ __launch_bounds__(NT) void lora_down_kernel(const uint16_t *__restric
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
   for (int64_t k = 0; k < Kc; k += 16) {
     const int64_t kk = k + (lane >> 5) * 8;
-    const u32x4_t a = load8(IN, M, Kc, row, kk, vec);
+    const u32x4_t a = load8(IN, M, Kc, row, kk);
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const u32x4_t b = load8(WT, r, Kc, t * 32 + (lane & 31), kk, vec);
-      acc[t] = mfma32x32x16(a, b, acc[t]);
-    }
+    for (int t = 0; t < RT; ++t)
+      acc[t] = mfma32x32x16(a, load8(WT, r, Kc, t * 32 + (lane & 31), kk), acc[t]);
   }
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
@@ -70,51 +306,27 @@ __global__ __launch_bounds__(NT) void lora_down_kernel(const uint16_t *__restric
   }
 }
 
-__global__ __launch_bounds__(NT) void transpose_kernel(const uint16_t *__restrict__ IN, int64_t R,
-                                                       int64_t C, uint16_t *__restrict__ OUT) {
-  __shared__ uint16_t tile[64][65];
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < R && c < C) ? IN[r * C + c] : uint16_t(0);
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (r < R && c < C) OUT[c * R + r] = tile[tx][i];
-  }
-}
-
-// Partial reduction over a split of MS = 256 rows:
-//   P[s][no][j] = sum_{m in split s} IN[m][no] * S[m][j]
-// IN [M, No] and S [M, r] are staged 32 rows at a time in LDS (row-major) and read
-// column-wise into MFMA fragments (8 consecutive m per lane).  A workgroup covers 128
-// columns of IN (one 32-column tile per wave) and all RT * 32 >= r columns of S.
-constexpr int MS = 256;
-constexpr int RM_COLS = 128;
-
+// P[s][no][j] over splits of 256 rows, staged element-wise through LDS.
+constexpr int GMS = 256;
 template <int RT>
-__global__ __launch_bounds__(NT) void reduce_m_partial_kernel(const uint16_t *__restrict__ IN,
-                                                              int64_t M, int64_t No,
-                                                              const uint16_t *__restrict__ S, int r,
-                                                              float *__restrict__ P) {
-  __shared__ uint16_t sIn[32][RM_COLS + 2];
+__global__ __launch_bounds__(NT) void reduce_m_generic_kernel(
+    const uint16_t *__restrict__ IN, int64_t M, int64_t No, const uint16_t *__restrict__ S, int r,
+    float *__restrict__ P) {
+  __shared__ uint16_t sIn[32][128 + 2];
   __shared__ uint16_t sS[32][RT * 32 + 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * RM_COLS;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 128;
   const int64_t s_idx = blockIdx.y;
-  const int64_t mbeg = s_idx * MS, mend = min<int64_t>(M, mbeg + MS);
+  const int64_t mbeg = s_idx * GMS, mend = min<int64_t>(M, mbeg + GMS);
   f32x16_t acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
-
   for (int64_t mb = mbeg; mb < mend; mb += 32) {
     __syncthreads();
-    for (int i = tid; i < 32 * RM_COLS; i += NT) {
-      const int rr = i / RM_COLS, cc = i % RM_COLS;
+    for (int i = tid; i < 32 * 128; i += NT) {
+      const int rr = i / 128, cc = i % 128;
       const int64_t m = mb + rr, c = c0 + cc;
       sIn[rr][cc] = (m < mend && c < No) ? IN[m * No + c] : uint16_t(0);
     }
@@ -127,8 +339,8 @@ __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(const uint16_t *__
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int mm = ks * 16 + (lane >> 5) * 8;
-      u32x4_t a;
       const int ac = wave * 32 + (lane & 31);
+      u32x4_t a;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         a[e] = uint32_t(sIn[mm + 2 * e][ac]) | (uint32_t(sIn[mm + 2 * e + 1][ac]) << 16);
@@ -143,7 +355,6 @@ __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(const uint16_t *__
       }
     }
   }
-  // acc[t] holds rows = IN columns (no), columns = S columns (j)
   float *dst = P + s_idx * No * r;
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
@@ -157,10 +368,9 @@ __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(const uint16_t *__
   }
 }
 
-__global__ __launch_bounds__(NT) void reduce_m_final_kernel(const float *__restrict__ P,
-                                                            int64_t splits, int64_t No, int r,
-                                                            uint16_t *__restrict__ OUT,
-                                                            bool trans_out) {
+__global__ __launch_bounds__(NT) void reduce_m_generic_final_kernel(
+    const float *__restrict__ P, int64_t splits, int64_t No, int r, uint16_t *__restrict__ OUT,
+    bool trans_out) {
   const int64_t total = No * r;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * NT) {
@@ -174,24 +384,108 @@ __global__ __launch_bounds__(NT) void reduce_m_final_kernel(const float *__restr
   }
 }
 
+__global__ __launch_bounds__(NT) void transpose_kernel(const uint16_t *__restrict__ IN, int64_t R,
+                                                       int64_t C, uint16_t *__restrict__ OUT) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t rr = r0 + i, c = c0 + tx;
+    tile[i][tx] = (rr < R && c < C) ? IN[rr * C + c] : uint16_t(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, rr = r0 + tx;
+    if (rr < R && c < C) OUT[c * R + rr] = tile[tx][i];
+  }
+}
+
+// ---- split selection (shared by the workspace queries and the launches) -----------
+struct DownSplit {
+  int ksplit, KR;
+};
+DownSplit down_split(int64_t M, int64_t Kc) {
+  const int64_t row_tiles = (M + 63) / 64;
+  int64_t ks = (256 + row_tiles - 1) / row_tiles;
+  const int64_t kmax = (Kc + 255) / 256;
+  if (ks > kmax) ks = kmax;
+  if (ks < 1) ks = 1;
+  int64_t KR = ((Kc + ks - 1) / ks + 63) / 64 * 64;
+  ks = (Kc + KR - 1) / KR;
+  return {static_cast<int>(ks), static_cast<int>(KR)};
+}
+
+struct MSplit {
+  int splits, MR;
+};
+MSplit m_split(int64_t M, int64_t No) {
+  const int64_t tiles = (No + 63) / 64;
+  int64_t sp = (512 + tiles - 1) / tiles;
+  const int64_t smax = (M + 63) / 64;
+  if (sp > smax) sp = smax;
+  if (sp < 1) sp = 1;
+  int64_t MR = ((M + sp - 1) / sp + 31) / 32 * 32;
+  sp = (M + MR - 1) / MR;
+  return {static_cast<int>(sp), static_cast<int>(MR)};
+}
+
+bool down_fast(int64_t M, int64_t Kc, int r) {
+  return Kc % 8 == 0 && r % 8 == 0 && uint64_t(M) * Kc * 2 <= k4G && uint64_t(r) * Kc * 2 <= k4G &&
+         M < (int64_t(1) << 30);
+}
+bool reduce_fast(int64_t M, int64_t No, int r) {
+  return No % 8 == 0 && r % 8 == 0 && uint64_t(M) * No * 2 <= k4G && uint64_t(M) * r * 2 <= k4G &&
+         No < (int64_t(1) << 30);
+}
+
+hipError_t launch_finalize(const float *P, int splits, int64_t count, float scale, uint16_t *OUT,
+                           hipStream_t stream) {
+  int64_t blocks = (count / 4 + NT - 1) / NT;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(NT), 0, stream, P,
+                     splits, count, scale, OUT);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+size_t lora_down_workspace(int64_t M, int64_t Kc, int r) {
+  if (r <= 0 || !down_fast(M, Kc, r)) return 0;
+  return static_cast<size_t>(down_split(M, Kc).ksplit) * M * r * sizeof(float);
+}
+
 hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, const uint16_t *WT, int r,
-                            float scale, uint16_t *OUT, hipStream_t stream) {
-  const int64_t blocks = (M + 127) / 128;
-  dim3 grid(static_cast<unsigned>(blocks)), block(NT);
+                            float scale, uint16_t *OUT, float *ws, hipStream_t stream) {
   const int rt = (r + 31) / 32;
+  if (rt < 1 || rt > 8) return hipErrorInvalidValue;
+  if (down_fast(M, Kc, r)) {
+    const DownSplit sp = down_split(M, Kc);
+    dim3 grid(static_cast<unsigned>((M + 63) / 64), static_cast<unsigned>(sp.ksplit)), block(NT);
+    switch (rt) {
+#define QLORA_CASE(T)                                                                            \
+  case T:                                                                                        \
+    hipLaunchKernelGGL(lora_down_partial_kernel<T>, grid, block, 0, stream, IN,                  \
+                       static_cast<int>(M), static_cast<int>(Kc), WT, r, sp.KR, ws);             \
+    break;
+      QLORA_CASE(1) QLORA_CASE(2) QLORA_CASE(3) QLORA_CASE(4)
+      QLORA_CASE(5) QLORA_CASE(6) QLORA_CASE(7) QLORA_CASE(8)
+#undef QLORA_CASE
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_finalize(ws, sp.ksplit, M * r, scale, OUT, stream);
+  }
+  dim3 grid(static_cast<unsigned>((M + 127) / 128)), block(NT);
   switch (rt) {
-#define QLORA_CASE(T)                                                                        \
-  case T:                                                                                    \
-    hipLaunchKernelGGL(lora_down_kernel<T>, grid, block, 0, stream, IN, M, Kc, WT, r, scale, \
-                       OUT);                                                                 \
+#define QLORA_CASE(T)                                                                         \
+  case T:                                                                                     \
+    hipLaunchKernelGGL(lora_down_generic_kernel<T>, grid, block, 0, stream, IN, M, Kc, WT, r, \
+                       scale, OUT);                                                           \
     break;
     QLORA_CASE(1) QLORA_CASE(2) QLORA_CASE(3) QLORA_CASE(4)
     QLORA_CASE(5) QLORA_CASE(6) QLORA_CASE(7) QLORA_CASE(8)
 #undef QLORA_CASE
-    default:
-      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -204,34 +498,56 @@ hipError_t launch_transpose_bf16(const uint16_t *IN, int64_t R, int64_t C, uint1
 }
 
 size_t reduce_m_workspace(int64_t M, int64_t No, int r) {
-  const int64_t splits = (M + MS - 1) / MS;
+  if (r <= 0) return 0;
+  if (reduce_fast(M, No, r)) return static_cast<size_t>(m_split(M, No).splits) * No * r * sizeof(float);
+  const int64_t splits = (M + GMS - 1) / GMS;
   return static_cast<size_t>(splits) * No * r * sizeof(float);
 }
 
 hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, const uint16_t *S, int r,
                            float *partials, uint16_t *OUT, bool trans_out, hipStream_t stream) {
-  const int64_t splits = (M + MS - 1) / MS;
-  dim3 grid(static_cast<unsigned>((No + RM_COLS - 1) / RM_COLS), static_cast<unsigned>(splits));
-  dim3 block(NT);
   const int rt = (r + 31) / 32;
+  if (rt < 1 || rt > 8) return hipErrorInvalidValue;
+  if (reduce_fast(M, No, r)) {
+    const MSplit sp = m_split(M, No);
+    dim3 grid(static_cast<unsigned>((No + 63) / 64), static_cast<unsigned>(sp.splits)), block(NT);
+    const int Mi = static_cast<int>(M), Noi = static_cast<int>(No);
+    switch (rt * 2 + (trans_out ? 1 : 0)) {
+#define QLORA_CASE(T)                                                                              \
+  case 2 * T:                                                                                      \
+    hipLaunchKernelGGL((reduce_m_partial_kernel<T, false>), grid, block, 0, stream, IN, Mi, Noi, S, \
+                       r, sp.MR, partials);                                                        \
+    break;                                                                                         \
+  case 2 * T + 1:                                                                                  \
+    hipLaunchKernelGGL((reduce_m_partial_kernel<T, true>), grid, block, 0, stream, IN, Mi, Noi, S,  \
+                       r, sp.MR, partials);                                                        \
+    break;
+      QLORA_CASE(1) QLORA_CASE(2) QLORA_CASE(3) QLORA_CASE(4)
+      QLORA_CASE(5) QLORA_CASE(6) QLORA_CASE(7) QLORA_CASE(8)
+#undef QLORA_CASE
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_finalize(partials, sp.splits, No * r, 1.0f, OUT, stream);
+  }
+  const int64_t splits = (M + GMS - 1) / GMS;
+  dim3 grid(static_cast<unsigned>((No + 127) / 128), static_cast<unsigned>(splits)), block(NT);
   switch (rt) {
 #define QLORA_CASE(T)                                                                            \
   case T:                                                                                        \
-    hipLaunchKernelGGL(reduce_m_partial_kernel<T>, grid, block, 0, stream, IN, M, No, S, r,      \
+    hipLaunchKernelGGL(reduce_m_generic_kernel<T>, grid, block, 0, stream, IN, M, No, S, r,      \
                        partials);                                                                \
     break;
     QLORA_CASE(1) QLORA_CASE(2) QLORA_CASE(3) QLORA_CASE(4)
     QLORA_CASE(5) QLORA_CASE(6) QLORA_CASE(7) QLORA_CASE(8)
 #undef QLORA_CASE
-    default:
-      return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int64_t fb = (No * r + NT - 1) / NT;
   if (fb > 4096) fb = 4096;
-  hipLaunchKernelGGL(reduce_m_final_kernel, dim3(static_cast<unsigned>(fb)), dim3(NT), 0, stream,
-                     partials, splits, No, r, OUT, trans_out);
+  hipLaunchKernelGGL(reduce_m_generic_final_kernel, dim3(static_cast<unsigned>(fb)), dim3(NT), 0,
+                     stream, partials, splits, No, r, OUT, trans_out);
   return hipGetLastError();
 }
 

@@ -47,8 +47,10 @@ hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n_rows, int64_t n
 hipError_t launch_dequantize(const WeightView &w, void *out, bool out_bf16, hipStream_t stream);
 
 // OUT[M, r] (pitch r, bf16) = bf16(scale * IN[M, Kc] . WT[r, Kc]^T);  IN pitch Kc.
+// `ws` holds lora_down_workspace(M, Kc, r) bytes of fp32 partial sums.
+size_t lora_down_workspace(int64_t M, int64_t Kc, int r);
 hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, const uint16_t *WT, int r,
-                            float scale, uint16_t *OUT, hipStream_t stream);
+                            float scale, uint16_t *OUT, float *ws, hipStream_t stream);
 // OUT[C, R] = IN[R, C]^T for bf16 matrices (both dense row-major).
 hipError_t launch_transpose_bf16(const uint16_t *IN, int64_t R, int64_t C, uint16_t *OUT,
                                  hipStream_t stream);

@@ -130,7 +130,9 @@ int qlora_dequantize(const qlora_nf4_weight *w, void *out, int out_dtype, void *
  *   Y   = bf16(X . W'^T + U_s . B^T)                  [M, N], fp32 accumulation
  * X bf16 [M, K]; A bf16 [r, K]; B bf16 [N, r]; Y bf16 [M, N].
  * U_saved (nullable) receives U_s for the backward.  The decode of W' happens inside
- * the GEMM; no bf16 copy of the weight is written. */
+ * the GEMM; no bf16 copy of the weight is written.  When r > 0 the call needs
+ * qlora_workspace_bytes(0, M, K, N, r) bytes of workspace (fp32 partial sums of the
+ * down-projection, plus U_s when U_saved is NULL); with r = 0 it needs none. */
 int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
                      const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
                      void *workspace, size_t workspace_bytes, void *stream);
@@ -141,7 +143,8 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, co
  *   dX = bf16(dY . W' + V . A)                        [M, K]  (skipped if dX == NULL)
  *   dB = bf16(dY^T . U_s)                             [N, r]
  *   dA = bf16(V^T . X)                                [r, K]
- * U_saved is the forward's U_s; if NULL it is recomputed from X and A.
+ * U_saved is the forward's U_s; if NULL it is recomputed from X and A.  When r > 0 the
+ * call needs qlora_workspace_bytes(1, M, K, N, r) bytes of workspace.
  * dY bf16 [M, N]; X bf16 [M, K] (needed for dA, and for U_s when U_saved is NULL). */
 int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16_t *X, int64_t M,
                      const uint16_t *A, const uint16_t *B, int r, float alpha,

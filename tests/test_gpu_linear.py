@@ -56,6 +56,9 @@ SMALL = [  # (M, K, N, r)
     (16, 4096, 300, 16),
     (1, 1024, 1000, 8),
     (17, 512, 260, 32),    # just above the GEMV bound
+    (513, 768, 640, 128),  # rank 128
+    (130, 256, 136, 256),  # the largest rank
+    (2100, 1024, 512, 64), # several M-splits in the token reductions
 ]
 
 
