@@ -51,6 +51,12 @@ def load(path=LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m bit_quantized_lora_nf4_amd.build`")
+    # torch ships its own libamdhip64 under the same soname; load it first so that the
+    # library and torch share one HIP runtime (device memory, streams, events).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, I64, I32, SZ, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     W = ctypes.POINTER(qlora_nf4_weight)

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qlora_internal.h"
+
 namespace qlora {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -81,12 +83,92 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 constexpr uint32_t kOOB = 0xFFFFFFF0u;  // an offset past any buffer: reads as zero
 
+// Buffer resources over the three constant arrays of a quantized weight.
+struct ConstRsrc {
+  __amdgpu_buffer_rsrc_t q8, s, o;
+};
+__device__ __forceinline__ ConstRsrc make_const_rsrc(const int8_t *q8, const float *s, const float *o,
+                                                     uint32_t n_blocks) {
+  const uint32_t n_groups = (n_blocks + 255u) / 256u;
+  return {make_rsrc(q8, n_blocks), make_rsrc(s, n_groups * 4u), make_rsrc(o, n_groups * 4u)};
+}
+// Raw pieces of the constant of flat block b (zeros when !ok), loaded branch-free;
+// c' = fma(c8, s[b / 256], o[b / 256]) is formed later by const_value, so that a
+// prefetch does not force a wait on its own loads.
+struct ConstRaw {
+  uint32_t c8, s, o;
+};
+__device__ __forceinline__ ConstRaw fetch_constant(const ConstRsrc &r, uint32_t b, bool ok) {
+  const uint32_t ob = ok ? b : kOOB;
+  const uint32_t og = ok ? (b >> 8) * 4u : kOOB;
+  return {__builtin_amdgcn_raw_buffer_load_b8(r.q8, ob, 0, 0),
+          __builtin_amdgcn_raw_buffer_load_b32(r.s, og, 0, 0),
+          __builtin_amdgcn_raw_buffer_load_b32(r.o, og, 0, 0)};
+}
+__device__ __forceinline__ float const_value(const ConstRaw &c) {
+  const int c8 = static_cast<int8_t>(static_cast<uint8_t>(c.c8));
+  return __builtin_fmaf(static_cast<float>(c8), __uint_as_float(c.s), __uint_as_float(c.o));
+}
+
 // Pack the low halves / high halves of two dwords: (lo(a), lo(b)) and (hi(a), hi(b)).
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// ---- register-only NF4 decode -------------------------------------------------------
+// For one block constant c, the 16 possible decoded weights T[j] = bf16_rne(q[j] * c)
+// are kept as byte planes: L[p] holds the low bytes of T[4p..4p+3], H[p] the high bytes.
+struct Planes {
+  uint32_t L[4], H[4];
+};
+
+__device__ __forceinline__ Planes make_planes(float c, const LevelTable &lv) {
+  uint32_t t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = pack_bf16x2(lv.q[2 * i] * c, lv.q[2 * i + 1] * c);
+  Planes P;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    P.L[p] = __builtin_amdgcn_perm(t[2 * p + 1], t[2 * p], 0x06040200u);
+    P.H[p] = __builtin_amdgcn_perm(t[2 * p + 1], t[2 * p], 0x07050301u);
+  }
+  return P;
+}
+
+__device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t a, uint32_t b) {
+  return (m & a) | (~m & b);  // v_bfi_b32
+}
+
+// Eight codes (element e in bits 4e..4e+3 of w) -> four bf16 pairs in element order,
+// T[code] looked up with byte permutes: the low three code bits select a byte among
+// eight table bytes, the fourth picks between the two eight-entry halves through a
+// byte mask made by v_perm's sign-replicate selectors (8..11 copy bit 15/31/47/63).
+__device__ __forceinline__ u32x4_t lookup8(uint32_t w, const Planes &P) {
+  const uint32_t se = w & 0x07070707u;         // elements 0, 2, 4, 6
+  const uint32_t so = (w >> 4) & 0x07070707u;  // elements 1, 3, 5, 7
+  const uint32_t me = __builtin_amdgcn_perm(w << 12, w << 4, 0x090B080Au);
+  const uint32_t mo = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
+  const uint32_t Le = bitsel(me, __builtin_amdgcn_perm(P.L[3], P.L[2], se),
+                             __builtin_amdgcn_perm(P.L[1], P.L[0], se));
+  const uint32_t He = bitsel(me, __builtin_amdgcn_perm(P.H[3], P.H[2], se),
+                             __builtin_amdgcn_perm(P.H[1], P.H[0], se));
+  const uint32_t Lo = bitsel(mo, __builtin_amdgcn_perm(P.L[3], P.L[2], so),
+                             __builtin_amdgcn_perm(P.L[1], P.L[0], so));
+  const uint32_t Ho = bitsel(mo, __builtin_amdgcn_perm(P.H[3], P.H[2], so),
+                             __builtin_amdgcn_perm(P.H[1], P.H[0], so));
+  const uint32_t LL0 = __builtin_amdgcn_perm(Lo, Le, 0x05010400u);  // low bytes e0..e3
+  const uint32_t LL1 = __builtin_amdgcn_perm(Lo, Le, 0x07030602u);  // low bytes e4..e7
+  const uint32_t HH0 = __builtin_amdgcn_perm(Ho, He, 0x05010400u);
+  const uint32_t HH1 = __builtin_amdgcn_perm(Ho, He, 0x07030602u);
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_perm(HH0, LL0, 0x05010400u);
+  r[1] = __builtin_amdgcn_perm(HH0, LL0, 0x07030602u);
+  r[2] = __builtin_amdgcn_perm(HH1, LL1, 0x05010400u);
+  r[3] = __builtin_amdgcn_perm(HH1, LL1, 0x07030602u);
+  return r;
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -1,24 +1,39 @@
 // Fused NF4-decode GEMMs on bf16 MFMA (gfx950): the forward Y = X W'^T + U Bl^T
 // and the input gradient dX = dY W' + V At^T.
 //
-// W' is never written to HBM: each workgroup streams packed codes plus int8 block
-// constants, decodes them to bf16 in registers ([Digest] "方法步骤与流程" step 3 and
+// W' is never written to HBM: the kernels stream packed 4-bit codes plus int8 block
+// constants and decode them to bf16 on the fly ([Digest] "方法步骤与流程" step 3 and
 // [QLoRA note] "5. QLoRA 训练方式本身": the 4-bit weight is decoded to BF16 inside
-// the operator) and stages the decoded tile in LDS next to the bf16 activation tile.
-// The LoRA product (U . Bl^T or V . At^T) is added to the same fp32 accumulators as
-// r extra contraction steps before the single bf16 rounding of the output.
+// the operator): w' = bf16_rne(q[code] * c'), c' = fma(c8, s, o).  The LoRA product
+// is added to the same fp32 accumulators as r extra contraction steps before the
+// single bf16 rounding of each output.
 //
-// Tiling: a 256-thread workgroup computes a 256 x 256 output tile with four waves in
-// a 2 x 2 arrangement (128 x 128 per wave: 4 x 4 tiles of the 32x32x16 MFMA).  The
-// contraction advances 64 at a time through double-buffered LDS (row pitch 72 bf16,
-// which keeps 16-byte fragment reads of 16 consecutive rows on distinct banks).
-// Each weight element is decoded once per workgroup tile.
+// Tile: a 256-thread workgroup (four waves, one per SIMD) computes a 256 x 256 output
+// tile; wave w owns all 256 activation rows and output columns [64 w, 64 w + 64), i.e.
+// 8 x 2 tiles of the 32x32x16 MFMA (256 fp32 accumulators per lane).  The MFMA "A"
+// operand is the weight side (rows = output columns) and "B" the activation side
+// (columns = tokens), so each lane ends with 4 consecutive output columns of one
+// token: 8-byte stores.  The contraction advances 64 at a time.
 //
-// Forward:  output [M, N], contraction over K.  Thread t decodes weight row n0 + t,
-//           one 64-block (32 bytes of codes, one constant) per step: LDS layout [n][k].
-// Backward: output [M, K], contraction over N.  Thread t decodes rows kt + 2p and
-//           kt + 2p + 1 (p = t % 32) over 32 columns, and writes the two rows as bf16
-//           pairs into LDS transposed, [k][n], so the MFMA reads 8 consecutive n.
+// Activation tiles (X or dY, 256 rows x 64) are staged in LDS, double-buffered, with
+// an XOR swizzle of the eight 16-byte chunks of each 128-byte row, chunk c of row r
+// at slot c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): the 16-byte fragment reads of 16
+// consecutive rows hit distinct banks for either 32 or 64 LDS banks.
+//
+// Decode: per block constant c a lane builds the 16 possible outputs
+// bf16_rne(q[j] * c) as byte planes in registers and looks codes up with byte
+// permutes (no LDS table; about four VALU instructions per weight).
+//
+// Forward: the weight operand is decoded privately per lane straight into MFMA
+// fragments (lane l of wave w: weight rows 64 w + 32 j + l % 32, contraction half
+// l / 32 of each 64-step, i.e. one 16-byte code load and one block constant per row
+// and step); no weight bytes touch LDS.  The contraction order inside a step is
+// permuted identically on both operands (lane half h takes k in [32 h, 32 h + 32)).
+// Backward: the contraction runs over weight rows, so the 64 x 256 weight tile is
+// decoded cooperatively into LDS in its natural row-major layout (16-byte chunk c of
+// row n at slot c ^ g(n), g(n) = ((n & 3) << 2) | ((n >> 2) & 3)) and read with the
+// gfx950 transposing LDS read ds_read_b64_tr_b16, which hands each lane four
+// consecutive weight rows of one column.
 
 #include "device_common.h"
 #include "qlora_internal.h"
@@ -26,230 +41,497 @@
 namespace qlora {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int PITCH = BK + 8;  // bf16 elements per LDS row
 constexpr int NT = 256;
+constexpr int TM = 256, TN = 256, TK = 64;
+constexpr int TILE_BYTES = TM * TK * 2;  // 32 KB per staged operand tile
 
 struct GemmParams {
-  const uint16_t *A;  // fwd: X [M, K]; bwd: dY [M, N]; pitch Kc
+  const uint16_t *A;  // fwd: X [M, K]; bwd: dY [M, N]; row length Kc
   WeightView w;
   const uint16_t *A2;  // U or V [M, r]
   const uint16_t *B2;  // fwd: Bl [N, r]; bwd: At [K, r]
   uint16_t *C;         // [M, No]
-  int64_t M, No, Kc;
-  int r;
+  int M, No, Kc, r;
   LevelTable lvl;  // NF4 codebook
 };
 
-// Load 8 consecutive bf16 of row `row` starting at column `col` of a [rows, cols]
-// matrix with pitch `cols`; zero outside the matrix.  `vec_ok` = rows are 16-byte
-// aligned (cols % 8 == 0).
-__device__ __forceinline__ u32x4_t load8_bf16(const uint16_t *p, int64_t rows, int64_t cols,
-                                              int64_t row, int64_t col, bool vec_ok) {
-  u32x4_t v = {0u, 0u, 0u, 0u};
-  if (row >= rows || col >= cols) return v;
-  const uint16_t *src = p + row * cols + col;
-  if (vec_ok && col + 8 <= cols) return *reinterpret_cast<const u32x4_t *>(src);
-  uint16_t t[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = (col + e < cols) ? src[e] : uint16_t(0);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = uint32_t(t[2 * e]) | (uint32_t(t[2 * e + 1]) << 16);
-  return v;
-}
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-struct Prefetch {
-  u32x4_t a[8];       // activation tile chunks
-  u32x4_t code[2];    // packed codes
-  float c[2];         // decoded block constants
+// byte offset of 16-byte chunk c of row `row` in a swizzled 256 x 64 bf16 tile
+__device__ __forceinline__ int tile_off(int row, int c) { return row * 128 + ((c ^ swz(row)) << 4); }
+
+// ---- activation tile staging: 256 rows x 64 columns, 8 chunks of 16 B per thread ----
+struct ActStage {
+  u32x4_t v[8];
 };
 
-template <bool BWD>
-__device__ __forceinline__ void load_tile(const GemmParams &p, int64_t m0, int64_t n0, int64_t kt,
-                                          bool a_vec, Prefetch &f) {
+// thread t handles rows (t >> 3) + 32 i, chunk t & 7
+__device__ __forceinline__ void act_load(__amdgpu_buffer_rsrc_t rs, int m0, int M, int Kc, int kt,
+                                         bool vec, const uint16_t *base, ActStage &st) {
   const int tid = threadIdx.x;
-  // activation tile [BM rows, BK cols]: 8 lanes per 128-byte row
+  const int c = tid & 7;
+  const int col = kt + c * 8;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int ch = tid + i * NT;
-    const int row = ch >> 3, c8 = ch & 7;
-    f.a[i] = load8_bf16(p.A, p.M, p.Kc, m0 + row, kt + c8 * 8, a_vec);
-  }
-  const int64_t K = p.w.n_cols, N = p.w.n_rows;
-  if (!BWD) {
-    const int64_t n = n0 + tid;
-    if (n < N) {
-      const u32x4_t *src = reinterpret_cast<const u32x4_t *>(p.w.codes + n * (K / 2) + kt / 2);
-      f.code[0] = src[0];
-      f.code[1] = src[1];
-      f.c[0] = decode_constant(p.w.absmax_q, p.w.dq_scale, p.w.dq_offset, (n * K + kt) >> 6);
+    const int row = m0 + (tid >> 3) + 32 * i;
+    if (vec) {
+      const bool ok = row < M && col < Kc;
+      st.v[i] = buf_load16(rs, ok ? (static_cast<uint32_t>(row) * Kc + col) * 2 : kOOB);
     } else {
-      f.code[0] = f.code[1] = u32x4_t{0u, 0u, 0u, 0u};
-      f.c[0] = 0.0f;
-    }
-  } else {
-    const int pr = tid & 31, kc = tid >> 5;
-    const int64_t k = n0 + kc * 32;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (row < M) {
+        const uint16_t *src = base + static_cast<int64_t>(row) * Kc;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t n = kt + 2 * pr + h;
-      if (n < N && k < K) {
-        f.code[h] = *reinterpret_cast<const u32x4_t *>(p.w.codes + n * (K / 2) + k / 2);
-        f.c[h] = decode_constant(p.w.absmax_q, p.w.dq_scale, p.w.dq_offset, (n * K + k) >> 6);
-      } else {
-        f.code[h] = u32x4_t{0u, 0u, 0u, 0u};
-        f.c[h] = 0.0f;
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t lo = (col + e < Kc) ? src[col + e] : 0u;
+          const uint32_t hi = (col + e + 1 < Kc) ? src[col + e + 1] : 0u;
+          v[e / 2] = lo | (hi << 16);
+        }
       }
+      st.v[i] = v;
     }
   }
 }
 
-template <bool BWD>
-__device__ __forceinline__ void store_tile(const Prefetch &f, uint16_t *sA, uint16_t *sB,
-                                           const float *lut) {
+__device__ __forceinline__ void act_store(char *s, const ActStage &st) {
   const int tid = threadIdx.x;
+  const int c = tid & 7;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int ch = tid + i * NT;
-    const int row = ch >> 3, c8 = ch & 7;
-    *reinterpret_cast<u32x4_t *>(sA + row * PITCH + c8 * 8) = f.a[i];
-  }
-  if (!BWD) {
-    uint16_t *dst = sB + tid * PITCH;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4_t *>(dst + (h * 4 + i) * 8) = decode8(f.code[h][i], f.c[0], lut);
-  } else {
-    const int pr = tid & 31, kc = tid >> 5;
-    uint32_t *dst = reinterpret_cast<uint32_t *>(sB + (kc * 32) * PITCH) + pr;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t wa = f.code[0][i], wb = f.code[1][i];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float va = lut[(wa >> (4 * e)) & 15u] * f.c[0];
-        const float vb = lut[(wb >> (4 * e)) & 15u] * f.c[1];
-        dst[(i * 8 + e) * (PITCH / 2)] = pack_bf16x2(va, vb);
-      }
-    }
+    const int row = (tid >> 3) + 32 * i;
+    *reinterpret_cast<u32x4_t *>(s + tile_off(row, c)) = st.v[i];
   }
 }
 
-template <bool BWD>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
-    GemmParams p) {
-  __shared__ uint16_t sA[2][BM * PITCH];
-  __shared__ uint16_t sB[2][BN * PITCH];
-  __shared__ float lut[16];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
-  if (tid < 16) lut[tid] = p.lvl.q[tid];
-
-  const bool a_vec = (p.Kc % 8) == 0;
-  const int nk = static_cast<int>((p.Kc + BK - 1) / BK);
-
-  f32x16_t acc[4][4];
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[8][2]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+}
 
-  Prefetch f;
-  load_tile<BWD>(p, m0, n0, 0, a_vec, f);
-  __syncthreads();  // codebook in LDS
-  store_tile<BWD>(f, sA[0], sB[0], lut);
-  __syncthreads();
-
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nk) load_tile<BWD>(p, m0, n0, static_cast<int64_t>(it + 1) * BK, a_vec, f);
-    const uint16_t *a_base = sA[cur] + (wm * 128 + (lane & 31)) * PITCH + (lane >> 5) * 8;
-    const uint16_t *b_base = sB[cur] + (wn * 128 + (lane & 31)) * PITCH + (lane >> 5) * 8;
+// LoRA steps: acc[i][j] += A2 rows (tokens) x B2 rows (output columns), r in steps of 16.
+__device__ __forceinline__ void lora_steps(const GemmParams &p, int m0, int c0,
+                                           f32x16_t (&acc)[8][2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = p.r;
+  const bool vec = (r % 8) == 0;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A2, static_cast<uint32_t>(uint64_t(p.M) * r * 2));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B2, static_cast<uint32_t>(uint64_t(p.No) * r * 2));
+  for (int rk = 0; rk < r; rk += 16) {
+    const int j0 = rk + (lane >> 5) * 8;
+    u32x4_t wa[2], xb[8];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4_t a[4], b[4];
+    for (int j = 0; j < 2; ++j) {
+      const int col = c0 + wave * 64 + j * 32 + (lane & 31);
+      if (vec) {
+        wa[j] = buf_load16(rb, (col < p.No && j0 < r) ? (static_cast<uint32_t>(col) * r + j0) * 2 : kOOB);
+      } else {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (col < p.No)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const u32x4_t *>(a_base + i * 32 * PITCH + ks * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const u32x4_t *>(b_base + j * 32 * PITCH + ks * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
-    }
-    if (it + 1 < nk) store_tile<BWD>(f, sA[cur ^ 1], sB[cur ^ 1], lut);
-    __syncthreads();
-  }
-
-  // LoRA up-projection as r extra contraction steps: acc += A2 . B2^T
-  if (p.r > 0) {
-    const bool r_vec = (p.r % 8) == 0;
-    for (int rk = 0; rk < p.r; rk += 16) {
-      const int64_t j0 = rk + (lane >> 5) * 8;
-      u32x4_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = load8_bf16(p.A2, p.M, p.r, m0 + wm * 128 + i * 32 + (lane & 31), j0, r_vec);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = load8_bf16(p.B2, p.No, p.r, n0 + wn * 128 + j * 32 + (lane & 31), j0, r_vec);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
-    }
-  }
-
-  // epilogue: one bf16 rounding per output element
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
-      if (col >= p.No) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        if (row < p.M) p.C[row * p.No + col] = to_bf16(acc[i][j][e]);
+          for (int e = 0; e < 8; e += 2) {
+            const uint32_t lo = (j0 + e < r) ? p.B2[static_cast<int64_t>(col) * r + j0 + e] : 0u;
+            const uint32_t hi = (j0 + e + 1 < r) ? p.B2[static_cast<int64_t>(col) * r + j0 + e + 1] : 0u;
+            v[e / 2] = lo | (hi << 16);
+          }
+        wa[j] = v;
       }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = m0 + i * 32 + (lane & 31);
+      if (vec) {
+        xb[i] = buf_load16(ra, (row < p.M && j0 < r) ? (static_cast<uint32_t>(row) * r + j0) * 2 : kOOB);
+      } else {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (row < p.M)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const uint32_t lo = (j0 + e < r) ? p.A2[static_cast<int64_t>(row) * r + j0 + e] : 0u;
+            const uint32_t hi = (j0 + e + 1 < r) ? p.A2[static_cast<int64_t>(row) * r + j0 + e + 1] : 0u;
+            v[e / 2] = lo | (hi << 16);
+          }
+        xb[i] = v;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(wa[j], xb[i], acc[i][j]);
+  }
+}
+
+// Epilogue: lane holds token m = m0 + 32 i + l % 32 and output columns
+// c0 + 64 w + 32 j + 8 g + 4 (l / 32) + 0..3 for g = 0..3.
+__device__ __forceinline__ void store_out(const GemmParams &p, int m0, int c0,
+                                          const f32x16_t (&acc)[8][2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool vec = (p.No % 4) == 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + i * 32 + (lane & 31);
+    if (m >= p.M) continue;
+    uint16_t *row = p.C + static_cast<int64_t>(m) * p.No;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = c0 + wave * 64 + j * 32 + g * 8 + (lane >> 5) * 4;
+        const f32x16_t &a = acc[i][j];
+        if (vec) {
+          if (col < p.No) {
+            u32x2_t o = {pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+            *reinterpret_cast<u32x2_t *>(row + col) = o;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < p.No) row[col + e] = to_bf16(a[4 * g + e]);
+        }
+      }
+  }
+}
+
+// Map the linear workgroup id to (token tile, output tile): workgroups are dispatched
+// round-robin over the 8 XCDs, so consecutive tiles of the grouped raster order are
+// given to the same XCD (sharing its L2); groups of 4 token tiles sweep the outputs.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int T = tiles_m * tiles_n;
+  int b = blockIdx.x;
+  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
+  constexpr int G = 4;
+  const int group = b / (G * tiles_n);
+  const int first = group * G;
+  const int gsize = min(tiles_m - first, G);
+  const int in = b - group * G * tiles_n;
+  tm = first + in % gsize;
+  tn = in / gsize;
+}
+
+// ===================================== forward =====================================
+// Per-lane code prefetch for one contraction step: two weight rows (j = 0, 1).
+struct CodeStage {
+  u32x4_t code[2];
+  ConstRaw c[2];
+};
+
+__device__ __forceinline__ void code_load_fwd(const GemmParams &p, __amdgpu_buffer_rsrc_t rc,
+                                              const ConstRsrc &rq, int n_base, int kt,
+                                              CodeStage &cs) {
+  const int lane = threadIdx.x & 63;
+  const int K = p.Kc, N = p.No;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n_base + j * 32 + (lane & 31);
+    const bool ok = n < N;
+    cs.code[j] = buf_load16(rc, ok ? static_cast<uint32_t>(n) * (K / 2) + kt / 2 + (lane >> 5) * 16 : kOOB);
+    cs.c[j] = fetch_constant(rq, static_cast<uint32_t>(n) * (K / 64) + kt / 64, ok);
+  }
+}
+
+// Direct buffer -> LDS staging of a 256 x 64 activation tile (gfx950 LDS DMA): each
+// wave-wide load writes 1 KB contiguously (lane l at byte 16 l), so lane l fetches the
+// global chunk that belongs at that swizzled slot: tile row r = 8 q + l / 8, slot
+// l % 8 holds chunk (l % 8) ^ f(r).  Wave w issues the loads q = 8 w .. 8 w + 7; rows
+// past M read as zero.  No registers hold the tile.
+__device__ __forceinline__ void act_dma(__amdgpu_buffer_rsrc_t rs, int m0, int M, int Kc, int kt,
+                                        char *s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = wave * 8 + i;
+    const int r = q * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    const int row = m0 + r;
+    const uint32_t off = row < M ? (static_cast<uint32_t>(row) * Kc + kt + c * 8) * 2 : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(s + q * 1024),
+                                             16, off, 0, 0, 0);
+  }
+}
+
+// X fragments (B operand) of contraction sub-step s from a staged tile: rows
+// 32 i + l % 32, contraction half l / 32 -> chunk 4 (l / 32) + s.
+__device__ __forceinline__ void read_xfrags_fwd(const char *sx, int s, u32x4_t (&xb)[8]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    xb[i] = *reinterpret_cast<const u32x4_t *>(sx + tile_off(i * 32 + (lane & 31), (lane >> 5) * 4 + s));
+}
+
+// The forward is software-pipelined by contraction sub-step (16 of each 64-step):
+// while the 16 MFMAs of sub-step s run, the weight fragments of sub-step s + 1 are
+// decoded in registers and its activation fragments read from LDS.  Activation tiles
+// rotate through three LDS buffers so that the first fragments of the next step can
+// be read before the step's closing barrier: step i computes from buffer i % 3,
+// prefetches from (i + 1) % 3 and stores tile i + 2 into (i + 2) % 3.
+constexpr int NBUF = 3;
+
+// Instruction-scheduling template for one forward sub-step (16 MFMAs), applied to a
+// region fenced by sched_barrier: the 8 LDS fragment reads for the next sub-step go
+// first, then each MFMA is followed by `nv` VALU instructions of decode work.
+template <int NV>
+__device__ __forceinline__ void substep_schedule() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+  }
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_fwd_kernel(
+    GemmParams p) {
+  __shared__ __attribute__((aligned(16))) char sX[NBUF * TILE_BYTES];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int tmi, tni;
+  tile_coords((p.M + TM - 1) / TM, (p.No + TN - 1) / TN, tmi, tni);
+  const int m0 = tmi * TM, n0 = tni * TN;
+
+  const int K = p.Kc;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, static_cast<uint32_t>(uint64_t(p.M) * K * 2));
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.w.codes, static_cast<uint32_t>(uint64_t(p.No) * K / 2));
+  const ConstRsrc rq = make_const_rsrc(p.w.absmax_q, p.w.dq_scale, p.w.dq_offset,
+                                       static_cast<uint32_t>(uint64_t(p.No) * K / 64));
+  const int n_base = n0 + wave * 64;
+  const int nk = K / TK;
+  const int last = nk - 1;
+
+  f32x16_t acc[8][2];
+  zero_acc(acc);
+
+  CodeStage cur, nxt, nn;
+  act_dma(rx, m0, p.M, K, 0, sX);
+  act_dma(rx, m0, p.M, K, min(1, last) * TK, sX + TILE_BYTES);
+  code_load_fwd(p, rc, rq, n_base, 0, cur);
+  code_load_fwd(p, rc, rq, n_base, min(1, last) * TK, nxt);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  Planes pl[2];
+  u32x4_t wa[2], xb[8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    pl[j] = make_planes(const_value(cur.c[j]), p.lvl);
+    wa[j] = lookup8(cur.code[j][0], pl[j]);
+  }
+  read_xfrags_fwd(sX, 0, xb);
+
+  // Code stages rotate by register moves (cur <- nxt <- nn), so every iteration is
+  // the same single scheduling region.  All global loads of a step (tile DMA and the
+  // codes two steps ahead) are issued at its start; the wait before the closing
+  // barrier then covers loads that have had the whole step to arrive.
+  for (int it = 0; it < nk; ++it) {
+    const char *sx = sX + (it % NBUF) * TILE_BYTES;
+    const char *sxn = sX + ((it + 1) % NBUF) * TILE_BYTES;
+    char *sxw = sX + ((it + 2) % NBUF) * TILE_BYTES;
+    act_dma(rx, m0, p.M, K, min(it + 2, last) * TK, sxw);
+    code_load_fwd(p, rc, rq, n_base, min(it + 2, last) * TK, nn);
+    __builtin_amdgcn_sched_barrier(0);
+    Planes pln[2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t wan[2], xbn[8];
+      if (s < 3) {
+        read_xfrags_fwd(sx, s + 1, xbn);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) wan[j] = lookup8(cur.code[j][s + 1], pl[j]);
+      } else {
+        read_xfrags_fwd(sxn, 0, xbn);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          pln[j] = make_planes(const_value(nxt.c[j]), p.lvl);
+          wan[j] = lookup8(nxt.code[j][0], pln[j]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(wa[j], xb[i], acc[i][j]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wa[j] = wan[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xb[i] = xbn[i];
+      if (s < 3)
+        substep_schedule<4>();
+      else
+        substep_schedule<8>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur = nxt;
+    nxt = nn;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) pl[j] = pln[j];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this step's loads have landed
+    __syncthreads();
+  }
+  if (p.r > 0) lora_steps(p, m0, n0, acc);
+  store_out(p, m0, n0, acc);
+}
+
+// ===================================== backward ====================================
+// Weight tile for contraction rows [kt, kt + 64) and output columns [k0, k0 + 256),
+// natural layout: 64 rows of 512 bytes, 16-byte chunk c of row n at slot c ^ g(n).
+// Thread t decodes row kt + (t % 64), columns k0 + 64 (t / 64) .. + 64: one block
+// constant, 32 bytes of codes, eight 16-byte LDS stores (16 consecutive rows per
+// store instruction land on distinct banks).
+__device__ __forceinline__ int gswz(int n) { return ((n & 3) << 2) | ((n >> 2) & 3); }
+__device__ __forceinline__ int wtile_off(int n, int col) {
+  return n * 512 + ((((col >> 3) ^ gswz(n)) & 31) << 4) + (col & 7) * 2;
+}
+
+struct CodeStageB {
+  u32x4_t code[2];
+  ConstRaw c;
+};
+
+__device__ __forceinline__ void code_load_bwd(const GemmParams &p, __amdgpu_buffer_rsrc_t rc,
+                                              const ConstRsrc &rq, int k0, int kt, CodeStageB &cs) {
+  const int tid = threadIdx.x;
+  const int K = p.No, N = p.Kc;  // output columns are weight columns; contraction over rows
+  const int n = kt + (tid & 63);
+  const int k = k0 + (tid >> 6) * 64;
+  const bool ok = n < N && k < K;
+  const uint32_t off = static_cast<uint32_t>(n) * (K / 2) + k / 2;
+  cs.code[0] = buf_load16(rc, ok ? off : kOOB);
+  cs.code[1] = buf_load16(rc, ok ? off + 16 : kOOB);
+  cs.c = fetch_constant(rq, static_cast<uint32_t>(n) * (K / 64) + k / 64, ok);
+}
+
+__device__ __forceinline__ void code_store_bwd(const GemmParams &p, const CodeStageB &cs, char *sw) {
+  const int tid = threadIdx.x;
+  const int n = tid & 63, c0 = (tid >> 6) * 64;
+  const Planes pl = make_planes(const_value(cs.c), p.lvl);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t *>(sw + wtile_off(n, c0 + h * 32 + i * 8)) = lookup8(cs.code[h][i], pl);
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Weight-side MFMA fragment for contraction step s (16 rows) and output-column tile
+// j of this wave: two transposing reads of 4 rows each.  Within a 16-lane group, lane
+// i reads row nbase + i / 4 at column cbase + 4 (i % 4) and receives column cbase + i
+// of rows nbase .. nbase + 3.
+__device__ __forceinline__ u32x4_t wfrag_tr(const char *sw, int s, int j) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int cbase = wave * 64 + j * 32 + (g & 1) * 16;
+  const int col = cbase + 4 * (i & 3);
+  u32x4_t r;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int n = 16 * s + 8 * (g >> 1) + 4 * e + (i >> 2);
+    const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16_t *)(sw + wtile_off(n, col)));
+    const u32x2_t u = __builtin_bit_cast(u32x2_t, v);
+    r[2 * e] = u[0];
+    r[2 * e + 1] = u[1];
+  }
+  return r;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dx_kernel(
+    GemmParams p) {
+  __shared__ __attribute__((aligned(16))) char sX[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sW[2][TILE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  int tmi, tni;
+  tile_coords((p.M + TM - 1) / TM, (p.No + TN - 1) / TN, tmi, tni);
+  const int m0 = tmi * TM, k0 = tni * TN;
+
+  const int N = p.Kc, K = p.No;
+  const __amdgpu_buffer_rsrc_t rdy = make_rsrc(p.A, static_cast<uint32_t>(uint64_t(p.M) * N * 2));
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.w.codes, static_cast<uint32_t>(uint64_t(N) * K / 2));
+  const ConstRsrc rq = make_const_rsrc(p.w.absmax_q, p.w.dq_scale, p.w.dq_offset,
+                                       static_cast<uint32_t>(uint64_t(N) * K / 64));
+  const int nk = (N + TK - 1) / TK;
+  const int last = nk - 1;
+
+  f32x16_t acc[8][2];
+  zero_acc(acc);
+
+  ActStage st;
+  CodeStageB cs;
+  act_load(rdy, m0, p.M, N, 0, VEC, p.A, st);
+  code_load_bwd(p, rc, rq, k0, 0, cs);
+  act_store(sX[0], st);
+  code_store_bwd(p, cs, sW[0]);
+  __syncthreads();
+
+  auto step = [&](int it, const char *sx, const char *sw, char *sx_next, char *sw_next) {
+    const int nt = min(it + 1, last) * TK;
+    act_load(rdy, m0, p.M, N, nt, VEC, p.A, st);
+    code_load_bwd(p, rc, rq, k0, nt, cs);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t wa[2], xb[8];
+      const int chunk = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wa[j] = wfrag_tr(sw, s, j);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        xb[i] = *reinterpret_cast<const u32x4_t *>(sx + tile_off(i * 32 + (lane & 31), chunk));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(wa[j], xb[i], acc[i][j]);
+    }
+    act_store(sx_next, st);
+    code_store_bwd(p, cs, sw_next);
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it + 1 < nk; it += 2) {
+    step(it, sX[0], sW[0], sX[1], sW[1]);
+    step(it + 1, sX[1], sW[1], sX[0], sW[0]);
+  }
+  if (it < nk) step(it, sX[0], sW[0], sX[1], sW[1]);
+  if (p.r > 0) lora_steps(p, m0, k0, acc);
+  store_out(p, m0, k0, acc);
+}
+
+bool fits_32bit(int64_t M, int64_t N, int64_t K, int r) {
+  const uint64_t lim = 0xFFFFFFF0ull;
+  return uint64_t(M) * K * 2 <= lim && uint64_t(M) * N * 2 <= lim && uint64_t(N) * K / 2 <= lim &&
+         uint64_t(M) * r * 2 <= lim && uint64_t(N) * r * 2 <= lim && uint64_t(K) * r * 2 <= lim;
+}
+
+GemmParams make_params(const uint16_t *A, const WeightView &w, const uint16_t *A2,
+                       const uint16_t *B2, uint16_t *C, int64_t M, int64_t No, int64_t Kc, int r) {
+  GemmParams p{A, w, A2, B2, C, static_cast<int>(M), static_cast<int>(No), static_cast<int>(Kc), r, {}};
+  for (int i = 0; i < 16; ++i) p.lvl.q[i] = codebook().q[i];
+  return p;
+}
+
+unsigned grid_size(int64_t M, int64_t No) {
+  return static_cast<unsigned>(((M + TM - 1) / TM) * ((No + TN - 1) / TN));
 }
 
 }  // namespace
 
-static hipError_t launch_gemm(bool bwd, const GemmParams &p, hipStream_t stream) {
-  const int64_t tm = (p.M + BM - 1) / BM, tn = (p.No + BN - 1) / BN;
-  if (tm > 0x7fffffff || tn > 65535) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(tm), static_cast<unsigned>(tn)), block(NT);
-  if (bwd)
-    hipLaunchKernelGGL(gemm_kernel<true>, grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL(gemm_kernel<false>, grid, block, 0, stream, p);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
                            const uint16_t *Bl, int r, uint16_t *Y, hipStream_t stream) {
-  GemmParams p{X, w, U, Bl, Y, M, w.n_rows, w.n_cols, r, {}};
-  for (int i = 0; i < 16; ++i) p.lvl.q[i] = codebook().q[i];
-  return launch_gemm(false, p, stream);
+  if (!fits_32bit(M, w.n_rows, w.n_cols, r) || M > 0x7fffffff) return hipErrorInvalidValue;
+  const GemmParams p = make_params(X, w, U, Bl, Y, M, w.n_rows, w.n_cols, r);
+  hipLaunchKernelGGL(gemm_fwd_kernel, dim3(grid_size(M, w.n_rows)), dim3(NT), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_dx(const WeightView &w, const uint16_t *dY, int64_t M, const uint16_t *V,
                           const uint16_t *At, int r, uint16_t *dX, hipStream_t stream) {
-  GemmParams p{dY, w, V, At, dX, M, w.n_cols, w.n_rows, r, {}};
-  for (int i = 0; i < 16; ++i) p.lvl.q[i] = codebook().q[i];
-  return launch_gemm(true, p, stream);
+  if (!fits_32bit(M, w.n_rows, w.n_cols, r) || M > 0x7fffffff) return hipErrorInvalidValue;
+  const GemmParams p = make_params(dY, w, V, At, dX, M, w.n_cols, w.n_rows, r);
+  if (w.n_rows % 8 == 0)
+    hipLaunchKernelGGL(gemm_dx_kernel<true>, dim3(grid_size(M, w.n_cols)), dim3(NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_dx_kernel<false>, dim3(grid_size(M, w.n_cols)), dim3(NT), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace qlora
