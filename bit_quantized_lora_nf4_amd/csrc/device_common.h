@@ -106,7 +106,12 @@ __device__ __forceinline__ ConstRaw fetch_constant(const ConstRsrc &r, uint32_t 
           __builtin_amdgcn_raw_buffer_load_b32(r.o, og, 0, 0)};
 }
 __device__ __forceinline__ float const_value(const ConstRaw &c) {
-  const int c8 = static_cast<int8_t>(static_cast<uint8_t>(c.c8));
+  // The empty asm hides the loaded byte from instruction selection: otherwise the
+  // sign extension is folded into a sign-extending load that is re-issued next to
+  // this use, which then waits for every load in flight.
+  uint32_t u = c.c8;
+  asm("" : "+v"(u));
+  const int c8 = static_cast<int>(u << 24) >> 24;
   return __builtin_fmaf(static_cast<float>(c8), __uint_as_float(c.s), __uint_as_float(c.o));
 }
 

@@ -218,39 +218,10 @@ struct CodeStage {
   ConstRaw c[2];
 };
 
-__device__ __forceinline__ void code_load_fwd(const GemmParams &p, __amdgpu_buffer_rsrc_t rc,
-                                              const ConstRsrc &rq, int n_base, int kt,
-                                              CodeStage &cs) {
-  const int lane = threadIdx.x & 63;
-  const int K = p.Kc, N = p.No;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n_base + j * 32 + (lane & 31);
-    const bool ok = n < N;
-    cs.code[j] = buf_load16(rc, ok ? static_cast<uint32_t>(n) * (K / 2) + kt / 2 + (lane >> 5) * 16 : kOOB);
-    cs.c[j] = fetch_constant(rq, static_cast<uint32_t>(n) * (K / 64) + kt / 64, ok);
-  }
-}
-
-// Direct buffer -> LDS staging of a 256 x 64 activation tile (gfx950 LDS DMA): each
-// wave-wide load writes 1 KB contiguously (lane l at byte 16 l), so lane l fetches the
-// global chunk that belongs at that swizzled slot: tile row r = 8 q + l / 8, slot
-// l % 8 holds chunk (l % 8) ^ f(r).  Wave w issues the loads q = 8 w .. 8 w + 7; rows
-// past M read as zero.  No registers hold the tile.
-__device__ __forceinline__ void act_dma(__amdgpu_buffer_rsrc_t rs, int m0, int M, int Kc, int kt,
-                                        char *s) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int q = wave * 8 + i;
-    const int r = q * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    const int row = m0 + r;
-    const uint32_t off = row < M ? (static_cast<uint32_t>(row) * Kc + kt + c * 8) * 2 : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(s + q * 1024),
-                                             16, off, 0, 0, 0);
-  }
-}
+template <int V>
+struct Ic {
+  static constexpr int v = V;
+};
 
 // X fragments (B operand) of contraction sub-step s from a staged tile: rows
 // 32 i + l % 32, contraction half l / 32 -> chunk 4 (l / 32) + s.
@@ -261,31 +232,46 @@ __device__ __forceinline__ void read_xfrags_fwd(const char *sx, int s, u32x4_t (
     xb[i] = *reinterpret_cast<const u32x4_t *>(sx + tile_off(i * 32 + (lane & 31), (lane >> 5) * 4 + s));
 }
 
-// The forward is software-pipelined by contraction sub-step (16 of each 64-step):
-// while the 16 MFMAs of sub-step s run, the weight fragments of sub-step s + 1 are
-// decoded in registers and its activation fragments read from LDS.  Activation tiles
-// rotate through three LDS buffers so that the first fragments of the next step can
-// be read before the step's closing barrier: step i computes from buffer i % 3,
-// prefetches from (i + 1) % 3 and stores tile i + 2 into (i + 2) % 3.
-constexpr int NBUF = 3;
-
 // Instruction-scheduling template for one forward sub-step (16 MFMAs), applied to a
 // region fenced by sched_barrier: the 8 LDS fragment reads for the next sub-step go
-// first, then each MFMA is followed by `nv` VALU instructions of decode work.
-template <int NV>
+// first, then each MFMA is followed by `NV` VALU instructions of decode work; the
+// sub-step's `NG` global loads are spread evenly between the MFMAs, so that the four
+// waves of a workgroup (which run in step) never queue all their loads at once.
+template <int NV, int NG>
 __device__ __forceinline__ void substep_schedule() {
   __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (NG > 0)
+      if (q % (16 / NG) == 0) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
     __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
   }
 }
 
+// Global loads per wave and contraction step: per weight row (2) the codes and three
+// constant pieces, then eight activation DMA loads; four per sub-step, the last four
+// after the step's barrier.  The barrier's wait leaves the 12 issued before it in
+// flight, so it waits exactly for the previous step's loads.
+constexpr int LOADS_BEFORE_BARRIER = 12;
+
+// The forward is software-pipelined by contraction sub-step (16 of each 64-step):
+// while the 16 MFMAs of sub-step s run, the weight fragments of sub-step s + 1 are
+// decoded in registers and its activation fragments read from LDS.  Activation tiles
+// rotate through three LDS buffers filled by direct buffer -> LDS loads: step i
+// computes from buffer i % 3, issues the loads of tile i + 2 (into (i + 2) % 3, last
+// read in step i - 1) during its second half, and reads the first fragments of tile
+// i + 1 in its last sub-step, after a barrier that waits only for the loads of
+// earlier steps.  Code stages and
+// buffer indices are compile-time roles of a three-way unrolled loop, so no
+// register copy ever waits for a load in flight.
+constexpr int NBUF = 3;
+
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_fwd_kernel(
     GemmParams p) {
   __shared__ __attribute__((aligned(16))) char sX[NBUF * TILE_BYTES];
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int tmi, tni;
   tile_coords((p.M + TM - 1) / TM, (p.No + TN - 1) / TN, tmi, tni);
   const int m0 = tmi * TM, n0 = tni * TN;
@@ -295,78 +281,129 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.w.codes, static_cast<uint32_t>(uint64_t(p.No) * K / 2));
   const ConstRsrc rq = make_const_rsrc(p.w.absmax_q, p.w.dq_scale, p.w.dq_offset,
                                        static_cast<uint32_t>(uint64_t(p.No) * K / 64));
-  const int n_base = n0 + wave * 64;
   const int nk = K / TK;
   const int last = nk - 1;
+
+  // Per-lane load offsets; the contraction position enters as the scalar offset.
+  // Rows past M and weight rows past N are clamped to the last valid one: they feed
+  // only outputs that are never stored, and every load stays inside its buffer.
+  // DMA: each wave-wide load writes 1 KB of LDS contiguously (lane l at byte 16 l),
+  // so lane l fetches the chunk that belongs at that swizzled slot: tile row
+  // r = 8 q + l / 8, slot l % 8 holds chunk (l % 8) ^ f(r); wave w issues q = 8 w + i.
+  uint32_t xoff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (wave * 8 + i) * 8 + (lane >> 3);
+    const int row = min(m0 + r, p.M - 1);
+    xoff[i] = (static_cast<uint32_t>(row) * K + ((lane & 7) ^ swz(r)) * 8) * 2;
+  }
+  uint32_t coff[2], boff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = min(n0 + wave * 64 + j * 32 + (lane & 31), p.No - 1);
+    coff[j] = static_cast<uint32_t>(n) * (K / 2) + (lane >> 5) * 16;
+    boff[j] = static_cast<uint32_t>(n) * (K / 64);
+  }
+  auto issue_codes = [&](int kt, int j, CodeStage &cs) {
+    cs.code[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, coff[j], kt / 2, 0));
+    cs.c[j].c8 = __builtin_amdgcn_raw_buffer_load_b8(rq.q8, boff[j], kt / 64, 0);
+    const uint32_t g4 = ((boff[j] + kt / 64) >> 8) * 4u;
+    cs.c[j].s = __builtin_amdgcn_raw_buffer_load_b32(rq.s, g4, 0, 0);
+    cs.c[j].o = __builtin_amdgcn_raw_buffer_load_b32(rq.o, g4, 0, 0);
+  };
+  auto issue_dma = [&](int kt, int h, char *buf) {
+    char *dst = buf + wave * 8 * 1024;
+#pragma unroll
+    for (int i = 4 * h; i < 4 * h + 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)(dst + i * 1024),
+                                               16, xoff[i], kt * 2, 0, 0);
+  };
 
   f32x16_t acc[8][2];
   zero_acc(acc);
 
-  CodeStage cur, nxt, nn;
-  act_dma(rx, m0, p.M, K, 0, sX);
-  act_dma(rx, m0, p.M, K, min(1, last) * TK, sX + TILE_BYTES);
-  code_load_fwd(p, rc, rq, n_base, 0, cur);
-  code_load_fwd(p, rc, rq, n_base, min(1, last) * TK, nxt);
+  CodeStage S0, S1, S2;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    issue_codes(0, h, S0);
+    issue_codes(min(1, last) * TK, h, S1);
+    issue_dma(0, h, sX);
+    issue_dma(min(1, last) * TK, h, sX + TILE_BYTES);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  Planes pl[2];
+  Planes pl[2], pln[2];
   u32x4_t wa[2], xb[8];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    pl[j] = make_planes(const_value(cur.c[j]), p.lvl);
-    wa[j] = lookup8(cur.code[j][0], pl[j]);
+    pl[j] = make_planes(const_value(S0.c[j]), p.lvl);
+    wa[j] = lookup8(S0.code[j][0], pl[j]);
   }
   read_xfrags_fwd(sX, 0, xb);
 
-  // Code stages rotate by register moves (cur <- nxt <- nn), so every iteration is
-  // the same single scheduling region.  All global loads of a step (tile DMA and the
-  // codes two steps ahead) are issued at its start; the wait before the closing
-  // barrier then covers loads that have had the whole step to arrive.
-  for (int it = 0; it < nk; ++it) {
-    const char *sx = sX + (it % NBUF) * TILE_BYTES;
-    const char *sxn = sX + ((it + 1) % NBUF) * TILE_BYTES;
-    char *sxw = sX + ((it + 2) % NBUF) * TILE_BYTES;
-    act_dma(rx, m0, p.M, K, min(it + 2, last) * TK, sxw);
-    code_load_fwd(p, rc, rq, n_base, min(it + 2, last) * TK, nn);
-    __builtin_amdgcn_sched_barrier(0);
-    Planes pln[2];
+  auto mfmas = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(wa[j], xb[i], acc[i][j]);
+  };
+
+  // One contraction step; B is the LDS buffer of the step's tile (it % 3).
+  auto step = [&](auto B, int it, CodeStage &cur, CodeStage &nxt, CodeStage &nn) {
+    constexpr int b = decltype(B)::v;
+    const char *sx = sX + b * TILE_BYTES;
+    const char *sxn = sX + ((b + 1) % NBUF) * TILE_BYTES;
+    char *sxw = sX + ((b + 2) % NBUF) * TILE_BYTES;
+    const int ktn = min(it + 2, last) * TK;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4_t wan[2], xbn[8];
-      if (s < 3) {
+      if (s < 2) issue_codes(ktn, s, nn);  // codes first: they are needed soonest
+      if (s == 2) issue_dma(ktn, 0, sxw);
+      if (s == 3) {
+        // tile it + 1 (issued a step ago) must have landed for every wave, and no wave
+        // may still read the buffer that the next step's loads will overwrite
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS_BEFORE_BARRIER) : "memory");
+        issue_dma(ktn, 1, sxw);
+        read_xfrags_fwd(sxn, 0, xbn);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) wan[j] = lookup8(nxt.code[j][0], pln[j]);
+      } else {
         read_xfrags_fwd(sx, s + 1, xbn);
 #pragma unroll
         for (int j = 0; j < 2; ++j) wan[j] = lookup8(cur.code[j][s + 1], pl[j]);
-      } else {
-        read_xfrags_fwd(sxn, 0, xbn);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          pln[j] = make_planes(const_value(nxt.c[j]), p.lvl);
-          wan[j] = lookup8(nxt.code[j][0], pln[j]);
-        }
+        // block constants of the next step, one row per sub-step
+        if (s == 1) pln[0] = make_planes(const_value(nxt.c[0]), p.lvl);
+        if (s == 2) pln[1] = make_planes(const_value(nxt.c[1]), p.lvl);
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(wa[j], xb[i], acc[i][j]);
+      mfmas();
 #pragma unroll
       for (int j = 0; j < 2; ++j) wa[j] = wan[j];
 #pragma unroll
       for (int i = 0; i < 8; ++i) xb[i] = xbn[i];
-      if (s < 3)
-        substep_schedule<4>();
+      if (s == 0)
+        substep_schedule<4, 4>();
+      else if (s == 3)
+        substep_schedule<3, 4>();
       else
-        substep_schedule<8>();
+        substep_schedule<6, 4>();
       __builtin_amdgcn_sched_barrier(0);
     }
-    cur = nxt;
-    nxt = nn;
 #pragma unroll
     for (int j = 0; j < 2; ++j) pl[j] = pln[j];
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this step's loads have landed
-    __syncthreads();
+  };
+
+  int it = 0;
+  for (; it + 3 <= nk; it += 3) {
+    step(Ic<0>{}, it, S0, S1, S2);
+    step(Ic<1>{}, it + 1, S1, S2, S0);
+    step(Ic<2>{}, it + 2, S2, S0, S1);
   }
+  if (it < nk) step(Ic<0>{}, it, S0, S1, S2);
+  if (it + 1 < nk) step(Ic<1>{}, it + 1, S1, S2, S0);
+  // drain the clamped prefetches of the last steps before the epilogue
+  __builtin_amdgcn_s_waitcnt(0);
   if (p.r > 0) lora_steps(p, m0, n0, acc);
   store_out(p, m0, n0, acc);
 }
