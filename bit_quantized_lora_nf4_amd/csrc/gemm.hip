@@ -533,6 +533,263 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   store_out(p, m0, k0, acc);
 }
 
+// Pipelined dX for dY rows of whole 16-byte chunks (N % 8 == 0).
+//
+// Layout: wave w owns tokens m0 + 64 w .. + 64 (two 32-token MFMA tiles) and all 256
+// output columns of the block (eight 32-column tiles), acc[i][j].  Its dY fragments
+// are private, so they come straight from global memory into registers (lane l:
+// token 32 i + l % 32, 8 contraction rows at 16 s + 8 (l / 32)), one step ahead.
+// The decoded weight tile (64 rows x 256 columns) is shared by the four waves
+// through LDS and read with the transposing ds_read_b64_tr_b16.  During step i
+// every thread decodes its 64 weights of step i + 1 (one block constant, eight
+// lookups) into the other of two weight tiles, spread over the first three
+// sub-steps; the single barrier per step, before the last sub-step, publishes that
+// tile, whose first fragments the last sub-step then reads.  dY columns past N read
+// as zero and weight rows past N decode to zero, so the contraction tail adds nothing.
+
+// Weight-side fragment for contraction sub-step s and output-column tile j (32
+// columns) of the block: two transposing reads of 4 rows each.  Within a 16-lane
+// group, lane i reads row nbase + i / 4 at column cbase + 4 (i % 4) and receives
+// column cbase + i of rows nbase .. nbase + 3.
+__device__ __forceinline__ u32x4_t wfrag_tr_all(const char *sw, int s, int j) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int col = j * 32 + (g & 1) * 16 + 4 * (i & 3);
+  u32x4_t r;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int n = 16 * s + 8 * (g >> 1) + 4 * e + (i >> 2);
+    const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16_t *)(sw + wtile_off(n, col)));
+    const u32x2_t u = __builtin_bit_cast(u32x2_t, v);
+    r[2 * e] = u[0];
+    r[2 * e + 1] = u[1];
+  }
+  return r;
+}
+
+// Epilogue of the token-split layout: lane holds token m0 + 64 w + 32 i + l % 32 and
+// output columns c0 + 32 j + 8 g + 4 (l / 32) + 0..3 for g = 0..3.
+__device__ __forceinline__ void store_out_tok(const GemmParams &p, int m0, int c0,
+                                              const f32x16_t (&acc)[2][8]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool vec = (p.No % 4) == 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + wave * 64 + i * 32 + (lane & 31);
+    if (m >= p.M) continue;
+    uint16_t *row = p.C + static_cast<int64_t>(m) * p.No;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = c0 + j * 32 + g * 8 + (lane >> 5) * 4;
+        const f32x16_t &a = acc[i][j];
+        if (vec) {
+          if (col < p.No) {
+            u32x2_t o = {pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+            *reinterpret_cast<u32x2_t *>(row + col) = o;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < p.No) row[col + e] = to_bf16(a[4 * g + e]);
+        }
+      }
+  }
+}
+
+// LoRA steps of the token-split layout: acc[i][j] += A2 rows (tokens) x B2 rows
+// (output columns), rank in steps of 16.
+__device__ __forceinline__ void lora_steps_tok(const GemmParams &p, int m0, int c0,
+                                               f32x16_t (&acc)[2][8]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = p.r;
+  const bool vec = (r % 8) == 0;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A2, static_cast<uint32_t>(uint64_t(p.M) * r * 2));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B2, static_cast<uint32_t>(uint64_t(p.No) * r * 2));
+  auto frag = [&](__amdgpu_buffer_rsrc_t rs, const uint16_t *base, int row, int rows, int j0) {
+    if (vec) return buf_load16(rs, (row < rows && j0 < r) ? (static_cast<uint32_t>(row) * r + j0) * 2 : kOOB);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (row < rows)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t lo = (j0 + e < r) ? base[static_cast<int64_t>(row) * r + j0 + e] : 0u;
+        const uint32_t hi = (j0 + e + 1 < r) ? base[static_cast<int64_t>(row) * r + j0 + e + 1] : 0u;
+        v[e / 2] = lo | (hi << 16);
+      }
+    return v;
+  };
+  for (int rk = 0; rk < r; rk += 16) {
+    const int j0 = rk + (lane >> 5) * 8;
+    u32x4_t wa[8], vb[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wa[j] = frag(rb, p.B2, c0 + j * 32 + (lane & 31), p.No, j0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) vb[i] = frag(ra, p.A2, m0 + wave * 64 + i * 32 + (lane & 31), p.M, j0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = mfma32x32x16(wa[j], vb[i], acc[i][j]);
+  }
+}
+
+template <int NR, int NV, int NG, int NW>
+__device__ __forceinline__ void dx_schedule() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS reads
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (NG > 0)
+      if (q % (16 / NG) == 0) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+    if constexpr (NW > 0)
+      if (q % (16 / NW) == (16 / NW) - 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+  }
+}
+
+// dY fragments of one contraction step: [sub-step][token tile].
+struct YStage {
+  u32x4_t v[4][2];
+};
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dx_pipe_kernel(
+    GemmParams p) {
+  __shared__ __attribute__((aligned(16))) char sW[2 * TILE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tmi, tni;
+  tile_coords((p.M + TM - 1) / TM, (p.No + TN - 1) / TN, tmi, tni);
+  const int m0 = tmi * TM, k0 = tni * TN;
+
+  const int N = p.Kc, K = p.No;  // contraction over weight rows, outputs are weight columns
+  const __amdgpu_buffer_rsrc_t rdy = make_rsrc(p.A, static_cast<uint32_t>(uint64_t(p.M) * N * 2));
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.w.codes, static_cast<uint32_t>(uint64_t(N) * K / 2));
+  const ConstRsrc rq = make_const_rsrc(p.w.absmax_q, p.w.dq_scale, p.w.dq_offset,
+                                       static_cast<uint32_t>(uint64_t(N) * K / 64));
+  const int nk = (N + TK - 1) / TK;
+  const int last = nk - 1;
+
+  // dY rows of this lane (byte offsets, kOOB past M) and its contraction half
+  uint32_t yrow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + wave * 64 + i * 32 + (lane & 31);
+    yrow[i] = m < p.M ? static_cast<uint32_t>(m) * N * 2 : kOOB;
+  }
+  const int yh = (lane >> 5) * 8;
+  auto issue_y = [&](int kt, YStage &ys) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int n = kt + 16 * s + yh;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        ys.v[s][i] = buf_load16(rdy, (yrow[i] != kOOB && n < N) ? yrow[i] + n * 2 : kOOB);
+    }
+  };
+  // Weight decode: thread t owns tile row t % 64 and columns 64 (t / 64) .. + 64.
+  const int dn = tid & 63, dc = (tid >> 6) * 64;
+  const bool col_ok = k0 + dc < K;
+  auto issue_codes = [&](int kt, CodeStageB &cs) {
+    const int n = kt + dn;
+    const bool ok = col_ok && n < N;
+    const uint32_t off = static_cast<uint32_t>(n) * (K / 2) + (k0 + dc) / 2;
+    cs.code[0] = buf_load16(rc, ok ? off : kOOB);
+    cs.code[1] = buf_load16(rc, ok ? off + 16 : kOOB);
+    cs.c = fetch_constant(rq, static_cast<uint32_t>(n) * (K / 64) + (k0 + dc) / 64, ok);
+  };
+  // lookups q0 .. q1 - 1 of the eight (q = 4 h + i: 16-byte code half h, word i)
+  auto decode_part = [&](const CodeStageB &cs, const Planes &pd, char *sw, int q0, int q1) {
+#pragma unroll
+    for (int q = q0; q < q1; ++q)
+      *reinterpret_cast<u32x4_t *>(sw + wtile_off(dn, dc + q * 8)) = lookup8(cs.code[q >> 2][q & 3], pd);
+  };
+
+  f32x16_t acc[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  CodeStageB S0, S1;
+  YStage Y0, Y1;
+  issue_codes(0, S0);
+  issue_codes(min(1, last) * TK, S1);
+  issue_y(0, Y0);
+  {
+    const Planes pd = make_planes(const_value(S0.c), p.lvl);
+    decode_part(S0, pd, sW, 0, 8);
+  }
+  __syncthreads();
+
+  u32x4_t wa[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wa[j] = wfrag_tr_all(sW, 0, j);
+
+  // Step it: weight tile B2 = it % 2 and dY stage `yc` are this step's; `yn`
+  // receives the dY fragments of step it + 1, `dec` holds the codes of step it + 1
+  // (decoded now), `ld` receives those of step it + 2.
+  auto step = [&](auto B2, int it, YStage &yc, YStage &yn, CodeStageB &dec, CodeStageB &ld) {
+    constexpr int b2 = decltype(B2)::v;
+    const char *sw = sW + b2 * TILE_BYTES;
+    char *swn = sW + (1 - b2) * TILE_BYTES;
+    const int kt1 = min(it + 1, last) * TK, kt2 = min(it + 2, last) * TK;
+    Planes pd;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t wan[8];
+      if (s == 0) {
+        pd = make_planes(const_value(dec.c), p.lvl);
+        issue_y(kt1, yn);
+        decode_part(dec, pd, swn, 0, 2);
+      }
+      if (s == 1) {
+        issue_codes(kt2, ld);
+        decode_part(dec, pd, swn, 2, 5);
+      }
+      if (s == 2) decode_part(dec, pd, swn, 5, 8);
+      if (s == 3) {
+        // every thread's part of the next weight tile is written; no wave still
+        // reads the tile that the next step overwrites
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wan[j] = wfrag_tr_all(swn, 0, j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wan[j] = wfrag_tr_all(sw, s + 1, j);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma32x32x16(wa[j], yc.v[s][i], acc[i][j]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wa[j] = wan[j];
+      if (s == 0)
+        dx_schedule<16, 5, 8, 2>();
+      else if (s == 1)
+        dx_schedule<16, 4, 5, 3>();
+      else if (s == 2)
+        dx_schedule<16, 4, 0, 3>();
+      else
+        dx_schedule<16, 1, 0, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // two steps per trip (dY stages, code stages and weight tiles alternate)
+  int it = 0;
+  for (; it + 2 <= nk; it += 2) {
+    step(Ic<0>{}, it, Y0, Y1, S1, S0);
+    step(Ic<1>{}, it + 1, Y1, Y0, S0, S1);
+  }
+  if (it < nk) step(Ic<0>{}, it, Y0, Y1, S1, S0);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (p.r > 0) lora_steps_tok(p, m0, k0, acc);
+  store_out_tok(p, m0, k0, acc);
+}
+
 bool fits_32bit(int64_t M, int64_t N, int64_t K, int r) {
   const uint64_t lim = 0xFFFFFFF0ull;
   return uint64_t(M) * K * 2 <= lim && uint64_t(M) * N * 2 <= lim && uint64_t(N) * K / 2 <= lim &&
@@ -565,7 +822,7 @@ hipError_t launch_gemm_dx(const WeightView &w, const uint16_t *dY, int64_t M, co
   if (!fits_32bit(M, w.n_rows, w.n_cols, r) || M > 0x7fffffff) return hipErrorInvalidValue;
   const GemmParams p = make_params(dY, w, V, At, dX, M, w.n_cols, w.n_rows, r);
   if (w.n_rows % 8 == 0)
-    hipLaunchKernelGGL(gemm_dx_kernel<true>, dim3(grid_size(M, w.n_cols)), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL(gemm_dx_pipe_kernel, dim3(grid_size(M, w.n_cols)), dim3(NT), 0, stream, p);
   else
     hipLaunchKernelGGL(gemm_dx_kernel<false>, dim3(grid_size(M, w.n_cols)), dim3(NT), 0, stream, p);
   return hipGetLastError();
