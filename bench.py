@@ -187,35 +187,86 @@ def measure_m1(torch, q, synth, gc, ev, min_bytes=600 << 20, calls=200):
     return out
 
 
-def cpu_baseline(synth, sample_m=4096):
-    """The oracle (float64 numpy) on a bounded sample of the workload: each of the three
-    linears with the first `sample_m` tokens: decode of W' from the stored format,
-    forward and backward.  The oracle's own quantization of W is not timed."""
+def cpu_baseline(synth, sample_m=4096, min_seconds=10.0, max_passes=20):
+    """The oracle (float64 numpy) on a bounded sample of the workload: the three linears
+    with the first `sample_m` tokens (decode of W' from the stored format, forward and
+    backward), repeated until at least `min_seconds` of CPU work.  The oracle's own
+    quantization of W is done once, untimed."""
     import numpy as np
     from oracle import linear, nf4
     wl = synth.WORKLOADS[2]
-    dt = fl = 0.0
+    cases = []
     for i, (K, N) in enumerate(wl.linears):
         d = synth.workload_linear(2, i)
         qw = nf4.quantize_nf4(synth.bf16_bits_to_f32(d["W"]))
         f = lambda k: synth.bf16_bits_to_f32(d[k]).astype(np.float64)  # noqa: E731
-        X, A, B, dY = f("X")[:sample_m], f("A"), f("B"), f("dY")[:sample_m]
+        cases.append((K, N, qw, f("X")[:sample_m], f("A"), f("B"), f("dY")[:sample_m]))
         del d
-        t0 = time.perf_counter()
-        Wd = nf4.dequantize_bf16(qw)
-        linear.forward(X, Wd, A, B, wl.alpha, wl.r)
-        linear.backward(dY, X, Wd, A, B, wl.alpha, wl.r)
-        dt += time.perf_counter() - t0
-        fl += linear_flops(sample_m, K, N, wl.r)
+    dt = fl = 0.0
+    passes = 0
+    while passes < max_passes and (passes == 0 or dt < min_seconds):
+        for K, N, qw, X, A, B, dY in cases:
+            t0 = time.perf_counter()
+            Wd = nf4.dequantize_bf16(qw)
+            linear.forward(X, Wd, A, B, wl.alpha, wl.r)
+            linear.backward(dY, X, Wd, A, B, wl.alpha, wl.r)
+            dt += time.perf_counter() - t0
+            fl += linear_flops(sample_m, K, N, wl.r)
+        passes += 1
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count()
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"the three linears of the workload with the first {sample_m} of 4096 tokens: "
-                      "decode W' + forward + backward in float64 numpy (quantization untimed)"}
+            "seconds": round(dt, 2), "passes": passes,
+            "sample": f"the three linears of the workload with the first {sample_m} of 4096 tokens, "
+                      f"{passes} passes: decode W' + forward + backward in float64 numpy "
+                      "(quantization untimed)"}
+
+
+GEMM_SOURCES = ("bit_quantized_lora_nf4_amd/csrc/gemm.hip", "bit_quantized_lora_nf4_amd/csrc/device_common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nf4_workload2_traffic.md")
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per fused-GEMM launch from the committed counter summary, or None when
+    the kernels have changed since the counters were taken."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    kv = {}
+    for line in lines:
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            kv[k.strip()] = v.strip().strip("`")
+    if kv.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(torch, mib=1024, reps=5):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib * (1 << 20) // 2
+    src = torch.randn(n, device="cuda").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 2, "copy_bytes_written": n * 2, "reps": reps}), flush=True)
 
 
 def main():
@@ -225,6 +276,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the M=1 and quantize legs")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; --gpus must be 1 "
@@ -232,9 +285,12 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     import bit_quantized_lora_nf4_amd as q
     import synth
-    from tests import gpu_cases as gc
+    from synth import device as gc
 
     print("bench: setting up workload 2 (3 linears, M=4096)", file=sys.stderr, flush=True)
     wl, M, L = setup_workload2(torch, q, synth, gc)
@@ -271,7 +327,8 @@ def main():
         per[key][2] += 1
     achieved = g_fl / (g_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel": "fused NF4-decode GEMM (forward and dX launches)",
             "per_launch_flops": "fwd 2MNK + 2MNr; dX 2MNK + 2MKr",
             "avg_launch_us": round(g_ms * 1e3 / max(1, len(rec)), 2),

@@ -7,21 +7,12 @@ import synth
 from oracle import linear, nf4
 
 
+from synth.device import dev_bf16, dev_f32, dev_weight  # noqa: F401
+
+
 def torch_mod():
     import torch
     return torch
-
-
-def dev_bf16(bits):
-    """uint16 bf16 bit patterns (numpy) -> bf16 CUDA tensor."""
-    torch = torch_mod()
-    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
-    return t.view(torch.bfloat16).cuda()
-
-
-def dev_f32(a):
-    torch = torch_mod()
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
 def host_bits(t):
@@ -38,11 +29,6 @@ def weight_f32(d):
     """The weight of a case as float32 values (fp32 input, or bf16 widened)."""
     W = d["W"]
     return W if W.dtype == np.float32 else synth.bf16_bits_to_f32(W)
-
-
-def dev_weight(d):
-    W = d["W"]
-    return dev_f32(W) if W.dtype == np.float32 else dev_bf16(W)
 
 
 def oracle_group_slice(Wf, g0, g1):
