@@ -120,7 +120,7 @@ def linear_fwd(qw, X, A=None, B=None, alpha=16.0, save_u=True, Y=None, U=None, w
         Y = torch.empty((M, qw.n_rows), dtype=torch.bfloat16, device=dev)
     if r and save_u and U is None:
         U = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
-    if r and ws is None:
+    if ws is None and qlora_workspace_bytes(0, M, K, qw.n_rows, r) > 0:
         ws = workspace(0, M, K, qw.n_rows, r, dev)
     _lib.check(qlora_linear_fwd(qw.descriptor(), X.data_ptr(), M, _ptr(A), _ptr(B), r, float(alpha),
                                 Y.data_ptr(), _ptr(U) if save_u else None, _ptr(ws),

@@ -116,9 +116,15 @@ qlora::WeightView view(const qlora_nf4_weight *w) {
 struct FwdLayout {
   size_t u = 0, part = 0, total = 0;
 };
-// U_s (when the caller does not keep it) then the fp32 partial sums of lora_down.
-FwdLayout fwd_layout(int64_t M, int64_t K, int r, bool need_u) {
+// M <= 16: the fp32 partial sums of the GEMV (weight stream and LoRA down-projection).
+// Otherwise U_s (when the caller does not keep it) then the fp32 partial sums of
+// lora_down; nothing when r = 0.
+FwdLayout fwd_layout(int64_t M, int64_t K, int64_t N, int r, bool need_u) {
   FwdLayout L;
+  if (M <= 16) {
+    L.total = qlora::gemv_workspace(M, K, N, r);
+    return L;
+  }
   if (r == 0) return L;
   size_t off = 0;
   L.u = off;
@@ -194,7 +200,7 @@ int qlora_nf4_sizes(int64_t n_rows, int64_t n_cols, size_t *code_bytes, int64_t 
 
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int r) {
   if (M < 1 || K < 1 || N < 1 || K % 64 != 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
-  if (op == 0) return fwd_layout(M, K, r, true).total;
+  if (op == 0) return fwd_layout(M, K, N, r, true).total;
   if (op == 1) return bwd_layout(M, K, N, r).total;
   return 0;
 }
@@ -246,7 +252,7 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, co
       (U_saved && !aligned16(U_saved)))
     return fail(QLORA_ERR_ALIGN, "linear_fwd: tensors must be 16-byte aligned");
   const int64_t K = w->n_cols;
-  const FwdLayout L = fwd_layout(M, K, r, !U_saved);
+  const FwdLayout L = fwd_layout(M, K, w->n_rows, r, !U_saved);
   const bool need_ws = L.total > 0;
   if (need_ws && (!workspace || workspace_bytes < L.total))
     return fail(QLORA_ERR_WORKSPACE, "linear_fwd: workspace of %zu bytes needed, %zu given", L.total,
@@ -256,19 +262,26 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, co
   s = check_device();
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const qlora::WeightView wv = view(w);
+  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  if (M <= 16) {
+    if (!qlora::gemv_supported(wv, M, r))
+      return fail(QLORA_ERR_SHAPE, "linear_fwd: shape exceeds 32-bit buffer offsets");
+    s = launched(timed_launch(st, [&] { return qlora::launch_gemv_stream(wv, X, M, A, r, workspace, st); }),
+                 "gemv_stream");
+    if (s != QLORA_OK) return s;
+    return launched(qlora::launch_gemv_finalize(wv, M, B, r, scale, Y, U_saved, workspace, st),
+                    "gemv_finalize");
+  }
   uint16_t *U = nullptr;
   if (r > 0) {
     char *ws = static_cast<char *>(workspace);
     U = U_saved ? U_saved : reinterpret_cast<uint16_t *>(ws + L.u);
-    s = launched(qlora::launch_lora_down(X, M, K, A, r, alpha / static_cast<float>(r), U,
+    s = launched(qlora::launch_lora_down(X, M, K, A, r, scale, U,
                                          reinterpret_cast<float *>(ws + L.part), st),
                  "lora_down");
     if (s != QLORA_OK) return s;
   }
-  const qlora::WeightView wv = view(w);
-  if (M <= 16)
-    return launched(timed_launch(st, [&] { return qlora::launch_gemv_fwd(wv, X, M, U, B, r, Y, st); }),
-                    "gemv_fwd");
   return launched(timed_launch(st, [&] { return qlora::launch_gemm_fwd(wv, X, M, U, B, r, Y, st); }),
                   "gemm_fwd");
 }

@@ -1,10 +1,28 @@
 // Small-M forward (M <= 16): a bandwidth-oriented dequant-GEMV (gfx950).
 //
-// Y[m, n] = bf16(sum_k X[m, k] W'[n, k] + sum_j U[m, j] Bl[n, j]) for M <= 16.  At
-// such M the layer is bound by the weight stream (0.516 B per weight), so each
-// wave streams one weight row with 16-byte coalesced loads of packed codes,
-// decodes them to W' = bf16_rne(q[code] * c') ([Digest] "数学公式与关键细节"
-// item 3) and accumulates in fp32; a wave reduction finishes the row.
+// Y[m, n] = bf16(sum_k X[m, k] W'[n, k] + sum_j U_s[m, j] Bl[n, j]),
+// U_s = bf16(scale * X . A^T)  ([Paper note] "关键设计 3"; [Repro] "LoRA 的公式和张量形状").
+//
+// At such M the layer is bound by the weight stream (0.516 B per weight), so the work
+// is cut into many independent pieces, each of which issues all of its loads at once:
+//
+//   stream kernel   workgroup (row group g, contraction slice s): 64 weight rows x
+//                   1024 columns.  The slice of X (M rows, pre-permuted, see below) is
+//                   staged in LDS once; each wave owns 16 rows, and lane l decodes the
+//                   whole 64-weight blocks s * 16 + 4 i + l / 16 (i = 0..3) of row
+//                   l % 16: one block constant, 32 bytes of codes, eight register
+//                   lookups ([Digest] "数学公式与关键细节" item 3: w' = bf16(q[code] c')).
+//                   The dot products run on 16x16x32 bf16 MFMA (tokens padded to 16),
+//                   fp32 partial sums P[s][n][m] go to the workspace.  Extra workgroups
+//                   of the same launch compute the LoRA down-projection partials
+//                   UP[s][m][j] over the same slices.
+//   finalize        per weight row: U_s from UP (summed in slice order, scaled, rounded
+//                   once), then Y = bf16(sum_s P + U_s . Bl^T), one rounding.
+//
+// Decoded weights come out of the byte-permute lookup as bf16 pairs (e0,e2), (e4,e6),
+// (e1,e3), (e5,e7) of each 8-element group; the X slice is staged with the same
+// permutation inside every 8-element group, so the contraction pairs the right
+// elements without re-interleaving the decoded weights.
 
 #include "device_common.h"
 #include "qlora_internal.h"
@@ -12,75 +30,361 @@
 namespace qlora {
 namespace {
 
-constexpr int NT = 256;
+constexpr int GT = 256;                  // threads per workgroup (4 waves)
+constexpr int GROWS = 64;                // weight rows per workgroup, 16 per wave
+#ifndef GEMV_GIT
+#define GEMV_GIT 4
+#endif
+constexpr int GIT = GEMV_GIT;            // 64-blocks per lane and workgroup
+constexpr int GSLICE = 4 * GIT * 64;     // contraction elements per workgroup (1024)
+constexpr int XPITCH = GSLICE * 2 + 16;  // bytes per staged token row (padded)
+constexpr int GMAXM = 16;
 
-__global__ __launch_bounds__(NT) void gemv_kernel(WeightView w, const uint16_t *__restrict__ X,
-                                                  int M, const uint16_t *__restrict__ U,
-                                                  const uint16_t *__restrict__ Bl, int r,
-                                                  uint16_t *__restrict__ Y, LevelTable lvl) {
-  __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = lvl.q[threadIdx.x];
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  const int64_t N = w.n_rows, K = w.n_cols;
-  if (n >= N) return;
-  float acc[16];
+struct GemvArgs {
+  WeightView w;
+  const uint16_t *X;  // [M, K]
+  const uint16_t *A;  // [r, K] (unused when r = 0)
+  float *P;           // [S][N][M]
+  float *UP;          // [S][M][r]
+  int M, r, S;
+  LevelTable lvl;
+};
+
+// Eight codes (element e in bits 4e..4e+3 of w) -> bf16 pairs (e0,e2), (e4,e6),
+// (e1,e3), (e5,e7): the lookup of lookup8 without its final re-interleave.
+__device__ __forceinline__ u32x4_t lookup8_pairs(uint32_t w, const Planes &P) {
+  const uint32_t se = w & 0x07070707u;
+  const uint32_t so = (w >> 4) & 0x07070707u;
+  const uint32_t me = __builtin_amdgcn_perm(w << 12, w << 4, 0x090B080Au);
+  const uint32_t mo = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
+  const uint32_t Le = bitsel(me, __builtin_amdgcn_perm(P.L[3], P.L[2], se),
+                             __builtin_amdgcn_perm(P.L[1], P.L[0], se));
+  const uint32_t He = bitsel(me, __builtin_amdgcn_perm(P.H[3], P.H[2], se),
+                             __builtin_amdgcn_perm(P.H[1], P.H[0], se));
+  const uint32_t Lo = bitsel(mo, __builtin_amdgcn_perm(P.L[3], P.L[2], so),
+                             __builtin_amdgcn_perm(P.L[1], P.L[0], so));
+  const uint32_t Ho = bitsel(mo, __builtin_amdgcn_perm(P.H[3], P.H[2], so),
+                             __builtin_amdgcn_perm(P.H[1], P.H[0], so));
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_perm(He, Le, 0x05010400u);
+  r[1] = __builtin_amdgcn_perm(He, Le, 0x07030602u);
+  r[2] = __builtin_amdgcn_perm(Ho, Lo, 0x05010400u);
+  r[3] = __builtin_amdgcn_perm(Ho, Lo, 0x07030602u);
+  return r;
+}
+
+// An 8-element bf16 group x0..x7 in the element order of lookup8_pairs.
+__device__ __forceinline__ u32x4_t permute8(u32x4_t d) {
+  return u32x4_t{pack_lo(d[0], d[1]), pack_lo(d[2], d[3]), pack_hi(d[0], d[1]), pack_hi(d[2], d[3])};
+}
+
+// LDS of the stream kernel (one dynamic object): per wave its 16 rows x 512 bytes of
+// codes (16-byte chunk cr of row r at slot cr ^ (r & 15)), per wave 16 rows x 16
+// int8 block constants, then the staged X slice (M rows of XPITCH bytes).
+constexpr int CROW = 4 * GIT * 32;   // code bytes per row and slice (512)
+constexpr int WCODE = 16 * CROW;     // code bytes per wave (8 KB)
+constexpr int SC_BYTES = 4 * WCODE;  // 32 KB
+constexpr int SQ_BYTES = 4 * 256;    // 1 KB
+int gemv_xl(int M) { return M <= 2 ? 1 : M <= 4 ? 2 : M <= 8 ? 4 : 8; }
+// staged X rows = XL * 256 * 8 / GSLICE = 2 XL (rows past M hold zeros)
+size_t gemv_lds_bytes(int M) {
+  return SC_BYTES + SQ_BYTES + static_cast<size_t>(2 * gemv_xl(M)) * XPITCH;
+}
+
+// XL: 16-byte X loads per thread (M * 128 / 256 rounded up to a power of two);
+// C8W: the rows' int8 constants are dword aligned (K % 256 == 0).
+template <int XL, bool C8W>
+__global__ __launch_bounds__(GT) void gemv_stream_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char *const sc = lds;
+  char *const sq = lds + SC_BYTES;
+  char *const sx = lds + SC_BYTES + SQ_BYTES;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = static_cast<int>(a.w.n_rows), K = static_cast<int>(a.w.n_cols), KB = K / 64;
+  const int lora_wgs = a.r > 0 ? a.S : 0;
+  const int bid = blockIdx.x;
+  const bool lora = bid < lora_wgs;
+  const int s = lora ? bid : (bid - lora_wgs) % a.S;
+  const int rg = lora ? 0 : (bid - lora_wgs) / a.S;
+  const int k0 = s * GSLICE;
+  const int ml = lane & 15, g = lane >> 4;
+  const int row0 = rg * GROWS + wave * 16;  // first weight row of this wave
+
+  // ---- issue every global load of the workgroup up front ----
+  // X slice, tokens < M only (16-byte chunks; columns past K read as zero)
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, static_cast<uint32_t>(a.M) * K * 2);
+  u32x4_t xs[XL];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) acc[m] = 0.0f;
-  const int64_t chunks = K / 32;  // 16 bytes of codes = 32 weights
-  const u32x4_t *crow = reinterpret_cast<const u32x4_t *>(w.codes + n * (K / 2));
-  for (int64_t ch = lane; ch < chunks; ch += 64) {
-    const u32x4_t code = crow[ch];
-    const float c = decode_constant(w.absmax_q, w.dq_scale, w.dq_offset, (n * K) / 64 + ch / 2);
-    float v[32];
+  for (int j = 0; j < XL; ++j) {
+    const int c = tid + j * GT;
+    const int m = c / (GSLICE / 8), k = k0 + (c % (GSLICE / 8)) * 8;
+    xs[j] = buf_load16(rx, (m < a.M && k < K) ? (static_cast<uint32_t>(m) * K + k) * 2 : kOOB);
+  }
+  uint32_t c8w = 0, sv[2] = {0u, 0u}, ov[2] = {0u, 0u};
+  uint8_t c8b[4] = {0, 0, 0, 0};
+  int gfirst = 0;
+  {
+    // Straight-line for every workgroup (the LoRA ones read nothing: all offsets out of
+    // range), so that the compiler's waits stay exact counts.  Order: constants, then
+    // the codes block group by block group, so that decoding can follow the arrivals.
+    const int nlim = lora ? 0 : N;
+    const ConstRsrc rq = make_const_rsrc(a.w.absmax_q, a.w.dq_scale, a.w.dq_offset,
+                                         static_cast<uint32_t>(uint64_t(N) * KB));
+    // group scale and offset: the slice of one row spans at most two groups
+    {
+      const int n = row0 + ml;
+      const uint32_t bfirst = static_cast<uint32_t>(n) * KB + s * 16;
+      gfirst = static_cast<int>(bfirst >> 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4_t d = decode8(code[i], c, lut);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        v[i * 8 + 2 * p] = bf16_lo(d[p]);
-        v[i * 8 + 2 * p + 1] = bf16_hi(d[p]);
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t og = n < nlim ? (bfirst / 256 + e) * 4u : kOOB;
+        sv[e] = __builtin_amdgcn_raw_buffer_load_b32(rq.s, og, 0, 0);
+        ov[e] = __builtin_amdgcn_raw_buffer_load_b32(rq.o, og, 0, 0);
       }
     }
+    // int8 constants: lane l loads blocks s * 16 + 4 (l % 4) .. + 3 of row l / 4
+    {
+      const int n = row0 + (lane >> 2);
+      const uint32_t b = static_cast<uint32_t>(n) * KB + s * 16 + 4 * (lane & 3);
+      if constexpr (C8W) {
+        c8w = __builtin_amdgcn_raw_buffer_load_b32(rq.q8, n < nlim ? b : kOOB, 0, 0);
+      } else {  // rows not dword aligned: four byte loads, stored to LDS one by one
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      if (m >= M) break;
-      const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(X + m * K + ch * 32);
-      float s = acc[m];
+        for (int e = 0; e < 4; ++e) c8b[e] = __builtin_amdgcn_raw_buffer_load_b8(rq.q8, n < nlim ? b + e : kOOB, 0, 0);
+      }
+    }
+    // codes: for block group i (blocks 4 i .. 4 i + 3 of the slice, 128 bytes per row)
+    // two 1 KB direct-to-LDS loads of 8 rows each; lane l fills slot l % 8 of row
+    // 8 h + l / 8 with the row's 16-byte chunk (l % 8) ^ f(row), f(r) = (r / 2) % 8
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.w.codes, static_cast<uint32_t>(uint64_t(N) * K / 2));
+    char *const wc = sc + wave * WCODE;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4_t xv = xr[q];
+    for (int i = 0; i < GIT; ++i)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          s = __builtin_fmaf(bf16_lo(xv[p]), v[q * 8 + 2 * p], s);
-          s = __builtin_fmaf(bf16_hi(xv[p]), v[q * 8 + 2 * p + 1], s);
+      for (int h = 0; h < 2; ++h) {
+        const int rl = 8 * h + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((rl >> 1) & 7);
+        const int n = row0 + rl;
+        const int kbyte = s * CROW + i * 128 + chunk * 16;
+        const uint32_t off = (n < nlim && kbyte < K / 2) ? static_cast<uint32_t>(n) * (K / 2) + kbyte : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rc, (__attribute__((address_space(3))) void *)(wc + i * 2048 + h * 1024), 16, off, 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order that the waits below count on
+  }
+  // ---- stage X (permuted per 8-element group) and the int8 constants in LDS ----
+#pragma unroll
+  for (int j = 0; j < XL; ++j) {  // staged rows past M (up to the power of two) are zero
+    const int c = tid + j * GT;
+    const int m = c / (GSLICE / 8), q = c % (GSLICE / 8);
+    *reinterpret_cast<u32x4_t *>(sx + m * XPITCH + q * 16) = permute8(xs[j]);
+  }
+  if constexpr (C8W) {
+    *reinterpret_cast<uint32_t *>(sq + wave * 256 + lane * 4) = c8w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sq[wave * 256 + lane * 4 + e] = static_cast<char>(c8b[e]);
+  }
+  // the X slice is shared by the four waves; the codes are per wave and are waited
+  // for block group by block group below
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  const int xrow = ml < a.M ? ml : a.M - 1;  // tokens past M only feed unused outputs
+  auto xfrag = [&](int kk) {  // B operand: token xrow, 8 elements at slice column kk
+    return *reinterpret_cast<const u32x4_t *>(sx + xrow * XPITCH + kk * 2);
+  };
+
+  if (!lora) {
+    // ---- weight stream: lane = (row ml of this wave's 16, lane group g) ----
+    const char *const wc = sc + wave * WCODE + ml * 128;
+    const u32x4_t q8 = *reinterpret_cast<const u32x4_t *>(sq + wave * 256 + ml * 16);
+    const int n = row0 + ml;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < GIT; ++i) {
+      // block group i of this wave has landed: 2 (GIT - 1 - i) code loads remain
+      if (i == 0) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      if (i == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      if (i == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      if (i == 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const int blk = 4 * i + g;  // block of the slice
+      u32x4_t code[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        code[h] = *reinterpret_cast<const u32x4_t *>(wc + i * 2048 + (((2 * g + h) ^ ((ml >> 1) & 7)) << 4));
+      const int kk = blk * 64;
+      u32x4_t xb[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) xb[t] = xfrag(kk + 8 * t);
+      // constant of block blk: byte g of dword i of the row's 16 bytes
+      const int gi = static_cast<int>((static_cast<uint32_t>(n) * KB + s * 16 + blk) >> 8) - gfirst;
+      const ConstRaw cr{(q8[i] >> (8 * g)) & 0xFFu, gi ? sv[1] : sv[0], gi ? ov[1] : ov[0]};
+      const Planes pl = make_planes(const_value(cr), a.lvl);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc = mfma16x16x32(lookup8_pairs(code[t >> 2][t & 3], pl), xb[t], acc);
+    }
+    // lane holds rows 4 g + e of the wave's 16, token ml
+    if (ml < a.M) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int nn = row0 + 4 * g + e;
+        if (nn < N) a.P[(static_cast<int64_t>(s) * N + nn) * a.M + ml] = acc[e];
+      }
+    }
+  } else {
+    // ---- LoRA down-projection partials over this slice: wave w takes rank tiles w, w + 4, ...
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, static_cast<uint32_t>(a.r) * K * 2);
+    for (int jt = wave; jt * 16 < a.r; jt += 4) {
+      const int j = jt * 16 + ml;
+      const bool jok = j < a.r;
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+      for (int st = 0; st < GSLICE / 32; ++st) {
+        const int kk = st * 32 + 8 * g;
+        const int k = k0 + kk;
+        const u32x4_t av = buf_load16(ra, (jok && k < K) ? (static_cast<uint32_t>(j) * K + k) * 2 : kOOB);
+        acc = mfma16x16x32(permute8(av), xfrag(kk), acc);
+      }
+      if (ml < a.M) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int jj = jt * 16 + 4 * g + e;
+          if (jj < a.r) a.UP[(static_cast<int64_t>(s) * a.M + ml) * a.r + jj] = acc[e];
         }
       }
-      acc[m] = s;
     }
   }
+}
+
+// Sum of x[0], x[stride], ..., x[(S - 1) stride] in that order, with the loads of
+// eight terms in flight at a time (the additions stay in slice order).
+__device__ __forceinline__ float ordered_sum(const float *__restrict__ x, int64_t stride, int S) {
+  float sum = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v[8];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    if (m >= M) break;
-    float s = wave_sum(acc[m]);
-    if (lane == 0) {
-      for (int j = 0; j < r; ++j) s += bf16_to_f32(U[m * r + j]) * bf16_to_f32(Bl[n * r + j]);
-      Y[m * N + n] = to_bf16(s);
+    for (int e = 0; e < 8; ++e) v[e] = (s0 + e < S) ? x[(s0 + e) * stride] : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (s0 + e < S) sum += v[e];
+  }
+  return sum;
+}
+
+constexpr int FT = 64;  // finalize threads per workgroup
+
+// Y[m, n] = bf16(sum_s P[s][n][m] + sum_j U_s[m, j] Bl[n, j]); U_s = bf16(scale * sum_s UP).
+__global__ __launch_bounds__(FT) void gemv_finalize_kernel(const float *__restrict__ P,
+                                                           const float *__restrict__ UP, int S, int N,
+                                                           int M, const uint16_t *__restrict__ Bl,
+                                                           int r, float scale, uint16_t *__restrict__ Y,
+                                                           uint16_t *__restrict__ U_saved) {
+  __shared__ float us[GMAXM * kMaxRank];
+  if (r > 0) {
+    for (int e = threadIdx.x; e < M * r; e += FT) {
+      const int m = e / r, j = e % r;
+      const uint16_t u = to_bf16(scale * ordered_sum(UP + m * r + j, static_cast<int64_t>(M) * r, S));
+      us[e] = bf16_to_f32(u);
+      if (U_saved && blockIdx.x == 0) U_saved[m * r + j] = u;
     }
+    __syncthreads();
+  }
+  const int n = blockIdx.x * FT + threadIdx.x;
+  if (n >= N) return;
+  const uint16_t *brow = Bl + static_cast<int64_t>(n) * r;
+  for (int m = 0; m < M; ++m) {
+    float y = ordered_sum(P + static_cast<int64_t>(n) * M + m, static_cast<int64_t>(N) * M, S);
+    if ((r & 7) == 0) {
+      for (int j0 = 0; j0 < r; j0 += 8) {
+        const u32x4_t bv = *reinterpret_cast<const u32x4_t *>(brow + j0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y = __builtin_fmaf(us[m * r + j0 + 2 * e], bf16_lo(bv[e]), y);
+          y = __builtin_fmaf(us[m * r + j0 + 2 * e + 1], bf16_hi(bv[e]), y);
+        }
+      }
+    } else {
+      for (int j = 0; j < r; ++j) y = __builtin_fmaf(us[m * r + j], bf16_to_f32(brow[j]), y);
+    }
+    Y[static_cast<int64_t>(m) * N + n] = to_bf16(y);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
-                           const uint16_t *Bl, int r, uint16_t *Y, hipStream_t stream) {
-  if (M < 1 || M > 16) return hipErrorInvalidValue;
-  LevelTable lvl;
-  for (int i = 0; i < 16; ++i) lvl.q[i] = codebook().q[i];
-  dim3 grid(static_cast<unsigned>((w.n_rows + 3) / 4)), block(NT);
-  hipLaunchKernelGGL(gemv_kernel, grid, block, 0, stream, w, X, static_cast<int>(M), U, Bl, r, Y,
-                     lvl);
+int gemv_slices(int64_t K) { return static_cast<int>((K + GSLICE - 1) / GSLICE); }
+
+namespace {
+size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
+float *gemv_p(void *ws) { return static_cast<float *>(ws); }
+float *gemv_up(void *ws, int64_t M, int64_t K, int64_t N) {
+  return reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                   up256(size_t(gemv_slices(K)) * size_t(N) * size_t(M) * 4));
+}
+}  // namespace
+
+size_t gemv_workspace(int64_t M, int64_t K, int64_t N, int r) {
+  const size_t S = static_cast<size_t>(gemv_slices(K));
+  return up256(S * size_t(N) * size_t(M) * 4) + up256(S * size_t(M) * size_t(r) * 4);
+}
+
+bool gemv_supported(const WeightView &w, int64_t M, int r) {
+  const int64_t N = w.n_rows, K = w.n_cols;
+  return M >= 1 && M <= GMAXM && r >= 0 && r <= kMaxRank && N <= 0x7fffffff &&
+         uint64_t(N) * K / 2 <= 0xFFFFFFF0ull && uint64_t(M) * K * 2 <= 0xFFFFFFF0ull &&
+         uint64_t(r) * K * 2 <= 0xFFFFFFF0ull;
+}
+
+hipError_t launch_gemv_stream(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *A,
+                              int r, void *ws, hipStream_t stream) {
+  if (!gemv_supported(w, M, r)) return hipErrorInvalidValue;
+  const int64_t N = w.n_rows, K = w.n_cols;
+  GemvArgs a;
+  a.w = w;
+  a.X = X;
+  a.A = A;
+  a.M = static_cast<int>(M);
+  a.r = r;
+  a.S = gemv_slices(K);
+  a.P = gemv_p(ws);
+  a.UP = gemv_up(ws, M, K, N);
+  for (int i = 0; i < 16; ++i) a.lvl.q[i] = codebook().q[i];
+  const unsigned groups = static_cast<unsigned>((N + GROWS - 1) / GROWS);
+  const unsigned grid = groups * static_cast<unsigned>(a.S) + (r > 0 ? static_cast<unsigned>(a.S) : 0u);
+  const bool c8w = (K / 64) % 4 == 0;
+  auto go = [&](auto kern) -> hipError_t {
+    // dynamic LDS above 64 KB (M > 8) has to be allowed once per instantiation
+    static bool allowed[2] = {false, false};
+    if (gemv_xl(a.M) == 8 && !allowed[c8w ? 1 : 0]) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(gemv_lds_bytes(GMAXM)));
+      if (e != hipSuccess) return e;
+      allowed[c8w ? 1 : 0] = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(GT), gemv_lds_bytes(a.M), stream, a);
+    return hipGetLastError();
+  };
+  switch (gemv_xl(a.M) * 2 + (c8w ? 1 : 0)) {
+    case 3: return go(gemv_stream_kernel<1, true>);
+    case 2: return go(gemv_stream_kernel<1, false>);
+    case 5: return go(gemv_stream_kernel<2, true>);
+    case 4: return go(gemv_stream_kernel<2, false>);
+    case 9: return go(gemv_stream_kernel<4, true>);
+    case 8: return go(gemv_stream_kernel<4, false>);
+    case 17: return go(gemv_stream_kernel<8, true>);
+    default: return go(gemv_stream_kernel<8, false>);
+  }
+}
+
+hipError_t launch_gemv_finalize(const WeightView &w, int64_t M, const uint16_t *Bl, int r, float scale,
+                                uint16_t *Y, uint16_t *U_saved, void *ws, hipStream_t stream) {
+  if (!gemv_supported(w, M, r)) return hipErrorInvalidValue;
+  const int64_t N = w.n_rows, K = w.n_cols;
+  hipLaunchKernelGGL(gemv_finalize_kernel, dim3(static_cast<unsigned>((N + FT - 1) / FT)), dim3(FT), 0,
+                     stream, gemv_p(ws), gemv_up(ws, M, K, N), gemv_slices(K), static_cast<int>(N),
+                     static_cast<int>(M), Bl, r, scale, Y, U_saved);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@ namespace qlora {
 constexpr int kBlock = 64;     // weights per first-level block
 constexpr int kGroup = 256;    // block constants per double-quantization group
 constexpr int kBuckets = 129;  // quantizer bucket table entries (x in [-1, 1])
+constexpr int kMaxRank = 256;  // largest LoRA rank
 
 struct Codebook {
   float q[16];                  // NF4 levels, ascending
@@ -63,9 +64,17 @@ hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, const uint
 // Y[M, N] = bf16(X . W'^T + U . Bl^T)  (U [M, r] pitch r, Bl [N, r]); r may be 0.
 hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
                            const uint16_t *Bl, int r, uint16_t *Y, hipStream_t stream);
-// Small-M forward (M <= 16): same contract as launch_gemm_fwd.
-hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
-                           const uint16_t *Bl, int r, uint16_t *Y, hipStream_t stream);
+// Small-M forward (M <= 16) in two launches sharing `ws` (gemv_workspace bytes):
+// the weight stream with the LoRA down-projection partials, then the finalize that
+// forms U_s = bf16(scale X A^T) (written to U_saved if not NULL) and
+// Y = bf16(X W'^T + U_s Bl^T).
+int gemv_slices(int64_t K);
+size_t gemv_workspace(int64_t M, int64_t K, int64_t N, int r);
+bool gemv_supported(const WeightView &w, int64_t M, int r);
+hipError_t launch_gemv_stream(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *A,
+                              int r, void *ws, hipStream_t stream);
+hipError_t launch_gemv_finalize(const WeightView &w, int64_t M, const uint16_t *Bl, int r, float scale,
+                                uint16_t *Y, uint16_t *U_saved, void *ws, hipStream_t stream);
 // dX[M, K] = bf16(dY . W' + V . At^T)  (V [M, r], At [K, r]); r may be 0.
 hipError_t launch_gemm_dx(const WeightView &w, const uint16_t *dY, int64_t M, const uint16_t *V,
                           const uint16_t *At, int r, uint16_t *dX, hipStream_t stream);

@@ -130,9 +130,11 @@ int qlora_dequantize(const qlora_nf4_weight *w, void *out, int out_dtype, void *
  *   Y   = bf16(X . W'^T + U_s . B^T)                  [M, N], fp32 accumulation
  * X bf16 [M, K]; A bf16 [r, K]; B bf16 [N, r]; Y bf16 [M, N].
  * U_saved (nullable) receives U_s for the backward.  The decode of W' happens inside
- * the GEMM; no bf16 copy of the weight is written.  When r > 0 the call needs
- * qlora_workspace_bytes(0, M, K, N, r) bytes of workspace (fp32 partial sums of the
- * down-projection, plus U_s when U_saved is NULL); with r = 0 it needs none. */
+ * the GEMM; no bf16 copy of the weight is written.  The call needs
+ * qlora_workspace_bytes(0, M, K, N, r) bytes of workspace: for M <= 16 the fp32
+ * partial sums of the split-contraction GEMV (also when r = 0); for M > 16 the fp32
+ * partial sums of the down-projection plus U_s when U_saved is NULL, and none when
+ * r = 0. */
 int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
                      const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
                      void *workspace, size_t workspace_bytes, void *stream);

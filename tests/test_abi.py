@@ -59,6 +59,9 @@ def test_sizes_reject_bad_shapes():
 
 def test_workspace_bytes():
     assert _lib.qlora_workspace_bytes(0, 4096, 4096, 4096, 0) == 0
+    # M <= 16 runs a split-contraction GEMV: fp32 partials even without an adapter
+    assert _lib.qlora_workspace_bytes(0, 1, 4096, 11008, 0) >= 4 * 11008 * 4
+    assert _lib.qlora_workspace_bytes(0, 16, 11008, 4096, 16) >= 11 * 4096 * 16 * 4 + 11 * 16 * 16 * 4
     assert _lib.qlora_workspace_bytes(0, 4096, 4096, 4096, 64) >= 4096 * 64 * 2
     assert _lib.qlora_workspace_bytes(1, 4096, 4096, 11008, 64) > 0
     assert _lib.qlora_workspace_bytes(1, 1, 100, 4, 8) == 0       # K % 64 != 0
