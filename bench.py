@@ -187,6 +187,32 @@ def measure_m1(torch, q, synth, gc, ev, min_bytes=600 << 20, calls=200):
     return out
 
 
+def measure_adamw(torch, q, reps=20):
+    """AdamW step over the adapters of the LLaMA-65B layer (r = 64 on all seven linears):
+    fp32 parameter and moments, bf16 gradient, bf16 parameter copy; 28 bytes per value."""
+    n = 4 * 64 * (8192 + 8192) + 2 * 64 * (8192 + 22016) + 64 * (22016 + 8192)
+    g = torch.Generator(device="cuda").manual_seed(4)
+    p = torch.randn(n, device="cuda", generator=g) * 0.02
+    grad = (torch.randn(n, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    m = torch.zeros_like(p)
+    v = torch.zeros_like(p)
+    pb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    for t in range(1, 4):
+        q.adamw_step(p, grad, m, v, t, 2e-4, weight_decay=0.01, param_bf16=pb)
+    torch.cuda.synchronize()
+    s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for t in range(4, 4 + reps):
+        q.adamw_step(p, grad, m, v, t, 2e-4, weight_decay=0.01, param_bf16=pb)
+    f.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(f) / reps
+    gbs = 28 * n / (ms * 1e-3) / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(ms * 1e3, 2), "params": n,
+            "bytes_per_param": 28, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "what": "AdamW step on the 65B layer's LoRA adapters (fp32 state, bf16 grad and copy)"}
+
+
 def cpu_baseline(synth, sample_m=4096, min_seconds=10.0, max_passes=20):
     """The oracle (float64 numpy) on a bounded sample of the workload: the three linears
     with the first `sample_m` tokens (decode of W' from the stored format, forward and
@@ -352,6 +378,7 @@ def main():
         result["weight_stream_m1"] = measure_m1(torch, q, synth, gc, ev)
         ev.close()
         result["quantize"] = measure_quantize(torch, q, L)
+        result["adamw"] = measure_adamw(torch, q)
     if not args.no_cpu_baseline:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(synth)

@@ -14,13 +14,14 @@ a gfx950.
 from dataclasses import dataclass
 
 from . import _lib
-from ._lib import (QLORA_BF16, QLORA_F32, QloraError, qlora_dequantize, qlora_linear_bwd,  # noqa: F401
-                   qlora_linear_fwd, qlora_nf4_codebook, qlora_nf4_sizes, qlora_quantize_nf4,
-                   qlora_workspace_bytes)
+from ._lib import (QLORA_BF16, QLORA_F32, QloraError, qlora_adamw_step, qlora_dequantize,  # noqa: F401
+                   qlora_linear_bwd, qlora_linear_fwd, qlora_nf4_codebook, qlora_nf4_sizes,
+                   qlora_quantize_nf4, qlora_workspace_bytes)
 
 __all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "workspace",
-           "QloraError", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
-           "qlora_linear_bwd", "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes"]
+           "adamw_step", "QloraError", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
+           "qlora_linear_bwd", "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes",
+           "qlora_adamw_step"]
 
 
 def _torch():
@@ -151,3 +152,27 @@ def linear_bwd(qw, dY, X, A=None, B=None, alpha=16.0, U=None, need_dx=True, dX=N
                                 _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dY)),
                "qlora_linear_bwd")
     return (dX if need_dx else None), dA, dB
+
+
+def adamw_step(param, grad, exp_avg, exp_avg_sq, step, lr, betas=(0.9, 0.999), eps=1e-8,
+               weight_decay=0.0, param_bf16=None):
+    """In-place AdamW step on an fp32 adapter parameter (any shape, contiguous) with its
+    bf16 gradient; optionally writes the bf16 copy the layer reads into ``param_bf16``."""
+    torch = _torch()
+    _need(param, torch.float32, "param")
+    _need(exp_avg, torch.float32, "exp_avg")
+    _need(exp_avg_sq, torch.float32, "exp_avg_sq")
+    _need(grad, torch.bfloat16, "grad")
+    n = param.numel()
+    for t, name in ((grad, "grad"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, param has {n}")
+    if param_bf16 is not None:
+        _need(param_bf16, torch.bfloat16, "param_bf16")
+        if param_bf16.numel() != n:
+            raise ValueError("param_bf16 size mismatch")
+    _lib.check(qlora_adamw_step(param.data_ptr(), _ptr(param_bf16), grad.data_ptr(), exp_avg.data_ptr(),
+                                exp_avg_sq.data_ptr(), n, float(lr), float(betas[0]), float(betas[1]),
+                                float(eps), float(weight_decay), int(step), _stream(param)),
+               "qlora_adamw_step")
+    return param

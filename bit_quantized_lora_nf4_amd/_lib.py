@@ -20,13 +20,14 @@ QLORA_ERR_WORKSPACE = -5
 QLORA_ERR_ALIGN = -6
 QLORA_ERR_DEVICE = -7
 QLORA_ERR_LAUNCH = -8
+QLORA_ERR_VALUE = -9
 QLORA_F32 = 0
 QLORA_BF16 = 1
 
 EXPORTED = (
     "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes", "qlora_status_string",
     "qlora_last_error", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
-    "qlora_linear_bwd", "qlora_time_next_gemm",
+    "qlora_linear_bwd", "qlora_time_next_gemm", "qlora_adamw_step",
 )
 
 
@@ -80,6 +81,9 @@ def load(path=LIB_PATH):
     lib.qlora_linear_bwd.restype = I32
     lib.qlora_time_next_gemm.argtypes = [P, P]
     lib.qlora_time_next_gemm.restype = None
+    D = ctypes.c_double
+    lib.qlora_adamw_step.argtypes = [P, P, P, P, P, I64, D, D, D, D, D, I64, P]
+    lib.qlora_adamw_step.restype = I32
     _lib = lib
     return lib
 
@@ -142,3 +146,9 @@ def qlora_linear_bwd(w, dY, X, M, A, B, r, alpha, U_saved, dX, dA, dB, workspace
 
 def qlora_time_next_gemm(start_event, stop_event):
     load().qlora_time_next_gemm(start_event, stop_event)
+
+
+def qlora_adamw_step(param, param_bf16, grad, exp_avg, exp_avg_sq, n, lr, beta1, beta2, eps,
+                     weight_decay, step, stream):
+    return load().qlora_adamw_step(param, param_bf16, grad, exp_avg, exp_avg_sq, n, lr, beta1, beta2,
+                                   eps, weight_decay, step, stream)

@@ -172,6 +172,7 @@ const char *qlora_status_string(int status) {
     case QLORA_ERR_RANK: return "invalid rank or alpha";
     case QLORA_ERR_DTYPE: return "unsupported dtype";
     case QLORA_ERR_WORKSPACE: return "workspace too small";
+    case QLORA_ERR_VALUE: return "scalar argument out of range";
     case QLORA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case QLORA_ERR_DEVICE: return "no usable gfx950 device";
     case QLORA_ERR_LAUNCH: return "kernel launch failed";
@@ -349,3 +350,36 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16
 }
 
 }  // extern "C"
+
+int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, float *exp_avg,
+                     float *exp_avg_sq, int64_t n, double lr, double beta1, double beta2, double eps,
+                     double weight_decay, int64_t step, void *stream) {
+  if (!param || !grad || !exp_avg || !exp_avg_sq)
+    return fail(QLORA_ERR_NULL, "adamw_step: param, grad, exp_avg and exp_avg_sq are required");
+  if (n < 1 || n > (int64_t(1) << 40)) return fail(QLORA_ERR_SHAPE, "adamw_step: n = %lld", (long long)n);
+  if (step < 1) return fail(QLORA_ERR_VALUE, "adamw_step: step = %lld must be >= 1", (long long)step);
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps > 0.0) ||
+      !std::isfinite(eps) || !(lr >= 0.0) || !std::isfinite(lr) || !(weight_decay >= 0.0) ||
+      !std::isfinite(weight_decay))
+    return fail(QLORA_ERR_VALUE, "adamw_step: hyper-parameter out of range");
+  if (!aligned16(param) || !aligned16(grad) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) ||
+      (param_bf16 && !aligned16(param_bf16)))
+    return fail(QLORA_ERR_ALIGN, "adamw_step: pointers must be 16-byte aligned");
+  int s = check_device();
+  if (s != QLORA_OK) return s;
+  const double t = static_cast<double>(step);
+  qlora::AdamConsts c;
+  c.decay = static_cast<float>(1.0 - lr * weight_decay);
+  c.b1 = static_cast<float>(beta1);
+  c.ob1 = static_cast<float>(1.0 - beta1);
+  c.b2 = static_cast<float>(beta2);
+  c.ob2 = static_cast<float>(1.0 - beta2);
+  c.step_size = static_cast<float>(lr / (1.0 - std::pow(beta1, t)));
+  c.bc2s = static_cast<float>(std::sqrt(1.0 - std::pow(beta2, t)));
+  c.eps = static_cast<float>(eps);
+  if (!std::isfinite(c.step_size) || !(c.bc2s > 0.0f))
+    return fail(QLORA_ERR_VALUE, "adamw_step: bias correction underflows at this step");
+  return launched(qlora::launch_adamw(param, param_bf16, grad, exp_avg, exp_avg_sq, n, c,
+                                      static_cast<hipStream_t>(stream)),
+                  "adamw");
+}

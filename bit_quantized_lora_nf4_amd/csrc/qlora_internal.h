@@ -61,6 +61,13 @@ size_t reduce_m_workspace(int64_t M, int64_t No, int r);
 hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, const uint16_t *S, int r,
                            float *partials, uint16_t *OUT, bool trans_out, hipStream_t stream);
 
+// AdamW step (fp32 parameter and moments, bf16 gradient, optional bf16 parameter copy).
+struct AdamConsts {
+  float decay, b1, ob1, b2, ob2, step_size, bc2s, eps;
+};
+hipError_t launch_adamw(float *p, uint16_t *pb, const uint16_t *g, float *m, float *v, int64_t n,
+                        const AdamConsts &c, hipStream_t stream);
+
 // Y[M, N] = bf16(X . W'^T + U . Bl^T)  (U [M, r] pitch r, Bl [N, r]); r may be 0.
 hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
                            const uint16_t *Bl, int r, uint16_t *Y, hipStream_t stream);

@@ -52,7 +52,8 @@ typedef enum {
   QLORA_ERR_WORKSPACE = -5, /* workspace smaller than qlora_workspace_bytes()     */
   QLORA_ERR_ALIGN = -6,     /* a pointer is not 16-byte aligned                   */
   QLORA_ERR_DEVICE = -7,    /* no usable gfx950 device                            */
-  QLORA_ERR_LAUNCH = -8     /* the HIP runtime refused a kernel launch            */
+  QLORA_ERR_LAUNCH = -8,    /* the HIP runtime refused a kernel launch            */
+  QLORA_ERR_VALUE = -9      /* a scalar argument is out of range                  */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -152,6 +153,24 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16
                      const uint16_t *A, const uint16_t *B, int r, float alpha,
                      const uint16_t *U_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* AdamW step on adapter parameters ([Digest] "方法步骤与流程" step 5: only the LoRA
+ * matrices are updated, by an optimizer such as Adam; the pages give no formula, so
+ * this is AdamW with decoupled weight decay and bias correction).  For i < n:
+ *   g = grad[i] (bf16);  p = param[i] * fp32(1 - lr * weight_decay)
+ *   m = b1 * m + (1 - b1) * g;  v = b2 * v + (1 - b2) * g * g
+ *   param[i] = p - fp32(lr / (1 - b1^step)) * m / (sqrt(v) / fp32(sqrt(1 - b2^step)) + eps)
+ * every operation one fp32 rounding (no fused multiply-add); the factors are formed in
+ * double from the double hyper-parameters and rounded once.
+ *   param, exp_avg, exp_avg_sq  fp32 [n], updated in place (exp_avg = m, exp_avg_sq = v)
+ *   grad                        bf16 [n] (e.g. dA or dB of qlora_linear_bwd)
+ *   param_bf16                  nullable bf16 [n]: receives bf16_rne(param) after the step
+ * step >= 1 counts the steps taken including this one; 0 <= beta1, beta2 < 1; eps > 0;
+ * lr and weight_decay finite and >= 0 (else QLORA_ERR_VALUE).  All pointers 16-byte
+ * aligned. */
+int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, float *exp_avg,
+                     float *exp_avg_sq, int64_t n, double lr, double beta1, double beta2, double eps,
+                     double weight_decay, int64_t step, void *stream);
 
 #ifdef __cplusplus
 }

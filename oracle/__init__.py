@@ -26,11 +26,12 @@ Module map:
                         double quantization, decoding.
 * ``oracle.linear``     forward / backward of the linear layer in float64.
 * ``oracle.accounting`` closed-form storage and parameter counts.
+* ``oracle.adamw``      the AdamW step on the adapter parameters.
 
 Every function is pinned by ``tests/test_oracle_*.py`` to facts the pages or
 mathematics fix; none is "parity unpinned".
 """
 
-from . import fp, nf4, linear, accounting  # noqa: F401
+from . import fp, nf4, linear, accounting, adamw  # noqa: F401
 
-__all__ = ["fp", "nf4", "linear", "accounting"]
+__all__ = ["fp", "nf4", "linear", "accounting", "adamw"]

@@ -151,3 +151,27 @@ def test_no_device_reports_device_error():
     # valid arguments: the call reaches the device check and stops there
     st = _lib.qlora_dequantize(_w(), FAKE, 1, None)
     assert st == _lib.QLORA_ERR_DEVICE
+
+
+def test_adamw_argument_errors():
+    f = _lib.qlora_adamw_step
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 64, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["p", "pb", "g", "m", "v", "n", "lr", "b1", "b2", "eps", "wd", "step", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(p=None) == _lib.QLORA_ERR_NULL
+    assert call(g=None) == _lib.QLORA_ERR_NULL
+    assert call(n=0) == _lib.QLORA_ERR_SHAPE
+    assert call(step=0) == _lib.QLORA_ERR_VALUE
+    assert call(b1=1.0) == _lib.QLORA_ERR_VALUE
+    assert call(b2=-0.1) == _lib.QLORA_ERR_VALUE
+    assert call(eps=0.0) == _lib.QLORA_ERR_VALUE
+    assert call(lr=float("inf")) == _lib.QLORA_ERR_VALUE
+    assert call(wd=-1.0) == _lib.QLORA_ERR_VALUE
+    assert call(m=FAKE + 4) == _lib.QLORA_ERR_ALIGN
+    assert call(pb=FAKE + 2) == _lib.QLORA_ERR_ALIGN
