@@ -213,6 +213,38 @@ def measure_adamw(torch, q, reps=20):
             "what": "AdamW step on the 65B layer's LoRA adapters (fp32 state, bf16 grad and copy)"}
 
 
+def measure_merge(torch, q, reps=10):
+    """LoRA merge into bf16 (and unmerge) on the 65B layer's 8192 -> 22016 weight, r = 64:
+    algorithmic HBM bytes 0.516 + 2 per weight (merge), 2 + 2 (unmerge)."""
+    N, K, r = 22016, 8192, 64
+    g = torch.Generator(device="cuda").manual_seed(5)
+    W = (torch.randn(N, K, device="cuda", generator=g) * 0.015).to(torch.bfloat16)
+    qw = q.quantize(W)
+    del W
+    A = (torch.randn(r, K, device="cuda", generator=g) * (1.0 / r) ** 0.5).to(torch.bfloat16)
+    B = (torch.randn(N, r, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    out = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+    back = torch.empty_like(out)
+    res = {}
+    for name, fn, bpw in (("merge", lambda: q.lora_merge(qw, A, B, 16.0, out=out), 0.5 + 1 / 64 + 2),
+                          ("unmerge", lambda: q.lora_unmerge(out, A, B, 16.0, out=back), 4.0)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        f.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(f) / reps
+        gbs = bpw * N * K / (ms * 1e-3) / 1e9
+        res[name] = {"value": round(gbs, 1), "unit": "GB/s", "us": round(ms * 1e3, 2),
+                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    res["what"] = "LoRA merge / unmerge, 22016 x 8192 bf16 output, r = 64"
+    return res
+
+
 def cpu_baseline(synth, sample_m=4096, min_seconds=10.0, max_passes=20):
     """The oracle (float64 numpy) on a bounded sample of the workload: the three linears
     with the first `sample_m` tokens (decode of W' from the stored format, forward and
@@ -379,6 +411,7 @@ def main():
         ev.close()
         result["quantize"] = measure_quantize(torch, q, L)
         result["adamw"] = measure_adamw(torch, q)
+        result["lora_merge"] = measure_merge(torch, q)
     if not args.no_cpu_baseline:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(synth)

@@ -9,19 +9,20 @@ a gfx950.
     qw = quantize(W)                                   # W [N, K] fp32 or bf16, on the GPU
     Y, U = linear_fwd(qw, X, A, B, alpha)              # Y = X W'^T + (alpha/r) X A^T B^T
     dX, dA, dB = linear_bwd(qw, dY, X, A, B, alpha, U)
+    Wm = lora_merge(qw, A, B, alpha)                   # bf16(W' + (alpha/r) B A)
 """
 
 from dataclasses import dataclass
 
 from . import _lib
 from ._lib import (QLORA_BF16, QLORA_F32, QloraError, qlora_adamw_step, qlora_dequantize,  # noqa: F401
-                   qlora_linear_bwd, qlora_linear_fwd, qlora_nf4_codebook, qlora_nf4_sizes,
-                   qlora_quantize_nf4, qlora_workspace_bytes)
+                   qlora_linear_bwd, qlora_linear_fwd, qlora_lora_merge, qlora_lora_unmerge,
+                   qlora_nf4_codebook, qlora_nf4_sizes, qlora_quantize_nf4, qlora_workspace_bytes)
 
 __all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "workspace",
-           "adamw_step", "QloraError", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
+           "adamw_step", "lora_merge", "lora_unmerge", "QloraError", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
            "qlora_linear_bwd", "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes",
-           "qlora_adamw_step"]
+           "qlora_adamw_step", "qlora_lora_merge", "qlora_lora_unmerge"]
 
 
 def _torch():
@@ -176,3 +177,41 @@ def adamw_step(param, grad, exp_avg, exp_avg_sq, step, lr, betas=(0.9, 0.999), e
                                 float(eps), float(weight_decay), int(step), _stream(param)),
                "qlora_adamw_step")
     return param
+
+
+def _adapter(A, B, N, K):
+    torch = _torch()
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _need(A, torch.bfloat16, "A")
+        _need(B, torch.bfloat16, "B")
+        if tuple(A.shape) != (r, K) or tuple(B.shape) != (N, r):
+            raise ValueError(f"A {tuple(A.shape)} / B {tuple(B.shape)} do not fit a [{N}, {K}] weight")
+    return r
+
+
+def lora_merge(qw, A, B, alpha=16.0, out=None):
+    """bf16 [n_rows, n_cols] weight with the adapter folded in: bf16(W' + (alpha/r) B A)."""
+    torch = _torch()
+    N, K = qw.shape
+    r = _adapter(A, B, N, K)
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=qw.codes.device)
+    _need(out, torch.bfloat16, "out")
+    _lib.check(qlora_lora_merge(qw.descriptor(), _ptr(A), _ptr(B), r, float(alpha), out.data_ptr(),
+                                _stream(out)), "qlora_lora_merge")
+    return out
+
+
+def lora_unmerge(Wm, A, B, alpha=16.0, out=None):
+    """bf16(Wm - (alpha/r) B A); ``out=Wm`` works in place."""
+    torch = _torch()
+    _need(Wm, torch.bfloat16, "Wm")
+    N, K = Wm.shape
+    r = _adapter(A, B, N, K)
+    if out is None:
+        out = torch.empty_like(Wm)
+    _need(out, torch.bfloat16, "out")
+    _lib.check(qlora_lora_unmerge(Wm.data_ptr(), N, K, _ptr(A), _ptr(B), r, float(alpha), out.data_ptr(),
+                                  _stream(Wm)), "qlora_lora_unmerge")
+    return out

@@ -27,7 +27,8 @@ QLORA_BF16 = 1
 EXPORTED = (
     "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes", "qlora_status_string",
     "qlora_last_error", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
-    "qlora_linear_bwd", "qlora_time_next_gemm", "qlora_adamw_step",
+    "qlora_linear_bwd", "qlora_time_next_gemm", "qlora_adamw_step", "qlora_lora_merge",
+    "qlora_lora_unmerge",
 )
 
 
@@ -84,6 +85,10 @@ def load(path=LIB_PATH):
     D = ctypes.c_double
     lib.qlora_adamw_step.argtypes = [P, P, P, P, P, I64, D, D, D, D, D, I64, P]
     lib.qlora_adamw_step.restype = I32
+    lib.qlora_lora_merge.argtypes = [W, P, P, I32, F32, P, P]
+    lib.qlora_lora_merge.restype = I32
+    lib.qlora_lora_unmerge.argtypes = [P, I64, I64, P, P, I32, F32, P, P]
+    lib.qlora_lora_unmerge.restype = I32
     _lib = lib
     return lib
 
@@ -152,3 +157,11 @@ def qlora_adamw_step(param, param_bf16, grad, exp_avg, exp_avg_sq, n, lr, beta1,
                      weight_decay, step, stream):
     return load().qlora_adamw_step(param, param_bf16, grad, exp_avg, exp_avg_sq, n, lr, beta1, beta2,
                                    eps, weight_decay, step, stream)
+
+
+def qlora_lora_merge(w, A, B, r, alpha, out, stream):
+    return load().qlora_lora_merge(ctypes.byref(w), A, B, r, alpha, out, stream)
+
+
+def qlora_lora_unmerge(W_merged, n_rows, n_cols, A, B, r, alpha, out, stream):
+    return load().qlora_lora_unmerge(W_merged, n_rows, n_cols, A, B, r, alpha, out, stream)

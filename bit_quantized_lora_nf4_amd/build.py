@@ -30,7 +30,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-SOURCES = ["codebook.cpp", "api.cpp", "quantize.hip", "dequant.hip", "lora.hip", "gemm.hip", "adamw.hip",
+SOURCES = ["codebook.cpp", "api.cpp", "quantize.hip", "dequant.hip", "lora.hip", "gemm.hip", "adamw.hip", "merge.hip",
            "gemv.hip"]
 
 

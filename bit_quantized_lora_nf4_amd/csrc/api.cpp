@@ -349,6 +349,40 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16
   return QLORA_OK;
 }
 
+int qlora_lora_merge(const qlora_nf4_weight *w, const uint16_t *A, const uint16_t *B, int r,
+                     float alpha, uint16_t *out, void *stream) {
+  int s = check_weight(w);
+  if (s == QLORA_OK) s = check_rank(r, alpha);
+  if (s != QLORA_OK) return s;
+  if (!out) return fail(QLORA_ERR_NULL, "lora_merge: out is NULL");
+  if (r > 0 && (!A || !B)) return fail(QLORA_ERR_NULL, "lora_merge: A and B are required when r > 0");
+  if (!aligned16(out) || (r > 0 && (!aligned16(A) || !aligned16(B))))
+    return fail(QLORA_ERR_ALIGN, "lora_merge: tensors must be 16-byte aligned");
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  return launched(qlora::launch_lora_merge(view(w), A, B, r, scale, out,
+                                           static_cast<hipStream_t>(stream)),
+                  "lora_merge");
+}
+
+int qlora_lora_unmerge(const uint16_t *W_merged, int64_t n_rows, int64_t n_cols, const uint16_t *A,
+                       const uint16_t *B, int r, float alpha, uint16_t *out, void *stream) {
+  int s = check_weight_shape(n_rows, n_cols);
+  if (s == QLORA_OK) s = check_rank(r, alpha);
+  if (s != QLORA_OK) return s;
+  if (!W_merged || !out) return fail(QLORA_ERR_NULL, "lora_unmerge: W_merged and out are required");
+  if (r > 0 && (!A || !B)) return fail(QLORA_ERR_NULL, "lora_unmerge: A and B are required when r > 0");
+  if (!aligned16(W_merged) || !aligned16(out) || (r > 0 && (!aligned16(A) || !aligned16(B))))
+    return fail(QLORA_ERR_ALIGN, "lora_unmerge: tensors must be 16-byte aligned");
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  return launched(qlora::launch_lora_unmerge(W_merged, n_rows, n_cols, A, B, r, scale, out,
+                                             static_cast<hipStream_t>(stream)),
+                  "lora_unmerge");
+}
+
 }  // extern "C"
 
 int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, float *exp_avg,

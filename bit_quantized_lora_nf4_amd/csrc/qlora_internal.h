@@ -68,6 +68,14 @@ struct AdamConsts {
 hipError_t launch_adamw(float *p, uint16_t *pb, const uint16_t *g, float *m, float *v, int64_t n,
                         const AdamConsts &c, hipStream_t stream);
 
+// LoRA merge / unmerge of one adapter into a bf16 weight [N, K]:
+// out = bf16(W' + scale . B A) from the NF4 weight, or bf16(Wm - scale . B A).
+hipError_t launch_lora_merge(const WeightView &w, const uint16_t *A, const uint16_t *B, int r,
+                             float scale, uint16_t *out, hipStream_t stream);
+hipError_t launch_lora_unmerge(const uint16_t *Wm, int64_t n_rows, int64_t n_cols, const uint16_t *A,
+                               const uint16_t *B, int r, float scale, uint16_t *out,
+                               hipStream_t stream);
+
 // Y[M, N] = bf16(X . W'^T + U . Bl^T)  (U [M, r] pitch r, Bl [N, r]); r may be 0.
 hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
                            const uint16_t *Bl, int r, uint16_t *Y, hipStream_t stream);

@@ -172,6 +172,27 @@ int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, f
                      float *exp_avg_sq, int64_t n, double lr, double beta1, double beta2, double eps,
                      double weight_decay, int64_t step, void *stream);
 
+/* LoRA merge ([Repro] "官方代码阅读路线": the scaled update B A can be folded into
+ * the frozen weight for inference and removed again; [QLoRA note], on the error that
+ * merging adds: merge into a higher-precision copy of the base, here bf16).
+ *   out[n, k] = bf16_rne(W'[n, k] + RN(scale * D[n, k])),  D = B A,  scale = alpha / r
+ * W' the bf16 weight decode (as qlora_dequantize with QLORA_BF16); D is accumulated
+ * in fp32 (its summation order is unspecified).  r = 0 writes W' itself.
+ *   A bf16 [r, K];  B bf16 [N, r];  out bf16 [N, K] (must not alias the weight arrays)
+ * Merge exactly once ([Repro] "失败排查清单" item 4): a second merge adds B A again.
+ * Check a merge by comparing the logits of qlora_linear_fwd with those of the merged
+ * weight on the same input (item 6 of that list). */
+int qlora_lora_merge(const qlora_nf4_weight *w, const uint16_t *A, const uint16_t *B, int r,
+                     float alpha, uint16_t *out, void *stream);
+
+/* LoRA unmerge, the inverse of qlora_lora_merge on a bf16 weight:
+ *   out[n, k] = bf16_rne(W_merged[n, k] - RN(scale * D[n, k]))
+ * W_merged, out bf16 [n_rows, n_cols]; out may equal W_merged (in place: each element
+ * is read before it is written by the same thread).  A bf16 [r, n_cols], B bf16
+ * [n_rows, r].  Merge then unmerge returns W' to within two bf16 roundings. */
+int qlora_lora_unmerge(const uint16_t *W_merged, int64_t n_rows, int64_t n_cols, const uint16_t *A,
+                       const uint16_t *B, int r, float alpha, uint16_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,11 +27,12 @@ Module map:
 * ``oracle.linear``     forward / backward of the linear layer in float64.
 * ``oracle.accounting`` closed-form storage and parameter counts.
 * ``oracle.adamw``      the AdamW step on the adapter parameters.
+* ``oracle.merge``      LoRA merge / unmerge into a bf16 copy of the base.
 
 Every function is pinned by ``tests/test_oracle_*.py`` to facts the pages or
 mathematics fix; none is "parity unpinned".
 """
 
-from . import fp, nf4, linear, accounting, adamw  # noqa: F401
+from . import fp, nf4, linear, accounting, adamw, merge  # noqa: F401
 
-__all__ = ["fp", "nf4", "linear", "accounting", "adamw"]
+__all__ = ["fp", "nf4", "linear", "accounting", "adamw", "merge"]

@@ -175,3 +175,21 @@ def test_adamw_argument_errors():
     assert call(wd=-1.0) == _lib.QLORA_ERR_VALUE
     assert call(m=FAKE + 4) == _lib.QLORA_ERR_ALIGN
     assert call(pb=FAKE + 2) == _lib.QLORA_ERR_ALIGN
+
+
+def test_merge_argument_errors():
+    w = _w()
+    f = _lib.qlora_lora_merge
+    assert f(w, FAKE, FAKE, 300, 16.0, FAKE, None) == _lib.QLORA_ERR_RANK
+    assert f(w, FAKE, FAKE, 8, float("nan"), FAKE, None) == _lib.QLORA_ERR_RANK
+    assert f(w, None, FAKE, 8, 16.0, FAKE, None) == _lib.QLORA_ERR_NULL
+    assert f(w, FAKE, FAKE, 8, 16.0, None, None) == _lib.QLORA_ERR_NULL
+    assert f(w, FAKE, FAKE + 2, 8, 16.0, FAKE, None) == _lib.QLORA_ERR_ALIGN
+    assert f(w, FAKE, FAKE, 8, 16.0, FAKE, None) == _lib.QLORA_ERR_DEVICE
+    assert f(w, None, None, 0, 16.0, FAKE, None) == _lib.QLORA_ERR_DEVICE
+    g = _lib.qlora_lora_unmerge
+    assert g(FAKE, 64, 100, FAKE, FAKE, 8, 16.0, FAKE, None) == _lib.QLORA_ERR_SHAPE
+    assert g(None, 64, 128, FAKE, FAKE, 8, 16.0, FAKE, None) == _lib.QLORA_ERR_NULL
+    assert g(FAKE, 64, 128, FAKE, FAKE, -1, 16.0, FAKE, None) == _lib.QLORA_ERR_RANK
+    assert g(FAKE + 8, 64, 128, FAKE, FAKE, 8, 16.0, FAKE, None) == _lib.QLORA_ERR_ALIGN
+    assert g(FAKE, 64, 128, FAKE, FAKE, 8, 16.0, FAKE, None) == _lib.QLORA_ERR_DEVICE
