@@ -16,13 +16,17 @@ from dataclasses import dataclass
 
 from . import _lib
 from ._lib import (QLORA_BF16, QLORA_F32, QloraError, qlora_adamw_step, qlora_dequantize,  # noqa: F401
-                   qlora_linear_bwd, qlora_linear_fwd, qlora_lora_merge, qlora_lora_unmerge,
-                   qlora_nf4_codebook, qlora_nf4_sizes, qlora_quantize_nf4, qlora_workspace_bytes)
+                   qlora_linear_bwd, qlora_linear_bwd_fused, qlora_linear_fwd, qlora_linear_fwd_fused,
+                   qlora_lora_merge, qlora_lora_unmerge, qlora_nf4_codebook, qlora_nf4_concat_rows,
+                   qlora_nf4_sizes, qlora_quantize_nf4, qlora_workspace_bytes,
+                   qlora_workspace_bytes_fused)
 
 __all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "workspace",
-           "adamw_step", "lora_merge", "lora_unmerge", "QloraError", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
+           "adamw_step", "lora_merge", "lora_unmerge", "concat_rows", "linear_fwd_fused",
+           "linear_bwd_fused", "QloraError", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
            "qlora_linear_bwd", "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes",
-           "qlora_adamw_step", "qlora_lora_merge", "qlora_lora_unmerge"]
+           "qlora_adamw_step", "qlora_lora_merge", "qlora_lora_unmerge", "qlora_linear_fwd_fused",
+           "qlora_linear_bwd_fused", "qlora_workspace_bytes_fused", "qlora_nf4_concat_rows"]
 
 
 def _torch():
@@ -215,3 +219,81 @@ def lora_unmerge(Wm, A, B, alpha=16.0, out=None):
     _lib.check(qlora_lora_unmerge(Wm.data_ptr(), N, K, _ptr(A), _ptr(B), r, float(alpha), out.data_ptr(),
                                   _stream(Wm)), "qlora_lora_unmerge")
     return out
+
+
+# ---- horizontally fused linears (shared X; stacked weights and adapters) -------------
+
+def concat_rows(qws):
+    """One NF4Weight holding the given weights stacked along rows (every part but the
+    last must hold a multiple of 16384 weights so that its DQ groups end with it)."""
+    torch = _torch()
+    K = qws[0].n_cols
+    N = sum(q.n_rows for q in qws)
+    cb, nb, ng = qlora_nf4_sizes(N, K)
+    dev = qws[0].codes.device
+    out = NF4Weight(torch.empty(cb, dtype=torch.uint8, device=dev),
+                    torch.empty(nb, dtype=torch.int8, device=dev),
+                    torch.empty(ng, dtype=torch.float32, device=dev),
+                    torch.empty(ng, dtype=torch.float32, device=dev), N, K)
+    _lib.check(qlora_nf4_concat_rows([q.descriptor() for q in qws], out.descriptor(), _stream(out.codes)),
+               "qlora_nf4_concat_rows")
+    return out
+
+
+def linear_fwd_fused(qw, n_parts, X, A=None, B=None, alpha=16.0, save_u=True, Y=None, U=None, ws=None):
+    """Fused forward of n_parts linears sharing X: A [n_parts r, K] and B [N, r] stack the
+    parts' adapters; Y [M, N] holds the parts' outputs side by side."""
+    torch = _torch()
+    _need(X, torch.bfloat16, "X")
+    M, K = X.shape
+    N = qw.n_rows
+    R = 0 if A is None else A.shape[0]
+    if R % n_parts:
+        raise ValueError(f"A has {R} rows, not a multiple of n_parts = {n_parts}")
+    r = R // n_parts
+    if r:
+        _need(A, torch.bfloat16, "A")
+        _need(B, torch.bfloat16, "B")
+        if tuple(B.shape) != (N, r):
+            raise ValueError(f"B is {tuple(B.shape)}, expected {(N, r)}")
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if r and save_u and U is None:
+        U = torch.empty((M, R), dtype=torch.bfloat16, device=dev)
+    nbytes = qlora_workspace_bytes_fused(0, M, K, N, r, n_parts)
+    if ws is None and nbytes > 0:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _lib.check(qlora_linear_fwd_fused(qw.descriptor(), n_parts, X.data_ptr(), M, _ptr(A), _ptr(B), r,
+                                      float(alpha), Y.data_ptr(), _ptr(U) if save_u else None, _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(X)),
+               "qlora_linear_fwd_fused")
+    return Y, (U if save_u else None)
+
+
+def linear_bwd_fused(qw, n_parts, dY, X, A=None, B=None, alpha=16.0, U=None, need_dx=True, dX=None,
+                     dA=None, dB=None, ws=None):
+    """(dX, dA, dB) of the fused linears; dA and dB are stacked like A and B."""
+    torch = _torch()
+    _need(dY, torch.bfloat16, "dY")
+    M = dY.shape[0]
+    K, N = qw.n_cols, qw.n_rows
+    R = 0 if A is None else A.shape[0]
+    r = R // n_parts
+    dev = dY.device
+    if need_dx and dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if r:
+        if dA is None:
+            dA = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
+        if dB is None:
+            dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+        if ws is None:
+            ws = torch.empty(max(qlora_workspace_bytes_fused(1, M, K, N, r, n_parts), 256),
+                             dtype=torch.uint8, device=dev)
+    _lib.check(qlora_linear_bwd_fused(qw.descriptor(), n_parts, dY.data_ptr(), _ptr(X), M, _ptr(A),
+                                      _ptr(B), r, float(alpha), _ptr(U), _ptr(dX) if need_dx else None,
+                                      _ptr(dA), _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(),
+                                      _stream(dY)),
+               "qlora_linear_bwd_fused")
+    return (dX if need_dx else None), dA, dB

@@ -21,6 +21,7 @@ QLORA_ERR_ALIGN = -6
 QLORA_ERR_DEVICE = -7
 QLORA_ERR_LAUNCH = -8
 QLORA_ERR_VALUE = -9
+QLORA_MAX_PARTS = 8
 QLORA_F32 = 0
 QLORA_BF16 = 1
 
@@ -28,7 +29,8 @@ EXPORTED = (
     "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes", "qlora_status_string",
     "qlora_last_error", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
     "qlora_linear_bwd", "qlora_time_next_gemm", "qlora_adamw_step", "qlora_lora_merge",
-    "qlora_lora_unmerge",
+    "qlora_lora_unmerge", "qlora_workspace_bytes_fused", "qlora_linear_fwd_fused",
+    "qlora_linear_bwd_fused", "qlora_nf4_concat_rows",
 )
 
 
@@ -89,6 +91,14 @@ def load(path=LIB_PATH):
     lib.qlora_lora_merge.restype = I32
     lib.qlora_lora_unmerge.argtypes = [P, I64, I64, P, P, I32, F32, P, P]
     lib.qlora_lora_unmerge.restype = I32
+    lib.qlora_workspace_bytes_fused.argtypes = [I32, I64, I64, I64, I32, I32]
+    lib.qlora_workspace_bytes_fused.restype = SZ
+    lib.qlora_linear_fwd_fused.argtypes = [W, I32, P, I64, P, P, I32, F32, P, P, P, SZ, P]
+    lib.qlora_linear_fwd_fused.restype = I32
+    lib.qlora_linear_bwd_fused.argtypes = [W, I32, P, P, I64, P, P, I32, F32, P, P, P, P, P, SZ, P]
+    lib.qlora_linear_bwd_fused.restype = I32
+    lib.qlora_nf4_concat_rows.argtypes = [W, I32, W, P]
+    lib.qlora_nf4_concat_rows.restype = I32
     _lib = lib
     return lib
 
@@ -165,3 +175,25 @@ def qlora_lora_merge(w, A, B, r, alpha, out, stream):
 
 def qlora_lora_unmerge(W_merged, n_rows, n_cols, A, B, r, alpha, out, stream):
     return load().qlora_lora_unmerge(W_merged, n_rows, n_cols, A, B, r, alpha, out, stream)
+
+
+def qlora_workspace_bytes_fused(op, M, K, N, r, n_parts):
+    return load().qlora_workspace_bytes_fused(op, M, K, N, r, n_parts)
+
+
+def qlora_linear_fwd_fused(w, n_parts, X, M, A, B, r, alpha, Y, U_saved, workspace, workspace_bytes,
+                           stream):
+    return load().qlora_linear_fwd_fused(ctypes.byref(w), n_parts, X, M, A, B, r, alpha, Y, U_saved,
+                                         workspace, workspace_bytes, stream)
+
+
+def qlora_linear_bwd_fused(w, n_parts, dY, X, M, A, B, r, alpha, U_saved, dX, dA, dB, workspace,
+                           workspace_bytes, stream):
+    return load().qlora_linear_bwd_fused(ctypes.byref(w), n_parts, dY, X, M, A, B, r, alpha, U_saved, dX,
+                                         dA, dB, workspace, workspace_bytes, stream)
+
+
+def qlora_nf4_concat_rows(parts, out, stream):
+    """parts: a sequence of qlora_nf4_weight descriptors."""
+    arr = (qlora_nf4_weight * len(parts))(*parts)
+    return load().qlora_nf4_concat_rows(arr, len(parts), ctypes.byref(out), stream)

@@ -138,26 +138,168 @@ FwdLayout fwd_layout(int64_t M, int64_t K, int64_t N, int r, bool need_u) {
 struct BwdLayout {
   size_t u, bt, v, at, part, total;
 };
-BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N, int r) {
+// U_s [M, R], B^T [r, N], V [M, R], A^T [K, R] (R = parts r), then the fp32 partial sums
+// of the largest LoRA reduction.
+BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N, int r, int parts) {
   BwdLayout L{};
   if (r == 0) return L;
+  const int R = r * parts;
+  const int64_t Np = N / parts;
   size_t off = 0;
   L.u = off;
-  off += align_up(size_t(M) * r * 2);
+  off += align_up(size_t(M) * R * 2);
   L.bt = off;
   off += align_up(size_t(N) * r * 2);
   L.v = off;
-  off += align_up(size_t(M) * r * 2);
+  off += align_up(size_t(M) * R * 2);
   L.at = off;
-  off += align_up(size_t(K) * r * 2);
+  off += align_up(size_t(K) * R * 2);
   L.part = off;
-  size_t p = qlora::reduce_m_workspace(M, N, r);
-  const size_t others[] = {qlora::reduce_m_workspace(M, K, r), qlora::lora_down_workspace(M, K, r),
-                           qlora::lora_down_workspace(M, N, r)};
+  size_t p = qlora::reduce_m_workspace(M, Np, r);
+  const size_t others[] = {qlora::reduce_m_workspace(M, K, R), qlora::lora_down_workspace(M, K, R),
+                           qlora::lora_down_workspace(M, Np, r)};
   for (size_t o : others) p = o > p ? o : p;
   off += align_up(p);
   L.total = off;
   return L;
+}
+
+// Horizontally fused linears: `parts` linears of N / parts weight rows each share X;
+// their adapters are stacked (A [parts r, K], B [N, r]).  parts = 1 is one linear.
+int check_parts(const char *who, int64_t N, int r, int parts) {
+  if (parts < 1 || parts > QLORA_MAX_PARTS)
+    return fail(QLORA_ERR_SHAPE, "%s: n_parts = %d outside [1, %d]", who, parts, QLORA_MAX_PARTS);
+  if (N % parts != 0)
+    return fail(QLORA_ERR_SHAPE, "%s: %lld weight rows do not split into %d equal parts", who,
+                (long long)N, parts);
+  if (int64_t(r) * parts > QLORA_MAX_RANK)
+    return fail(QLORA_ERR_RANK, "%s: stacked rank %d x %d exceeds %d", who, parts, r, QLORA_MAX_RANK);
+  if (parts > 1 && r > 0 && (N / parts) % 256 != 0)
+    return fail(QLORA_ERR_SHAPE, "%s: part rows %lld must be a multiple of 256", who,
+                (long long)(N / parts));
+  return QLORA_OK;
+}
+
+int fwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16_t *X, int64_t M,
+             const uint16_t *A, const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
+             void *workspace, size_t workspace_bytes, void *stream) {
+  int s = check_weight(w);
+  if (s == QLORA_OK) s = check_m(M);
+  if (s == QLORA_OK) s = check_rank(r, alpha);
+  if (s == QLORA_OK) s = check_parts(who, w->n_rows, r, parts);
+  if (s != QLORA_OK) return s;
+  if (!X || !Y) return fail(QLORA_ERR_NULL, "%s: X and Y are required", who);
+  if (r > 0 && (!A || !B)) return fail(QLORA_ERR_NULL, "%s: A and B are required when r > 0", who);
+  if (!aligned16(X) || !aligned16(Y) || (r > 0 && (!aligned16(A) || !aligned16(B))) ||
+      (U_saved && !aligned16(U_saved)))
+    return fail(QLORA_ERR_ALIGN, "%s: tensors must be 16-byte aligned", who);
+  const int64_t K = w->n_cols, N = w->n_rows;
+  const int R = r * parts;
+  const int64_t part_rows = parts > 1 ? N / parts : 0;
+  const FwdLayout L = fwd_layout(M, K, N, R, !U_saved);
+  const bool need_ws = L.total > 0;
+  if (need_ws && (!workspace || workspace_bytes < L.total))
+    return fail(QLORA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, L.total,
+                workspace_bytes);
+  if (need_ws && !aligned16(workspace))
+    return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const qlora::WeightView wv = view(w);
+  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  if (M <= 16) {
+    if (!qlora::gemv_supported(wv, M, R))
+      return fail(QLORA_ERR_SHAPE, "%s: shape exceeds 32-bit buffer offsets", who);
+    s = launched(timed_launch(st, [&] { return qlora::launch_gemv_stream(wv, X, M, A, R, workspace, st); }),
+                 "gemv_stream");
+    if (s != QLORA_OK) return s;
+    return launched(
+        qlora::launch_gemv_finalize(wv, M, B, r, R, part_rows, scale, Y, U_saved, workspace, st),
+        "gemv_finalize");
+  }
+  uint16_t *U = nullptr;
+  if (r > 0) {
+    char *ws = static_cast<char *>(workspace);
+    U = U_saved ? U_saved : reinterpret_cast<uint16_t *>(ws + L.u);
+    s = launched(qlora::launch_lora_down(X, M, K, K, A, K, R, scale, U, R,
+                                         reinterpret_cast<float *>(ws + L.part), st),
+                 "lora_down");
+    if (s != QLORA_OK) return s;
+  }
+  return launched(
+      timed_launch(st, [&] { return qlora::launch_gemm_fwd(wv, X, M, U, R, B, r, part_rows, Y, st); }),
+      "gemm_fwd");
+}
+
+int bwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16_t *dY,
+             const uint16_t *X, int64_t M, const uint16_t *A, const uint16_t *B, int r, float alpha,
+             const uint16_t *U_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB, void *workspace,
+             size_t workspace_bytes, void *stream) {
+  int s = check_weight(w);
+  if (s == QLORA_OK) s = check_m(M);
+  if (s == QLORA_OK) s = check_rank(r, alpha);
+  if (s == QLORA_OK) s = check_parts(who, w->n_rows, r, parts);
+  if (s != QLORA_OK) return s;
+  if (!dY) return fail(QLORA_ERR_NULL, "%s: dY is required", who);
+  if (r > 0 && (!A || !B || !X || !dA || !dB))
+    return fail(QLORA_ERR_NULL, "%s: X, A, B, dA and dB are required when r > 0", who);
+  if (r == 0 && !dX) return fail(QLORA_ERR_NULL, "%s: nothing to compute (r = 0, dX NULL)", who);
+  const void *ptrs[] = {dY, X, A, B, U_saved, dX, dA, dB};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(QLORA_ERR_ALIGN, "%s: tensors must be 16-byte aligned", who);
+  const int64_t K = w->n_cols, N = w->n_rows;
+  const int R = r * parts;
+  const int64_t Np = N / parts;
+  const BwdLayout L = bwd_layout(M, K, N, r, parts);
+  if (r > 0 && (!workspace || workspace_bytes < L.total))
+    return fail(QLORA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, L.total,
+                workspace_bytes);
+  if (r > 0 && !aligned16(workspace))
+    return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const qlora::WeightView wv = view(w);
+  char *ws = static_cast<char *>(workspace);
+  const uint16_t *V = nullptr, *At = nullptr;
+  if (r > 0) {
+    const float scale = alpha / static_cast<float>(r);
+    float *part = reinterpret_cast<float *>(ws + L.part);
+    const uint16_t *U = U_saved;
+    if (!U) {
+      uint16_t *Uw = reinterpret_cast<uint16_t *>(ws + L.u);
+      s = launched(qlora::launch_lora_down(X, M, K, K, A, K, R, scale, Uw, R, part, st), "lora_down(U)");
+      if (s != QLORA_OK) return s;
+      U = Uw;
+    }
+    uint16_t *Bt = reinterpret_cast<uint16_t *>(ws + L.bt);
+    uint16_t *Vw = reinterpret_cast<uint16_t *>(ws + L.v);
+    uint16_t *Atw = reinterpret_cast<uint16_t *>(ws + L.at);
+    s = launched(qlora::launch_transpose_bf16(B, N, r, Bt, st), "transpose(B)");
+    // part q: V[:, q r ..] = bf16(scale dY_q B_q) and dB_q = bf16(dY_q^T U_q), where dY_q is
+    // columns [q Np, (q + 1) Np) of dY and U_q columns [q r, (q + 1) r) of U_s
+    for (int q = 0; q < parts && s == QLORA_OK; ++q) {
+      s = launched(qlora::launch_lora_down(dY + q * Np, M, Np, N, Bt + q * Np, N, r, scale, Vw + q * r, R,
+                                           part, st),
+                   "lora_down(V)");
+      if (s == QLORA_OK)
+        s = launched(qlora::launch_reduce_m(dY + q * Np, M, Np, N, U + q * r, R, r, part, dB + q * Np * r,
+                                            false, st),
+                     "reduce(dB)");
+    }
+    if (s == QLORA_OK)
+      s = launched(qlora::launch_reduce_m(X, M, K, K, Vw, R, R, part, dA, true, st), "reduce(dA)");
+    if (s == QLORA_OK && dX)
+      s = launched(qlora::launch_transpose_bf16(A, R, K, Atw, st), "transpose(A)");
+    if (s != QLORA_OK) return s;
+    V = Vw;
+    At = Atw;
+  }
+  if (dX)
+    return launched(timed_launch(st, [&] { return qlora::launch_gemm_dx(wv, dY, M, V, At, R, dX, st); }),
+                    "gemm_dx");
+  return QLORA_OK;
 }
 
 }  // namespace
@@ -200,9 +342,15 @@ int qlora_nf4_sizes(int64_t n_rows, int64_t n_cols, size_t *code_bytes, int64_t 
 }
 
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int r) {
-  if (M < 1 || K < 1 || N < 1 || K % 64 != 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
-  if (op == 0) return fwd_layout(M, K, N, r, true).total;
-  if (op == 1) return bwd_layout(M, K, N, r).total;
+  return qlora_workspace_bytes_fused(op, M, K, N, r, 1);
+}
+
+size_t qlora_workspace_bytes_fused(int op, int64_t M, int64_t K, int64_t N, int r, int n_parts) {
+  if (M < 1 || K < 1 || N < 1 || K % 64 != 0 || r < 0 || n_parts < 1 || n_parts > QLORA_MAX_PARTS ||
+      N % n_parts != 0 || int64_t(r) * n_parts > QLORA_MAX_RANK)
+    return 0;
+  if (op == 0) return fwd_layout(M, K, N, r * n_parts, true).total;
+  if (op == 1) return bwd_layout(M, K, N, r, n_parts).total;
   return 0;
 }
 
@@ -243,109 +391,84 @@ int qlora_dequantize(const qlora_nf4_weight *w, void *out, int out_dtype, void *
 int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
                      const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
                      void *workspace, size_t workspace_bytes, void *stream) {
-  int s = check_weight(w);
-  if (s == QLORA_OK) s = check_m(M);
-  if (s == QLORA_OK) s = check_rank(r, alpha);
-  if (s != QLORA_OK) return s;
-  if (!X || !Y) return fail(QLORA_ERR_NULL, "linear_fwd: X and Y are required");
-  if (r > 0 && (!A || !B)) return fail(QLORA_ERR_NULL, "linear_fwd: A and B are required when r > 0");
-  if (!aligned16(X) || !aligned16(Y) || (r > 0 && (!aligned16(A) || !aligned16(B))) ||
-      (U_saved && !aligned16(U_saved)))
-    return fail(QLORA_ERR_ALIGN, "linear_fwd: tensors must be 16-byte aligned");
-  const int64_t K = w->n_cols;
-  const FwdLayout L = fwd_layout(M, K, w->n_rows, r, !U_saved);
-  const bool need_ws = L.total > 0;
-  if (need_ws && (!workspace || workspace_bytes < L.total))
-    return fail(QLORA_ERR_WORKSPACE, "linear_fwd: workspace of %zu bytes needed, %zu given", L.total,
-                workspace_bytes);
-  if (need_ws && !aligned16(workspace))
-    return fail(QLORA_ERR_ALIGN, "linear_fwd: workspace must be 16-byte aligned");
-  s = check_device();
-  if (s != QLORA_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const qlora::WeightView wv = view(w);
-  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
-  if (M <= 16) {
-    if (!qlora::gemv_supported(wv, M, r))
-      return fail(QLORA_ERR_SHAPE, "linear_fwd: shape exceeds 32-bit buffer offsets");
-    s = launched(timed_launch(st, [&] { return qlora::launch_gemv_stream(wv, X, M, A, r, workspace, st); }),
-                 "gemv_stream");
-    if (s != QLORA_OK) return s;
-    return launched(qlora::launch_gemv_finalize(wv, M, B, r, scale, Y, U_saved, workspace, st),
-                    "gemv_finalize");
-  }
-  uint16_t *U = nullptr;
-  if (r > 0) {
-    char *ws = static_cast<char *>(workspace);
-    U = U_saved ? U_saved : reinterpret_cast<uint16_t *>(ws + L.u);
-    s = launched(qlora::launch_lora_down(X, M, K, A, r, scale, U,
-                                         reinterpret_cast<float *>(ws + L.part), st),
-                 "lora_down");
-    if (s != QLORA_OK) return s;
-  }
-  return launched(timed_launch(st, [&] { return qlora::launch_gemm_fwd(wv, X, M, U, B, r, Y, st); }),
-                  "gemm_fwd");
+  return fwd_impl("linear_fwd", w, 1, X, M, A, B, r, alpha, Y, U_saved, workspace, workspace_bytes,
+                  stream);
+}
+
+int qlora_linear_fwd_fused(const qlora_nf4_weight *w, int n_parts, const uint16_t *X, int64_t M,
+                           const uint16_t *A, const uint16_t *B, int r, float alpha, uint16_t *Y,
+                           uint16_t *U_saved, void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_impl("linear_fwd_fused", w, n_parts, X, M, A, B, r, alpha, Y, U_saved, workspace,
+                  workspace_bytes, stream);
 }
 
 int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16_t *X, int64_t M,
                      const uint16_t *A, const uint16_t *B, int r, float alpha,
                      const uint16_t *U_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB,
                      void *workspace, size_t workspace_bytes, void *stream) {
-  int s = check_weight(w);
-  if (s == QLORA_OK) s = check_m(M);
-  if (s == QLORA_OK) s = check_rank(r, alpha);
+  return bwd_impl("linear_bwd", w, 1, dY, X, M, A, B, r, alpha, U_saved, dX, dA, dB, workspace,
+                  workspace_bytes, stream);
+}
+
+int qlora_linear_bwd_fused(const qlora_nf4_weight *w, int n_parts, const uint16_t *dY, const uint16_t *X,
+                           int64_t M, const uint16_t *A, const uint16_t *B, int r, float alpha,
+                           const uint16_t *U_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_impl("linear_bwd_fused", w, n_parts, dY, X, M, A, B, r, alpha, U_saved, dX, dA, dB,
+                  workspace, workspace_bytes, stream);
+}
+
+int qlora_nf4_concat_rows(const qlora_nf4_weight *parts, int n_parts, const qlora_nf4_weight *out,
+                          void *stream) {
+  if (!parts || !out) return fail(QLORA_ERR_NULL, "nf4_concat_rows: parts and out are required");
+  if (n_parts < 1 || n_parts > QLORA_MAX_PARTS)
+    return fail(QLORA_ERR_SHAPE, "nf4_concat_rows: n_parts = %d outside [1, %d]", n_parts, QLORA_MAX_PARTS);
+  int64_t rows = 0;
+  const int64_t K = parts[0].n_cols;
+  for (int i = 0; i < n_parts; ++i) {
+    int s = check_weight(&parts[i]);
+    if (s != QLORA_OK) return s;
+    if (parts[i].n_cols != K)
+      return fail(QLORA_ERR_SHAPE, "nf4_concat_rows: part %d has %lld columns, part 0 %lld", i,
+                  (long long)parts[i].n_cols, (long long)K);
+    // the double-quantization groups of a part must end on a group boundary for the
+    // concatenated arrays to be the quantization of the concatenated matrix
+    if (i + 1 < n_parts && (parts[i].n_rows * K / qlora::kBlock) % qlora::kGroup != 0)
+      return fail(QLORA_ERR_SHAPE,
+                  "nf4_concat_rows: part %d holds %lld blocks, not a multiple of %d (its last "
+                  "double-quantization group would straddle the next part)",
+                  i, (long long)(parts[i].n_rows * K / qlora::kBlock), qlora::kGroup);
+    rows += parts[i].n_rows;
+  }
+  int s = check_weight(out);
   if (s != QLORA_OK) return s;
-  if (!dY) return fail(QLORA_ERR_NULL, "linear_bwd: dY is required");
-  if (r > 0 && (!A || !B || !X || !dA || !dB))
-    return fail(QLORA_ERR_NULL, "linear_bwd: X, A, B, dA and dB are required when r > 0");
-  if (r == 0 && !dX) return fail(QLORA_ERR_NULL, "linear_bwd: nothing to compute (r = 0, dX NULL)");
-  const void *ptrs[] = {dY, X, A, B, U_saved, dX, dA, dB};
-  for (const void *p : ptrs)
-    if (p && !aligned16(p)) return fail(QLORA_ERR_ALIGN, "linear_bwd: tensors must be 16-byte aligned");
-  const int64_t K = w->n_cols, N = w->n_rows;
-  const BwdLayout L = bwd_layout(M, K, N, r);
-  if (r > 0 && (!workspace || workspace_bytes < L.total))
-    return fail(QLORA_ERR_WORKSPACE, "linear_bwd: workspace of %zu bytes needed, %zu given", L.total,
-                workspace_bytes);
-  if (r > 0 && !aligned16(workspace))
-    return fail(QLORA_ERR_ALIGN, "linear_bwd: workspace must be 16-byte aligned");
+  if (out->n_rows != rows || out->n_cols != K)
+    return fail(QLORA_ERR_SHAPE, "nf4_concat_rows: out is [%lld, %lld], the parts make [%lld, %lld]",
+                (long long)out->n_rows, (long long)out->n_cols, (long long)rows, (long long)K);
   s = check_device();
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const qlora::WeightView wv = view(w);
-  char *ws = static_cast<char *>(workspace);
-  const uint16_t *V = nullptr, *At = nullptr;
-  if (r > 0) {
-    const float scale = alpha / static_cast<float>(r);
-    const uint16_t *U = U_saved;
-    if (!U) {
-      uint16_t *Uw = reinterpret_cast<uint16_t *>(ws + L.u);
-      s = launched(qlora::launch_lora_down(X, M, K, A, r, scale, Uw,
-                                           reinterpret_cast<float *>(ws + L.part), st),
-                   "lora_down(U)");
-      if (s != QLORA_OK) return s;
-      U = Uw;
-    }
-    uint16_t *Bt = reinterpret_cast<uint16_t *>(ws + L.bt);
-    uint16_t *Vw = reinterpret_cast<uint16_t *>(ws + L.v);
-    uint16_t *Atw = reinterpret_cast<uint16_t *>(ws + L.at);
-    float *part = reinterpret_cast<float *>(ws + L.part);
-    s = launched(qlora::launch_transpose_bf16(B, N, r, Bt, st), "transpose(B)");
-    if (s == QLORA_OK)
-      s = launched(qlora::launch_lora_down(dY, M, N, Bt, r, scale, Vw, part, st), "lora_down(V)");
-    if (s == QLORA_OK)
-      s = launched(qlora::launch_reduce_m(dY, M, N, U, r, part, dB, false, st), "reduce(dB)");
-    if (s == QLORA_OK)
-      s = launched(qlora::launch_reduce_m(X, M, K, Vw, r, part, dA, true, st), "reduce(dA)");
-    if (s == QLORA_OK && dX)
-      s = launched(qlora::launch_transpose_bf16(A, r, K, Atw, st), "transpose(A)");
+  size_t oc = 0, ob = 0, og = 0;
+  for (int i = 0; i < n_parts; ++i) {
+    const int64_t nb = parts[i].n_rows * K / qlora::kBlock;
+    const int64_t ng = (nb + qlora::kGroup - 1) / qlora::kGroup;
+    const size_t cb = static_cast<size_t>(parts[i].n_rows * K / 2);
+    // the descriptor's arrays are declared const for the compute entries; here they
+    // are the caller's destination
+    auto dst = [](const void *p, size_t off) { return static_cast<char *>(const_cast<void *>(p)) + off; };
+    hipError_t e = hipMemcpyAsync(dst(out->codes, oc), parts[i].codes, cb, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(dst(out->absmax_q, ob), parts[i].absmax_q, nb, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(dst(out->dq_scale, og * 4), parts[i].dq_scale, ng * 4, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(dst(out->dq_offset, og * 4), parts[i].dq_offset, ng * 4, hipMemcpyDeviceToDevice, st);
+    s = launched(e, "nf4_concat_rows");
     if (s != QLORA_OK) return s;
-    V = Vw;
-    At = Atw;
+    oc += cb;
+    ob += nb;
+    og += ng;
   }
-  if (dX)
-    return launched(timed_launch(st, [&] { return qlora::launch_gemm_dx(wv, dY, M, V, At, r, dX, st); }),
-                    "gemm_dx");
   return QLORA_OK;
 }
 

@@ -53,6 +53,9 @@ struct GemmParams {
   uint16_t *C;         // [M, No]
   int M, No, Kc, r;
   LevelTable lvl;  // NF4 codebook
+  int lda2;       // row pitch of A2 (r, or the stacked rank of fused linears)
+  int part_rows;  // fused linears: output columns [q P, q P + P) use A2 columns
+                  // [q r, q r + r); 0 = one linear (tiles never straddle parts)
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -116,9 +119,11 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[8][2]) {
 __device__ __forceinline__ void lora_steps(const GemmParams &p, int m0, int c0,
                                            f32x16_t (&acc)[8][2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = p.r;
-  const bool vec = (r % 8) == 0;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A2, static_cast<uint32_t>(uint64_t(p.M) * r * 2));
+  const int r = p.r, lda2 = p.lda2;
+  const bool vec = (r % 8) == 0 && (lda2 % 8) == 0;
+  // fused linears: this tile's part picks its rank columns of A2
+  const uint16_t *const A2 = p.A2 + (p.part_rows > 0 ? (c0 / p.part_rows) * r : 0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A2, static_cast<uint32_t>(uint64_t(p.M) * lda2 * 2));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B2, static_cast<uint32_t>(uint64_t(p.No) * r * 2));
   for (int rk = 0; rk < r; rk += 16) {
     const int j0 = rk + (lane >> 5) * 8;
@@ -144,14 +149,14 @@ __device__ __forceinline__ void lora_steps(const GemmParams &p, int m0, int c0,
     for (int i = 0; i < 8; ++i) {
       const int row = m0 + i * 32 + (lane & 31);
       if (vec) {
-        xb[i] = buf_load16(ra, (row < p.M && j0 < r) ? (static_cast<uint32_t>(row) * r + j0) * 2 : kOOB);
+        xb[i] = buf_load16(ra, (row < p.M && j0 < r) ? (static_cast<uint32_t>(row) * lda2 + j0) * 2 : kOOB);
       } else {
         u32x4_t v = {0u, 0u, 0u, 0u};
         if (row < p.M)
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            const uint32_t lo = (j0 + e < r) ? p.A2[static_cast<int64_t>(row) * r + j0 + e] : 0u;
-            const uint32_t hi = (j0 + e + 1 < r) ? p.A2[static_cast<int64_t>(row) * r + j0 + e + 1] : 0u;
+            const uint32_t lo = (j0 + e < r) ? A2[static_cast<int64_t>(row) * lda2 + j0 + e] : 0u;
+            const uint32_t hi = (j0 + e + 1 < r) ? A2[static_cast<int64_t>(row) * lda2 + j0 + e + 1] : 0u;
             v[e / 2] = lo | (hi << 16);
           }
         xb[i] = v;
@@ -798,7 +803,7 @@ bool fits_32bit(int64_t M, int64_t N, int64_t K, int r) {
 
 GemmParams make_params(const uint16_t *A, const WeightView &w, const uint16_t *A2,
                        const uint16_t *B2, uint16_t *C, int64_t M, int64_t No, int64_t Kc, int r) {
-  GemmParams p{A, w, A2, B2, C, static_cast<int>(M), static_cast<int>(No), static_cast<int>(Kc), r, {}};
+  GemmParams p{A, w, A2, B2, C, static_cast<int>(M), static_cast<int>(No), static_cast<int>(Kc), r, {}, r, 0};
   for (int i = 0; i < 16; ++i) p.lvl.q[i] = codebook().q[i];
   return p;
 }
@@ -810,9 +815,13 @@ unsigned grid_size(int64_t M, int64_t No) {
 }  // namespace
 
 hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
-                           const uint16_t *Bl, int r, uint16_t *Y, hipStream_t stream) {
-  if (!fits_32bit(M, w.n_rows, w.n_cols, r) || M > 0x7fffffff) return hipErrorInvalidValue;
-  const GemmParams p = make_params(X, w, U, Bl, Y, M, w.n_rows, w.n_cols, r);
+                           int ldu, const uint16_t *Bl, int r, int64_t part_rows, uint16_t *Y,
+                           hipStream_t stream) {
+  if (!fits_32bit(M, w.n_rows, w.n_cols, ldu) || M > 0x7fffffff) return hipErrorInvalidValue;
+  if (part_rows > 0 && (part_rows % TN != 0 || w.n_rows % part_rows != 0)) return hipErrorInvalidValue;
+  GemmParams p = make_params(X, w, U, Bl, Y, M, w.n_rows, w.n_cols, r);
+  p.lda2 = ldu;
+  p.part_rows = static_cast<int>(part_rows);
   hipLaunchKernelGGL(gemm_fwd_kernel, dim3(grid_size(M, w.n_rows)), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }

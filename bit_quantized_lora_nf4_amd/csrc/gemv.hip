@@ -274,25 +274,28 @@ __device__ __forceinline__ float ordered_sum(const float *__restrict__ x, int64_
 
 constexpr int FT = 64;  // finalize threads per workgroup
 
-// Y[m, n] = bf16(sum_s P[s][n][m] + sum_j U_s[m, j] Bl[n, j]); U_s = bf16(scale * sum_s UP).
+// Y[m, n] = bf16(sum_s P[s][n][m] + sum_j U_s[m, q r + j] Bl[n, j]); U_s = bf16(scale * sum_s UP)
+// over the R stacked ranks; q = n / part_rows is the part of a fused linear (0 for one).
 __global__ __launch_bounds__(FT) void gemv_finalize_kernel(const float *__restrict__ P,
                                                            const float *__restrict__ UP, int S, int N,
                                                            int M, const uint16_t *__restrict__ Bl,
-                                                           int r, float scale, uint16_t *__restrict__ Y,
+                                                           int r, int R, int part_rows, float scale,
+                                                           uint16_t *__restrict__ Y,
                                                            uint16_t *__restrict__ U_saved) {
   __shared__ float us[GMAXM * kMaxRank];
-  if (r > 0) {
-    for (int e = threadIdx.x; e < M * r; e += FT) {
-      const int m = e / r, j = e % r;
-      const uint16_t u = to_bf16(scale * ordered_sum(UP + m * r + j, static_cast<int64_t>(M) * r, S));
+  if (R > 0) {
+    for (int e = threadIdx.x; e < M * R; e += FT) {
+      const int m = e / R, j = e % R;
+      const uint16_t u = to_bf16(scale * ordered_sum(UP + m * R + j, static_cast<int64_t>(M) * R, S));
       us[e] = bf16_to_f32(u);
-      if (U_saved && blockIdx.x == 0) U_saved[m * r + j] = u;
+      if (U_saved && blockIdx.x == 0) U_saved[m * R + j] = u;
     }
     __syncthreads();
   }
   const int n = blockIdx.x * FT + threadIdx.x;
   if (n >= N) return;
   const uint16_t *brow = Bl + static_cast<int64_t>(n) * r;
+  const float *uq = us + (part_rows > 0 ? (n / part_rows) * r : 0);
   for (int m = 0; m < M; ++m) {
     float y = ordered_sum(P + static_cast<int64_t>(n) * M + m, static_cast<int64_t>(N) * M, S);
     if ((r & 7) == 0) {
@@ -300,12 +303,12 @@ __global__ __launch_bounds__(FT) void gemv_finalize_kernel(const float *__restri
         const u32x4_t bv = *reinterpret_cast<const u32x4_t *>(brow + j0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          y = __builtin_fmaf(us[m * r + j0 + 2 * e], bf16_lo(bv[e]), y);
-          y = __builtin_fmaf(us[m * r + j0 + 2 * e + 1], bf16_hi(bv[e]), y);
+          y = __builtin_fmaf(uq[m * R + j0 + 2 * e], bf16_lo(bv[e]), y);
+          y = __builtin_fmaf(uq[m * R + j0 + 2 * e + 1], bf16_hi(bv[e]), y);
         }
       }
     } else {
-      for (int j = 0; j < r; ++j) y = __builtin_fmaf(us[m * r + j], bf16_to_f32(brow[j]), y);
+      for (int j = 0; j < r; ++j) y = __builtin_fmaf(uq[m * R + j], bf16_to_f32(brow[j]), y);
     }
     Y[static_cast<int64_t>(m) * N + n] = to_bf16(y);
   }
@@ -378,13 +381,15 @@ hipError_t launch_gemv_stream(const WeightView &w, const uint16_t *X, int64_t M,
   }
 }
 
-hipError_t launch_gemv_finalize(const WeightView &w, int64_t M, const uint16_t *Bl, int r, float scale,
-                                uint16_t *Y, uint16_t *U_saved, void *ws, hipStream_t stream) {
-  if (!gemv_supported(w, M, r)) return hipErrorInvalidValue;
+hipError_t launch_gemv_finalize(const WeightView &w, int64_t M, const uint16_t *Bl, int r, int R,
+                                int64_t part_rows, float scale, uint16_t *Y, uint16_t *U_saved,
+                                void *ws, hipStream_t stream) {
+  if (!gemv_supported(w, M, R) || R < r || (part_rows > 0 && w.n_rows % part_rows != 0))
+    return hipErrorInvalidValue;
   const int64_t N = w.n_rows, K = w.n_cols;
   hipLaunchKernelGGL(gemv_finalize_kernel, dim3(static_cast<unsigned>((N + FT - 1) / FT)), dim3(FT), 0,
                      stream, gemv_p(ws), gemv_up(ws, M, K, N), gemv_slices(K), static_cast<int>(N),
-                     static_cast<int>(M), Bl, r, scale, Y, U_saved);
+                     static_cast<int>(M), Bl, r, R, static_cast<int>(part_rows), scale, Y, U_saved);
   return hipGetLastError();
 }
 

@@ -34,8 +34,8 @@ constexpr uint64_t k4G = 0xFFFFFFF0ull;
 // ends with 4 consecutive j of one m: 16-byte partial stores.
 template <int RT>
 __global__ __launch_bounds__(NT) void lora_down_partial_kernel(
-    const uint16_t *__restrict__ IN, int M, int Kc, const uint16_t *__restrict__ WT, int r, int KR,
-    float *__restrict__ P) {
+    const uint16_t *__restrict__ IN, int M, int Kc, int ldin, const uint16_t *__restrict__ WT, int ldwt,
+    int r, int KR, float *__restrict__ P) {
   __shared__ f32x16_t red[3][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m0 = blockIdx.x * 64;
@@ -43,8 +43,8 @@ __global__ __launch_bounds__(NT) void lora_down_partial_kernel(
   const int kq = KR / 4;
   const int wbeg = ks * KR + wave * kq;
   const int wend = min(Kc, wbeg + kq);
-  const __amdgpu_buffer_rsrc_t rin = make_rsrc(IN, static_cast<uint32_t>(uint64_t(M) * Kc * 2));
-  const __amdgpu_buffer_rsrc_t rwt = make_rsrc(WT, static_cast<uint32_t>(uint64_t(r) * Kc * 2));
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(IN, static_cast<uint32_t>(uint64_t(M) * ldin * 2));
+  const __amdgpu_buffer_rsrc_t rwt = make_rsrc(WT, static_cast<uint32_t>(uint64_t(r) * ldwt * 2));
   const int kl = (lane >> 5) * 8;
 
   f32x16_t acc[2][RT];
@@ -61,13 +61,13 @@ __global__ __launch_bounds__(NT) void lora_down_partial_kernel(
   for (int i = 0; i < 2; ++i) {
     const int row = m0 + i * 32 + (lane & 31);
     in_ok[i] = row < M;
-    in_row[i] = static_cast<uint32_t>(row) * Kc * 2;
+    in_row[i] = static_cast<uint32_t>(row) * ldin * 2;
   }
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int j = t * 32 + (lane & 31);
     wt_ok[t] = j < r;
-    wt_row[t] = static_cast<uint32_t>(j) * Kc * 2;
+    wt_row[t] = static_cast<uint32_t>(j) * ldwt * 2;
   }
 
   for (int k = wbeg; k < wend; k += 64) {
@@ -132,16 +132,16 @@ constexpr int PD = 20;  // dwords per LDS row: 16 m-pairs + 4 padding
 
 template <int RT, bool JMAJOR>
 __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
-    const uint16_t *__restrict__ IN, int M, int No, const uint16_t *__restrict__ S, int r, int MR,
-    float *__restrict__ P) {
+    const uint16_t *__restrict__ IN, int M, int No, int ldin, const uint16_t *__restrict__ S, int lds,
+    int r, int MR, float *__restrict__ P) {
   __shared__ __attribute__((aligned(16))) uint32_t sIn[64 * PD];
   __shared__ __attribute__((aligned(16))) uint32_t sS[RT * 32 * PD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb0 = blockIdx.x * 64;
   const int sp = blockIdx.y;
   const int mb = sp * MR, me = min(M, mb + MR);
-  const __amdgpu_buffer_rsrc_t rin = make_rsrc(IN, static_cast<uint32_t>(uint64_t(M) * No * 2));
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, static_cast<uint32_t>(uint64_t(M) * r * 2));
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(IN, static_cast<uint32_t>(uint64_t(M) * ldin * 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, static_cast<uint32_t>(uint64_t(M) * lds * 2));
 
   // load tasks: (pair p, 8-column chunk c) of IN (128 tasks) then of S (RT*64 tasks)
   constexpr int NTASK = 128 + RT * 64;
@@ -157,8 +157,8 @@ __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
         const int p = task & 15, c = task >> 4;
         const int m = mstep + 2 * p, col = nb0 + c * 8;
         if (col < No) {
-          if (m < me) oa = (static_cast<uint32_t>(m) * No + col) * 2;
-          if (m + 1 < me) ob = (static_cast<uint32_t>(m + 1) * No + col) * 2;
+          if (m < me) oa = (static_cast<uint32_t>(m) * ldin + col) * 2;
+          if (m + 1 < me) ob = (static_cast<uint32_t>(m + 1) * ldin + col) * 2;
         }
         ra[q] = buf_load16(rin, oa);
         rb[q] = buf_load16(rin, ob);
@@ -167,8 +167,8 @@ __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
         const int p = t2 & 15, c = t2 >> 4;
         const int m = mstep + 2 * p, col = c * 8;
         if (col < r) {
-          if (m < me) oa = (static_cast<uint32_t>(m) * r + col) * 2;
-          if (m + 1 < me) ob = (static_cast<uint32_t>(m + 1) * r + col) * 2;
+          if (m < me) oa = (static_cast<uint32_t>(m) * lds + col) * 2;
+          if (m + 1 < me) ob = (static_cast<uint32_t>(m + 1) * lds + col) * 2;
         }
         ra[q] = buf_load16(rs, oa);
         rb[q] = buf_load16(rs, ob);
@@ -245,27 +245,29 @@ __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
   }
 }
 
-// OUT[i] = bf16(scale * sum_s P[s][i]) for i < count (count % 4 == 0), fixed order.
+// OUT = bf16(scale * sum_s P[s]) for the `count` partial sums (count % 4 == 0) laid out
+// as rows of `cols` values (cols % 4 == 0), written with row pitch ldout; fixed order.
 __global__ __launch_bounds__(NT) void finalize_kernel(const float *__restrict__ P, int splits,
-                                                      int64_t count, float scale,
-                                                      uint16_t *__restrict__ OUT) {
+                                                      int64_t count, int64_t cols, int64_t ldout,
+                                                      float scale, uint16_t *__restrict__ OUT) {
   const int64_t n4 = count / 4;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < n4;
        i += static_cast<int64_t>(gridDim.x) * NT) {
     f32x4_t s = reinterpret_cast<const f32x4_t *>(P)[i];
     for (int k = 1; k < splits; ++k) s += reinterpret_cast<const f32x4_t *>(P + k * count)[i];
     u32x2_t o = {pack_bf16x2(s[0] * scale, s[1] * scale), pack_bf16x2(s[2] * scale, s[3] * scale)};
-    reinterpret_cast<u32x2_t *>(OUT)[i] = o;
+    const int64_t e = 4 * i, row = e / cols, col = e % cols;
+    *reinterpret_cast<u32x2_t *>(OUT + row * ldout + col) = o;
   }
 }
 
 // ---------------------------------------------------------------------------------
 // Generic kernels (any row length or rank): simple and unvectorized.
-__device__ __forceinline__ u32x4_t load8(const uint16_t *p, int64_t rows, int64_t cols, int64_t row,
-                                         int64_t col) {
+__device__ __forceinline__ u32x4_t load8(const uint16_t *p, int64_t rows, int64_t cols, int64_t ld,
+                                         int64_t row, int64_t col) {
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (row >= rows || col >= cols) return v;
-  const uint16_t *src = p + row * cols + col;
+  const uint16_t *src = p + row * ld + col;
   uint16_t t[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) t[e] = (col + e < cols) ? src[e] : uint16_t(0);
@@ -277,8 +279,8 @@ __device__ __forceinline__ u32x4_t load8(const uint16_t *p, int64_t rows, int64_
 // OUT[M, r] = bf16(scale * IN[M, Kc] . WT[r, Kc]^T); one wave per 32 rows.
 template <int RT>
 __global__ __launch_bounds__(NT) void lora_down_generic_kernel(
-    const uint16_t *__restrict__ IN, int64_t M, int64_t Kc, const uint16_t *__restrict__ WT, int r,
-    float scale, uint16_t *__restrict__ OUT) {
+    const uint16_t *__restrict__ IN, int64_t M, int64_t Kc, int64_t ldin, const uint16_t *__restrict__ WT,
+    int64_t ldwt, int r, float scale, uint16_t *__restrict__ OUT, int64_t ldout) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 128 + wave * 32 + (lane & 31);
   f32x16_t acc[RT];
@@ -288,10 +290,10 @@ __global__ __launch_bounds__(NT) void lora_down_generic_kernel(
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
   for (int64_t k = 0; k < Kc; k += 16) {
     const int64_t kk = k + (lane >> 5) * 8;
-    const u32x4_t a = load8(IN, M, Kc, row, kk);
+    const u32x4_t a = load8(IN, M, Kc, ldin, row, kk);
 #pragma unroll
     for (int t = 0; t < RT; ++t)
-      acc[t] = mfma32x32x16(a, load8(WT, r, Kc, t * 32 + (lane & 31), kk), acc[t]);
+      acc[t] = mfma32x32x16(a, load8(WT, r, Kc, ldwt, t * 32 + (lane & 31), kk), acc[t]);
   }
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(NT) void lora_down_generic_kernel(
     for (int e = 0; e < 16; ++e) {
       const int64_t orow = static_cast<int64_t>(blockIdx.x) * 128 + wave * 32 + (e >> 2) * 8 +
                            (lane >> 5) * 4 + (e & 3);
-      if (orow < M) OUT[orow * r + col] = to_bf16(acc[t][e] * scale);
+      if (orow < M) OUT[orow * ldout + col] = to_bf16(acc[t][e] * scale);
     }
   }
 }
@@ -310,8 +312,8 @@ __global__ __launch_bounds__(NT) void lora_down_generic_kernel(
 constexpr int GMS = 256;
 template <int RT>
 __global__ __launch_bounds__(NT) void reduce_m_generic_kernel(
-    const uint16_t *__restrict__ IN, int64_t M, int64_t No, const uint16_t *__restrict__ S, int r,
-    float *__restrict__ P) {
+    const uint16_t *__restrict__ IN, int64_t M, int64_t No, int64_t ldin, const uint16_t *__restrict__ S,
+    int64_t lds, int r, float *__restrict__ P) {
   __shared__ uint16_t sIn[32][128 + 2];
   __shared__ uint16_t sS[32][RT * 32 + 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -328,12 +330,12 @@ __global__ __launch_bounds__(NT) void reduce_m_generic_kernel(
     for (int i = tid; i < 32 * 128; i += NT) {
       const int rr = i / 128, cc = i % 128;
       const int64_t m = mb + rr, c = c0 + cc;
-      sIn[rr][cc] = (m < mend && c < No) ? IN[m * No + c] : uint16_t(0);
+      sIn[rr][cc] = (m < mend && c < No) ? IN[m * ldin + c] : uint16_t(0);
     }
     for (int i = tid; i < 32 * RT * 32; i += NT) {
       const int rr = i / (RT * 32), cc = i % (RT * 32);
       const int64_t m = mb + rr;
-      sS[rr][cc] = (m < mend && cc < r) ? S[m * r + cc] : uint16_t(0);
+      sS[rr][cc] = (m < mend && cc < r) ? S[m * lds + cc] : uint16_t(0);
     }
     __syncthreads();
 #pragma unroll
@@ -429,44 +431,50 @@ MSplit m_split(int64_t M, int64_t No) {
   return {static_cast<int>(sp), static_cast<int>(MR)};
 }
 
-bool down_fast(int64_t M, int64_t Kc, int r) {
-  return Kc % 8 == 0 && r % 8 == 0 && uint64_t(M) * Kc * 2 <= k4G && uint64_t(r) * Kc * 2 <= k4G &&
-         M < (int64_t(1) << 30);
+bool down_fast(int64_t M, int64_t Kc, int64_t ldin, int64_t ldwt, int r, int64_t ldout) {
+  return Kc % 8 == 0 && r % 8 == 0 && ldin % 8 == 0 && ldwt % 8 == 0 && ldout % 4 == 0 &&
+         uint64_t(M) * ldin * 2 <= k4G && uint64_t(r) * ldwt * 2 <= k4G && M < (int64_t(1) << 30) &&
+         ldin < (int64_t(1) << 30) && ldwt < (int64_t(1) << 30);
 }
-bool reduce_fast(int64_t M, int64_t No, int r) {
-  return No % 8 == 0 && r % 8 == 0 && uint64_t(M) * No * 2 <= k4G && uint64_t(M) * r * 2 <= k4G &&
-         No < (int64_t(1) << 30);
+bool reduce_fast(int64_t M, int64_t No, int64_t ldin, int64_t lds, int r) {
+  return No % 8 == 0 && r % 8 == 0 && ldin % 8 == 0 && lds % 8 == 0 && uint64_t(M) * ldin * 2 <= k4G &&
+         uint64_t(M) * lds * 2 <= k4G && No < (int64_t(1) << 30) && ldin < (int64_t(1) << 30) &&
+         lds < (int64_t(1) << 30);
 }
 
-hipError_t launch_finalize(const float *P, int splits, int64_t count, float scale, uint16_t *OUT,
-                           hipStream_t stream) {
+hipError_t launch_finalize(const float *P, int splits, int64_t count, int64_t cols, int64_t ldout,
+                           float scale, uint16_t *OUT, hipStream_t stream) {
   int64_t blocks = (count / 4 + NT - 1) / NT;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(NT), 0, stream, P,
-                     splits, count, scale, OUT);
+                     splits, count, cols, ldout, scale, OUT);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Sized for dense operands: any strided call that takes the fast path is also fast
+// dense (the pitches only add conditions), so the same bound holds for slices.
 size_t lora_down_workspace(int64_t M, int64_t Kc, int r) {
-  if (r <= 0 || !down_fast(M, Kc, r)) return 0;
+  if (r <= 0 || !down_fast(M, Kc, Kc, Kc, r, r)) return 0;
   return static_cast<size_t>(down_split(M, Kc).ksplit) * M * r * sizeof(float);
 }
 
-hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, const uint16_t *WT, int r,
-                            float scale, uint16_t *OUT, float *ws, hipStream_t stream) {
+hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, int64_t ldin, const uint16_t *WT,
+                            int64_t ldwt, int r, float scale, uint16_t *OUT, int64_t ldout, float *ws,
+                            hipStream_t stream) {
   const int rt = (r + 31) / 32;
   if (rt < 1 || rt > 8) return hipErrorInvalidValue;
-  if (down_fast(M, Kc, r)) {
+  if (down_fast(M, Kc, ldin, ldwt, r, ldout)) {
     const DownSplit sp = down_split(M, Kc);
     dim3 grid(static_cast<unsigned>((M + 63) / 64), static_cast<unsigned>(sp.ksplit)), block(NT);
     switch (rt) {
 #define QLORA_CASE(T)                                                                            \
   case T:                                                                                        \
     hipLaunchKernelGGL(lora_down_partial_kernel<T>, grid, block, 0, stream, IN,                  \
-                       static_cast<int>(M), static_cast<int>(Kc), WT, r, sp.KR, ws);             \
+                       static_cast<int>(M), static_cast<int>(Kc), static_cast<int>(ldin), WT,     \
+                       static_cast<int>(ldwt), r, sp.KR, ws);                                     \
     break;
       QLORA_CASE(1) QLORA_CASE(2) QLORA_CASE(3) QLORA_CASE(4)
       QLORA_CASE(5) QLORA_CASE(6) QLORA_CASE(7) QLORA_CASE(8)
@@ -474,14 +482,14 @@ hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, const uin
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_finalize(ws, sp.ksplit, M * r, scale, OUT, stream);
+    return launch_finalize(ws, sp.ksplit, M * r, r, ldout, scale, OUT, stream);
   }
   dim3 grid(static_cast<unsigned>((M + 127) / 128)), block(NT);
   switch (rt) {
 #define QLORA_CASE(T)                                                                         \
   case T:                                                                                     \
-    hipLaunchKernelGGL(lora_down_generic_kernel<T>, grid, block, 0, stream, IN, M, Kc, WT, r, \
-                       scale, OUT);                                                           \
+    hipLaunchKernelGGL(lora_down_generic_kernel<T>, grid, block, 0, stream, IN, M, Kc, ldin, WT, \
+                       ldwt, r, scale, OUT, ldout);                                              \
     break;
     QLORA_CASE(1) QLORA_CASE(2) QLORA_CASE(3) QLORA_CASE(4)
     QLORA_CASE(5) QLORA_CASE(6) QLORA_CASE(7) QLORA_CASE(8)
@@ -499,28 +507,30 @@ hipError_t launch_transpose_bf16(const uint16_t *IN, int64_t R, int64_t C, uint1
 
 size_t reduce_m_workspace(int64_t M, int64_t No, int r) {
   if (r <= 0) return 0;
-  if (reduce_fast(M, No, r)) return static_cast<size_t>(m_split(M, No).splits) * No * r * sizeof(float);
+  if (reduce_fast(M, No, No, r, r)) return static_cast<size_t>(m_split(M, No).splits) * No * r * sizeof(float);
   const int64_t splits = (M + GMS - 1) / GMS;
   return static_cast<size_t>(splits) * No * r * sizeof(float);
 }
 
-hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, const uint16_t *S, int r,
-                           float *partials, uint16_t *OUT, bool trans_out, hipStream_t stream) {
+hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, int64_t ldin, const uint16_t *S,
+                           int64_t lds, int r, float *partials, uint16_t *OUT, bool trans_out,
+                           hipStream_t stream) {
   const int rt = (r + 31) / 32;
   if (rt < 1 || rt > 8) return hipErrorInvalidValue;
-  if (reduce_fast(M, No, r)) {
+  if (reduce_fast(M, No, ldin, lds, r)) {
     const MSplit sp = m_split(M, No);
     dim3 grid(static_cast<unsigned>((No + 63) / 64), static_cast<unsigned>(sp.splits)), block(NT);
     const int Mi = static_cast<int>(M), Noi = static_cast<int>(No);
+    const int Ldi = static_cast<int>(ldin), Lds = static_cast<int>(lds);
     switch (rt * 2 + (trans_out ? 1 : 0)) {
 #define QLORA_CASE(T)                                                                              \
   case 2 * T:                                                                                      \
-    hipLaunchKernelGGL((reduce_m_partial_kernel<T, false>), grid, block, 0, stream, IN, Mi, Noi, S, \
-                       r, sp.MR, partials);                                                        \
+    hipLaunchKernelGGL((reduce_m_partial_kernel<T, false>), grid, block, 0, stream, IN, Mi, Noi,    \
+                       Ldi, S, Lds, r, sp.MR, partials);                                           \
     break;                                                                                         \
   case 2 * T + 1:                                                                                  \
-    hipLaunchKernelGGL((reduce_m_partial_kernel<T, true>), grid, block, 0, stream, IN, Mi, Noi, S,  \
-                       r, sp.MR, partials);                                                        \
+    hipLaunchKernelGGL((reduce_m_partial_kernel<T, true>), grid, block, 0, stream, IN, Mi, Noi,     \
+                       Ldi, S, Lds, r, sp.MR, partials);                                           \
     break;
       QLORA_CASE(1) QLORA_CASE(2) QLORA_CASE(3) QLORA_CASE(4)
       QLORA_CASE(5) QLORA_CASE(6) QLORA_CASE(7) QLORA_CASE(8)
@@ -528,15 +538,16 @@ hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, const uint
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_finalize(partials, sp.splits, No * r, 1.0f, OUT, stream);
+    // [No, r] (or [r, No] for trans_out) dense rows
+    return launch_finalize(partials, sp.splits, No * r, No * r, No * r, 1.0f, OUT, stream);
   }
   const int64_t splits = (M + GMS - 1) / GMS;
   dim3 grid(static_cast<unsigned>((No + 127) / 128), static_cast<unsigned>(splits)), block(NT);
   switch (rt) {
 #define QLORA_CASE(T)                                                                            \
   case T:                                                                                        \
-    hipLaunchKernelGGL(reduce_m_generic_kernel<T>, grid, block, 0, stream, IN, M, No, S, r,      \
-                       partials);                                                                \
+    hipLaunchKernelGGL(reduce_m_generic_kernel<T>, grid, block, 0, stream, IN, M, No, ldin, S, \
+                       lds, r, partials);                                                        \
     break;
     QLORA_CASE(1) QLORA_CASE(2) QLORA_CASE(3) QLORA_CASE(4)
     QLORA_CASE(5) QLORA_CASE(6) QLORA_CASE(7) QLORA_CASE(8)

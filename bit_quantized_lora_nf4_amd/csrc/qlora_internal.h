@@ -47,19 +47,23 @@ hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n_rows, int64_t n
                            float *absmax_f32, hipStream_t stream);
 hipError_t launch_dequantize(const WeightView &w, void *out, bool out_bf16, hipStream_t stream);
 
-// OUT[M, r] (pitch r, bf16) = bf16(scale * IN[M, Kc] . WT[r, Kc]^T);  IN pitch Kc.
+// OUT[M, r] (row pitch ldout, bf16) = bf16(scale * IN[M, Kc] . WT[r, Kc]^T);  IN rows
+// have pitch ldin, WT rows pitch ldwt (column slices of wider matrices are allowed).
 // `ws` holds lora_down_workspace(M, Kc, r) bytes of fp32 partial sums.
 size_t lora_down_workspace(int64_t M, int64_t Kc, int r);
-hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, const uint16_t *WT, int r,
-                            float scale, uint16_t *OUT, float *ws, hipStream_t stream);
+hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, int64_t ldin, const uint16_t *WT,
+                            int64_t ldwt, int r, float scale, uint16_t *OUT, int64_t ldout, float *ws,
+                            hipStream_t stream);
 // OUT[C, R] = IN[R, C]^T for bf16 matrices (both dense row-major).
 hipError_t launch_transpose_bf16(const uint16_t *IN, int64_t R, int64_t C, uint16_t *OUT,
                                  hipStream_t stream);
 // P[s][No][r] fp32 partials of sum over m in split s of IN[m][no] * S[m][j]; then
 // OUT = bf16(sum_s P) written as [No, r] (trans_out = false) or [r, No] (true).
+// IN rows have pitch ldin, S rows pitch lds.
 size_t reduce_m_workspace(int64_t M, int64_t No, int r);
-hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, const uint16_t *S, int r,
-                           float *partials, uint16_t *OUT, bool trans_out, hipStream_t stream);
+hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, int64_t ldin, const uint16_t *S,
+                           int64_t lds, int r, float *partials, uint16_t *OUT, bool trans_out,
+                           hipStream_t stream);
 
 // AdamW step (fp32 parameter and moments, bf16 gradient, optional bf16 parameter copy).
 struct AdamConsts {
@@ -76,9 +80,12 @@ hipError_t launch_lora_unmerge(const uint16_t *Wm, int64_t n_rows, int64_t n_col
                                const uint16_t *B, int r, float scale, uint16_t *out,
                                hipStream_t stream);
 
-// Y[M, N] = bf16(X . W'^T + U . Bl^T)  (U [M, r] pitch r, Bl [N, r]); r may be 0.
+// Y[M, N] = bf16(X . W'^T + U . Bl^T)  (U [M, r] pitch ldu, Bl [N, r]); r may be 0.
+// part_rows > 0 (a multiple of 256 dividing N): output rows of part q = n / part_rows
+// use U columns [q r, q r + r) (horizontally fused linears with stacked adapters).
 hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
-                           const uint16_t *Bl, int r, uint16_t *Y, hipStream_t stream);
+                           int ldu, const uint16_t *Bl, int r, int64_t part_rows, uint16_t *Y,
+                           hipStream_t stream);
 // Small-M forward (M <= 16) in two launches sharing `ws` (gemv_workspace bytes):
 // the weight stream with the LoRA down-projection partials, then the finalize that
 // forms U_s = bf16(scale X A^T) (written to U_saved if not NULL) and
@@ -88,8 +95,12 @@ size_t gemv_workspace(int64_t M, int64_t K, int64_t N, int r);
 bool gemv_supported(const WeightView &w, int64_t M, int r);
 hipError_t launch_gemv_stream(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *A,
                               int r, void *ws, hipStream_t stream);
-hipError_t launch_gemv_finalize(const WeightView &w, int64_t M, const uint16_t *Bl, int r, float scale,
-                                uint16_t *Y, uint16_t *U_saved, void *ws, hipStream_t stream);
+// The finalize of fused linears: the stream kernel ran with the stacked rank R;
+// output row n uses U_s columns [q r, q r + r), q = n / part_rows (part_rows = 0: one
+// linear, R = r).  U_saved is [M, R].
+hipError_t launch_gemv_finalize(const WeightView &w, int64_t M, const uint16_t *Bl, int r, int R,
+                                int64_t part_rows, float scale, uint16_t *Y, uint16_t *U_saved,
+                                void *ws, hipStream_t stream);
 // dX[M, K] = bf16(dY . W' + V . At^T)  (V [M, r], At [K, r]); r may be 0.
 hipError_t launch_gemm_dx(const WeightView &w, const uint16_t *dY, int64_t M, const uint16_t *V,
                           const uint16_t *At, int r, uint16_t *dX, hipStream_t stream);

@@ -58,7 +58,7 @@ typedef enum {
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
 
-enum { QLORA_BLOCK = 64, QLORA_GROUP = 256, QLORA_MAX_RANK = 256 };
+enum { QLORA_BLOCK = 64, QLORA_GROUP = 256, QLORA_MAX_RANK = 256, QLORA_MAX_PARTS = 8 };
 
 /* A quantized weight W[n_rows = d_out, n_cols = d_in] ([Digest] "数学公式与关键细节"
  * items 1-2; [Ch. 11.3] "核心创新二").  Block b holds the 64 consecutive elements
@@ -95,6 +95,10 @@ void qlora_nf4_codebook(float q[16], float thresholds[15]);
 /* Bytes of caller workspace needed by qlora_linear_fwd (op = 0) or qlora_linear_bwd
  * (op = 1) for the given shapes; 0 for invalid arguments. */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t K, int64_t N, int r);
+
+/* Bytes of caller workspace for qlora_linear_fwd_fused (op = 0) or
+ * qlora_linear_bwd_fused (op = 1): N is the fused row count, r the rank of each part. */
+size_t qlora_workspace_bytes_fused(int op, int64_t M, int64_t K, int64_t N, int r, int n_parts);
 
 const char *qlora_status_string(int status);
 const char *qlora_last_error(void);
@@ -153,6 +157,42 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16
                      const uint16_t *A, const uint16_t *B, int r, float alpha,
                      const uint16_t *U_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Horizontal fusion of linears that read the same X (the query, key and value
+ * projections, or the gate and up projections, of a decoder layer; [Ch. 11.3] and
+ * [Paper note] apply LoRA to all linear layers of the block, so each of them has its
+ * own adapter).  The fused weight stacks n_parts weights of equal shape along rows
+ * (qlora_nf4_concat_rows), the adapters are stacked too:
+ *   A  bf16 [n_parts r, K]  rows [q r, q r + r) are part q's A
+ *   B  bf16 [N, r]          rows [q P, q P + P) are part q's B  (P = N / n_parts)
+ * and one call computes, for every part q at once (one weight stream, one GEMM),
+ *   Y[:, qP .. qP + P) = bf16(X W_q'^T + U_q B_q^T),  U_q = bf16((alpha/r) X A_q^T)
+ * which is bit-for-bit the output of qlora_linear_fwd on part q alone.  U_saved (if
+ * not NULL) receives the stacked [M, n_parts r] U.  Requirements: N % n_parts == 0,
+ * 1 <= n_parts <= QLORA_MAX_PARTS, n_parts r <= 256, and P % 256 == 0 when r > 0.
+ * Workspace: qlora_workspace_bytes_fused(0, M, K, N, r, n_parts). */
+int qlora_linear_fwd_fused(const qlora_nf4_weight *w, int n_parts, const uint16_t *X, int64_t M,
+                           const uint16_t *A, const uint16_t *B, int r, float alpha, uint16_t *Y,
+                           uint16_t *U_saved, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward of qlora_linear_fwd_fused: dY bf16 [M, N] holds the parts' output
+ * gradients side by side.  dA [n_parts r, K] and dB [N, r] are stacked like A and B
+ * and equal, part by part, what qlora_linear_bwd gives for that part; dX [M, K] is the
+ * gradient of X through all parts together, bf16(sum_q (dY_q W_q' + V_q A_q)), rounded
+ * once.  Workspace: qlora_workspace_bytes_fused(1, M, K, N, r, n_parts). */
+int qlora_linear_bwd_fused(const qlora_nf4_weight *w, int n_parts, const uint16_t *dY, const uint16_t *X,
+                           int64_t M, const uint16_t *A, const uint16_t *B, int r, float alpha,
+                           const uint16_t *U_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Concatenate quantized weights along rows into `out` (device copies on `stream`):
+ * codes, block constants and group constants are appended part after part.  Every
+ * part but the last must hold a multiple of 256 blocks (of 16384 weights), so that its
+ * double-quantization groups end with it; the result is then exactly the
+ * quantization of the row-concatenated matrix.  All parts share n_cols; out must be
+ * [sum n_rows, n_cols] with arrays sized by qlora_nf4_sizes. */
+int qlora_nf4_concat_rows(const qlora_nf4_weight *parts, int n_parts, const qlora_nf4_weight *out,
+                          void *stream);
 
 /* AdamW step on adapter parameters ([Digest] "方法步骤与流程" step 5: only the LoRA
  * matrices are updated, by an optimizer such as Adam; the pages give no formula, so

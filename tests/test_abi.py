@@ -193,3 +193,45 @@ def test_merge_argument_errors():
     assert g(FAKE, 64, 128, FAKE, FAKE, -1, 16.0, FAKE, None) == _lib.QLORA_ERR_RANK
     assert g(FAKE + 8, 64, 128, FAKE, FAKE, 8, 16.0, FAKE, None) == _lib.QLORA_ERR_ALIGN
     assert g(FAKE, 64, 128, FAKE, FAKE, 8, 16.0, FAKE, None) == _lib.QLORA_ERR_DEVICE
+
+
+def test_fused_argument_errors():
+    f = _lib.qlora_linear_fwd_fused
+    w = _w(n_rows=768, n_cols=128)
+    ok = dict(w=w, parts=3, X=FAKE, M=64, A=FAKE, B=FAKE, r=8, alpha=16.0, Y=FAKE, U=None, ws=FAKE,
+              wsb=1 << 30, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["w"], a["parts"], a["X"], a["M"], a["A"], a["B"], a["r"], a["alpha"], a["Y"], a["U"],
+                 a["ws"], a["wsb"], a["st"])
+
+    assert call(parts=0) == _lib.QLORA_ERR_SHAPE
+    assert call(parts=9) == _lib.QLORA_ERR_SHAPE
+    assert call(parts=5) == _lib.QLORA_ERR_SHAPE            # 768 rows do not split in 5
+    assert call(r=100) == _lib.QLORA_ERR_RANK               # 3 x 100 > 256
+    assert call(w=_w(n_rows=300, n_cols=128)) == _lib.QLORA_ERR_SHAPE  # 100-row parts
+    assert call(w=_w(n_rows=300, n_cols=128), r=0, A=None, B=None) == _lib.QLORA_ERR_DEVICE
+    assert call() == _lib.QLORA_ERR_DEVICE
+    g = _lib.qlora_linear_bwd_fused
+    assert g(w, 4, FAKE, FAKE, 64, FAKE, FAKE, 8, 16.0, None, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+             None) == _lib.QLORA_ERR_SHAPE                  # 192-row parts
+    assert g(w, 3, FAKE, FAKE, 64, FAKE, FAKE, 8, 16.0, None, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+             None) == _lib.QLORA_ERR_DEVICE
+    assert _lib.qlora_workspace_bytes_fused(1, 64, 128, 768, 8, 3) > 0
+    assert _lib.qlora_workspace_bytes_fused(1, 64, 128, 768, 8, 5) == 0
+    # the one-part query is the single-linear one
+    assert _lib.qlora_workspace_bytes_fused(1, 300, 512, 256, 16, 1) == _lib.qlora_workspace_bytes(
+        1, 300, 512, 256, 16)
+
+
+def test_concat_rows_argument_errors():
+    c = _lib.qlora_nf4_concat_rows
+    a = _w(n_rows=256, n_cols=64)      # 256 blocks: one whole group
+    b = _w(n_rows=100, n_cols=64)      # 100 blocks
+    assert c([a, b], _w(n_rows=356, n_cols=64), None) == _lib.QLORA_ERR_DEVICE
+    assert c([b, a], _w(n_rows=356, n_cols=64), None) == _lib.QLORA_ERR_SHAPE   # b is not last
+    assert c([a, _w(n_rows=256, n_cols=128)], _w(n_rows=512, n_cols=64), None) == _lib.QLORA_ERR_SHAPE
+    assert c([a, b], _w(n_rows=300, n_cols=64), None) == _lib.QLORA_ERR_SHAPE   # wrong out shape
+    assert c([a, _w(n_rows=256, n_cols=64, codes=None)], _w(n_rows=512, n_cols=64),
+             None) == _lib.QLORA_ERR_NULL
