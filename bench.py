@@ -245,6 +245,75 @@ def measure_merge(torch, q, reps=10):
     return res
 
 
+def measure_layer65b(torch, q, reps=5):
+    """LLaMA-65B decoder layer (M = 2048, r = 64, all seven linears, fwd + bwd): the
+    linears one by one, and with q/k/v and gate/up horizontally fused (one weight stream
+    and one GEMM each for the shared X)."""
+    M, r, alpha, D, F = 2048, 64, 16.0, 8192, 22016
+    g = torch.Generator(device="cuda").manual_seed(6)
+
+    def weight(N, K):
+        W = (torch.randn(N, K, device="cuda", generator=g) * 0.015).to(torch.bfloat16)
+        qw = q.quantize(W)
+        del W
+        return qw
+
+    def bf(*shape, std=1.0):
+        return (torch.randn(*shape, device="cuda", generator=g) * std).to(torch.bfloat16)
+
+    names = ("q", "k", "v", "o", "gate", "up", "down")
+    shapes = {"q": (D, D), "k": (D, D), "v": (D, D), "o": (D, D), "gate": (F, D), "up": (F, D),
+              "down": (D, F)}  # (N, K)
+    qw = {n: weight(*shapes[n]) for n in names}
+    A = {n: bf(r, shapes[n][1], std=(1.0 / r) ** 0.5) for n in names}
+    B = {n: bf(shapes[n][0], r, std=0.01) for n in names}
+    X = bf(M, D)
+    Xd = bf(M, F)  # the down projection's input
+    dY = {n: bf(M, shapes[n][0]) for n in names}
+    flops = sum(linear_flops(M, shapes[n][1], shapes[n][0], r) for n in names)
+
+    def separate():
+        for n in names:
+            x = Xd if n == "down" else X
+            Y, U = q.linear_fwd(qw[n], x, A[n], B[n], alpha)
+            q.linear_bwd(qw[n], dY[n], x, A[n], B[n], alpha, U)
+
+    fq = q.concat_rows([qw["q"], qw["k"], qw["v"]])
+    fg = q.concat_rows([qw["gate"], qw["up"]])
+    Aq, Bq = torch.cat([A["q"], A["k"], A["v"]]), torch.cat([B["q"], B["k"], B["v"]])
+    Ag, Bg = torch.cat([A["gate"], A["up"]]), torch.cat([B["gate"], B["up"]])
+    dYq = torch.cat([dY["q"], dY["k"], dY["v"]], dim=1)
+    dYg = torch.cat([dY["gate"], dY["up"]], dim=1)
+
+    def fused():
+        Y, U = q.linear_fwd_fused(fq, 3, X, Aq, Bq, alpha)
+        q.linear_bwd_fused(fq, 3, dYq, X, Aq, Bq, alpha, U)
+        Y, U = q.linear_fwd(qw["o"], X, A["o"], B["o"], alpha)
+        q.linear_bwd(qw["o"], dY["o"], X, A["o"], B["o"], alpha, U)
+        Y, U = q.linear_fwd_fused(fg, 2, X, Ag, Bg, alpha)
+        q.linear_bwd_fused(fg, 2, dYg, X, Ag, Bg, alpha, U)
+        Y, U = q.linear_fwd(qw["down"], Xd, A["down"], B["down"], alpha)
+        q.linear_bwd(qw["down"], dY["down"], Xd, A["down"], B["down"], alpha, U)
+
+    res = {}
+    for name, fn in (("separate", separate), ("fused", fused)):
+        fn()
+        torch.cuda.synchronize()
+        s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        f.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(f) / reps
+        res[name] = {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+    res["speedup"] = round(res["separate"]["ms"] / res["fused"]["ms"], 3)
+    res["what"] = ("LLaMA-65B layer, M=2048, r=64, 7 linears fwd+bwd; fused = q/k/v and gate/up as "
+                   "one weight each (qlora_linear_*_fused)")
+    res["flops_per_layer"] = flops
+    return res
+
+
 def cpu_baseline(synth, sample_m=4096, min_seconds=10.0, max_passes=20):
     """The oracle (float64 numpy) on a bounded sample of the workload: the three linears
     with the first `sample_m` tokens (decode of W' from the stored format, forward and
@@ -412,6 +481,7 @@ def main():
         result["quantize"] = measure_quantize(torch, q, L)
         result["adamw"] = measure_adamw(torch, q)
         result["lora_merge"] = measure_merge(torch, q)
+        result["layer65b"] = measure_layer65b(torch, q)
     if not args.no_cpu_baseline:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(synth)
