@@ -29,11 +29,12 @@ Module map:
 * ``oracle.adamw``      the AdamW step on the adapter parameters.
 * ``oracle.merge``      LoRA merge / unmerge into a bf16 copy of the base.
 * ``oracle.fusion``     horizontally fused linears (stacked weights and adapters).
+* ``oracle.variants``   FP4 levels, FP8-coded and fp32 block constants.
 
 Every function is pinned by ``tests/test_oracle_*.py`` to facts the pages or
 mathematics fix; none is "parity unpinned".
 """
 
-from . import fp, nf4, linear, accounting, adamw, merge, fusion  # noqa: F401
+from . import fp, nf4, linear, accounting, adamw, merge, fusion, variants  # noqa: F401
 
-__all__ = ["fp", "nf4", "linear", "accounting", "adamw", "merge", "fusion"]
+__all__ = ["fp", "nf4", "linear", "accounting", "adamw", "merge", "fusion", "variants"]
