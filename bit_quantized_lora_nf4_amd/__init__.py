@@ -15,18 +15,21 @@ a gfx950.
 from dataclasses import dataclass
 
 from . import _lib
-from ._lib import (QLORA_BF16, QLORA_F32, QloraError, qlora_adamw_step, qlora_dequantize,  # noqa: F401
-                   qlora_linear_bwd, qlora_linear_bwd_fused, qlora_linear_fwd, qlora_linear_fwd_fused,
-                   qlora_lora_merge, qlora_lora_unmerge, qlora_nf4_codebook, qlora_nf4_concat_rows,
-                   qlora_nf4_sizes, qlora_quantize_nf4, qlora_workspace_bytes,
-                   qlora_workspace_bytes_fused)
+from ._lib import (QLORA_BF16, QLORA_CONST_DQ_FP8, QLORA_CONST_DQ_INT8, QLORA_CONST_FP32,  # noqa: F401
+                   QLORA_F32, QLORA_QUANT_FP4, QLORA_QUANT_NF4, QloraError, qlora_adamw_step,
+                   qlora_codebook, qlora_dequantize, qlora_linear_bwd, qlora_linear_bwd_fused,
+                   qlora_linear_fwd, qlora_linear_fwd_fused, qlora_lora_merge, qlora_lora_unmerge,
+                   qlora_nf4_codebook, qlora_nf4_concat_rows, qlora_nf4_sizes, qlora_quantize,
+                   qlora_quantize_nf4, qlora_workspace_bytes, qlora_workspace_bytes_fused)
 
 __all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "workspace",
            "adamw_step", "lora_merge", "lora_unmerge", "concat_rows", "linear_fwd_fused",
            "linear_bwd_fused", "QloraError", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
            "qlora_linear_bwd", "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes",
            "qlora_adamw_step", "qlora_lora_merge", "qlora_lora_unmerge", "qlora_linear_fwd_fused",
-           "qlora_linear_bwd_fused", "qlora_workspace_bytes_fused", "qlora_nf4_concat_rows"]
+           "qlora_linear_bwd_fused", "qlora_workspace_bytes_fused", "qlora_nf4_concat_rows",
+           "qlora_quantize", "qlora_codebook", "QLORA_QUANT_NF4", "QLORA_QUANT_FP4", "QLORA_CONST_DQ_INT8",
+           "QLORA_CONST_DQ_FP8", "QLORA_CONST_FP32"]
 
 
 def _torch():
@@ -36,18 +39,23 @@ def _torch():
 
 @dataclass
 class NF4Weight:
-    """Device arrays of a quantized weight W[n_rows = d_out, n_cols = d_in]."""
+    """Device arrays of a quantized weight W[n_rows = d_out, n_cols = d_in].  The
+    double-quantized constant types use absmax_q / dq_scale / dq_offset; the fp32
+    constant type uses absmax (the others are None)."""
     codes: "object"      # uint8 [n_rows * n_cols / 2]
-    absmax_q: "object"   # int8 [n_blocks]
+    absmax_q: "object"   # int8 [n_blocks] (int8 codes, or E4M3 bytes for QLORA_CONST_DQ_FP8)
     dq_scale: "object"   # float32 [n_groups]
     dq_offset: "object"  # float32 [n_groups]
     n_rows: int
     n_cols: int
+    absmax: "object" = None   # float32 [n_blocks] (QLORA_CONST_FP32)
+    quant_type: int = QLORA_QUANT_NF4
+    const_type: int = QLORA_CONST_DQ_INT8
 
     def descriptor(self):
-        return _lib.qlora_nf4_weight(self.codes.data_ptr(), self.absmax_q.data_ptr(),
-                                     self.dq_scale.data_ptr(), self.dq_offset.data_ptr(),
-                                     self.n_rows, self.n_cols)
+        return _lib.qlora_nf4_weight(self.codes.data_ptr(), _ptr(self.absmax_q), _ptr(self.dq_scale),
+                                     _ptr(self.dq_offset), self.n_rows, self.n_cols, _ptr(self.absmax),
+                                     self.quant_type, self.const_type)
 
     @property
     def shape(self):
@@ -72,25 +80,36 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def quantize(W, return_absmax=False):
-    """NF4 + double quantization of W [n_rows, n_cols] (fp32 or bf16, on the GPU)."""
+def _alloc_weight(n_rows, n_cols, quant_type, const_type, device):
+    torch = _torch()
+    code_bytes, n_blocks, n_groups = qlora_nf4_sizes(n_rows, n_cols)
+    codes = torch.empty(code_bytes, dtype=torch.uint8, device=device)
+    if const_type == QLORA_CONST_FP32:
+        return NF4Weight(codes, None, None, None, n_rows, n_cols,
+                         torch.empty(n_blocks, dtype=torch.float32, device=device), quant_type, const_type)
+    return NF4Weight(codes, torch.empty(n_blocks, dtype=torch.int8, device=device),
+                     torch.empty(n_groups, dtype=torch.float32, device=device),
+                     torch.empty(n_groups, dtype=torch.float32, device=device), n_rows, n_cols,
+                     None, quant_type, const_type)
+
+
+def quantize(W, return_absmax=False, quant_type=QLORA_QUANT_NF4, const_type=QLORA_CONST_DQ_INT8):
+    """Blockwise 4-bit quantization of W [n_rows, n_cols] (fp32 or bf16, on the GPU):
+    NF4 (or FP4) codes with int8 double-quantized constants by default, FP8-coded
+    (QLORA_CONST_DQ_FP8) or plain fp32 constants (QLORA_CONST_FP32) on request."""
     torch = _torch()
     if W.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("W must be float32 or bfloat16")
     _need(W, W.dtype, "W")
     n_rows, n_cols = W.shape
-    code_bytes, n_blocks, n_groups = qlora_nf4_sizes(n_rows, n_cols)
-    dev = W.device
-    codes = torch.empty(code_bytes, dtype=torch.uint8, device=dev)
-    absmax_q = torch.empty(n_blocks, dtype=torch.int8, device=dev)
-    s = torch.empty(n_groups, dtype=torch.float32, device=dev)
-    o = torch.empty(n_groups, dtype=torch.float32, device=dev)
-    c = torch.empty(n_blocks, dtype=torch.float32, device=dev) if return_absmax else None
+    qw = _alloc_weight(n_rows, n_cols, quant_type, const_type, W.device)
+    c = qw.absmax
+    if c is None and return_absmax:
+        c = torch.empty(qw.absmax_q.numel(), dtype=torch.float32, device=W.device)
     dt = QLORA_BF16 if W.dtype == torch.bfloat16 else QLORA_F32
-    _lib.check(qlora_quantize_nf4(W.data_ptr(), dt, n_rows, n_cols, codes.data_ptr(),
-                                  absmax_q.data_ptr(), s.data_ptr(), o.data_ptr(), _ptr(c),
-                                  _stream(W)), "qlora_quantize_nf4")
-    qw = NF4Weight(codes, absmax_q, s, o, n_rows, n_cols)
+    _lib.check(qlora_quantize(W.data_ptr(), dt, n_rows, n_cols, quant_type, const_type, qw.codes.data_ptr(),
+                              _ptr(qw.absmax_q), _ptr(qw.dq_scale), _ptr(qw.dq_offset), _ptr(c),
+                              _stream(W)), "qlora_quantize")
     return (qw, c) if return_absmax else qw
 
 
@@ -226,15 +245,9 @@ def lora_unmerge(Wm, A, B, alpha=16.0, out=None):
 def concat_rows(qws):
     """One NF4Weight holding the given weights stacked along rows (every part but the
     last must hold a multiple of 16384 weights so that its DQ groups end with it)."""
-    torch = _torch()
     K = qws[0].n_cols
     N = sum(q.n_rows for q in qws)
-    cb, nb, ng = qlora_nf4_sizes(N, K)
-    dev = qws[0].codes.device
-    out = NF4Weight(torch.empty(cb, dtype=torch.uint8, device=dev),
-                    torch.empty(nb, dtype=torch.int8, device=dev),
-                    torch.empty(ng, dtype=torch.float32, device=dev),
-                    torch.empty(ng, dtype=torch.float32, device=dev), N, K)
+    out = _alloc_weight(N, K, qws[0].quant_type, qws[0].const_type, qws[0].codes.device)
     _lib.check(qlora_nf4_concat_rows([q.descriptor() for q in qws], out.descriptor(), _stream(out.codes)),
                "qlora_nf4_concat_rows")
     return out

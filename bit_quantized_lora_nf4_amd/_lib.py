@@ -24,13 +24,18 @@ QLORA_ERR_VALUE = -9
 QLORA_MAX_PARTS = 8
 QLORA_F32 = 0
 QLORA_BF16 = 1
+QLORA_QUANT_NF4 = 0
+QLORA_QUANT_FP4 = 1
+QLORA_CONST_DQ_INT8 = 0
+QLORA_CONST_DQ_FP8 = 1
+QLORA_CONST_FP32 = 2
 
 EXPORTED = (
     "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes", "qlora_status_string",
     "qlora_last_error", "qlora_quantize_nf4", "qlora_dequantize", "qlora_linear_fwd",
     "qlora_linear_bwd", "qlora_time_next_gemm", "qlora_adamw_step", "qlora_lora_merge",
     "qlora_lora_unmerge", "qlora_workspace_bytes_fused", "qlora_linear_fwd_fused",
-    "qlora_linear_bwd_fused", "qlora_nf4_concat_rows",
+    "qlora_linear_bwd_fused", "qlora_nf4_concat_rows", "qlora_quantize", "qlora_codebook",
 )
 
 
@@ -42,6 +47,9 @@ class qlora_nf4_weight(ctypes.Structure):
         ("dq_offset", ctypes.c_void_p),
         ("n_rows", ctypes.c_int64),
         ("n_cols", ctypes.c_int64),
+        ("absmax", ctypes.c_void_p),
+        ("quant_type", ctypes.c_int32),
+        ("const_type", ctypes.c_int32),
     ]
 
 
@@ -99,6 +107,10 @@ def load(path=LIB_PATH):
     lib.qlora_linear_bwd_fused.restype = I32
     lib.qlora_nf4_concat_rows.argtypes = [W, I32, W, P]
     lib.qlora_nf4_concat_rows.restype = I32
+    lib.qlora_quantize.argtypes = [P, I32, I64, I64, I32, I32, P, P, P, P, P, P]
+    lib.qlora_quantize.restype = I32
+    lib.qlora_codebook.argtypes = [I32, ctypes.POINTER(F32), ctypes.POINTER(F32)]
+    lib.qlora_codebook.restype = I32
     _lib = lib
     return lib
 
@@ -134,6 +146,14 @@ def qlora_nf4_codebook():
     return list(q), list(t)
 
 
+def qlora_codebook(quant_type):
+    lib = load()
+    q = (ctypes.c_float * 16)()
+    t = (ctypes.c_float * 15)()
+    check(lib.qlora_codebook(quant_type, q, t), "qlora_codebook")
+    return list(q), list(t)
+
+
 def qlora_workspace_bytes(op, M, K, N, r):
     return load().qlora_workspace_bytes(op, M, K, N, r)
 
@@ -142,6 +162,12 @@ def qlora_quantize_nf4(W, w_dtype, n_rows, n_cols, codes, absmax_q, dq_scale, dq
                        absmax_f32, stream):
     return load().qlora_quantize_nf4(W, w_dtype, n_rows, n_cols, codes, absmax_q, dq_scale,
                                      dq_offset, absmax_f32, stream)
+
+
+def qlora_quantize(W, w_dtype, n_rows, n_cols, quant_type, const_type, codes, absmax_q, dq_scale,
+                   dq_offset, absmax, stream):
+    return load().qlora_quantize(W, w_dtype, n_rows, n_cols, quant_type, const_type, codes, absmax_q,
+                                 dq_scale, dq_offset, absmax, stream)
 
 
 def qlora_dequantize(w, out, out_dtype, stream):

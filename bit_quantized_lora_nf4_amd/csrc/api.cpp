@@ -56,12 +56,31 @@ int check_weight_shape(int64_t n_rows, int64_t n_cols) {
   return QLORA_OK;
 }
 
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_types(int quant_type, int const_type) {
+  if (quant_type != QLORA_QUANT_NF4 && quant_type != QLORA_QUANT_FP4)
+    return fail(QLORA_ERR_DTYPE, "quant_type %d: expected QLORA_QUANT_NF4 or QLORA_QUANT_FP4", quant_type);
+  if (const_type != QLORA_CONST_DQ_INT8 && const_type != QLORA_CONST_DQ_FP8 && const_type != QLORA_CONST_FP32)
+    return fail(QLORA_ERR_DTYPE, "const_type %d: expected QLORA_CONST_DQ_INT8, _DQ_FP8 or _FP32", const_type);
+  return QLORA_OK;
+}
+
 int check_weight(const qlora_nf4_weight *w) {
   if (!w) return fail(QLORA_ERR_NULL, "weight descriptor is NULL");
   int s = check_weight_shape(w->n_rows, w->n_cols);
+  if (s == QLORA_OK) s = check_types(w->quant_type, w->const_type);
   if (s != QLORA_OK) return s;
-  if (!w->codes || !w->absmax_q || !w->dq_scale || !w->dq_offset)
-    return fail(QLORA_ERR_NULL, "weight descriptor has a NULL array");
+  if (w->const_type == QLORA_CONST_FP32) {
+    if (!w->codes || !w->absmax)
+      return fail(QLORA_ERR_NULL, "weight descriptor (fp32 constants) needs codes and absmax");
+    if (!aligned4(w->absmax)) return fail(QLORA_ERR_ALIGN, "absmax must be 4-byte aligned");
+  } else {
+    if (!w->codes || !w->absmax_q || !w->dq_scale || !w->dq_offset)
+      return fail(QLORA_ERR_NULL, "weight descriptor has a NULL array");
+    if (!aligned4(w->dq_scale) || !aligned4(w->dq_offset))
+      return fail(QLORA_ERR_ALIGN, "dq_scale and dq_offset must be 4-byte aligned");
+  }
   if (!aligned16(w->codes))
     return fail(QLORA_ERR_ALIGN, "weight codes must be 16-byte aligned");
   return QLORA_OK;
@@ -108,8 +127,8 @@ int launched(hipError_t e, const char *what) {
 }
 
 qlora::WeightView view(const qlora_nf4_weight *w) {
-  return qlora::WeightView{w->codes, w->absmax_q, w->dq_scale, w->dq_offset, w->n_rows,
-                           w->n_cols};
+  return qlora::WeightView{w->codes,  w->absmax_q, w->dq_scale,   w->dq_offset,  w->n_rows,
+                           w->n_cols, w->absmax,   w->quant_type, w->const_type};
 }
 
 // ---- workspace layouts ------------------------------------------------------
@@ -354,24 +373,35 @@ size_t qlora_workspace_bytes_fused(int op, int64_t M, int64_t K, int64_t N, int 
   return 0;
 }
 
-int qlora_quantize_nf4(const void *W, int w_dtype, int64_t n_rows, int64_t n_cols, uint8_t *codes,
-                       int8_t *absmax_q, float *dq_scale, float *dq_offset, float *absmax_f32,
-                       void *stream) {
+int qlora_quantize(const void *W, int w_dtype, int64_t n_rows, int64_t n_cols, int quant_type, int const_type,
+                   uint8_t *codes, int8_t *absmax_q, float *dq_scale, float *dq_offset, float *absmax,
+                   void *stream) {
   int s = check_weight_shape(n_rows, n_cols);
+  if (s == QLORA_OK) s = check_types(quant_type, const_type);
   if (s != QLORA_OK) return s;
   if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16)
     return fail(QLORA_ERR_DTYPE, "w_dtype %d: expected QLORA_F32 or QLORA_BF16", w_dtype);
-  if (!W || !codes || !absmax_q || !dq_scale || !dq_offset)
-    return fail(QLORA_ERR_NULL, "quantize: NULL input or output");
+  if (!W || !codes) return fail(QLORA_ERR_NULL, "quantize: NULL input or codes");
+  if (const_type == QLORA_CONST_FP32 ? !absmax : (!absmax_q || !dq_scale || !dq_offset))
+    return fail(QLORA_ERR_NULL, "quantize: NULL constant output for const_type %d", const_type);
   if (!aligned16(W) || !aligned16(codes))
     return fail(QLORA_ERR_ALIGN, "quantize: W and codes must be 16-byte aligned");
-  if (!qlora::codebook().bucket_ok) return fail(QLORA_ERR_DEVICE, "internal: bucket table");
+  if (!aligned4(absmax) || !aligned4(dq_scale) || !aligned4(dq_offset))
+    return fail(QLORA_ERR_ALIGN, "quantize: fp32 outputs must be 4-byte aligned");
+  if (!qlora::codebook(quant_type).bucket_ok) return fail(QLORA_ERR_DEVICE, "internal: bucket table");
   s = check_device();
   if (s != QLORA_OK) return s;
-  return launched(qlora::launch_quantize(W, w_dtype == QLORA_BF16, n_rows, n_cols, codes, absmax_q,
-                                         dq_scale, dq_offset, absmax_f32,
+  return launched(qlora::launch_quantize(W, w_dtype == QLORA_BF16, n_rows, n_cols, quant_type, const_type,
+                                         codes, absmax_q, dq_scale, dq_offset, absmax,
                                          static_cast<hipStream_t>(stream)),
                   "quantize");
+}
+
+int qlora_quantize_nf4(const void *W, int w_dtype, int64_t n_rows, int64_t n_cols, uint8_t *codes,
+                       int8_t *absmax_q, float *dq_scale, float *dq_offset, float *absmax_f32,
+                       void *stream) {
+  return qlora_quantize(W, w_dtype, n_rows, n_cols, QLORA_QUANT_NF4, QLORA_CONST_DQ_INT8, codes, absmax_q,
+                        dq_scale, dq_offset, absmax_f32, stream);
 }
 
 int qlora_dequantize(const qlora_nf4_weight *w, void *out, int out_dtype, void *stream) {
@@ -425,15 +455,19 @@ int qlora_nf4_concat_rows(const qlora_nf4_weight *parts, int n_parts, const qlor
     return fail(QLORA_ERR_SHAPE, "nf4_concat_rows: n_parts = %d outside [1, %d]", n_parts, QLORA_MAX_PARTS);
   int64_t rows = 0;
   const int64_t K = parts[0].n_cols;
+  const bool dq = out->const_type != QLORA_CONST_FP32;
   for (int i = 0; i < n_parts; ++i) {
     int s = check_weight(&parts[i]);
     if (s != QLORA_OK) return s;
     if (parts[i].n_cols != K)
       return fail(QLORA_ERR_SHAPE, "nf4_concat_rows: part %d has %lld columns, part 0 %lld", i,
                   (long long)parts[i].n_cols, (long long)K);
+    if (parts[i].quant_type != out->quant_type || parts[i].const_type != out->const_type)
+      return fail(QLORA_ERR_DTYPE, "nf4_concat_rows: part %d has types (%d, %d), out (%d, %d)", i,
+                  parts[i].quant_type, parts[i].const_type, out->quant_type, out->const_type);
     // the double-quantization groups of a part must end on a group boundary for the
     // concatenated arrays to be the quantization of the concatenated matrix
-    if (i + 1 < n_parts && (parts[i].n_rows * K / qlora::kBlock) % qlora::kGroup != 0)
+    if (dq && i + 1 < n_parts && (parts[i].n_rows * K / qlora::kBlock) % qlora::kGroup != 0)
       return fail(QLORA_ERR_SHAPE,
                   "nf4_concat_rows: part %d holds %lld blocks, not a multiple of %d (its last "
                   "double-quantization group would straddle the next part)",
@@ -457,12 +491,17 @@ int qlora_nf4_concat_rows(const qlora_nf4_weight *parts, int n_parts, const qlor
     // are the caller's destination
     auto dst = [](const void *p, size_t off) { return static_cast<char *>(const_cast<void *>(p)) + off; };
     hipError_t e = hipMemcpyAsync(dst(out->codes, oc), parts[i].codes, cb, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(dst(out->absmax_q, ob), parts[i].absmax_q, nb, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(dst(out->dq_scale, og * 4), parts[i].dq_scale, ng * 4, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(dst(out->dq_offset, og * 4), parts[i].dq_offset, ng * 4, hipMemcpyDeviceToDevice, st);
+    if (!dq) {
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(dst(out->absmax, ob * 4), parts[i].absmax, nb * 4, hipMemcpyDeviceToDevice, st);
+    } else {
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(dst(out->absmax_q, ob), parts[i].absmax_q, nb, hipMemcpyDeviceToDevice, st);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(dst(out->dq_scale, og * 4), parts[i].dq_scale, ng * 4, hipMemcpyDeviceToDevice, st);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(dst(out->dq_offset, og * 4), parts[i].dq_offset, ng * 4, hipMemcpyDeviceToDevice, st);
+    }
     s = launched(e, "nf4_concat_rows");
     if (s != QLORA_OK) return s;
     oc += cb;

@@ -13,7 +13,16 @@
 //
 // The quantile function here is a bisection on Phi(x) = erfc(-x / sqrt 2) / 2
 // (libm erfc), run until the bracket stops shrinking.
+//
+// The FP4 table is the baseline 4-bit float of the pages' data-type comparison
+// ([Digest] "6. 实验结果与分析", "核心结果分析" item 2), which gives no value set.
+// Reading: the E2M1 float (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 with a sign bit)
+// divided by 6 so that the block absmax maps to +-1 as for NF4; its two zeros give
+// the ascending table -1 .. -1/12, 0, 0, 1/12 .. 1 (each value m / 6 computed in
+// double and rounded once to float).  Thresholds and the bucket table follow the same
+// rules as for NF4 (the threshold between the two zeros is 0: x = 0 takes code 7).
 
+#include "../../include/qlora_nf4.h"
 #include "qlora_internal.h"
 
 #include <cmath>
@@ -36,8 +45,7 @@ double phi_inv(double p) {
   }
 }
 
-Codebook build() {
-  Codebook cb{};
+void nf4_levels(float q[16]) {
   const double delta = 31.0 / 32.0;
   const double z = phi_inv(delta);
   double lv[16];
@@ -47,7 +55,26 @@ Codebook build() {
   for (int j = 1; j <= 8; ++j) lv[7 + j] = phi_inv(0.5 + j * (delta - 0.5) / 8.0) / z;
   lv[0] = -1.0;
   lv[15] = 1.0;
-  for (int i = 0; i < 16; ++i) cb.q[i] = static_cast<float>(lv[i]);
+  for (int i = 0; i < 16; ++i) q[i] = static_cast<float>(lv[i]);
+}
+
+void fp4_levels(float q[16]) {
+  // E2M1 magnitudes in halves: 0, 1, 2, 3, 4, 6, 8, 12 (i.e. 0 .. 6)
+  static const int halves[8] = {0, 1, 2, 3, 4, 6, 8, 12};
+  for (int i = 0; i < 8; ++i) {
+    const double v = halves[i] / 12.0;  // (halves / 2) / 6
+    q[8 + i] = static_cast<float>(v);
+    q[7 - i] = static_cast<float>(-v);
+  }
+  q[7] = 0.0f;  // the negative zero code decodes to +0 like the positive one
+}
+
+Codebook build(int quant_type) {
+  Codebook cb{};
+  if (quant_type == kQuantFP4)
+    fp4_levels(cb.q);
+  else
+    nf4_levels(cb.q);
 
   // T[j] = largest float <= (q[j] + q[j+1]) / 2 (the double sum of two floats in
   // [-1, 1] is exact), so that for float x: x > T[j] <=> x > the exact midpoint;
@@ -89,19 +116,35 @@ Codebook build() {
 
 }  // namespace
 
-const Codebook &codebook() {
+const Codebook &codebook(int quant_type) {
   static std::once_flag once;
-  static Codebook cb;
-  std::call_once(once, [] { cb = build(); });
-  return cb;
+  static Codebook cb[2];
+  std::call_once(once, [] {
+    cb[0] = build(kQuantNF4);
+    cb[1] = build(kQuantFP4);
+  });
+  return cb[quant_type == kQuantFP4 ? 1 : 0];
+}
+
+LevelTable level_table(int quant_type) {
+  LevelTable lv;
+  const Codebook &cb = codebook(quant_type);
+  for (int i = 0; i < 16; ++i) lv.q[i] = cb.q[i];
+  return lv;
 }
 
 }  // namespace qlora
 
 extern "C" void qlora_nf4_codebook(float q[16], float thresholds[15]) {
-  const qlora::Codebook &cb = qlora::codebook();
+  qlora_codebook(QLORA_QUANT_NF4, q, thresholds);
+}
+
+extern "C" int qlora_codebook(int quant_type, float q[16], float thresholds[15]) {
+  if (quant_type != qlora::kQuantNF4 && quant_type != qlora::kQuantFP4) return QLORA_ERR_DTYPE;
+  const qlora::Codebook &cb = qlora::codebook(quant_type);
   if (q)
     for (int i = 0; i < 16; ++i) q[i] = cb.q[i];
   if (thresholds)
     for (int j = 0; j < 15; ++j) thresholds[j] = cb.thr[j];
+  return QLORA_OK;
 }

@@ -1,7 +1,8 @@
 // Standalone doubleDequant of an NF4 + DQ weight (gfx950).
 //
 // out = RN(q[code] * c') (fp32) or bf16_rne of it, with c' = fma(c8, s, o)
-// ([Digest] "数学公式与关键细节" item 3, doubleDequant equation).  Each thread
+// ([Digest] "数学公式与关键细节" item 3, doubleDequant equation), or the stored fp32
+// constant c' = c for the constant type without double quantization.  Each thread
 // decodes 32 weights (16 bytes of codes, half a block, one constant) per
 // iteration; a wave therefore reads 1 KB of codes and writes 4 KB of bf16.
 // HBM-bound: reads 0.516 B and writes 2 (bf16) or 4 (fp32) bytes per weight.
@@ -14,11 +15,10 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(
-    const u32x4_t *__restrict__ codes, const int8_t *__restrict__ absmax_q,
-    const float *__restrict__ s, const float *__restrict__ o, int64_t n_chunks,
-    void *__restrict__ out, LevelTable lv) {
+template <bool OUT_BF16, int CT>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(WeightView wv, int64_t n_chunks,
+                                                           void *__restrict__ out, LevelTable lv) {
+  const u32x4_t *__restrict__ codes = reinterpret_cast<const u32x4_t *>(wv.codes);
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = lv.q[threadIdx.x];
   __syncthreads();
@@ -26,7 +26,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
   for (int64_t ch = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; ch < n_chunks;
        ch += stride) {
     const u32x4_t w = codes[ch];
-    const float c = decode_constant(absmax_q, s, o, ch >> 1);  // 2 chunks per block
+    const float c = decode_constant<CT>(wv, ch >> 1);  // 2 chunks per block
     if (OUT_BF16) {
       u32x4_t *dst = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(out) + ch * 32);
 #pragma unroll
@@ -51,21 +51,24 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 }  // namespace
 
 hipError_t launch_dequantize(const WeightView &w, void *out, bool out_bf16, hipStream_t stream) {
-  LevelTable lv;
-  const Codebook &cb = codebook();
-  for (int i = 0; i < 16; ++i) lv.q[i] = cb.q[i];
+  const LevelTable lv = level_table(w.quant_type);
   const int64_t n_chunks = w.n_rows * w.n_cols / 32;
   int64_t blocks = (n_chunks + kThreads - 1) / kThreads;
   if (blocks > 256 * 16) blocks = 256 * 16;
   dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
-  const u32x4_t *codes = reinterpret_cast<const u32x4_t *>(w.codes);
-  if (out_bf16)
-    hipLaunchKernelGGL(dequant_kernel<true>, grid, block, 0, stream, codes, w.absmax_q,
-                       w.dq_scale, w.dq_offset, n_chunks, out, lv);
-  else
-    hipLaunchKernelGGL(dequant_kernel<false>, grid, block, 0, stream, codes, w.absmax_q,
-                       w.dq_scale, w.dq_offset, n_chunks, out, lv);
-  return hipGetLastError();
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, w, n_chunks, out, lv);
+    return hipGetLastError();
+  };
+  switch (w.const_type * 2 + (out_bf16 ? 1 : 0)) {
+    case 0: return go(dequant_kernel<false, kConstDqInt8>);
+    case 1: return go(dequant_kernel<true, kConstDqInt8>);
+    case 2: return go(dequant_kernel<false, kConstDqFp8>);
+    case 3: return go(dequant_kernel<true, kConstDqFp8>);
+    case 4: return go(dequant_kernel<false, kConstF32>);
+    case 5: return go(dequant_kernel<true, kConstF32>);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace qlora

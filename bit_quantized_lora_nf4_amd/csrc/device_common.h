@@ -46,12 +46,33 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Decoded first-level constant of flat block b: c' = fma(c8, s[g], o[g]), g = b / 256,
-// rounded once ([Digest] "数学公式与关键细节" item 3: dequant(c1, c2)).
-__device__ __forceinline__ float decode_constant(const int8_t *absmax_q, const float *s,
-                                                 const float *o, int64_t b) {
+// Exact value of an FP8 E4M3 byte (sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; exponent field 0 holds the subnormals m 2^-9).  The normal values are made
+// by moving the byte into an fp32 bit pattern and re-biasing the exponent.
+__device__ __forceinline__ float e4m3_value(uint32_t u) {
+  const uint32_t mag = u & 0x7Fu;
+  const float normal = __uint_as_float((mag << 20) + (120u << 23));
+  const float sub = static_cast<float>(mag & 7u) * 0x1p-9f;
+  const float v = (mag >> 3) ? normal : sub;
+  return __uint_as_float(__float_as_uint(v) | ((u & 0x80u) << 24));
+}
+
+// The second-level code of a block constant as a float: a sign-extended int8, or an
+// E4M3 value for the FP8-coded double quantization.
+template <int CT>
+__device__ __forceinline__ float c8_value(uint32_t byte) {
+  if constexpr (CT == kConstDqFp8) return e4m3_value(byte);
+  return static_cast<float>(static_cast<int>(byte << 24) >> 24);
+}
+
+// Decoded first-level constant of flat block b ([Digest] "数学公式与关键细节" item 3:
+// dequant(c1, c2)): c' = fma(c8, s[b / 256], o[b / 256]), rounded once, for the
+// double-quantized types; the stored fp32 constant for kConstF32.
+template <int CT>
+__device__ __forceinline__ float decode_constant(const WeightView &w, int64_t b) {
+  if constexpr (CT == kConstF32) return w.absmax[b];
   const int64_t g = b >> 8;
-  return __builtin_fmaf(static_cast<float>(absmax_q[b]), s[g], o[g]);
+  return __builtin_fmaf(c8_value<CT>(static_cast<uint8_t>(w.absmax_q[b])), w.dq_scale[g], w.dq_offset[g]);
 }
 
 // Eight codes of one u32 (element e in bits 4e..4e+3) -> four packed bf16 pairs of
@@ -83,36 +104,47 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 constexpr uint32_t kOOB = 0xFFFFFFF0u;  // an offset past any buffer: reads as zero
 
-// Buffer resources over the three constant arrays of a quantized weight.
+// Buffer resources over the constant arrays of a quantized weight: the 8-bit codes,
+// group scales and offsets of the double-quantized types, or (kConstF32) the fp32
+// block constants in `s`.
 struct ConstRsrc {
   __amdgpu_buffer_rsrc_t q8, s, o;
 };
-__device__ __forceinline__ ConstRsrc make_const_rsrc(const int8_t *q8, const float *s, const float *o,
-                                                     uint32_t n_blocks) {
+template <int CT>
+__device__ __forceinline__ ConstRsrc make_const_rsrc(const WeightView &w, uint32_t n_blocks) {
+  if constexpr (CT == kConstF32) {
+    const __amdgpu_buffer_rsrc_t s = make_rsrc(w.absmax, n_blocks * 4u);
+    return {s, s, s};
+  }
   const uint32_t n_groups = (n_blocks + 255u) / 256u;
-  return {make_rsrc(q8, n_blocks), make_rsrc(s, n_groups * 4u), make_rsrc(o, n_groups * 4u)};
+  return {make_rsrc(w.absmax_q, n_blocks), make_rsrc(w.dq_scale, n_groups * 4u),
+          make_rsrc(w.dq_offset, n_groups * 4u)};
 }
 // Raw pieces of the constant of flat block b (zeros when !ok), loaded branch-free;
-// c' = fma(c8, s[b / 256], o[b / 256]) is formed later by const_value, so that a
-// prefetch does not force a wait on its own loads.
+// c' is formed later by const_value, so that a prefetch does not force a wait on its
+// own loads.  kConstF32 loads the one fp32 constant (into s).
 struct ConstRaw {
   uint32_t c8, s, o;
 };
+template <int CT>
 __device__ __forceinline__ ConstRaw fetch_constant(const ConstRsrc &r, uint32_t b, bool ok) {
+  if constexpr (CT == kConstF32)
+    return {0u, __builtin_amdgcn_raw_buffer_load_b32(r.s, ok ? b * 4u : kOOB, 0, 0), 0u};
   const uint32_t ob = ok ? b : kOOB;
   const uint32_t og = ok ? (b >> 8) * 4u : kOOB;
   return {__builtin_amdgcn_raw_buffer_load_b8(r.q8, ob, 0, 0),
           __builtin_amdgcn_raw_buffer_load_b32(r.s, og, 0, 0),
           __builtin_amdgcn_raw_buffer_load_b32(r.o, og, 0, 0)};
 }
+template <int CT>
 __device__ __forceinline__ float const_value(const ConstRaw &c) {
+  if constexpr (CT == kConstF32) return __uint_as_float(c.s);
   // The empty asm hides the loaded byte from instruction selection: otherwise the
   // sign extension is folded into a sign-extending load that is re-issued next to
   // this use, which then waits for every load in flight.
   uint32_t u = c.c8;
   asm("" : "+v"(u));
-  const int c8 = static_cast<int>(u << 24) >> 24;
-  return __builtin_fmaf(static_cast<float>(c8), __uint_as_float(c.s), __uint_as_float(c.o));
+  return __builtin_fmaf(c8_value<CT>(u), __uint_as_float(c.s), __uint_as_float(c.o));
 }
 
 // Pack the low halves / high halves of two dwords: (lo(a), lo(b)) and (hi(a), hi(b)).

@@ -272,6 +272,7 @@ constexpr int LOADS_BEFORE_BARRIER = 12;
 // register copy ever waits for a load in flight.
 constexpr int NBUF = 3;
 
+template <int CT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_fwd_kernel(
     GemmParams p) {
   __shared__ __attribute__((aligned(16))) char sX[NBUF * TILE_BYTES];
@@ -284,8 +285,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int K = p.Kc;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, static_cast<uint32_t>(uint64_t(p.M) * K * 2));
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.w.codes, static_cast<uint32_t>(uint64_t(p.No) * K / 2));
-  const ConstRsrc rq = make_const_rsrc(p.w.absmax_q, p.w.dq_scale, p.w.dq_offset,
-                                       static_cast<uint32_t>(uint64_t(p.No) * K / 64));
+  const ConstRsrc rq = make_const_rsrc<CT>(p.w, static_cast<uint32_t>(uint64_t(p.No) * K / 64));
   const int nk = K / TK;
   const int last = nk - 1;
 
@@ -311,10 +311,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   }
   auto issue_codes = [&](int kt, int j, CodeStage &cs) {
     cs.code[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, coff[j], kt / 2, 0));
-    cs.c[j].c8 = __builtin_amdgcn_raw_buffer_load_b8(rq.q8, boff[j], kt / 64, 0);
-    const uint32_t g4 = ((boff[j] + kt / 64) >> 8) * 4u;
-    cs.c[j].s = __builtin_amdgcn_raw_buffer_load_b32(rq.s, g4, 0, 0);
-    cs.c[j].o = __builtin_amdgcn_raw_buffer_load_b32(rq.o, g4, 0, 0);
+    if constexpr (CT == kConstF32) {
+      cs.c[j] = {0u, __builtin_amdgcn_raw_buffer_load_b32(rq.s, boff[j] * 4u, kt / 16, 0), 0u};
+    } else {
+      cs.c[j].c8 = __builtin_amdgcn_raw_buffer_load_b8(rq.q8, boff[j], kt / 64, 0);
+      const uint32_t g4 = ((boff[j] + kt / 64) >> 8) * 4u;
+      cs.c[j].s = __builtin_amdgcn_raw_buffer_load_b32(rq.s, g4, 0, 0);
+      cs.c[j].o = __builtin_amdgcn_raw_buffer_load_b32(rq.o, g4, 0, 0);
+    }
   };
   auto issue_dma = [&](int kt, int h, char *buf) {
     char *dst = buf + wave * 8 * 1024;
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   u32x4_t wa[2], xb[8];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    pl[j] = make_planes(const_value(S0.c[j]), p.lvl);
+    pl[j] = make_planes(const_value<CT>(S0.c[j]), p.lvl);
     wa[j] = lookup8(S0.code[j][0], pl[j]);
   }
   read_xfrags_fwd(sX, 0, xb);
@@ -379,8 +383,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
         for (int j = 0; j < 2; ++j) wan[j] = lookup8(cur.code[j][s + 1], pl[j]);
         // block constants of the next step, one row per sub-step
-        if (s == 1) pln[0] = make_planes(const_value(nxt.c[0]), p.lvl);
-        if (s == 2) pln[1] = make_planes(const_value(nxt.c[1]), p.lvl);
+        if (s == 1) pln[0] = make_planes(const_value<CT>(nxt.c[0]), p.lvl);
+        if (s == 2) pln[1] = make_planes(const_value<CT>(nxt.c[1]), p.lvl);
       }
       mfmas();
 #pragma unroll
@@ -429,6 +433,7 @@ struct CodeStageB {
   ConstRaw c;
 };
 
+template <int CT>
 __device__ __forceinline__ void code_load_bwd(const GemmParams &p, __amdgpu_buffer_rsrc_t rc,
                                               const ConstRsrc &rq, int k0, int kt, CodeStageB &cs) {
   const int tid = threadIdx.x;
@@ -439,13 +444,14 @@ __device__ __forceinline__ void code_load_bwd(const GemmParams &p, __amdgpu_buff
   const uint32_t off = static_cast<uint32_t>(n) * (K / 2) + k / 2;
   cs.code[0] = buf_load16(rc, ok ? off : kOOB);
   cs.code[1] = buf_load16(rc, ok ? off + 16 : kOOB);
-  cs.c = fetch_constant(rq, static_cast<uint32_t>(n) * (K / 64) + k / 64, ok);
+  cs.c = fetch_constant<CT>(rq, static_cast<uint32_t>(n) * (K / 64) + k / 64, ok);
 }
 
+template <int CT>
 __device__ __forceinline__ void code_store_bwd(const GemmParams &p, const CodeStageB &cs, char *sw) {
   const int tid = threadIdx.x;
   const int n = tid & 63, c0 = (tid >> 6) * 64;
-  const Planes pl = make_planes(const_value(cs.c), p.lvl);
+  const Planes pl = make_planes(const_value<CT>(cs.c), p.lvl);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -477,7 +483,7 @@ __device__ __forceinline__ u32x4_t wfrag_tr(const char *sw, int s, int j) {
   return r;
 }
 
-template <bool VEC>
+template <bool VEC, int CT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dx_kernel(
     GemmParams p) {
   __shared__ __attribute__((aligned(16))) char sX[2][TILE_BYTES];
@@ -490,8 +496,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int N = p.Kc, K = p.No;
   const __amdgpu_buffer_rsrc_t rdy = make_rsrc(p.A, static_cast<uint32_t>(uint64_t(p.M) * N * 2));
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.w.codes, static_cast<uint32_t>(uint64_t(N) * K / 2));
-  const ConstRsrc rq = make_const_rsrc(p.w.absmax_q, p.w.dq_scale, p.w.dq_offset,
-                                       static_cast<uint32_t>(uint64_t(N) * K / 64));
+  const ConstRsrc rq = make_const_rsrc<CT>(p.w, static_cast<uint32_t>(uint64_t(N) * K / 64));
   const int nk = (N + TK - 1) / TK;
   const int last = nk - 1;
 
@@ -501,15 +506,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   ActStage st;
   CodeStageB cs;
   act_load(rdy, m0, p.M, N, 0, VEC, p.A, st);
-  code_load_bwd(p, rc, rq, k0, 0, cs);
+  code_load_bwd<CT>(p, rc, rq, k0, 0, cs);
   act_store(sX[0], st);
-  code_store_bwd(p, cs, sW[0]);
+  code_store_bwd<CT>(p, cs, sW[0]);
   __syncthreads();
 
   auto step = [&](int it, const char *sx, const char *sw, char *sx_next, char *sw_next) {
     const int nt = min(it + 1, last) * TK;
     act_load(rdy, m0, p.M, N, nt, VEC, p.A, st);
-    code_load_bwd(p, rc, rq, k0, nt, cs);
+    code_load_bwd<CT>(p, rc, rq, k0, nt, cs);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4_t wa[2], xb[8];
@@ -525,7 +530,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(wa[j], xb[i], acc[i][j]);
     }
     act_store(sx_next, st);
-    code_store_bwd(p, cs, sw_next);
+    code_store_bwd<CT>(p, cs, sw_next);
     __syncthreads();
   };
   int it = 0;
@@ -658,6 +663,7 @@ struct YStage {
   u32x4_t v[4][2];
 };
 
+template <int CT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dx_pipe_kernel(
     GemmParams p) {
   __shared__ __attribute__((aligned(16))) char sW[2 * TILE_BYTES];
@@ -670,8 +676,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int N = p.Kc, K = p.No;  // contraction over weight rows, outputs are weight columns
   const __amdgpu_buffer_rsrc_t rdy = make_rsrc(p.A, static_cast<uint32_t>(uint64_t(p.M) * N * 2));
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.w.codes, static_cast<uint32_t>(uint64_t(N) * K / 2));
-  const ConstRsrc rq = make_const_rsrc(p.w.absmax_q, p.w.dq_scale, p.w.dq_offset,
-                                       static_cast<uint32_t>(uint64_t(N) * K / 64));
+  const ConstRsrc rq = make_const_rsrc<CT>(p.w, static_cast<uint32_t>(uint64_t(N) * K / 64));
   const int nk = (N + TK - 1) / TK;
   const int last = nk - 1;
 
@@ -701,7 +706,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const uint32_t off = static_cast<uint32_t>(n) * (K / 2) + (k0 + dc) / 2;
     cs.code[0] = buf_load16(rc, ok ? off : kOOB);
     cs.code[1] = buf_load16(rc, ok ? off + 16 : kOOB);
-    cs.c = fetch_constant(rq, static_cast<uint32_t>(n) * (K / 64) + (k0 + dc) / 64, ok);
+    cs.c = fetch_constant<CT>(rq, static_cast<uint32_t>(n) * (K / 64) + (k0 + dc) / 64, ok);
   };
   // lookups q0 .. q1 - 1 of the eight (q = 4 h + i: 16-byte code half h, word i)
   auto decode_part = [&](const CodeStageB &cs, const Planes &pd, char *sw, int q0, int q1) {
@@ -724,7 +729,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   issue_codes(min(1, last) * TK, S1);
   issue_y(0, Y0);
   {
-    const Planes pd = make_planes(const_value(S0.c), p.lvl);
+    const Planes pd = make_planes(const_value<CT>(S0.c), p.lvl);
     decode_part(S0, pd, sW, 0, 8);
   }
   __syncthreads();
@@ -746,7 +751,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int s = 0; s < 4; ++s) {
       u32x4_t wan[8];
       if (s == 0) {
-        pd = make_planes(const_value(dec.c), p.lvl);
+        pd = make_planes(const_value<CT>(dec.c), p.lvl);
         issue_y(kt1, yn);
         decode_part(dec, pd, swn, 0, 2);
       }
@@ -804,7 +809,7 @@ bool fits_32bit(int64_t M, int64_t N, int64_t K, int r) {
 GemmParams make_params(const uint16_t *A, const WeightView &w, const uint16_t *A2,
                        const uint16_t *B2, uint16_t *C, int64_t M, int64_t No, int64_t Kc, int r) {
   GemmParams p{A, w, A2, B2, C, static_cast<int>(M), static_cast<int>(No), static_cast<int>(Kc), r, {}, r, 0};
-  for (int i = 0; i < 16; ++i) p.lvl.q[i] = codebook().q[i];
+  p.lvl = level_table(w.quant_type);
   return p;
 }
 
@@ -822,7 +827,13 @@ hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, co
   GemmParams p = make_params(X, w, U, Bl, Y, M, w.n_rows, w.n_cols, r);
   p.lda2 = ldu;
   p.part_rows = static_cast<int>(part_rows);
-  hipLaunchKernelGGL(gemm_fwd_kernel, dim3(grid_size(M, w.n_rows)), dim3(NT), 0, stream, p);
+  const dim3 grid(grid_size(M, w.n_rows));
+  switch (w.const_type) {
+    case kConstDqInt8: hipLaunchKernelGGL(gemm_fwd_kernel<kConstDqInt8>, grid, dim3(NT), 0, stream, p); break;
+    case kConstDqFp8: hipLaunchKernelGGL(gemm_fwd_kernel<kConstDqFp8>, grid, dim3(NT), 0, stream, p); break;
+    case kConstF32: hipLaunchKernelGGL(gemm_fwd_kernel<kConstF32>, grid, dim3(NT), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -830,11 +841,21 @@ hipError_t launch_gemm_dx(const WeightView &w, const uint16_t *dY, int64_t M, co
                           const uint16_t *At, int r, uint16_t *dX, hipStream_t stream) {
   if (!fits_32bit(M, w.n_rows, w.n_cols, r) || M > 0x7fffffff) return hipErrorInvalidValue;
   const GemmParams p = make_params(dY, w, V, At, dX, M, w.n_cols, w.n_rows, r);
-  if (w.n_rows % 8 == 0)
-    hipLaunchKernelGGL(gemm_dx_pipe_kernel, dim3(grid_size(M, w.n_cols)), dim3(NT), 0, stream, p);
-  else
-    hipLaunchKernelGGL(gemm_dx_kernel<false>, dim3(grid_size(M, w.n_cols)), dim3(NT), 0, stream, p);
-  return hipGetLastError();
+  const dim3 grid(grid_size(M, w.n_cols));
+  const bool pipe = w.n_rows % 8 == 0;
+  auto go = [&](auto pipe_kern, auto plain_kern) {
+    if (pipe)
+      hipLaunchKernelGGL(pipe_kern, grid, dim3(NT), 0, stream, p);
+    else
+      hipLaunchKernelGGL(plain_kern, grid, dim3(NT), 0, stream, p);
+    return hipGetLastError();
+  };
+  switch (w.const_type) {
+    case kConstDqInt8: return go(gemm_dx_pipe_kernel<kConstDqInt8>, gemm_dx_kernel<false, kConstDqInt8>);
+    case kConstDqFp8: return go(gemm_dx_pipe_kernel<kConstDqFp8>, gemm_dx_kernel<false, kConstDqFp8>);
+    case kConstF32: return go(gemm_dx_pipe_kernel<kConstF32>, gemm_dx_kernel<false, kConstF32>);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace qlora

@@ -80,25 +80,27 @@ __device__ __forceinline__ u32x4_t permute8(u32x4_t d) {
 
 // LDS of the stream kernel (one dynamic object): per wave its 16 rows x 512 bytes of
 // codes (16-byte chunk cr of row r at slot cr ^ (r & 15)), per wave 16 rows x 16
-// int8 block constants, then the staged X slice (M rows of XPITCH bytes).
+// 8-bit block constants (or 16 fp32 constants for the type without double
+// quantization), then the staged X slice (M rows of XPITCH bytes).
 constexpr int CROW = 4 * GIT * 32;   // code bytes per row and slice (512)
 constexpr int WCODE = 16 * CROW;     // code bytes per wave (8 KB)
 constexpr int SC_BYTES = 4 * WCODE;  // 32 KB
-constexpr int SQ_BYTES = 4 * 256;    // 1 KB
+constexpr int sq_wave(int ct) { return ct == kConstF32 ? 1024 : 256; }  // constant bytes per wave
 int gemv_xl(int M) { return M <= 2 ? 1 : M <= 4 ? 2 : M <= 8 ? 4 : 8; }
 // staged X rows = XL * 256 * 8 / GSLICE = 2 XL (rows past M hold zeros)
-size_t gemv_lds_bytes(int M) {
-  return SC_BYTES + SQ_BYTES + static_cast<size_t>(2 * gemv_xl(M)) * XPITCH;
+size_t gemv_lds_bytes(int M, int ct) {
+  return SC_BYTES + 4 * sq_wave(ct) + static_cast<size_t>(2 * gemv_xl(M)) * XPITCH;
 }
 
 // XL: 16-byte X loads per thread (M * 128 / 256 rounded up to a power of two);
 // C8W: the rows' int8 constants are dword aligned (K % 256 == 0).
-template <int XL, bool C8W>
+template <int XL, bool C8W, int CT>
 __global__ __launch_bounds__(GT) void gemv_stream_kernel(GemvArgs a) {
+  constexpr int SQW = sq_wave(CT);
   extern __shared__ __attribute__((aligned(16))) char lds[];
   char *const sc = lds;
   char *const sq = lds + SC_BYTES;
-  char *const sx = lds + SC_BYTES + SQ_BYTES;
+  char *const sx = lds + SC_BYTES + 4 * SQW;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = static_cast<int>(a.w.n_rows), K = static_cast<int>(a.w.n_cols), KB = K / 64;
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(GT) void gemv_stream_kernel(GemvArgs a) {
     const int m = c / (GSLICE / 8), k = k0 + (c % (GSLICE / 8)) * 8;
     xs[j] = buf_load16(rx, (m < a.M && k < K) ? (static_cast<uint32_t>(m) * K + k) * 2 : kOOB);
   }
-  uint32_t c8w = 0, sv[2] = {0u, 0u}, ov[2] = {0u, 0u};
+  uint32_t c8w = 0, sv[2] = {0u, 0u}, ov[2] = {0u, 0u}, cf[4] = {0u, 0u, 0u, 0u};
   uint8_t c8b[4] = {0, 0, 0, 0};
   int gfirst = 0;
   {
@@ -129,10 +131,9 @@ __global__ __launch_bounds__(GT) void gemv_stream_kernel(GemvArgs a) {
     // range), so that the compiler's waits stay exact counts.  Order: constants, then
     // the codes block group by block group, so that decoding can follow the arrivals.
     const int nlim = lora ? 0 : N;
-    const ConstRsrc rq = make_const_rsrc(a.w.absmax_q, a.w.dq_scale, a.w.dq_offset,
-                                         static_cast<uint32_t>(uint64_t(N) * KB));
+    const ConstRsrc rq = make_const_rsrc<CT>(a.w, static_cast<uint32_t>(uint64_t(N) * KB));
     // group scale and offset: the slice of one row spans at most two groups
-    {
+    if constexpr (CT != kConstF32) {
       const int n = row0 + ml;
       const uint32_t bfirst = static_cast<uint32_t>(n) * KB + s * 16;
       gfirst = static_cast<int>(bfirst >> 8);
@@ -143,11 +144,15 @@ __global__ __launch_bounds__(GT) void gemv_stream_kernel(GemvArgs a) {
         ov[e] = __builtin_amdgcn_raw_buffer_load_b32(rq.o, og, 0, 0);
       }
     }
-    // int8 constants: lane l loads blocks s * 16 + 4 (l % 4) .. + 3 of row l / 4
+    // 8-bit constants: lane l loads blocks s * 16 + 4 (l % 4) .. + 3 of row l / 4
+    // (fp32 constants: the same blocks, one dword each)
     {
       const int n = row0 + (lane >> 2);
       const uint32_t b = static_cast<uint32_t>(n) * KB + s * 16 + 4 * (lane & 3);
-      if constexpr (C8W) {
+      if constexpr (CT == kConstF32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cf[e] = __builtin_amdgcn_raw_buffer_load_b32(rq.s, n < nlim ? (b + e) * 4u : kOOB, 0, 0);
+      } else if constexpr (C8W) {
         c8w = __builtin_amdgcn_raw_buffer_load_b32(rq.q8, n < nlim ? b : kOOB, 0, 0);
       } else {  // rows not dword aligned: four byte loads, stored to LDS one by one
 #pragma unroll
@@ -180,7 +185,9 @@ __global__ __launch_bounds__(GT) void gemv_stream_kernel(GemvArgs a) {
     const int m = c / (GSLICE / 8), q = c % (GSLICE / 8);
     *reinterpret_cast<u32x4_t *>(sx + m * XPITCH + q * 16) = permute8(xs[j]);
   }
-  if constexpr (C8W) {
+  if constexpr (CT == kConstF32) {
+    *reinterpret_cast<u32x4_t *>(sq + wave * SQW + lane * 16) = u32x4_t{cf[0], cf[1], cf[2], cf[3]};
+  } else if constexpr (C8W) {
     *reinterpret_cast<uint32_t *>(sq + wave * 256 + lane * 4) = c8w;
   } else {
 #pragma unroll
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(GT) void gemv_stream_kernel(GemvArgs a) {
   if (!lora) {
     // ---- weight stream: lane = (row ml of this wave's 16, lane group g) ----
     const char *const wc = sc + wave * WCODE + ml * 128;
-    const u32x4_t q8 = *reinterpret_cast<const u32x4_t *>(sq + wave * 256 + ml * 16);
+    const u32x4_t q8 = *reinterpret_cast<const u32x4_t *>(sq + wave * SQW + ml * (SQW / 16));
     const int n = row0 + ml;
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -217,10 +224,15 @@ __global__ __launch_bounds__(GT) void gemv_stream_kernel(GemvArgs a) {
       u32x4_t xb[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) xb[t] = xfrag(kk + 8 * t);
-      // constant of block blk: byte g of dword i of the row's 16 bytes
-      const int gi = static_cast<int>((static_cast<uint32_t>(n) * KB + s * 16 + blk) >> 8) - gfirst;
-      const ConstRaw cr{(q8[i] >> (8 * g)) & 0xFFu, gi ? sv[1] : sv[0], gi ? ov[1] : ov[0]};
-      const Planes pl = make_planes(const_value(cr), a.lvl);
+      float cval;
+      if constexpr (CT == kConstF32) {  // fp32 constant blk of the row's 16
+        cval = *reinterpret_cast<const float *>(sq + wave * SQW + ml * 64 + blk * 4);
+      } else {  // constant of block blk: byte g of dword i of the row's 16 bytes
+        const int gi = static_cast<int>((static_cast<uint32_t>(n) * KB + s * 16 + blk) >> 8) - gfirst;
+        const ConstRaw cr{(q8[i] >> (8 * g)) & 0xFFu, gi ? sv[1] : sv[0], gi ? ov[1] : ov[0]};
+        cval = const_value<CT>(cr);
+      }
+      const Planes pl = make_planes(cval, a.lvl);
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc = mfma16x16x32(lookup8_pairs(code[t >> 2][t & 3], pl), xb[t], acc);
     }
@@ -339,6 +351,35 @@ bool gemv_supported(const WeightView &w, int64_t M, int r) {
          uint64_t(r) * K * 2 <= 0xFFFFFFF0ull;
 }
 
+namespace {
+template <int CT>
+hipError_t launch_stream(const GemvArgs &a, unsigned grid, bool c8w, hipStream_t stream) {
+  auto go = [&](auto kern) -> hipError_t {
+    // dynamic LDS above 64 KB (M > 8) has to be allowed once per instantiation
+    static bool allowed = false;
+    if (gemv_xl(a.M) == 8 && !allowed) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(gemv_lds_bytes(GMAXM, CT)));
+      if (e != hipSuccess) return e;
+      allowed = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(GT), gemv_lds_bytes(a.M, CT), stream, a);
+    return hipGetLastError();
+  };
+  switch (gemv_xl(a.M) * 2 + (c8w ? 1 : 0)) {
+    case 3: return go(gemv_stream_kernel<1, true, CT>);
+    case 2: return go(gemv_stream_kernel<1, false, CT>);
+    case 5: return go(gemv_stream_kernel<2, true, CT>);
+    case 4: return go(gemv_stream_kernel<2, false, CT>);
+    case 9: return go(gemv_stream_kernel<4, true, CT>);
+    case 8: return go(gemv_stream_kernel<4, false, CT>);
+    case 17: return go(gemv_stream_kernel<8, true, CT>);
+    default: return go(gemv_stream_kernel<8, false, CT>);
+  }
+}
+}  // namespace
+
 hipError_t launch_gemv_stream(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *A,
                               int r, void *ws, hipStream_t stream) {
   if (!gemv_supported(w, M, r)) return hipErrorInvalidValue;
@@ -352,32 +393,15 @@ hipError_t launch_gemv_stream(const WeightView &w, const uint16_t *X, int64_t M,
   a.S = gemv_slices(K);
   a.P = gemv_p(ws);
   a.UP = gemv_up(ws, M, K, N);
-  for (int i = 0; i < 16; ++i) a.lvl.q[i] = codebook().q[i];
+  a.lvl = level_table(w.quant_type);
   const unsigned groups = static_cast<unsigned>((N + GROWS - 1) / GROWS);
   const unsigned grid = groups * static_cast<unsigned>(a.S) + (r > 0 ? static_cast<unsigned>(a.S) : 0u);
   const bool c8w = (K / 64) % 4 == 0;
-  auto go = [&](auto kern) -> hipError_t {
-    // dynamic LDS above 64 KB (M > 8) has to be allowed once per instantiation
-    static bool allowed[2] = {false, false};
-    if (gemv_xl(a.M) == 8 && !allowed[c8w ? 1 : 0]) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(gemv_lds_bytes(GMAXM)));
-      if (e != hipSuccess) return e;
-      allowed[c8w ? 1 : 0] = true;
-    }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(GT), gemv_lds_bytes(a.M), stream, a);
-    return hipGetLastError();
-  };
-  switch (gemv_xl(a.M) * 2 + (c8w ? 1 : 0)) {
-    case 3: return go(gemv_stream_kernel<1, true>);
-    case 2: return go(gemv_stream_kernel<1, false>);
-    case 5: return go(gemv_stream_kernel<2, true>);
-    case 4: return go(gemv_stream_kernel<2, false>);
-    case 9: return go(gemv_stream_kernel<4, true>);
-    case 8: return go(gemv_stream_kernel<4, false>);
-    case 17: return go(gemv_stream_kernel<8, true>);
-    default: return go(gemv_stream_kernel<8, false>);
+  switch (w.const_type) {
+    case kConstDqInt8: return launch_stream<kConstDqInt8>(a, grid, c8w, stream);
+    case kConstDqFp8: return launch_stream<kConstDqFp8>(a, grid, c8w, stream);
+    case kConstF32: return launch_stream<kConstF32>(a, grid, c8w, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

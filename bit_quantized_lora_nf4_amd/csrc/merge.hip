@@ -58,6 +58,7 @@ struct MergeArgs {
   const int8_t *absmax_q;
   const float *dq_scale;
   const float *dq_offset;
+  const float *absmax;  // fp32 block constants (weights without double quantization)
   const uint16_t *Wm;  // unmerge input (bf16 [N, K])
   const uint16_t *A;   // [r, K]
   const uint16_t *B;   // [N, r]
@@ -77,6 +78,7 @@ struct TileRsrc {
   __amdgpu_buffer_rsrc_t codes, c8, s, o, wm, b, out;
 };
 
+template <int CT = kConstDqInt8>
 __device__ __forceinline__ TileRsrc tile_rsrc(const MergeArgs &a, int tile, bool unmerge) {
   const int64_t n0 = static_cast<int64_t>(tile) * TR;
   const int64_t left = a.N - n0;
@@ -93,9 +95,13 @@ __device__ __forceinline__ TileRsrc tile_rsrc(const MergeArgs &a, int tile, bool
     const uint32_t nb = rows * (kb / 64u);
     const uint32_t ng = nb == 0u ? 0u : ((static_cast<uint32_t>(b0 & 255) + nb + 255u) >> 8);
     t.codes = make_rsrc(a.codes + e0 / 2, rows * (kb / 2u));
-    t.c8 = make_rsrc(a.absmax_q + b0, nb);
-    t.s = make_rsrc(a.dq_scale + g0, ng * 4u);
-    t.o = make_rsrc(a.dq_offset + g0, ng * 4u);
+    if constexpr (CT == kConstF32) {  // the tile's fp32 block constants
+      t.c8 = t.s = t.o = make_rsrc(a.absmax + b0, nb * 4u);
+    } else {
+      t.c8 = make_rsrc(a.absmax_q + b0, nb);
+      t.s = make_rsrc(a.dq_scale + g0, ng * 4u);
+      t.o = make_rsrc(a.dq_offset + g0, ng * 4u);
+    }
     t.wm = t.codes;
   }
   t.b = make_rsrc(a.B + n0 * a.r, rows * static_cast<uint32_t>(a.r) * 2u);
@@ -135,12 +141,20 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const MergeArgs &a, int64_t 
   return lo;
 }
 
-template <bool UNMERGE>
+template <bool UNMERGE, int CT>
 __device__ __forceinline__ void issue_base(const MergeArgs &a, const TileRsrc &t, int tile,
                                            const LaneOffsets &lo, bool col_ok, BaseStage &st) {
   if (UNMERGE) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) st.wm[p] = buf_load16(t.wm, lo.wm[p]);
+    return;
+  }
+  if constexpr (CT == kConstF32) {  // codes and the block's fp32 constant
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      st.code[p] = buf_load4(t.codes, lo.code[p]);
+      st.s[p] = __builtin_amdgcn_raw_buffer_load_b32(t.s, col_ok ? lo.blk[p] * 4u : kOOB, 0, 0);
+    }
     return;
   }
   // The 8-bit constants are read as the aligned dword holding each one (the tile's
@@ -166,9 +180,16 @@ __device__ __forceinline__ void issue_base(const MergeArgs &a, const TileRsrc &t
 
 // c' = fma(c8, s, o) of pass p; the constant's byte sits at byte (block % 4) of c8w,
 // and tiles start on a multiple of four blocks, so the position depends on the lane only.
+// Weights without double quantization hold c' itself in s.
+template <int CT>
 __device__ __forceinline__ float stage_constant(const BaseStage &st, int p, int byte) {
-  const int c8 = static_cast<int>(st.c8w[p] << (24 - 8 * byte)) >> 24;
-  return __builtin_fmaf(static_cast<float>(c8), __uint_as_float(st.s[p]), __uint_as_float(st.o[p]));
+  if constexpr (CT == kConstF32) return __uint_as_float(st.s[p]);
+  float c8;
+  if constexpr (CT == kConstDqFp8)
+    c8 = e4m3_value(st.c8w[p] >> (8 * byte));
+  else
+    c8 = static_cast<float>(static_cast<int>(st.c8w[p] << (24 - 8 * byte)) >> 24);
+  return __builtin_fmaf(c8, __uint_as_float(st.s[p]), __uint_as_float(st.o[p]));
 }
 
 // B fragments of one tile: sub-step s (ranks 16 s .. 16 s + 15) of lane l holds
@@ -214,7 +235,7 @@ __device__ __forceinline__ u32x4_t afrag(const char *sa, int s, int cb) {
   return v;
 }
 
-template <bool UNMERGE, bool RVEC, int NCH>
+template <bool UNMERGE, bool RVEC, int NCH, int CT>
 __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -262,17 +283,17 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   BaseStage st0, st1;
   u32x4_t bf0[4 * NCH], bf1[4 * NCH];
   {
-    const TileRsrc t0 = tile_rsrc(a, tile_of(0), UNMERGE);
-    const TileRsrc t1 = tile_rsrc(a, tile_of(1), UNMERGE);
+    const TileRsrc t0 = tile_rsrc<CT>(a, tile_of(0), UNMERGE);
+    const TileRsrc t1 = tile_rsrc<CT>(a, tile_of(1), UNMERGE);
     // same order as inside the loop (B, then base), so that the wait counts the
     // compiler derives for the loop entry match the steady state
     issue_b<NCH, RVEC>(a, t0, bf0);
     issue_fence();
-    issue_base<UNMERGE>(a, t0, tile_of(0), lo, col_ok, st0);
+    issue_base<UNMERGE, CT>(a, t0, tile_of(0), lo, col_ok, st0);
     issue_fence();
     issue_b<NCH, RVEC>(a, t1, bf1);
     issue_fence();
-    issue_base<UNMERGE>(a, t1, tile_of(1), lo, col_ok, st1);
+    issue_base<UNMERGE, CT>(a, t1, tile_of(1), lo, col_ok, st1);
     issue_fence();
   }
 
@@ -292,7 +313,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) acc[t] = mfma32x32x16(af[s][t], bf[s], acc[t]);
     issue_fence();
-    const TileRsrc tn = tile_rsrc(a, tile_of(i + 2), UNMERGE);
+    const TileRsrc tn = tile_rsrc<CT>(a, tile_of(i + 2), UNMERGE);
     issue_b<NCH, RVEC>(a, tn, bf);
     issue_fence();
     // acc[t][4 q + e]: row l % 32, wave column 32 t + 8 q + 4 (l / 32) + e
@@ -313,7 +334,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
       const float d[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
       const int byte = static_cast<int>(lo.blk[p] & 3u);
       const u32x4_t base =
-          UNMERGE ? st.wm[p] : lookup8(st.code[p], make_planes(stage_constant(st, p, byte), a.lvl));
+          UNMERGE ? st.wm[p] : lookup8(st.code[p], make_planes(stage_constant<CT>(st, p, byte), a.lvl));
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const float t0 = a.scale * d[2 * h], t1 = a.scale * d[2 * h + 1];
@@ -322,9 +343,9 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
       }
     }
     issue_fence();
-    issue_base<UNMERGE>(a, tn, tile_of(i + 2), lo, col_ok, st);
+    issue_base<UNMERGE, CT>(a, tn, tile_of(i + 2), lo, col_ok, st);
     issue_fence();
-    const TileRsrc tc = tile_rsrc(a, tile_of(i), UNMERGE);
+    const TileRsrc tc = tile_rsrc<CT>(a, tile_of(i), UNMERGE);
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) __builtin_amdgcn_raw_buffer_store_b128(o[p], tc.out, lo.wm[p], 0, 0);
     issue_fence();
@@ -336,19 +357,21 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   }
 }
 
-template <bool UNMERGE, bool RVEC, int NCH>
+template <bool UNMERGE, bool RVEC, int NCH, int CT>
 hipError_t launch_one(MergeArgs args, hipStream_t stream) {
   static int per_cu = -1;
   if (per_cu < 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, merge_kernel<UNMERGE, RVEC, NCH>, NT, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, merge_kernel<UNMERGE, RVEC, NCH, CT>, NT, 0) !=
             hipSuccess ||
         nb < 1)
       nb = 1;
     per_cu = nb;
   }
   int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
   const int64_t slots = static_cast<int64_t>(per_cu) * cus;
   int64_t per_strip = (slots + args.strips - 1) / args.strips;
   if (per_strip > args.tiles) per_strip = args.tiles;
@@ -356,12 +379,12 @@ hipError_t launch_one(MergeArgs args, hipStream_t stream) {
   args.per_strip = static_cast<int>(per_strip);
   const int64_t grid = per_strip * args.strips;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((merge_kernel<UNMERGE, RVEC, NCH>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0,
+  hipLaunchKernelGGL((merge_kernel<UNMERGE, RVEC, NCH, CT>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0,
                      stream, args);
   return hipGetLastError();
 }
 
-template <bool UNMERGE>
+template <bool UNMERGE, int CT>
 hipError_t launch(MergeArgs args, hipStream_t stream) {
   args.strips = static_cast<int>((args.K + TC - 1) / TC);
   args.tiles = static_cast<int>((args.N + TR - 1) / TR);
@@ -369,7 +392,7 @@ hipError_t launch(MergeArgs args, hipStream_t stream) {
   const bool rvec = args.r % 8 == 0;
 #define QLORA_MERGE_CASE(C)                                                                        \
   case C:                                                                                          \
-    return rvec ? launch_one<UNMERGE, true, C>(args, stream) : launch_one<UNMERGE, false, C>(args, stream);
+    return rvec ? launch_one<UNMERGE, true, C, CT>(args, stream) : launch_one<UNMERGE, false, C, CT>(args, stream);
   switch (nch) {
     QLORA_MERGE_CASE(1)
     QLORA_MERGE_CASE(2)
@@ -389,6 +412,7 @@ hipError_t launch_lora_merge(const WeightView &w, const uint16_t *A, const uint1
   args.absmax_q = w.absmax_q;
   args.dq_scale = w.dq_scale;
   args.dq_offset = w.dq_offset;
+  args.absmax = w.absmax;
   args.A = A;
   args.B = B;
   args.out = out;
@@ -396,9 +420,13 @@ hipError_t launch_lora_merge(const WeightView &w, const uint16_t *A, const uint1
   args.K = w.n_cols;
   args.r = r;
   args.scale = scale;
-  const Codebook &cb = codebook();
-  for (int i = 0; i < 16; ++i) args.lvl.q[i] = cb.q[i];
-  return launch<false>(args, stream);
+  args.lvl = level_table(w.quant_type);
+  switch (w.const_type) {
+    case kConstDqInt8: return launch<false, kConstDqInt8>(args, stream);
+    case kConstDqFp8: return launch<false, kConstDqFp8>(args, stream);
+    case kConstF32: return launch<false, kConstF32>(args, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_lora_unmerge(const uint16_t *Wm, int64_t n_rows, int64_t n_cols, const uint16_t *A,
@@ -413,7 +441,7 @@ hipError_t launch_lora_unmerge(const uint16_t *Wm, int64_t n_rows, int64_t n_col
   args.K = n_cols;
   args.r = r;
   args.scale = scale;
-  return launch<true>(args, stream);
+  return launch<true, kConstDqInt8>(args, stream);
 }
 
 }  // namespace qlora

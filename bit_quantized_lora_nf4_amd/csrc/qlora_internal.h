@@ -12,15 +12,21 @@ constexpr int kGroup = 256;    // block constants per double-quantization group
 constexpr int kBuckets = 129;  // quantizer bucket table entries (x in [-1, 1])
 constexpr int kMaxRank = 256;  // largest LoRA rank
 
+// Level tables of the 4-bit codes and encodings of the block constants (the values
+// of the weight descriptor's quant_type and const_type).
+enum : int { kQuantNF4 = 0, kQuantFP4 = 1 };
+enum : int { kConstDqInt8 = 0, kConstDqFp8 = 1, kConstF32 = 2 };
+
 struct Codebook {
-  float q[16];                  // NF4 levels, ascending
+  float q[16];                  // levels, ascending
   float thr[15];                // decision thresholds
   float bucket_thr[kBuckets];   // the threshold inside each bucket window (2.0 if none)
   int bucket_base[kBuckets];    // thresholds below each bucket window
   bool bucket_ok;               // every window holds at most one threshold
 };
 
-const Codebook &codebook();
+// kQuantNF4 or kQuantFP4 (any other value: NF4).
+const Codebook &codebook(int quant_type = kQuantNF4);
 
 // Kernel arguments passed by value (kernarg segment).
 struct QuantTable {
@@ -30,8 +36,10 @@ struct QuantTable {
 struct LevelTable {
   float q[16];
 };
+LevelTable level_table(int quant_type);
 
-// Device view of a quantized weight.
+// Device view of a quantized weight.  Double-quantized constants (kConstDqInt8,
+// kConstDqFp8) use absmax_q / dq_scale / dq_offset; kConstF32 uses absmax.
 struct WeightView {
   const uint8_t *codes;
   const int8_t *absmax_q;
@@ -39,12 +47,17 @@ struct WeightView {
   const float *dq_offset;
   int64_t n_rows;  // N = d_out
   int64_t n_cols;  // K = d_in
+  const float *absmax;
+  int quant_type;
+  int const_type;
 };
 
 // ---- launchers (each returns the HIP error of its launches) -----------------
-hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n_rows, int64_t n_cols,
-                           uint8_t *codes, int8_t *absmax_q, float *dq_scale, float *dq_offset,
-                           float *absmax_f32, hipStream_t stream);
+// absmax_f32 receives the fp32 block constants (required for kConstF32, optional
+// otherwise); absmax_q / dq_scale / dq_offset are written for the double-quantized types.
+hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n_rows, int64_t n_cols, int quant_type,
+                           int const_type, uint8_t *codes, int8_t *absmax_q, float *dq_scale,
+                           float *dq_offset, float *absmax_f32, hipStream_t stream);
 hipError_t launch_dequantize(const WeightView &w, void *out, bool out_bf16, hipStream_t stream);
 
 // OUT[M, r] (row pitch ldout, bf16) = bf16(scale * IN[M, Kc] . WT[r, Kc]^T);  IN rows

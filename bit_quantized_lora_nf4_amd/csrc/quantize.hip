@@ -13,6 +13,13 @@
 // c < 2^-126 gets the zero code.  Per group (after a barrier): o = RN(min+max)
 // * 0.5, h = max |RN(c - o)|, s = RN(h/127), c8 = clamp(rint(RN(RN(c-o)/s))).
 // HBM-bound: 2.516 B per bf16 weight (4.516 for fp32 input).
+//
+// Variants of the pages' data-type comparison ([Digest] "6. 实验结果与分析",
+// "核心结果分析" item 2; [Digest] "数学公式与关键细节" item 2 writes the second-level
+// codes as FP8): the FP4 level table replaces the NF4 one through the bucket table;
+// the FP8-coded double quantization uses s = RN(h / 448) and the E4M3 code of
+// RN(RN(c - o) / s) (nearest, ties to the even code, saturated at 448); the fp32
+// constant type keeps c itself (written to the absmax output) and skips the group pass.
 
 #include "device_common.h"
 #include "qlora_internal.h"
@@ -42,11 +49,27 @@ __device__ __forceinline__ float block_reduce_min(float v, float *red) {
   return v;
 }
 
+// E4M3 code of x: the nearest value to |x| (saturated at 448), ties to the even code;
+// the sign bit is set for x < 0.  Magnitudes below 2^-6 are the subnormal codes
+// rint(|x| 2^9) (0 .. 8, where 8 is 2^-6 itself); above, the fp32 pattern is re-biased
+// and its mantissa rounded to 3 bits, a carry moving into the exponent.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const float a = fminf(fabsf(x), 448.0f);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = static_cast<uint32_t>(rintf(a * 512.0f));
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    code = (bits + 0x7FFFFu + ((bits >> 20) & 1u) - (120u << 23)) >> 20;
+  }
+  return code | (x < 0.0f ? 0x80u : 0u);
+}
+
 template <bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const void *__restrict__ W, int64_t n_blocks, uint32_t *__restrict__ codes,
     int8_t *__restrict__ absmax_q, float *__restrict__ dq_scale, float *__restrict__ dq_offset,
-    float *__restrict__ absmax_out, QuantTable tab) {
+    float *__restrict__ absmax_out, int const_type, QuantTable tab) {
   __shared__ float2 s_tab[kBuckets];
   __shared__ float s_c[kGroup];
   __shared__ float s_red[4];
@@ -127,6 +150,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   }
   __syncthreads();
 
+  if (const_type == kConstF32) return;  // uniform: the constants went to absmax_out
+
   // ---- double quantization of this group's 256 constants --------------------
   const bool valid = tid < nbg;
   const float c = valid ? s_c[tid] : 0.0f;
@@ -135,14 +160,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   const float o = (mn + mx) * 0.5f;
   const float d = c - o;
   const float h = block_reduce_max(valid ? fabsf(d) : 0.0f, s_red);
-  int q8 = 0;
+  uint32_t q8 = 0;
   float s = 0.0f;
   if (h != 0.0f) {
-    s = h / 127.0f;  // correctly rounded
-    const float r = rintf(d / s);
-    q8 = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
+    if (const_type == kConstDqFp8) {
+      s = h / 448.0f;  // correctly rounded
+      q8 = e4m3_encode(d / s);
+    } else {
+      s = h / 127.0f;
+      const float r = rintf(d / s);
+      q8 = static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f))) & 0xFFu;
+    }
   }
-  if (valid) absmax_q[b0 + tid] = static_cast<int8_t>(q8);
+  if (valid) absmax_q[b0 + tid] = static_cast<int8_t>(static_cast<uint8_t>(q8));
   if (tid == 0) {
     dq_scale[g] = s;
     dq_offset[g] = o;
@@ -151,10 +181,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 
 }  // namespace
 
-hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n_rows, int64_t n_cols,
-                           uint8_t *codes, int8_t *absmax_q, float *dq_scale, float *dq_offset,
-                           float *absmax_f32, hipStream_t stream) {
-  const Codebook &cb = codebook();
+hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n_rows, int64_t n_cols, int quant_type,
+                           int const_type, uint8_t *codes, int8_t *absmax_q, float *dq_scale,
+                           float *dq_offset, float *absmax_f32, hipStream_t stream) {
+  if (const_type == kConstF32 && !absmax_f32) return hipErrorInvalidValue;
+  const Codebook &cb = codebook(quant_type);
   QuantTable tab;
   for (int i = 0; i < kBuckets; ++i) {
     tab.thr[i] = cb.bucket_thr[i];
@@ -167,11 +198,11 @@ hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n_rows, int64_t n
   if (w_bf16)
     hipLaunchKernelGGL(quantize_kernel<true>, grid, block, 0, stream, W, n_blocks,
                        reinterpret_cast<uint32_t *>(codes), absmax_q, dq_scale, dq_offset,
-                       absmax_f32, tab);
+                       absmax_f32, const_type, tab);
   else
     hipLaunchKernelGGL(quantize_kernel<false>, grid, block, 0, stream, W, n_blocks,
                        reinterpret_cast<uint32_t *>(codes), absmax_q, dq_scale, dq_offset,
-                       absmax_f32, tab);
+                       absmax_f32, const_type, tab);
   return hipGetLastError();
 }
 

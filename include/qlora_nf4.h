@@ -58,16 +58,39 @@ typedef enum {
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
 
+/* Data-type variants of the stored weight, after the data-type comparison of [Digest]
+ * "6. 实验结果与分析" ("核心结果分析" item 2: Float4, NF4, NF4 with double quantization)
+ * and the FP8 notation of the second-level codes in [Digest] "数学公式与关键细节" item 2.
+ * The pages fix neither value set; the library's readings:
+ *   QLORA_QUANT_FP4      the E2M1 float (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, signed)
+ *                        divided by 6; levels -1, -2/3, -1/2, -1/3, -1/4, -1/6, -1/12, 0,
+ *                        0, 1/12, 1/6, 1/4, 1/3, 1/2, 2/3, 1 (each rounded once to fp32)
+ *   QLORA_CONST_DQ_FP8   the double quantization with E4M3 second-level codes (bias 7, 3
+ *                        mantissa bits, subnormals, largest value 448): s = RN(h / 448),
+ *                        code = E4M3 nearest to RN(RN(c - o) / s) (ties to the even code,
+ *                        saturated at 448; sign bit set for a negative value),
+ *                        c' = fma(e4m3(code), s, o)
+ *   QLORA_CONST_FP32     no double quantization: c' = c, stored as fp32 */
+typedef enum { QLORA_QUANT_NF4 = 0, QLORA_QUANT_FP4 = 1 } qlora_quant_type;
+typedef enum { QLORA_CONST_DQ_INT8 = 0, QLORA_CONST_DQ_FP8 = 1, QLORA_CONST_FP32 = 2 } qlora_const_type;
+
 enum { QLORA_BLOCK = 64, QLORA_GROUP = 256, QLORA_MAX_RANK = 256, QLORA_MAX_PARTS = 8 };
 
 /* A quantized weight W[n_rows = d_out, n_cols = d_in] ([Digest] "数学公式与关键细节"
  * items 1-2; [Ch. 11.3] "核心创新二").  Block b holds the 64 consecutive elements
  * [64 b, 64 b + 64) of the row-major weight; group g holds blocks [256 g, 256 g + 256).
  *   codes      [n_rows * n_cols / 2]   byte i = code(2i) | code(2i+1) << 4
- *   absmax_q   [n_blocks]              int8 double-quantized block constant
- *   dq_scale   [n_groups]              fp32 group scale s
- *   dq_offset  [n_groups]              fp32 group offset o
- * Block constant decode: c' = fma(absmax_q[b], s[g], o[g]) (one rounding).
+ *   absmax_q   [n_blocks]              8-bit double-quantized block constant: int8
+ *                                      (QLORA_CONST_DQ_INT8) or an E4M3 byte (_DQ_FP8)
+ *   dq_scale   [n_groups]              fp32 group scale s        (double-quantized types)
+ *   dq_offset  [n_groups]              fp32 group offset o       (double-quantized types)
+ *   absmax     [n_blocks]              fp32 block constant c     (QLORA_CONST_FP32 only)
+ *   quant_type                         level table q: QLORA_QUANT_NF4 or QLORA_QUANT_FP4
+ *   const_type                         QLORA_CONST_DQ_INT8, _DQ_FP8 or _FP32
+ * Arrays a type does not use may be NULL.  A zero tail (types 0, absmax NULL) is the
+ * NF4 weight with int8 double quantization.  fp32 arrays must be 4-byte aligned.
+ * Block constant decode: c' = fma(absmax_q[b], s[g], o[g]) (int8; one rounding),
+ *                        c' = fma(e4m3(absmax_q[b]), s[g], o[g]) (FP8), c' = absmax[b].
  * Weight decode:          W'  = bf16_rne(q[code] * c')   (fp32 product, RN). */
 typedef struct {
   const uint8_t *codes;
@@ -76,6 +99,9 @@ typedef struct {
   const float *dq_offset;
   int64_t n_rows;
   int64_t n_cols;
+  const float *absmax;
+  int32_t quant_type;
+  int32_t const_type;
 } qlora_nf4_weight;
 
 /* ---- host-only helpers (no GPU needed) ------------------------------------ */
@@ -91,6 +117,11 @@ int qlora_nf4_sizes(int64_t n_rows, int64_t n_cols, size_t *code_bytes, int64_t 
  * [Paper note] "关键设计 1", quantile-midpoint equation; [Digest] item 1, "特点":
  * exact zero through asymmetric halves).  Either pointer may be NULL. */
 void qlora_nf4_codebook(float q[16], float thresholds[15]);
+
+/* The level table and thresholds of quant_type (QLORA_QUANT_NF4: as qlora_nf4_codebook;
+ * QLORA_QUANT_FP4: the E2M1 / 6 levels above, thresholds by the same rule, the one
+ * between the two zeros being 0).  QLORA_ERR_DTYPE for another quant_type. */
+int qlora_codebook(int quant_type, float q[16], float thresholds[15]);
 
 /* Bytes of caller workspace needed by qlora_linear_fwd (op = 0) or qlora_linear_bwd
  * (op = 1) for the given shapes; 0 for invalid arguments. */
@@ -124,6 +155,17 @@ void qlora_time_next_gemm(void *start_event, void *stop_event);
 int qlora_quantize_nf4(const void *W, int w_dtype, int64_t n_rows, int64_t n_cols, uint8_t *codes,
                        int8_t *absmax_q, float *dq_scale, float *dq_offset, float *absmax_f32,
                        void *stream);
+
+/* Blockwise quantization with a chosen level table and block-constant type (the
+ * variants of the data-type comparison; see qlora_quant_type / qlora_const_type).
+ * Codes as in qlora_quantize_nf4 with the quant_type's thresholds.  Constants:
+ * QLORA_CONST_DQ_INT8 as qlora_quantize_nf4; QLORA_CONST_DQ_FP8 writes E4M3 bytes to
+ * absmax_q and s = RN(h / 448), o to dq_scale, dq_offset; QLORA_CONST_FP32 writes c to
+ * absmax (required) and leaves absmax_q, dq_scale, dq_offset untouched (may be NULL).
+ * For the double-quantized types absmax (nullable) receives c as well. */
+int qlora_quantize(const void *W, int w_dtype, int64_t n_rows, int64_t n_cols, int quant_type, int const_type,
+                   uint8_t *codes, int8_t *absmax_q, float *dq_scale, float *dq_offset, float *absmax,
+                   void *stream);
 
 /* doubleDequant ([Digest] item 3, doubleDequant equation): out[n_rows, n_cols] =
  * RN(q[code] * c') as fp32 (out_dtype = QLORA_F32) or its bf16 rounding (QLORA_BF16). */
@@ -186,11 +228,12 @@ int qlora_linear_bwd_fused(const qlora_nf4_weight *w, int n_parts, const uint16_
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* Concatenate quantized weights along rows into `out` (device copies on `stream`):
- * codes, block constants and group constants are appended part after part.  Every
- * part but the last must hold a multiple of 256 blocks (of 16384 weights), so that its
- * double-quantization groups end with it; the result is then exactly the
- * quantization of the row-concatenated matrix.  All parts share n_cols; out must be
- * [sum n_rows, n_cols] with arrays sized by qlora_nf4_sizes. */
+ * codes, block constants and group constants are appended part after part.  With
+ * double-quantized constants every part but the last must hold a multiple of 256
+ * blocks (of 16384 weights), so that its double-quantization groups end with it; the
+ * result is then exactly the quantization of the row-concatenated matrix.  All parts
+ * share n_cols, quant_type and const_type with out; out must be [sum n_rows, n_cols]
+ * with arrays sized by qlora_nf4_sizes. */
 int qlora_nf4_concat_rows(const qlora_nf4_weight *parts, int n_parts, const qlora_nf4_weight *out,
                           void *stream);
 

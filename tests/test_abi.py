@@ -235,3 +235,58 @@ def test_concat_rows_argument_errors():
     assert c([a, b], _w(n_rows=300, n_cols=64), None) == _lib.QLORA_ERR_SHAPE   # wrong out shape
     assert c([a, _w(n_rows=256, n_cols=64, codes=None)], _w(n_rows=512, n_cols=64),
              None) == _lib.QLORA_ERR_NULL
+
+
+def _wt(quant_type=0, const_type=0, absmax=None, n_rows=64, n_cols=128, absmax_q=FAKE, dq=FAKE):
+    return _lib.qlora_nf4_weight(FAKE, absmax_q, dq, dq, n_rows, n_cols, absmax, quant_type, const_type)
+
+
+def test_codebook_variants_match_oracle_bitwise():
+    from oracle import variants
+    for qt, levels in ((_lib.QLORA_QUANT_NF4, nf4.codebook()), (_lib.QLORA_QUANT_FP4, variants.fp4_levels())):
+        q, t = _lib.qlora_codebook(qt)
+        q = np.array(q, np.float32)
+        t = np.array(t, np.float32)
+        assert np.array_equal(q.view(np.uint32), levels.view(np.uint32))
+        assert np.array_equal(t.view(np.uint32), nf4.thresholds(levels).view(np.uint32))
+    with pytest.raises(_lib.QloraError) as e:
+        _lib.qlora_codebook(2)
+    assert e.value.status == _lib.QLORA_ERR_DTYPE
+
+
+def test_weight_type_errors():
+    d = _lib.qlora_dequantize
+    F32 = _lib.QLORA_CONST_FP32
+    assert d(_wt(quant_type=2), FAKE, 1, None) == _lib.QLORA_ERR_DTYPE
+    assert d(_wt(const_type=3), FAKE, 1, None) == _lib.QLORA_ERR_DTYPE
+    assert d(_wt(const_type=F32), FAKE, 1, None) == _lib.QLORA_ERR_NULL             # absmax missing
+    assert d(_wt(const_type=F32, absmax=FAKE + 2), FAKE, 1, None) == _lib.QLORA_ERR_ALIGN
+    # the fp32 type needs no double-quantization arrays: valid on the host
+    assert d(_wt(const_type=F32, absmax=FAKE, absmax_q=None, dq=None), FAKE, 1,
+             None) == _lib.QLORA_ERR_DEVICE
+    assert d(_wt(const_type=_lib.QLORA_CONST_DQ_FP8, dq=None), FAKE, 1, None) == _lib.QLORA_ERR_NULL
+    assert d(_wt(dq=FAKE + 2), FAKE, 1, None) == _lib.QLORA_ERR_ALIGN
+    assert d(_wt(quant_type=1, const_type=1), FAKE, 1, None) == _lib.QLORA_ERR_DEVICE
+
+
+def test_quantize_variant_argument_errors():
+    q = _lib.qlora_quantize
+    F32 = _lib.QLORA_CONST_FP32
+    assert q(FAKE, 1, 4, 128, 2, 0, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.QLORA_ERR_DTYPE
+    assert q(FAKE, 1, 4, 128, 0, 3, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.QLORA_ERR_DTYPE
+    assert q(FAKE, 1, 4, 128, 1, F32, FAKE, None, None, None, None, None) == _lib.QLORA_ERR_NULL
+    assert q(FAKE, 1, 4, 128, 1, F32, FAKE, None, None, None, FAKE + 1, None) == _lib.QLORA_ERR_ALIGN
+    assert q(FAKE, 1, 4, 128, 1, F32, FAKE, None, None, None, FAKE, None) == _lib.QLORA_ERR_DEVICE
+    assert q(FAKE, 1, 4, 128, 0, 1, FAKE, None, FAKE, FAKE, None, None) == _lib.QLORA_ERR_NULL
+    assert q(FAKE, 1, 4, 128, 1, 1, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.QLORA_ERR_DEVICE
+
+
+def test_concat_rows_variant_errors():
+    c = _lib.qlora_nf4_concat_rows
+    F32 = _lib.QLORA_CONST_FP32
+    a = _wt(n_rows=100, n_cols=64, const_type=F32, absmax=FAKE)     # 100 blocks: no group rule
+    out = _wt(n_rows=200, n_cols=64, const_type=F32, absmax=FAKE)
+    assert c([a, a], out, None) == _lib.QLORA_ERR_DEVICE
+    assert c([a, _wt(n_rows=100, n_cols=64)], out, None) == _lib.QLORA_ERR_DTYPE
+    assert c([a, a], _wt(n_rows=200, n_cols=64, quant_type=1, const_type=F32, absmax=FAKE),
+             None) == _lib.QLORA_ERR_DTYPE
