@@ -187,6 +187,70 @@ def measure_m1(torch, q, synth, gc, ev, min_bytes=600 << 20, calls=200):
     return out
 
 
+def weight_bytes(qw):
+    """Stored bytes of a quantized weight (codes and block / group constants)."""
+    return sum(a.numel() * a.element_size() for a in (qw.codes, qw.absmax_q, qw.dq_scale, qw.dq_offset,
+                                                      qw.absmax) if a is not None)
+
+
+def measure_variants(torch, q, synth, gc, wl, L, ev, steps=5, min_bytes=600 << 20, calls=20):
+    """The data-type variants (level table x block-constant type) on the same work: the
+    M = 4096 training step of the three workload-2 linears, and the M = 1 forward
+    kernel on the 4096 -> 11008 weight streamed over distinct copies (bytes as stored)."""
+    import dataclasses
+    out = {}
+    names = {(0, 0): "nf4+dq_int8", (0, 1): "nf4+dq_fp8", (0, 2): "nf4+fp32",
+             (1, 0): "fp4+dq_int8", (1, 1): "fp4+dq_fp8", (1, 2): "fp4+fp32"}
+    M = L[0]["X"].shape[0]
+    flops = sum(linear_flops(M, e["K"], e["N"], wl.r) for e in L)
+    d1 = synth.workload_linear(3, 0, M=1, parts=("W", "X", "A", "B"))
+    w1 = gc.dev_weight(d1)
+    X1, A1, B1 = gc.dev_bf16(d1["X"]), gc.dev_bf16(d1["A"]), gc.dev_bf16(d1["B"])
+    r1, alpha1 = A1.shape[0], synth.WORKLOADS[3].alpha
+    K1, N1 = w1.shape[1], w1.shape[0]
+    Y1 = torch.empty((1, N1), dtype=torch.bfloat16, device="cuda")
+    ws1 = q.workspace(0, 1, K1, N1, r1, "cuda")
+    for (qt, ct), name in names.items():
+        Lv = [dict(e, qw=q.quantize(e["W"], quant_type=qt, const_type=ct)) for e in L]
+        for _ in range(2):
+            run_step(q, wl, Lv)
+        torch.cuda.synchronize()
+        s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            run_step(q, wl, Lv)
+        f.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(f) / steps
+        del Lv
+        qw0 = q.quantize(w1, quant_type=qt, const_type=ct)
+        wb = weight_bytes(qw0)
+        copies = max(2, -(-min_bytes // wb))
+        qws = [dataclasses.replace(qw0, **{k: (getattr(qw0, k).clone() if getattr(qw0, k) is not None else None)
+                                           for k in ("codes", "absmax_q", "dq_scale", "dq_offset", "absmax")})
+               for _ in range(copies)]
+        for c in range(copies):
+            q.linear_fwd(qws[c], X1, A1, B1, alpha1, Y=Y1, save_u=False, ws=ws1)
+        torch.cuda.synchronize()
+        n0 = len(ev.pool)
+        for i in range(calls):
+            a, b = ev.pair()
+            q._lib.qlora_time_next_gemm(a, b)
+            q.linear_fwd(qws[i % copies], X1, A1, B1, alpha1, Y=Y1, save_u=False, ws=ws1)
+        torch.cuda.synchronize()
+        kms = sum(ev.ms(a, b) for a, b in ev.pool[n0:]) / calls
+        nb = wb + 2 * r1 * (K1 + N1) + 2 * K1 + 2 * N1
+        out[name] = {"step_ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "m1_kernel_us": round(kms * 1e3, 2), "m1_kernel_GB/s": round(nb / (kms * 1e-3) / 1e9, 1),
+                     "weight_bytes": wb}
+        del qws
+    ev.close()
+    out["what"] = ("per variant: fwd+bwd step of the three workload-2 linears at M=4096 (TFLOP/s as the "
+                   "headline); M=1 GEMV kernel on 4096->11008 over >512 MB of weight copies (GB/s of "
+                   "the bytes the variant stores, plus adapter, X and Y)")
+    return out
+
+
 def measure_adamw(torch, q, reps=20):
     """AdamW step over the adapters of the LLaMA-65B layer (r = 64 on all seven linears):
     fp32 parameter and moments, bf16 gradient, bf16 parameter copy; 28 bytes per value."""
@@ -482,6 +546,8 @@ def main():
         result["adamw"] = measure_adamw(torch, q)
         result["lora_merge"] = measure_merge(torch, q)
         result["layer65b"] = measure_layer65b(torch, q)
+        print("bench: data-type variants", file=sys.stderr, flush=True)
+        result["variants"] = measure_variants(torch, q, synth, gc, wl, L, ev)
     if not args.no_cpu_baseline:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(synth)
