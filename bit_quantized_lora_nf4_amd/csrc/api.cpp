@@ -155,10 +155,11 @@ FwdLayout fwd_layout(int64_t M, int64_t K, int64_t N, int r, bool need_u) {
 }
 
 struct BwdLayout {
-  size_t u, bt, v, at, part, total;
+  size_t u, bt, v, at, part, part2, total;
 };
 // U_s [M, R], B^T [r, N], V [M, R], A^T [K, R] (R = parts r), then the fp32 partial sums
-// of the largest LoRA reduction.
+// of the largest LoRA reduction, then those of dB (live together with V's partials when
+// V and dB run in one launch).
 BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N, int r, int parts) {
   BwdLayout L{};
   if (r == 0) return L;
@@ -179,6 +180,8 @@ BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N, int r, int parts) {
                            qlora::lora_down_workspace(M, Np, r)};
   for (size_t o : others) p = o > p ? o : p;
   off += align_up(p);
+  L.part2 = off;
+  off += align_up(qlora::vdb_workspace_db(M, Np, r));
   L.total = off;
   return L;
 }
@@ -295,10 +298,20 @@ int bwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16
     uint16_t *Bt = reinterpret_cast<uint16_t *>(ws + L.bt);
     uint16_t *Vw = reinterpret_cast<uint16_t *>(ws + L.v);
     uint16_t *Atw = reinterpret_cast<uint16_t *>(ws + L.at);
-    s = launched(qlora::launch_transpose_bf16(B, N, r, Bt, st), "transpose(B)");
+    // B^T for the V products and, when dX is wanted, A^T for the dX GEMM's rank steps
+    s = launched(qlora::launch_transpose2_bf16(B, N, r, Bt, dX ? A : nullptr, R, K, Atw, st), "transpose(B, A)");
     // part q: V[:, q r ..] = bf16(scale dY_q B_q) and dB_q = bf16(dY_q^T U_q), where dY_q is
-    // columns [q Np, (q + 1) Np) of dY and U_q columns [q r, (q + 1) r) of U_s
+    // columns [q Np, (q + 1) Np) of dY and U_q columns [q r, (q + 1) r) of U_s; both
+    // products in one launch (and one finalize launch) where the shapes allow
+    const bool vdb = qlora::vdb_fast(M, Np, N, R, r);
+    float *part2 = reinterpret_cast<float *>(ws + L.part2);
     for (int q = 0; q < parts && s == QLORA_OK; ++q) {
+      if (vdb) {
+        s = launched(qlora::launch_vdb(dY + q * Np, M, Np, N, Bt + q * Np, U + q * r, R, r, scale, Vw + q * r,
+                                       dB + q * Np * r, part, part2, st),
+                     "lora(V, dB)");
+        continue;
+      }
       s = launched(qlora::launch_lora_down(dY + q * Np, M, Np, N, Bt + q * Np, N, r, scale, Vw + q * r, R,
                                            part, st),
                    "lora_down(V)");
@@ -309,8 +322,6 @@ int bwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16
     }
     if (s == QLORA_OK)
       s = launched(qlora::launch_reduce_m(X, M, K, K, Vw, R, R, part, dA, true, st), "reduce(dA)");
-    if (s == QLORA_OK && dX)
-      s = launched(qlora::launch_transpose_bf16(A, R, K, Atw, st), "transpose(A)");
     if (s != QLORA_OK) return s;
     V = Vw;
     At = Atw;

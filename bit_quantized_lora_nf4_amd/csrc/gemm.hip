@@ -43,6 +43,9 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int TM = 256, TN = 256, TK = 64;
+#ifndef LORA_RQ
+#define LORA_RQ 4
+#endif
 constexpr int TILE_BYTES = TM * TK * 2;  // 32 KB per staged operand tile
 
 struct GemmParams {
@@ -115,7 +118,30 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[8][2]) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 }
 
+// One MFMA operand fragment of a LoRA matrix: 8 consecutive ranks j0 .. j0 + 7 of row
+// `row` (row pitch ld elements); rows past `rows` and ranks past r read as zero.  With
+// 16-byte aligned rows it is one 16-byte load, else eight 2-byte loads; both are
+// straight-line buffer loads.
+__device__ __forceinline__ u32x4_t lora_frag(__amdgpu_buffer_rsrc_t rs, bool vec, int row, int rows, int ld,
+                                             int j0, int r) {
+  const bool ok = row < rows;
+  if (vec) return buf_load16(rs, (ok && j0 < r) ? (static_cast<uint32_t>(row) * ld + j0) * 2 : kOOB);
+  u32x4_t v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = j0 + 2 * e;
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+        rs, (ok && j < r) ? (static_cast<uint32_t>(row) * ld + j) * 2 : kOOB, 0, 0);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+        rs, (ok && j + 1 < r) ? (static_cast<uint32_t>(row) * ld + j + 1) * 2 : kOOB, 0, 0);
+    v[e] = lo | (hi << 16);
+  }
+  return v;
+}
+
 // LoRA steps: acc[i][j] += A2 rows (tokens) x B2 rows (output columns), r in steps of 16.
+// LORA_RQ rank steps at a time: every fragment load of a chunk is issued before its
+// first MFMA, so the chunk pays one memory latency instead of one per 16 ranks.
 __device__ __forceinline__ void lora_steps(const GemmParams &p, int m0, int c0,
                                            f32x16_t (&acc)[8][2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -125,47 +151,26 @@ __device__ __forceinline__ void lora_steps(const GemmParams &p, int m0, int c0,
   const uint16_t *const A2 = p.A2 + (p.part_rows > 0 ? (c0 / p.part_rows) * r : 0);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A2, static_cast<uint32_t>(uint64_t(p.M) * lda2 * 2));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B2, static_cast<uint32_t>(uint64_t(p.No) * r * 2));
-  for (int rk = 0; rk < r; rk += 16) {
-    const int j0 = rk + (lane >> 5) * 8;
-    u32x4_t wa[2], xb[8];
+  constexpr int RQ = LORA_RQ;
+  for (int r0 = 0; r0 < r; r0 += 16 * RQ) {
+    u32x4_t wa[RQ][2], xb[RQ][8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = c0 + wave * 64 + j * 32 + (lane & 31);
-      if (vec) {
-        wa[j] = buf_load16(rb, (col < p.No && j0 < r) ? (static_cast<uint32_t>(col) * r + j0) * 2 : kOOB);
-      } else {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (col < p.No)
+    for (int q = 0; q < RQ; ++q) {
+      const int j0 = r0 + 16 * q + (lane >> 5) * 8;
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const uint32_t lo = (j0 + e < r) ? p.B2[static_cast<int64_t>(col) * r + j0 + e] : 0u;
-            const uint32_t hi = (j0 + e + 1 < r) ? p.B2[static_cast<int64_t>(col) * r + j0 + e + 1] : 0u;
-            v[e / 2] = lo | (hi << 16);
-          }
-        wa[j] = v;
-      }
+      for (int j = 0; j < 2; ++j) wa[q][j] = lora_frag(rb, vec, c0 + wave * 64 + j * 32 + (lane & 31), p.No, r, j0, r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xb[q][i] = lora_frag(ra, vec, m0 + i * 32 + (lane & 31), p.M, lda2, j0, r);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = m0 + i * 32 + (lane & 31);
-      if (vec) {
-        xb[i] = buf_load16(ra, (row < p.M && j0 < r) ? (static_cast<uint32_t>(row) * lda2 + j0) * 2 : kOOB);
-      } else {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (row < p.M)
+    for (int q = 0; q < RQ; ++q) {
+      if (r0 + 16 * q < r) {
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const uint32_t lo = (j0 + e < r) ? A2[static_cast<int64_t>(row) * lda2 + j0 + e] : 0u;
-            const uint32_t hi = (j0 + e + 1 < r) ? A2[static_cast<int64_t>(row) * lda2 + j0 + e + 1] : 0u;
-            v[e / 2] = lo | (hi << 16);
-          }
-        xb[i] = v;
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(wa[q][j], xb[q][i], acc[i][j]);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(wa[j], xb[i], acc[i][j]);
   }
 }
 
@@ -618,29 +623,26 @@ __device__ __forceinline__ void lora_steps_tok(const GemmParams &p, int m0, int 
   const bool vec = (r % 8) == 0;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A2, static_cast<uint32_t>(uint64_t(p.M) * r * 2));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B2, static_cast<uint32_t>(uint64_t(p.No) * r * 2));
-  auto frag = [&](__amdgpu_buffer_rsrc_t rs, const uint16_t *base, int row, int rows, int j0) {
-    if (vec) return buf_load16(rs, (row < rows && j0 < r) ? (static_cast<uint32_t>(row) * r + j0) * 2 : kOOB);
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (row < rows)
+  constexpr int RQ = LORA_RQ;  // rank steps per chunk, all loads before the MFMAs
+  for (int r0 = 0; r0 < r; r0 += 16 * RQ) {
+    u32x4_t wa[RQ][8], vb[RQ][2];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const uint32_t lo = (j0 + e < r) ? base[static_cast<int64_t>(row) * r + j0 + e] : 0u;
-        const uint32_t hi = (j0 + e + 1 < r) ? base[static_cast<int64_t>(row) * r + j0 + e + 1] : 0u;
-        v[e / 2] = lo | (hi << 16);
+    for (int q = 0; q < RQ; ++q) {
+      const int j0 = r0 + 16 * q + (lane >> 5) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wa[q][j] = lora_frag(rb, vec, c0 + j * 32 + (lane & 31), p.No, r, j0, r);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) vb[q][i] = lora_frag(ra, vec, m0 + wave * 64 + i * 32 + (lane & 31), p.M, r, j0, r);
+    }
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      if (r0 + 16 * q < r) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = mfma32x32x16(wa[q][j], vb[q][i], acc[i][j]);
       }
-    return v;
-  };
-  for (int rk = 0; rk < r; rk += 16) {
-    const int j0 = rk + (lane >> 5) * 8;
-    u32x4_t wa[8], vb[2];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) wa[j] = frag(rb, p.B2, c0 + j * 32 + (lane & 31), p.No, j0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) vb[i] = frag(ra, p.A2, m0 + wave * 64 + i * 32 + (lane & 31), p.M, j0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mfma32x32x16(wa[j], vb[i], acc[i][j]);
+    }
   }
 }
 

@@ -33,13 +33,13 @@ constexpr uint64_t k4G = 0xFFFFFFF0ull;
 // MFMA roles: A = WT fragment (rows j), B = IN fragment (columns m), so each lane
 // ends with 4 consecutive j of one m: 16-byte partial stores.
 template <int RT>
-__global__ __launch_bounds__(NT) void lora_down_partial_kernel(
-    const uint16_t *__restrict__ IN, int M, int Kc, int ldin, const uint16_t *__restrict__ WT, int ldwt,
-    int r, int KR, float *__restrict__ P) {
+__device__ __forceinline__ void lora_down_partial_body(
+    int bx, int by, const uint16_t *__restrict__ IN, int M, int Kc, int ldin, const uint16_t *__restrict__ WT,
+    int ldwt, int r, int KR, float *__restrict__ P) {
   __shared__ f32x16_t red[3][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m0 = blockIdx.x * 64;
-  const int ks = blockIdx.y;
+  const int m0 = bx * 64;
+  const int ks = by;
   const int kq = KR / 4;
   const int wbeg = ks * KR + wave * kq;
   const int wend = min(Kc, wbeg + kq);
@@ -70,8 +70,13 @@ __global__ __launch_bounds__(NT) void lora_down_partial_kernel(
     wt_row[t] = static_cast<uint32_t>(j) * ldwt * 2;
   }
 
-  for (int k = wbeg; k < wend; k += 64) {
-    u32x4_t a[4][RT], b[4][2];
+  // Three-stage register pipeline over the wave's 64-wide contraction steps: the loads
+  // of steps i + 1 and i + 2 are in flight while step i runs its MFMAs.  Loads past the
+  // wave's range read out of bounds (zeros, no memory traffic), so every stage issues
+  // the same loads and the compiler's wait counts stay exact across the loop.
+  typedef u32x4_t StageA[4][RT];
+  typedef u32x4_t StageB[4][2];
+  auto load = [&](int k, StageA &a, StageB &b) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int kk = k + s * 16 + kl;
@@ -83,13 +88,44 @@ __global__ __launch_bounds__(NT) void lora_down_partial_kernel(
       for (int i = 0; i < 2; ++i)
         b[s][i] = buf_load16(rin, (in_ok[i] && kin) ? in_row[i] + kk * 2 : kOOB);
     }
+  };
+  auto mma = [&](const StageA &a, const StageB &b) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int t = 0; t < RT; ++t) acc[i][t] = mfma32x32x16(a[s][t], b[s][i], acc[i][t]);
+  };
+  const int nsteps = wend > wbeg ? (wend - wbeg + 63) / 64 : 0;
+  StageA a0, a1, a2;
+  StageB b0, b1, b2;
+  load(wbeg, a0, b0);
+  load(wbeg + 64, a1, b1);
+  // the fences keep each group of loads ahead of the MFMAs that follow it (the
+  // scheduler would otherwise sink them, and the waits would then cover every stage)
+  auto fence = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  fence();
+  int i = 0;
+  for (; i + 3 <= nsteps; i += 3) {  // stage roles fixed by the three-way unroll
+    load(wbeg + (i + 2) * 64, a2, b2);
+    fence();
+    mma(a0, b0);
+    fence();
+    load(wbeg + (i + 3) * 64, a0, b0);
+    fence();
+    mma(a1, b1);
+    fence();
+    load(wbeg + (i + 4) * 64, a1, b1);
+    fence();
+    mma(a2, b2);
+    fence();
   }
+  if (i < nsteps) mma(a0, b0);
+  if (i + 1 < nsteps) mma(a1, b1);
 
   float *dst = P + static_cast<size_t>(ks) * M * r;
 #pragma unroll
@@ -121,6 +157,13 @@ __global__ __launch_bounds__(NT) void lora_down_partial_kernel(
   }
 }
 
+template <int RT>
+__global__ __launch_bounds__(NT) void lora_down_partial_kernel(
+    const uint16_t *__restrict__ IN, int M, int Kc, int ldin, const uint16_t *__restrict__ WT, int ldwt,
+    int r, int KR, float *__restrict__ P) {
+  lora_down_partial_body<RT>(blockIdx.x, blockIdx.y, IN, M, Kc, ldin, WT, ldwt, r, KR, P);
+}
+
 // ---------------------------------------------------------------------------------
 // reduce_m: partial sums over a split of rows m of IN[m][no] * S[m][j].
 // Workgroup: 64 columns of IN x all RT*32 >= r columns of S, one M-split.  Each
@@ -131,14 +174,17 @@ __global__ __launch_bounds__(NT) void lora_down_partial_kernel(
 constexpr int PD = 20;  // dwords per LDS row: 16 m-pairs + 4 padding
 
 template <int RT, bool JMAJOR>
-__global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
-    const uint16_t *__restrict__ IN, int M, int No, int ldin, const uint16_t *__restrict__ S, int lds,
-    int r, int MR, float *__restrict__ P) {
-  __shared__ __attribute__((aligned(16))) uint32_t sIn[64 * PD];
-  __shared__ __attribute__((aligned(16))) uint32_t sS[RT * 32 * PD];
+__device__ __forceinline__ void reduce_m_partial_body(
+    int bx, int by, const uint16_t *__restrict__ IN, int M, int No, int ldin, const uint16_t *__restrict__ S,
+    int lds, int r, int MR, float *__restrict__ P) {
+  // two LDS buffers: step i is staged into buffer i % 2, so one barrier per step
+  // separates its writes from its reads, and the previous step's barrier separates
+  // them from the reads of step i - 2 in the same buffer
+  __shared__ __attribute__((aligned(16))) uint32_t sIn[2][64 * PD];
+  __shared__ __attribute__((aligned(16))) uint32_t sS[2][RT * 32 * PD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nb0 = blockIdx.x * 64;
-  const int sp = blockIdx.y;
+  const int nb0 = bx * 64;
+  const int sp = by;
   const int mb = sp * MR, me = min(M, mb + MR);
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(IN, static_cast<uint32_t>(uint64_t(M) * ldin * 2));
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, static_cast<uint32_t>(uint64_t(M) * lds * 2));
@@ -146,48 +192,49 @@ __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
   // load tasks: (pair p, 8-column chunk c) of IN (128 tasks) then of S (RT*64 tasks)
   constexpr int NTASK = 128 + RT * 64;
   constexpr int TPT = (NTASK + NT - 1) / NT;  // tasks per thread
-  u32x4_t ra[TPT], rb[TPT];
+  struct Stage {
+    u32x4_t a[TPT], b[TPT];
+  };
 
-  auto issue = [&](int mstep) {
+  // Rows at or past the split's end read as zero (no memory traffic).  Task ranges are
+  // multiples of 64, so whether a task reads IN or S, or is idle, depends on the wave
+  // only.  The loads are straight-line (offsets by selects, idle tasks out of range),
+  // so the compiler's wait counts stay exact across the pipelined loop.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int mstep, Stage &st) {
 #pragma unroll
     for (int q = 0; q < TPT; ++q) {
-      const int task = tid + q * NT;
-      uint32_t oa = kOOB, ob = kOOB;
-      if (task < 128) {
-        const int p = task & 15, c = task >> 4;
-        const int m = mstep + 2 * p, col = nb0 + c * 8;
-        if (col < No) {
-          if (m < me) oa = (static_cast<uint32_t>(m) * ldin + col) * 2;
-          if (m + 1 < me) ob = (static_cast<uint32_t>(m + 1) * ldin + col) * 2;
-        }
-        ra[q] = buf_load16(rin, oa);
-        rb[q] = buf_load16(rin, ob);
-      } else if (task < NTASK) {
-        const int t2 = task - 128;
-        const int p = t2 & 15, c = t2 >> 4;
-        const int m = mstep + 2 * p, col = c * 8;
-        if (col < r) {
-          if (m < me) oa = (static_cast<uint32_t>(m) * lds + col) * 2;
-          if (m + 1 < me) ob = (static_cast<uint32_t>(m + 1) * lds + col) * 2;
-        }
-        ra[q] = buf_load16(rs, oa);
-        rb[q] = buf_load16(rs, ob);
-      }
+      const int task_w = wave_u * 64 + q * NT;  // the wave's first task
+      const bool is_in = task_w < 128;          // wave-uniform
+      const bool live = task_w < NTASK;         // wave-uniform
+      const int t2 = (is_in ? tid + q * NT : tid + q * NT - 128);
+      const int p = t2 & 15, c = t2 >> 4;
+      const int m = mstep + 2 * p;
+      const int col = is_in ? nb0 + c * 8 : c * 8;
+      const int lim = is_in ? No : r;
+      const uint32_t ld = static_cast<uint32_t>(is_in ? ldin : lds);
+      const bool ok = live && col < lim;
+      const uint32_t oa = (ok && m < me) ? (static_cast<uint32_t>(m) * ld + col) * 2 : kOOB;
+      const uint32_t ob = (ok && m + 1 < me) ? (static_cast<uint32_t>(m + 1) * ld + col) * 2 : kOOB;
+      const __amdgpu_buffer_rsrc_t rr = is_in ? rin : rs;
+      st.a[q] = buf_load16(rr, oa);
+      st.b[q] = buf_load16(rr, ob);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](const Stage &st, int buf) {
 #pragma unroll
     for (int q = 0; q < TPT; ++q) {
       const int task = tid + q * NT;
-      if (task >= NTASK) continue;
-      const bool is_in = task < 128;
+      const int task_w = wave_u * 64 + q * NT;
+      if (task_w >= NTASK) continue;
+      const bool is_in = task_w < 128;
       const int t2 = is_in ? task : task - 128;
       const int p = t2 & 15, c = t2 >> 4;
-      uint32_t *base = (is_in ? sIn : sS) + (c * 8) * PD + p;
+      uint32_t *base = (is_in ? sIn[buf] : sS[buf]) + (c * 8) * PD + p;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        base[(2 * e) * PD] = pack_lo(ra[q][e], rb[q][e]);
-        base[(2 * e + 1) * PD] = pack_hi(ra[q][e], rb[q][e]);
+        base[(2 * e) * PD] = pack_lo(st.a[q][e], st.b[q][e]);
+        base[(2 * e + 1) * PD] = pack_hi(st.a[q][e], st.b[q][e]);
       }
     }
   };
@@ -201,28 +248,55 @@ __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[u][e] = 0.0f;
 
-  if (mb < me) issue(mb);
-  for (int ms = mb; ms < me; ms += 32) {
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (ms + 32 < me) issue(ms + 32);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      const int tile = wave + 4 * u;
+      const int tile = wave_u + 4 * u;
       if (tile >= TILES) continue;
       const int nbk = tile & 1, t = tile >> 1;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int doff = kk * 8 + (lane >> 5) * 4;
         const u32x4_t fin =
-            *reinterpret_cast<const u32x4_t *>(sIn + (nbk * 32 + (lane & 31)) * PD + doff);
+            *reinterpret_cast<const u32x4_t *>(sIn[buf] + (nbk * 32 + (lane & 31)) * PD + doff);
         const u32x4_t fs =
-            *reinterpret_cast<const u32x4_t *>(sS + (t * 32 + (lane & 31)) * PD + doff);
+            *reinterpret_cast<const u32x4_t *>(sS[buf] + (t * 32 + (lane & 31)) * PD + doff);
         acc[u] = JMAJOR ? mfma32x32x16(fin, fs, acc[u]) : mfma32x32x16(fs, fin, acc[u]);
       }
     }
+  };
+  auto fence = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Four steps of 32 rows in flight: the loads of step i + 3 are issued before step i
+  // is staged.  Register stages have fixed roles in a four-way unrolled loop, so the
+  // compiler's wait counts leave the three later steps outstanding.
+  const int nst = me > mb ? (me - mb + 31) / 32 : 0;
+  Stage s0, s1, s2, s3;
+  issue(mb, s0);
+  issue(mb + 32, s1);
+  issue(mb + 64, s2);
+  fence();
+  auto one = [&](int i, Stage &cur, Stage &ahead, int buf) {
+    issue(mb + (i + 3) * 32, ahead);
+    fence();
+    stage(cur, buf);
+    __syncthreads();
+    compute(buf);
+    fence();
+  };
+  int i = 0;
+  for (; i + 4 <= nst; i += 4) {
+    one(i, s0, s3, 0);
+    one(i + 1, s1, s0, 1);
+    one(i + 2, s2, s1, 0);
+    one(i + 3, s3, s2, 1);
   }
+  if (i < nst) one(i, s0, s3, 0);
+  if (i + 1 < nst) one(i + 1, s1, s0, 1);
+  if (i + 2 < nst) one(i + 2, s2, s1, 0);
 
   float *dst = P + static_cast<size_t>(sp) * No * r;
 #pragma unroll
@@ -245,6 +319,44 @@ __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
   }
 }
 
+template <int RT, bool JMAJOR>
+__global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
+    const uint16_t *__restrict__ IN, int M, int No, int ldin, const uint16_t *__restrict__ S, int lds,
+    int r, int MR, float *__restrict__ P) {
+  reduce_m_partial_body<RT, JMAJOR>(blockIdx.x, blockIdx.y, IN, M, No, ldin, S, lds, r, MR, P);
+}
+
+// The two products of the backward that read only dY, in one launch: workgroups
+// [0, nd) compute the V partials (lora_down over dY and B^T), the rest the dB partials
+// (reduce over tokens of dY and U_s).  Same bodies, same partial sums as the separate
+// kernels.
+struct DownArgs {
+  const uint16_t *IN;
+  int M, Kc, ldin;
+  const uint16_t *WT;
+  int ldwt, r, KR;
+  float *P;
+  int gx;  // row-tile count (first grid dimension of the separate kernel)
+};
+struct ReduceArgs {
+  const uint16_t *IN;
+  int M, No, ldin;
+  const uint16_t *S;
+  int lds, r, MR;
+  float *P;
+  int gx;
+};
+template <int RT>
+__global__ __launch_bounds__(NT) void down_reduce_partial_kernel(DownArgs d, ReduceArgs q, int nd) {
+  const int b = blockIdx.x;
+  if (b < nd) {
+    lora_down_partial_body<RT>(b % d.gx, b / d.gx, d.IN, d.M, d.Kc, d.ldin, d.WT, d.ldwt, d.r, d.KR, d.P);
+  } else {
+    const int c = b - nd;
+    reduce_m_partial_body<RT, false>(c % q.gx, c / q.gx, q.IN, q.M, q.No, q.ldin, q.S, q.lds, q.r, q.MR, q.P);
+  }
+}
+
 // OUT = bf16(scale * sum_s P[s]) for the `count` partial sums (count % 4 == 0) laid out
 // as rows of `cols` values (cols % 4 == 0), written with row pitch ldout; fixed order.
 __global__ __launch_bounds__(NT) void finalize_kernel(const float *__restrict__ P, int splits,
@@ -258,6 +370,32 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const float *__restrict__ 
     u32x2_t o = {pack_bf16x2(s[0] * scale, s[1] * scale), pack_bf16x2(s[2] * scale, s[3] * scale)};
     const int64_t e = 4 * i, row = e / cols, col = e % cols;
     *reinterpret_cast<u32x2_t *>(OUT + row * ldout + col) = o;
+  }
+}
+
+// Two finalize passes in one launch (the same fixed order and rounding as finalize_kernel).
+struct FinJob {
+  const float *P;
+  int splits;
+  int64_t count, cols, ldout;
+  float scale;
+  uint16_t *OUT;
+};
+__device__ __forceinline__ void finalize_one(const FinJob &j, int64_t i) {
+  f32x4_t s = reinterpret_cast<const f32x4_t *>(j.P)[i];
+  for (int k = 1; k < j.splits; ++k) s += reinterpret_cast<const f32x4_t *>(j.P + k * j.count)[i];
+  u32x2_t o = {pack_bf16x2(s[0] * j.scale, s[1] * j.scale), pack_bf16x2(s[2] * j.scale, s[3] * j.scale)};
+  const int64_t e = 4 * i, row = e / j.cols, col = e % j.cols;
+  *reinterpret_cast<u32x2_t *>(j.OUT + row * j.ldout + col) = o;
+}
+__global__ __launch_bounds__(NT) void finalize2_kernel(FinJob a, FinJob b) {
+  const int64_t na = a.count / 4, n = na + b.count / 4;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * NT) {
+    if (i < na)
+      finalize_one(a, i);
+    else
+      finalize_one(b, i - na);
   }
 }
 
@@ -386,19 +524,63 @@ __global__ __launch_bounds__(NT) void reduce_m_generic_final_kernel(
   }
 }
 
-__global__ __launch_bounds__(NT) void transpose_kernel(const uint16_t *__restrict__ IN, int64_t R,
-                                                       int64_t C, uint16_t *__restrict__ OUT) {
-  __shared__ uint16_t tile[64][65];
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t rr = r0 + i, c = c0 + tx;
-    tile[i][tx] = (rr < R && c < C) ? IN[rr * C + c] : uint16_t(0);
+// Transposes of two bf16 matrices in one launch: OUT_q[C_q, R_q] = IN_q[R_q, C_q]^T for
+// q = 0, 1 (workgroups [0, n0) take matrix 0).  A workgroup moves one 64 x 64 tile
+// through LDS: 16-byte row loads when C % 8 == 0 and 16-byte stores when R % 8 == 0,
+// element accesses otherwise.
+struct TransposeJob {
+  const uint16_t *in;
+  uint16_t *out;
+  int64_t R, C;
+  int64_t tiles_c;  // ceil(C / 64)
+};
+
+__global__ __launch_bounds__(NT) void transpose2_kernel(TransposeJob j0, TransposeJob j1, int64_t n0) {
+  __shared__ uint16_t tile[64][72];  // row pitch 144 B: 16-byte aligned rows
+  const bool second = blockIdx.x >= n0;
+  const TransposeJob &jb = second ? j1 : j0;
+  const int64_t b = second ? blockIdx.x - n0 : blockIdx.x;
+  const int64_t r0 = (b / jb.tiles_c) * 64, c0 = (b % jb.tiles_c) * 64;
+  const int tid = threadIdx.x, ch = tid & 7;
+  const bool vin = jb.C % 8 == 0, vout = jb.R % 8 == 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = (tid >> 3) + 32 * i;
+    const int64_t row = r0 + rr, col = c0 + ch * 8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (row < jb.R && col < jb.C) {
+      const uint16_t *src = jb.in + row * jb.C + col;
+      if (vin) {
+        v = *reinterpret_cast<const u32x4_t *>(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t lo = col + e < jb.C ? src[e] : 0u;
+          const uint32_t hi = col + e + 1 < jb.C ? src[e + 1] : 0u;
+          v[e / 2] = lo | (hi << 16);
+        }
+      }
+    }
+    *reinterpret_cast<u32x4_t *>(&tile[rr][ch * 8]) = v;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, rr = r0 + tx;
-    if (rr < R && c < C) OUT[c * R + rr] = tile[tx][i];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int cc = (tid >> 3) + 32 * i;  // output row = input column c0 + cc
+    const int64_t orow = c0 + cc, ocol = r0 + ch * 8;
+    if (orow >= jb.C || ocol >= jb.R) continue;
+    uint16_t *dst = jb.out + orow * jb.R + ocol;
+    u32x4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = uint32_t(tile[ch * 8 + 2 * e][cc]) | (uint32_t(tile[ch * 8 + 2 * e + 1][cc]) << 16);
+    if (vout) {
+      *reinterpret_cast<u32x4_t *>(dst) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ocol + e < jb.R) dst[e] = static_cast<uint16_t>(v[e / 2] >> (16 * (e & 1)));
+    }
   }
 }
 
@@ -498,10 +680,14 @@ hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, int64_t l
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_bf16(const uint16_t *IN, int64_t R, int64_t C, uint16_t *OUT,
-                                 hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((R + 63) / 64)), block(NT);
-  hipLaunchKernelGGL(transpose_kernel, grid, block, 0, stream, IN, R, C, OUT);
+hipError_t launch_transpose2_bf16(const uint16_t *IN0, int64_t R0, int64_t C0, uint16_t *OUT0, const uint16_t *IN1,
+                                  int64_t R1, int64_t C1, uint16_t *OUT1, hipStream_t stream) {
+  TransposeJob j0{IN0, OUT0, R0, C0, (C0 + 63) / 64}, j1{IN1, OUT1, R1, C1, (C1 + 63) / 64};
+  const int64_t n0 = IN0 ? ((R0 + 63) / 64) * j0.tiles_c : 0;
+  const int64_t n1 = IN1 ? ((R1 + 63) / 64) * j1.tiles_c : 0;
+  if (n0 + n1 == 0) return hipSuccess;
+  if (n0 + n1 > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose2_kernel, dim3(static_cast<unsigned>(n0 + n1)), dim3(NT), 0, stream, j0, j1, n0);
   return hipGetLastError();
 }
 
@@ -559,6 +745,51 @@ hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, int64_t ld
   if (fb > 4096) fb = 4096;
   hipLaunchKernelGGL(reduce_m_generic_final_kernel, dim3(static_cast<unsigned>(fb)), dim3(NT), 0,
                      stream, partials, splits, No, r, OUT, trans_out);
+  return hipGetLastError();
+}
+
+bool vdb_fast(int64_t M, int64_t Np, int64_t ldy, int64_t ldu, int r) {
+  return down_fast(M, Np, ldy, ldy, r, ldu) && reduce_fast(M, Np, ldy, ldu, r);
+}
+
+size_t vdb_workspace_v(int64_t M, int64_t Np, int r) {
+  return static_cast<size_t>(down_split(M, Np).ksplit) * M * r * sizeof(float);
+}
+size_t vdb_workspace_db(int64_t M, int64_t Np, int r) {
+  return static_cast<size_t>(m_split(M, Np).splits) * Np * r * sizeof(float);
+}
+
+hipError_t launch_vdb(const uint16_t *dY, int64_t M, int64_t Np, int64_t ldy, const uint16_t *Bt, const uint16_t *U,
+                      int64_t ldu, int r, float scale, uint16_t *V, uint16_t *dB, float *ws_v, float *ws_db,
+                      hipStream_t stream) {
+  const int rt = (r + 31) / 32;
+  if (rt < 1 || rt > 8 || !vdb_fast(M, Np, ldy, ldu, r)) return hipErrorInvalidValue;
+  const DownSplit sd = down_split(M, Np);
+  const MSplit sq = m_split(M, Np);
+  DownArgs d{dY, static_cast<int>(M), static_cast<int>(Np), static_cast<int>(ldy), Bt, static_cast<int>(ldy), r,
+             sd.KR, ws_v, static_cast<int>((M + 63) / 64)};
+  ReduceArgs q{dY, static_cast<int>(M), static_cast<int>(Np), static_cast<int>(ldy), U, static_cast<int>(ldu), r,
+               sq.MR, ws_db, static_cast<int>((Np + 63) / 64)};
+  const int64_t nd = int64_t(d.gx) * sd.ksplit, nq = int64_t(q.gx) * sq.splits;
+  if (nd + nq > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(nd + nq)), block(NT);
+  switch (rt) {
+#define QLORA_CASE(T)                                                                                  \
+  case T:                                                                                              \
+    hipLaunchKernelGGL(down_reduce_partial_kernel<T>, grid, block, 0, stream, d, q, static_cast<int>(nd)); \
+    break;
+    QLORA_CASE(1) QLORA_CASE(2) QLORA_CASE(3) QLORA_CASE(4)
+    QLORA_CASE(5) QLORA_CASE(6) QLORA_CASE(7) QLORA_CASE(8)
+#undef QLORA_CASE
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // V = bf16(scale sum P_V) as [M, r] rows of pitch ldu; dB = bf16(sum P_dB) dense [Np, r]
+  const FinJob fv{ws_v, sd.ksplit, M * r, r, ldu, scale, V};
+  const FinJob fb{ws_db, sq.splits, Np * r, Np * r, Np * r, 1.0f, dB};
+  int64_t blocks = ((fv.count + fb.count) / 4 + NT - 1) / NT;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(finalize2_kernel, dim3(static_cast<unsigned>(blocks)), dim3(NT), 0, stream, fv, fb);
   return hipGetLastError();
 }
 

@@ -67,9 +67,10 @@ size_t lora_down_workspace(int64_t M, int64_t Kc, int r);
 hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, int64_t ldin, const uint16_t *WT,
                             int64_t ldwt, int r, float scale, uint16_t *OUT, int64_t ldout, float *ws,
                             hipStream_t stream);
-// OUT[C, R] = IN[R, C]^T for bf16 matrices (both dense row-major).
-hipError_t launch_transpose_bf16(const uint16_t *IN, int64_t R, int64_t C, uint16_t *OUT,
-                                 hipStream_t stream);
+// OUT_q[C_q, R_q] = IN_q[R_q, C_q]^T for two bf16 matrices (dense row-major) in one
+// launch; IN1 may be NULL (one transpose).
+hipError_t launch_transpose2_bf16(const uint16_t *IN0, int64_t R0, int64_t C0, uint16_t *OUT0, const uint16_t *IN1,
+                                  int64_t R1, int64_t C1, uint16_t *OUT1, hipStream_t stream);
 // P[s][No][r] fp32 partials of sum over m in split s of IN[m][no] * S[m][j]; then
 // OUT = bf16(sum_s P) written as [No, r] (trans_out = false) or [r, No] (true).
 // IN rows have pitch ldin, S rows pitch lds.
@@ -77,6 +78,18 @@ size_t reduce_m_workspace(int64_t M, int64_t No, int r);
 hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, int64_t ldin, const uint16_t *S,
                            int64_t lds, int r, float *partials, uint16_t *OUT, bool trans_out,
                            hipStream_t stream);
+
+// The backward's two products over dY in one launch plus one finalize launch:
+// V[M, r] (row pitch ldu) = bf16(scale dY Bt^T) and dB[Np, r] = bf16(dY^T U), where dY
+// has row pitch ldy (a column slice of width Np), Bt is [r, Np] with row pitch ldy and U
+// [M, r] with row pitch ldu.  Needs the fast-path shapes (vdb_fast) and the two fp32
+// partial regions sized by vdb_workspace_v / vdb_workspace_db.
+bool vdb_fast(int64_t M, int64_t Np, int64_t ldy, int64_t ldu, int r);
+size_t vdb_workspace_v(int64_t M, int64_t Np, int r);
+size_t vdb_workspace_db(int64_t M, int64_t Np, int r);
+hipError_t launch_vdb(const uint16_t *dY, int64_t M, int64_t Np, int64_t ldy, const uint16_t *Bt, const uint16_t *U,
+                      int64_t ldu, int r, float scale, uint16_t *V, uint16_t *dB, float *ws_v, float *ws_db,
+                      hipStream_t stream);
 
 // AdamW step (fp32 parameter and moments, bf16 gradient, optional bf16 parameter copy).
 struct AdamConsts {
