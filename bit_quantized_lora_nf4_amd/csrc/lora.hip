@@ -25,143 +25,139 @@ namespace {
 
 constexpr int NT = 256;
 constexpr uint64_t k4G = 0xFFFFFFF0ull;
+constexpr int64_t kDownWGs = 256;  // lora_down workgroups aimed at (one per CU)
 
 // ---------------------------------------------------------------------------------
 // lora_down: P[ks][m][j] = sum_{k in split ks} IN[m][k] WT[j][k]
-// Workgroup: 64 rows of IN x all RT*32 >= r columns, one K-split; the four waves
-// take consecutive quarters of the split and are summed in LDS (fixed order).
 // MFMA roles: A = WT fragment (rows j), B = IN fragment (columns m), so each lane
 // ends with 4 consecutive j of one m: 16-byte partial stores.
-template <int RT>
-__device__ __forceinline__ void lora_down_partial_body(
+//
+// lora_down with LDS-staged operands: the same partial sums P[ks][m][j] over one K-split,
+// with both operand tiles brought into LDS by direct buffer -> LDS loads.  A 64-wide
+// contraction step stages IN rows m0 .. m0 + 63 and WT rows 0 .. 32 RT - 1, 128 bytes
+// each; eight lanes read one whole row (the 16-byte chunk a lane fetches is the one that
+// belongs at its slot of the swizzled tile, chunk c of row x at slot c ^ f(x), as in the
+// forward GEMM), so every load instruction covers eight complete 128-byte lines.  NB
+// buffers keep NB - 1 steps of loads in flight; one barrier per step publishes a step's
+// tile and retires the buffer that the next loads overwrite.  Wave w owns output tiles
+// w, w + 4, ... of the 2 x RT tiles of 32 x 32 and accumulates them over the whole split,
+// so no cross-wave reduction is needed.
+__device__ __forceinline__ int stile_off(int row, int c) { return row * 128 + ((c ^ ((row & 7) ^ ((row >> 3) & 1))) << 4); }
+
+template <int RT, int NB>
+__device__ __forceinline__ void lora_down_dma_body(
     int bx, int by, const uint16_t *__restrict__ IN, int M, int Kc, int ldin, const uint16_t *__restrict__ WT,
     int ldwt, int r, int KR, float *__restrict__ P) {
-  __shared__ f32x16_t red[3][2][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int ROWS = 64 + 32 * RT;       // staged rows per step (IN then WT)
+  constexpr int BUF = ROWS * 128;          // bytes per buffer
+  constexpr int NLD = ROWS / 8;            // 1 KB loads per step
+  constexpr int LPW = NLD / 4;             // loads per wave and step
+  constexpr int TILES = 2 * RT, TPW = (TILES + 3) / 4;
+  __shared__ __attribute__((aligned(16))) char sbuf[NB * BUF];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m0 = bx * 64;
-  const int ks = by;
-  const int kq = KR / 4;
-  const int wbeg = ks * KR + wave * kq;
-  const int wend = min(Kc, wbeg + kq);
+  const int kbeg = by * KR, kend = min(Kc, kbeg + KR);
+  const int nsteps = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(IN, static_cast<uint32_t>(uint64_t(M) * ldin * 2));
   const __amdgpu_buffer_rsrc_t rwt = make_rsrc(WT, static_cast<uint32_t>(uint64_t(r) * ldwt * 2));
-  const int kl = (lane >> 5) * 8;
 
-  f32x16_t acc[2][RT];
+  // per-lane row byte offsets of this wave's loads (kOOB for rows past M or r) and the
+  // 16-byte chunk each lane fetches
+  uint32_t roff[LPW];
+  int chk[LPW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.0f;
-
-  uint32_t in_row[2], wt_row[RT];
-  bool in_ok[2], wt_ok[RT];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = m0 + i * 32 + (lane & 31);
-    in_ok[i] = row < M;
-    in_row[i] = static_cast<uint32_t>(row) * ldin * 2;
+  for (int u = 0; u < LPW; ++u) {
+    const int g = wave + 4 * u;            // load index: rows 8 g .. 8 g + 7 of the step tile
+    const int x = 8 * g + (lane >> 3);     // staged row
+    chk[u] = (lane & 7) ^ ((x & 7) ^ ((x >> 3) & 1));
+    if (x < 64)
+      roff[u] = m0 + x < M ? static_cast<uint32_t>(m0 + x) * ldin * 2 : kOOB;
+    else
+      roff[u] = x - 64 < r ? static_cast<uint32_t>(x - 64) * ldwt * 2 : kOOB;
   }
+  auto dma = [&](int step) {
+    char *dst = sbuf + (step % NB) * BUF;
+    const int kt = kbeg + step * 64;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int j = t * 32 + (lane & 31);
-    wt_ok[t] = j < r;
-    wt_row[t] = static_cast<uint32_t>(j) * ldwt * 2;
-  }
-
-  // Three-stage register pipeline over the wave's 64-wide contraction steps: the loads
-  // of steps i + 1 and i + 2 are in flight while step i runs its MFMAs.  Loads past the
-  // wave's range read out of bounds (zeros, no memory traffic), so every stage issues
-  // the same loads and the compiler's wait counts stay exact across the loop.
-  typedef u32x4_t StageA[4][RT];
-  typedef u32x4_t StageB[4][2];
-  auto load = [&](int k, StageA &a, StageB &b) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kk = k + s * 16 + kl;
-      const bool kin = kk < wend;
-#pragma unroll
-      for (int t = 0; t < RT; ++t)
-        a[s][t] = buf_load16(rwt, (wt_ok[t] && kin) ? wt_row[t] + kk * 2 : kOOB);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        b[s][i] = buf_load16(rin, (in_ok[i] && kin) ? in_row[i] + kk * 2 : kOOB);
+    for (int u = 0; u < LPW; ++u) {
+      const int g = wave + 4 * u;
+      const int k = kt + chk[u] * 8;
+      const uint32_t off = (roff[u] != kOOB && k < kend) ? roff[u] + k * 2 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(8 * g < 64 ? rin : rwt,
+                                               (__attribute__((address_space(3))) void *)(dst + g * 1024), 16,
+                                               off, 0, 0, 0);
     }
   };
-  auto mma = [&](const StageA &a, const StageB &b) {
+
+  f32x16_t acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[u][e] = 0.0f;
+
+#pragma unroll
+  for (int s = 0; s < NB - 1; ++s) dma(s);
+  for (int i = 0; i < nsteps; ++i) {
+    // step i has landed for every wave, and no wave still reads buffer (i - 1) % NB
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NB - 2) * LPW) : "memory");
+    dma(i + NB - 1);
+    const char *sb = sbuf + (i % NB) * BUF;
+    // all fragments of the step first, then the MFMAs (one LDS latency per step)
+    u32x4_t fa[TPW][4], fb[TPW][4];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = wave + 4 * u;
+      if (TILES % 4 != 0 && tile >= TILES) continue;
+      const int ti = tile & 1, tt = tile >> 1;  // row half of IN, rank tile of WT
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int c = 2 * s + (lane >> 5);
+        fa[u][s] = *reinterpret_cast<const u32x4_t *>(sb + stile_off(64 + 32 * tt + (lane & 31), c));
+        fb[u][s] = *reinterpret_cast<const u32x4_t *>(sb + stile_off(32 * ti + (lane & 31), c));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int t = 0; t < RT; ++t) acc[i][t] = mfma32x32x16(a[s][t], b[s][i], acc[i][t]);
-  };
-  const int nsteps = wend > wbeg ? (wend - wbeg + 63) / 64 : 0;
-  StageA a0, a1, a2;
-  StageB b0, b1, b2;
-  load(wbeg, a0, b0);
-  load(wbeg + 64, a1, b1);
-  // the fences keep each group of loads ahead of the MFMAs that follow it (the
-  // scheduler would otherwise sink them, and the waits would then cover every stage)
-  auto fence = [] {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  fence();
-  int i = 0;
-  for (; i + 3 <= nsteps; i += 3) {  // stage roles fixed by the three-way unroll
-    load(wbeg + (i + 2) * 64, a2, b2);
-    fence();
-    mma(a0, b0);
-    fence();
-    load(wbeg + (i + 3) * 64, a0, b0);
-    fence();
-    mma(a1, b1);
-    fence();
-    load(wbeg + (i + 4) * 64, a1, b1);
-    fence();
-    mma(a2, b2);
-    fence();
+      for (int u = 0; u < TPW; ++u) {
+        const int tile = wave + 4 * u;
+        if (TILES % 4 != 0 && tile >= TILES) continue;
+        acc[u] = mfma32x32x16(fa[u][s], fb[u][s], acc[u]);
+      }
   }
-  if (i < nsteps) mma(a0, b0);
-  if (i + 1 < nsteps) mma(a1, b1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land after the kernel ends
 
-  float *dst = P + static_cast<size_t>(ks) * M * r;
+  float *dst = P + static_cast<size_t>(by) * M * r;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    if (wave > 0) {
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = wave + 4 * u;
+    if (TILES % 4 != 0 && tile >= TILES) continue;
+    const int ti = tile & 1, tt = tile >> 1;
+    const int m = m0 + 32 * ti + (lane & 31);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) red[wave - 1][i][lane] = acc[i][t];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        f32x16_t v = acc[i][t];
-        v += red[0][i][lane];
-        v += red[1][i][lane];
-        v += red[2][i][lane];
-        const int m = m0 + i * 32 + (lane & 31);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int j0 = t * 32 + g * 8 + (lane >> 5) * 4;
-          if (m < M && j0 < r) {
-            f32x4_t o = {v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
-            *reinterpret_cast<f32x4_t *>(dst + static_cast<size_t>(m) * r + j0) = o;
-          }
-        }
+    for (int g = 0; g < 4; ++g) {
+      const int j0 = tt * 32 + g * 8 + (lane >> 5) * 4;
+      if (m < M && j0 < r) {
+        f32x4_t o = {acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
+        *reinterpret_cast<f32x4_t *>(dst + static_cast<size_t>(m) * r + j0) = o;
       }
     }
-    __syncthreads();
   }
+}
+
+// LDS buffers of the staged lora_down: as many as fit (at most 4) next to `other` bytes
+template <int RT>
+constexpr int down_nb(int other) {
+  return (4 * (64 + 32 * RT) * 128 + other <= 160 * 1024) ? 4 : (3 * (64 + 32 * RT) * 128 + other <= 160 * 1024) ? 3 : 2;
 }
 
 template <int RT>
 __global__ __launch_bounds__(NT) void lora_down_partial_kernel(
     const uint16_t *__restrict__ IN, int M, int Kc, int ldin, const uint16_t *__restrict__ WT, int ldwt,
     int r, int KR, float *__restrict__ P) {
-  lora_down_partial_body<RT>(blockIdx.x, blockIdx.y, IN, M, Kc, ldin, WT, ldwt, r, KR, P);
+  lora_down_dma_body<RT, down_nb<RT>(0)>(blockIdx.x, blockIdx.y, IN, M, Kc, ldin, WT, ldwt, r, KR, P);
 }
 
 // ---------------------------------------------------------------------------------
@@ -350,7 +346,9 @@ template <int RT>
 __global__ __launch_bounds__(NT) void down_reduce_partial_kernel(DownArgs d, ReduceArgs q, int nd) {
   const int b = blockIdx.x;
   if (b < nd) {
-    lora_down_partial_body<RT>(b % d.gx, b / d.gx, d.IN, d.M, d.Kc, d.ldin, d.WT, d.ldwt, d.r, d.KR, d.P);
+    constexpr int reduce_lds = (2 * 64 * PD + 2 * RT * 32 * PD) * 4;
+    lora_down_dma_body<RT, down_nb<RT>(reduce_lds)>(b % d.gx, b / d.gx, d.IN, d.M, d.Kc, d.ldin, d.WT, d.ldwt,
+                                                       d.r, d.KR, d.P);
   } else {
     const int c = b - nd;
     reduce_m_partial_body<RT, false>(c % q.gx, c / q.gx, q.IN, q.M, q.No, q.ldin, q.S, q.lds, q.r, q.MR, q.P);
@@ -590,7 +588,7 @@ struct DownSplit {
 };
 DownSplit down_split(int64_t M, int64_t Kc) {
   const int64_t row_tiles = (M + 63) / 64;
-  int64_t ks = (256 + row_tiles - 1) / row_tiles;
+  int64_t ks = (kDownWGs + row_tiles - 1) / row_tiles;
   const int64_t kmax = (Kc + 255) / 256;
   if (ks > kmax) ks = kmax;
   if (ks < 1) ks = 1;
