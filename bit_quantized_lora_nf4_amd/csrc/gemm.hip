@@ -464,7 +464,6 @@ __device__ __forceinline__ void code_store_bwd(const GemmParams &p, const CodeSt
       *reinterpret_cast<u32x4_t *>(sw + wtile_off(n, c0 + h * 32 + i * 8)) = lookup8(cs.code[h][i], pl);
 }
 
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 // Weight-side MFMA fragment for contraction step s (16 rows) and output-column tile
 // j of this wave: two transposing reads of 4 rows each.  Within a 16-lane group, lane

@@ -44,16 +44,26 @@ constexpr int64_t kDownWGs = 256;  // lora_down workgroups aimed at (one per CU)
 // so no cross-wave reduction is needed.
 __device__ __forceinline__ int stile_off(int row, int c) { return row * 128 + ((c ^ ((row & 7) ^ ((row >> 3) & 1))) << 4); }
 
+// LDS of the staged bodies: (64 + 32 RT) rows of 128 bytes per buffer, as many buffers
+// (at most 4) as fit in the 160 KB of a workgroup
+template <int RT>
+constexpr int staged_nb() {
+  return 4 * (64 + 32 * RT) * 128 <= 160 * 1024 ? 4 : 3 * (64 + 32 * RT) * 128 <= 160 * 1024 ? 3 : 2;
+}
+template <int RT>
+constexpr int staged_bytes() {
+  return staged_nb<RT>() * (64 + 32 * RT) * 128;
+}
+
 template <int RT, int NB>
 __device__ __forceinline__ void lora_down_dma_body(
-    int bx, int by, const uint16_t *__restrict__ IN, int M, int Kc, int ldin, const uint16_t *__restrict__ WT,
-    int ldwt, int r, int KR, float *__restrict__ P) {
+    char *sbuf, int bx, int by, const uint16_t *__restrict__ IN, int M, int Kc, int ldin,
+    const uint16_t *__restrict__ WT, int ldwt, int r, int KR, float *__restrict__ P) {
   constexpr int ROWS = 64 + 32 * RT;       // staged rows per step (IN then WT)
   constexpr int BUF = ROWS * 128;          // bytes per buffer
   constexpr int NLD = ROWS / 8;            // 1 KB loads per step
   constexpr int LPW = NLD / 4;             // loads per wave and step
   constexpr int TILES = 2 * RT, TPW = (TILES + 3) / 4;
-  __shared__ __attribute__((aligned(16))) char sbuf[NB * BUF];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m0 = bx * 64;
@@ -147,168 +157,168 @@ __device__ __forceinline__ void lora_down_dma_body(
   }
 }
 
-// LDS buffers of the staged lora_down: as many as fit (at most 4) next to `other` bytes
-template <int RT>
-constexpr int down_nb(int other) {
-  return (4 * (64 + 32 * RT) * 128 + other <= 160 * 1024) ? 4 : (3 * (64 + 32 * RT) * 128 + other <= 160 * 1024) ? 3 : 2;
-}
-
 template <int RT>
 __global__ __launch_bounds__(NT) void lora_down_partial_kernel(
     const uint16_t *__restrict__ IN, int M, int Kc, int ldin, const uint16_t *__restrict__ WT, int ldwt,
     int r, int KR, float *__restrict__ P) {
-  lora_down_dma_body<RT, down_nb<RT>(0)>(blockIdx.x, blockIdx.y, IN, M, Kc, ldin, WT, ldwt, r, KR, P);
+  __shared__ __attribute__((aligned(16))) char sbuf[staged_bytes<RT>()];
+  lora_down_dma_body<RT, staged_nb<RT>()>(sbuf, blockIdx.x, blockIdx.y, IN, M, Kc, ldin, WT, ldwt, r, KR, P);
 }
 
 // ---------------------------------------------------------------------------------
 // reduce_m: partial sums over a split of rows m of IN[m][no] * S[m][j].
-// Workgroup: 64 columns of IN x all RT*32 >= r columns of S, one M-split.  Each
-// 32-row step is loaded with 16-byte reads and written to LDS transposed as
-// packed (m, m+1) bf16 pairs, so the MFMA reads 8 consecutive m per lane.
 //   JMAJOR = false: P[s][no][j]  (A = S rows j, B = IN columns no)   -> dB [N, r]
 //   JMAJOR = true:  P[s][j][no]  (A = IN rows no, B = S columns j)   -> dA [r, K]
-constexpr int PD = 20;  // dwords per LDS row: 16 m-pairs + 4 padding
+// reduce_m with LDS-staged operands: the same partial sums over one M-split, with
+// row-major tiles of IN (64 rows m x 64 columns) and S (64 rows m x 32 RT columns)
+// brought into LDS by direct buffer -> LDS loads (eight lanes per 128 bytes of a row,
+// 16-byte chunks swizzled per row), and the MFMA operands, which need eight consecutive
+// m per lane, read with the transposing LDS read: within a 16-lane group, lane i reads 8
+// bytes of row base + i / 4 at column 4 (i % 4) of its 16-column half and receives
+// column i of those four rows.  NB buffers, one barrier per 64-row step; wave w owns
+// output tiles w, w + 4, ... of the 2 x RT tiles of 32 x 32.
+template <int RT>
+__device__ __forceinline__ int s_swz(int row) {
+  // the S tile's rows hold 4 RT chunks; swizzle within the row when that is a power of two
+  return ((4 * RT) & (4 * RT - 1)) == 0 ? (((row & 7) ^ ((row >> 3) & 1)) & (4 * RT - 1)) : 0;
+}
 
-template <int RT, bool JMAJOR>
-__device__ __forceinline__ void reduce_m_partial_body(
-    int bx, int by, const uint16_t *__restrict__ IN, int M, int No, int ldin, const uint16_t *__restrict__ S,
-    int lds, int r, int MR, float *__restrict__ P) {
-  // two LDS buffers: step i is staged into buffer i % 2, so one barrier per step
-  // separates its writes from its reads, and the previous step's barrier separates
-  // them from the reads of step i - 2 in the same buffer
-  __shared__ __attribute__((aligned(16))) uint32_t sIn[2][64 * PD];
-  __shared__ __attribute__((aligned(16))) uint32_t sS[2][RT * 32 * PD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int RT, bool JMAJOR, int NB>
+__device__ __forceinline__ void reduce_m_dma_body(
+    char *sbuf, int bx, int by, const uint16_t *__restrict__ IN, int M, int No, int ldin,
+    const uint16_t *__restrict__ S, int lds, int r, int MR, float *__restrict__ P) {
+  constexpr int INB = 64 * 128;        // IN tile bytes
+  constexpr int SROW = 64 * RT;        // S tile row bytes
+  constexpr int BUF = INB + 64 * SROW;
+  constexpr int NLD = BUF / 1024;      // 1 KB loads per step (8 + 4 RT)
+  constexpr int LPW = NLD / 4;
+  constexpr int TILES = 2 * RT, TPW = (TILES + 3) / 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb0 = bx * 64;
-  const int sp = by;
-  const int mb = sp * MR, me = min(M, mb + MR);
+  const int mb = by * MR, me = min(M, mb + MR);
+  const int nsteps = me > mb ? (me - mb + 63) / 64 : 0;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(IN, static_cast<uint32_t>(uint64_t(M) * ldin * 2));
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, static_cast<uint32_t>(uint64_t(M) * lds * 2));
 
-  // load tasks: (pair p, 8-column chunk c) of IN (128 tasks) then of S (RT*64 tasks)
-  constexpr int NTASK = 128 + RT * 64;
-  constexpr int TPT = (NTASK + NT - 1) / NT;  // tasks per thread
-  struct Stage {
-    u32x4_t a[TPT], b[TPT];
-  };
-
-  // Rows at or past the split's end read as zero (no memory traffic).  Task ranges are
-  // multiples of 64, so whether a task reads IN or S, or is idle, depends on the wave
-  // only.  The loads are straight-line (offsets by selects, idle tasks out of range),
-  // so the compiler's wait counts stay exact across the pipelined loop.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int mstep, Stage &st) {
+  // per-lane tile row and global column of this wave's loads: load g < 8 covers IN rows
+  // 8 g .. 8 g + 7; the others cover 1 KB of the S tile
+  int lrow[LPW];
+  uint32_t lcol[LPW];  // byte offset of the column inside the global row, kOOB if past the edge
 #pragma unroll
-    for (int q = 0; q < TPT; ++q) {
-      const int task_w = wave_u * 64 + q * NT;  // the wave's first task
-      const bool is_in = task_w < 128;          // wave-uniform
-      const bool live = task_w < NTASK;         // wave-uniform
-      const int t2 = (is_in ? tid + q * NT : tid + q * NT - 128);
-      const int p = t2 & 15, c = t2 >> 4;
-      const int m = mstep + 2 * p;
-      const int col = is_in ? nb0 + c * 8 : c * 8;
-      const int lim = is_in ? No : r;
-      const uint32_t ld = static_cast<uint32_t>(is_in ? ldin : lds);
-      const bool ok = live && col < lim;
-      const uint32_t oa = (ok && m < me) ? (static_cast<uint32_t>(m) * ld + col) * 2 : kOOB;
-      const uint32_t ob = (ok && m + 1 < me) ? (static_cast<uint32_t>(m + 1) * ld + col) * 2 : kOOB;
-      const __amdgpu_buffer_rsrc_t rr = is_in ? rin : rs;
-      st.a[q] = buf_load16(rr, oa);
-      st.b[q] = buf_load16(rr, ob);
+  for (int u = 0; u < LPW; ++u) {
+    const int g = wave + 4 * u;
+    if (g < 8) {
+      const int x = 8 * g + (lane >> 3);
+      const int c = (lane & 7) ^ ((x & 7) ^ ((x >> 3) & 1));
+      lrow[u] = x;
+      lcol[u] = nb0 + c * 8 < No ? static_cast<uint32_t>(nb0 + c * 8) * 2 : kOOB;
+    } else {
+      const int byte = (g - 8) * 1024 + lane * 16;
+      const int x = byte / SROW, slot = (byte % SROW) / 16;
+      const int c = slot ^ s_swz<RT>(x);
+      lrow[u] = x;
+      lcol[u] = c * 8 < r ? static_cast<uint32_t>(c * 8) * 2 : kOOB;
+    }
+  }
+  auto dma = [&](int step) {
+    char *dst = sbuf + (step % NB) * BUF;
+    const int m = mb + step * 64;
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int g = wave + 4 * u;
+      const int mm = m + lrow[u];
+      const uint32_t ld2 = static_cast<uint32_t>(g < 8 ? ldin : lds) * 2;
+      const uint32_t off = (lcol[u] != kOOB && mm < me) ? static_cast<uint32_t>(mm) * ld2 + lcol[u] : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < 8 ? rin : rs,
+                                               (__attribute__((address_space(3))) void *)(dst + g * 1024), 16, off, 0,
+                                               0, 0);
     }
   };
-  auto stage = [&](const Stage &st, int buf) {
+  // operand fragment: column cb + (lane % 32) of rows 16 s + 8 (lane / 32) .. + 7
+  auto frag_in = [&](const char *sb, int s, int cb) {
+    const int i = lane & 15, gq = lane >> 4;
+    const int col = cb + (gq & 1) * 16 + 4 * (i & 3);
+    u32x4_t v;
 #pragma unroll
-    for (int q = 0; q < TPT; ++q) {
-      const int task = tid + q * NT;
-      const int task_w = wave_u * 64 + q * NT;
-      if (task_w >= NTASK) continue;
-      const bool is_in = task_w < 128;
-      const int t2 = is_in ? task : task - 128;
-      const int p = t2 & 15, c = t2 >> 4;
-      uint32_t *base = (is_in ? sIn[buf] : sS[buf]) + (c * 8) * PD + p;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        base[(2 * e) * PD] = pack_lo(st.a[q][e], st.b[q][e]);
-        base[(2 * e + 1) * PD] = pack_hi(st.a[q][e], st.b[q][e]);
-      }
+    for (int e = 0; e < 2; ++e) {
+      const int row = 16 * s + 8 * (gq >> 1) + 4 * e + (i >> 2);
+      const int off = row * 128 + (((col >> 3) ^ ((row & 7) ^ ((row >> 3) & 1))) << 4) + (col & 7) * 2;
+      const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)(sb + off));
+      const u32x2_t w = __builtin_bit_cast(u32x2_t, t);
+      v[2 * e] = w[0];
+      v[2 * e + 1] = w[1];
     }
+    return v;
+  };
+  auto frag_s = [&](const char *sb, int s, int cb) {
+    const int i = lane & 15, gq = lane >> 4;
+    const int col = cb + (gq & 1) * 16 + 4 * (i & 3);
+    u32x4_t v;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int row = 16 * s + 8 * (gq >> 1) + 4 * e + (i >> 2);
+      const int off = INB + row * SROW + (((col >> 3) ^ s_swz<RT>(row)) << 4) + (col & 7) * 2;
+      const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)(sb + off));
+      const u32x2_t w = __builtin_bit_cast(u32x2_t, t);
+      v[2 * e] = w[0];
+      v[2 * e + 1] = w[1];
+    }
+    return v;
   };
 
-  // output tiles: 2 (no) x RT (j) tiles of 32x32 spread over the 4 waves
-  constexpr int TILES = 2 * RT;
-  constexpr int TPW = (TILES + 3) / 4;
   f32x16_t acc[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[u][e] = 0.0f;
 
-  auto compute = [&](int buf) {
+#pragma unroll
+  for (int s = 0; s < NB - 1; ++s) dma(s);
+  for (int i = 0; i < nsteps; ++i) {
+    // step i has landed for every wave, and no wave still reads buffer (i - 1) % NB
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NB - 2) * LPW) : "memory");
+    dma(i + NB - 1);
+    const char *sb = sbuf + (i % NB) * BUF;
+    u32x4_t fi[TPW][4], fs[TPW][4];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      const int tile = wave_u + 4 * u;
-      if (tile >= TILES) continue;
-      const int nbk = tile & 1, t = tile >> 1;
+      const int tile = wave + 4 * u;
+      if (TILES % 4 != 0 && tile >= TILES) continue;
+      const int tn = tile & 1, tj = tile >> 1;  // IN column tile, S column (rank) tile
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int doff = kk * 8 + (lane >> 5) * 4;
-        const u32x4_t fin =
-            *reinterpret_cast<const u32x4_t *>(sIn[buf] + (nbk * 32 + (lane & 31)) * PD + doff);
-        const u32x4_t fs =
-            *reinterpret_cast<const u32x4_t *>(sS[buf] + (t * 32 + (lane & 31)) * PD + doff);
-        acc[u] = JMAJOR ? mfma32x32x16(fin, fs, acc[u]) : mfma32x32x16(fs, fin, acc[u]);
+      for (int s = 0; s < 4; ++s) {
+        fi[u][s] = frag_in(sb, s, 32 * tn);
+        fs[u][s] = frag_s(sb, s, 32 * tj);
       }
     }
-  };
-  auto fence = [] {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // Four steps of 32 rows in flight: the loads of step i + 3 are issued before step i
-  // is staged.  Register stages have fixed roles in a four-way unrolled loop, so the
-  // compiler's wait counts leave the three later steps outstanding.
-  const int nst = me > mb ? (me - mb + 31) / 32 : 0;
-  Stage s0, s1, s2, s3;
-  issue(mb, s0);
-  issue(mb + 32, s1);
-  issue(mb + 64, s2);
-  fence();
-  auto one = [&](int i, Stage &cur, Stage &ahead, int buf) {
-    issue(mb + (i + 3) * 32, ahead);
-    fence();
-    stage(cur, buf);
-    __syncthreads();
-    compute(buf);
-    fence();
-  };
-  int i = 0;
-  for (; i + 4 <= nst; i += 4) {
-    one(i, s0, s3, 0);
-    one(i + 1, s1, s0, 1);
-    one(i + 2, s2, s1, 0);
-    one(i + 3, s3, s2, 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int tile = wave + 4 * u;
+        if (TILES % 4 != 0 && tile >= TILES) continue;
+        acc[u] = JMAJOR ? mfma32x32x16(fi[u][s], fs[u][s], acc[u]) : mfma32x32x16(fs[u][s], fi[u][s], acc[u]);
+      }
   }
-  if (i < nst) one(i, s0, s3, 0);
-  if (i + 1 < nst) one(i + 1, s1, s0, 1);
-  if (i + 2 < nst) one(i + 2, s2, s1, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land after the kernel ends
 
-  float *dst = P + static_cast<size_t>(sp) * No * r;
+  float *dst = P + static_cast<size_t>(by) * No * r;
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int tile = wave + 4 * u;
-    if (tile >= TILES) continue;
-    const int nbk = tile & 1, t = tile >> 1;
+    if (TILES % 4 != 0 && tile >= TILES) continue;
+    const int tn = tile & 1, tj = tile >> 1;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       f32x4_t o = {acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
       const int rq = g * 8 + (lane >> 5) * 4;  // first of 4 consecutive rows
       if (!JMAJOR) {
-        const int no = nb0 + nbk * 32 + (lane & 31), j0 = t * 32 + rq;
+        const int no = nb0 + tn * 32 + (lane & 31), j0 = tj * 32 + rq;
         if (no < No && j0 < r) *reinterpret_cast<f32x4_t *>(dst + static_cast<size_t>(no) * r + j0) = o;
       } else {
-        const int j = t * 32 + (lane & 31), no0 = nb0 + nbk * 32 + rq;
+        const int j = tj * 32 + (lane & 31), no0 = nb0 + tn * 32 + rq;
         if (j < r && no0 < No) *reinterpret_cast<f32x4_t *>(dst + static_cast<size_t>(j) * No + no0) = o;
       }
     }
@@ -319,7 +329,8 @@ template <int RT, bool JMAJOR>
 __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
     const uint16_t *__restrict__ IN, int M, int No, int ldin, const uint16_t *__restrict__ S, int lds,
     int r, int MR, float *__restrict__ P) {
-  reduce_m_partial_body<RT, JMAJOR>(blockIdx.x, blockIdx.y, IN, M, No, ldin, S, lds, r, MR, P);
+  __shared__ __attribute__((aligned(16))) char sbuf[staged_bytes<RT>()];
+  reduce_m_dma_body<RT, JMAJOR, staged_nb<RT>()>(sbuf, blockIdx.x, blockIdx.y, IN, M, No, ldin, S, lds, r, MR, P);
 }
 
 // The two products of the backward that read only dY, in one launch: workgroups
@@ -344,14 +355,15 @@ struct ReduceArgs {
 };
 template <int RT>
 __global__ __launch_bounds__(NT) void down_reduce_partial_kernel(DownArgs d, ReduceArgs q, int nd) {
+  __shared__ __attribute__((aligned(16))) char sbuf[staged_bytes<RT>()];  // used by either body
   const int b = blockIdx.x;
   if (b < nd) {
-    constexpr int reduce_lds = (2 * 64 * PD + 2 * RT * 32 * PD) * 4;
-    lora_down_dma_body<RT, down_nb<RT>(reduce_lds)>(b % d.gx, b / d.gx, d.IN, d.M, d.Kc, d.ldin, d.WT, d.ldwt,
-                                                       d.r, d.KR, d.P);
+    lora_down_dma_body<RT, staged_nb<RT>()>(sbuf, b % d.gx, b / d.gx, d.IN, d.M, d.Kc, d.ldin, d.WT, d.ldwt, d.r,
+                                             d.KR, d.P);
   } else {
     const int c = b - nd;
-    reduce_m_partial_body<RT, false>(c % q.gx, c / q.gx, q.IN, q.M, q.No, q.ldin, q.S, q.lds, q.r, q.MR, q.P);
+    reduce_m_dma_body<RT, false, staged_nb<RT>()>(sbuf, c % q.gx, c / q.gx, q.IN, q.M, q.No, q.ldin, q.S, q.lds,
+                                                   q.r, q.MR, q.P);
   }
 }
 

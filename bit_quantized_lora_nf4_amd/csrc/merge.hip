@@ -43,7 +43,6 @@ constexpr int SD_WAVE = TR * PD;       // 8704
 constexpr int SMEM = SA_BYTES > 4 * SD_WAVE ? SA_BYTES : 4 * SD_WAVE;
 constexpr int PASSES = 4;              // 32 x 64 outputs per wave = 4 passes of 8 per lane
 
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 // Keeps the memory operations on each side where they are: the empty asm with a
 // memory clobber orders them for the IR and instruction-selection passes, the
