@@ -550,10 +550,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // Pipelined dX for dY rows of whole 16-byte chunks (N % 8 == 0).
 //
 // Layout: wave w owns tokens m0 + 64 w .. + 64 (two 32-token MFMA tiles) and all 256
-// output columns of the block (eight 32-column tiles), acc[i][j].  Its dY fragments
-// are private, so they come straight from global memory into registers (lane l:
-// token 32 i + l % 32, 8 contraction rows at 16 s + 8 (l / 32)), one step ahead.
-// The decoded weight tile (64 rows x 256 columns) is shared by the four waves
+// output columns of the block (eight 32-column tiles), acc[i][j].  Its dY rows are
+// private: each step's 64 x 64 slice is fetched one step ahead by direct buffer ->
+// LDS loads into the wave's own 8 KB region of one of two stages (whole 128-byte row
+// segments per load, in the swizzled row layout of tile_off), and the MFMA fragments
+// are read back with ds_read_b128 (lane l: token 32 i + l % 32, 8 contraction rows
+// at 16 s + 8 (l / 32)).  No barrier guards these regions: a wave waits only for its
+// own loads.  The decoded weight tile (64 rows x 256 columns) is shared by the four waves
 // through LDS and read with the transposing ds_read_b64_tr_b16.  During step i
 // every thread decodes its 64 weights of step i + 1 (one block constant, eight
 // lookups) into the other of two weight tiles, spread over the first three
@@ -564,17 +567,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // Weight-side fragment for contraction sub-step s and output-column tile j (32
 // columns) of the block: two transposing reads of 4 rows each.  Within a 16-lane
 // group, lane i reads row nbase + i / 4 at column cbase + 4 (i % 4) and receives
-// column cbase + i of rows nbase .. nbase + 3.
-__device__ __forceinline__ u32x4_t wfrag_tr_all(const char *sw, int s, int j) {
+// column cbase + i of rows nbase .. nbase + 3.  The swizzle g(n) depends on the row
+// only through n % 16, and j / 4 moves the chunk index by 16, past the bits that
+// g(n) touches, so a lane's read addresses are eight per-lane bases trb[e][j % 4]
+// (sub-step 0, j < 4) plus the constants 8192 s + 256 (j / 4).
+__device__ __forceinline__ void wfrag_bases(uint32_t (&trb)[2][4]) {
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
-  const int col = j * 32 + (g & 1) * 16 + 4 * (i & 3);
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      trb[e][jj] = wtile_off(8 * (g >> 1) + 4 * e + (i >> 2), jj * 32 + (g & 1) * 16 + 4 * (i & 3));
+}
+__device__ __forceinline__ u32x4_t wfrag_tr_all(const char *sw, const uint32_t (&trb)[2][4], int s, int j) {
   u32x4_t r;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int n = 16 * s + 8 * (g >> 1) + 4 * e + (i >> 2);
     const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16_t *)(sw + wtile_off(n, col)));
+        (__attribute__((address_space(3))) v4i16_t *)(sw + trb[e][j & 3] + (8192 * s + 256 * (j >> 2))));
     const u32x2_t u = __builtin_bit_cast(u32x2_t, v);
     r[2 * e] = u[0];
     r[2 * e + 1] = u[1];
@@ -659,17 +670,22 @@ __device__ __forceinline__ void dx_schedule() {
   }
 }
 
-// dY fragments of one contraction step: [sub-step][token tile].
-struct YStage {
-  u32x4_t v[4][2];
-};
+// dY slice of one wave and step: 64 tokens x 64 contraction rows (8 KB); a stage
+// holds the four waves' slices.
+constexpr int YWAVE_BYTES = 64 * TK * 2;
 
 template <int CT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dx_pipe_kernel(
     GemmParams p) {
-  __shared__ __attribute__((aligned(16))) char sW[2 * TILE_BYTES];
+  // two weight tiles and two dY stages, 128 KB; separate objects, so that the
+  // compiler can tell reads of one stage or tile from the loads into the other stage
+  __shared__ __attribute__((aligned(16))) char sW0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sW1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sY0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sY1[TILE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  char *const sYw[2] = {sY0 + wave * YWAVE_BYTES, sY1 + wave * YWAVE_BYTES};
   int tmi, tni;
   tile_coords((p.M + TM - 1) / TM, (p.No + TN - 1) / TN, tmi, tni);
   const int m0 = tmi * TM, k0 = tni * TN;
@@ -681,23 +697,42 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int nk = (N + TK - 1) / TK;
   const int last = nk - 1;
 
-  // dY rows of this lane (byte offsets, kOOB past M) and its contraction half
-  uint32_t yrow[2];
+  // dY loads: load q of a step writes rows 8 q .. 8 q + 7 of the wave's slice (1 KB,
+  // lane l at byte 16 l), so lane l fetches the chunk that belongs at slot l % 8 of
+  // row r = 8 q + l / 8: chunk (l % 8) ^ swz(r), which depends on q only through its
+  // parity.  Rows past M are clamped to the last one; they feed only outputs that are
+  // never stored.
+  const int ych[2] = {(lane & 7) ^ (lane >> 3), (lane & 7) ^ (lane >> 3) ^ 1};
+  uint32_t yoff[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = m0 + wave * 64 + i * 32 + (lane & 31);
-    yrow[i] = m < p.M ? static_cast<uint32_t>(m) * N * 2 : kOOB;
+  for (int q = 0; q < 8; ++q) {
+    const int row = min(m0 + wave * 64 + 8 * q + (lane >> 3), p.M - 1);
+    yoff[q] = (static_cast<uint32_t>(row) * N + ych[q & 1] * 8) * 2;
   }
-  const int yh = (lane >> 5) * 8;
-  auto issue_y = [&](int kt, YStage &ys) {
+  // CHK: the step may reach past N (the last one); chunks at or past N read as zero
+  auto issue_y = [&](auto CHK, int kt, char *dst) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int n = kt + 16 * s + yh;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        ys.v[s][i] = buf_load16(rdy, (yrow[i] != kOOB && n < N) ? yrow[i] + n * 2 : kOOB);
+    for (int q = 0; q < 8; ++q) {
+      auto *d = (__attribute__((address_space(3))) void *)(dst + q * 1024);
+      if constexpr (decltype(CHK)::v) {
+        const uint32_t off = kt + ych[q & 1] * 8 < N ? yoff[q] + kt * 2 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rdy, d, 16, off, 0, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rdy, d, 16, yoff[q], kt * 2, 0, 0);
+      }
     }
   };
+  // dY fragments of sub-step s from a stage slice: swz() sees only the row's low five
+  // bits, so token tile i adds the constant 4096 to one base per sub-step
+  uint32_t yrb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) yrb[s] = tile_off(lane & 31, 2 * s + (lane >> 5));
+  auto read_y = [&](const char *sy, int s, u32x4_t (&yb)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) yb[i] = *reinterpret_cast<const u32x4_t *>(sy + yrb[s] + 4096 * i);
+  };
+  uint32_t trb[2][4];
+  wfrag_bases(trb);
   // Weight decode: thread t owns tile row t % 64 and columns 64 (t / 64) .. + 64.
   const int dn = tid & 63, dc = (tid >> 6) * 64;
   const bool col_ok = k0 + dc < K;
@@ -709,6 +744,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     cs.code[1] = buf_load16(rc, ok ? off + 16 : kOOB);
     cs.c = fetch_constant<CT>(rq, static_cast<uint32_t>(n) * (K / 64) + (k0 + dc) / 64, ok);
   };
+  // global loads of one issue_codes: two code chunks and the constant's pieces
+  constexpr int CODE_LOADS = 2 + (CT == kConstF32 ? 1 : 3);
   // lookups q0 .. q1 - 1 of the eight (q = 4 h + i: 16-byte code half h, word i)
   auto decode_part = [&](const CodeStageB &cs, const Planes &pd, char *sw, int q0, int q1) {
 #pragma unroll
@@ -725,35 +762,40 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   CodeStageB S0, S1;
-  YStage Y0, Y1;
   issue_codes(0, S0);
   issue_codes(min(1, last) * TK, S1);
-  issue_y(0, Y0);
+  issue_y(Ic<1>{}, 0, sYw[0]);
   {
     const Planes pd = make_planes(const_value<CT>(S0.c), p.lvl);
-    decode_part(S0, pd, sW, 0, 8);
+    decode_part(S0, pd, sW0, 0, 8);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  u32x4_t wa[8];
+  u32x4_t wa[8], yb[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) wa[j] = wfrag_tr_all(sW, 0, j);
+  for (int j = 0; j < 8; ++j) wa[j] = wfrag_tr_all(sW0, trb, 0, j);
+  read_y(sYw[0], 0, yb);
 
-  // Step it: weight tile B2 = it % 2 and dY stage `yc` are this step's; `yn`
-  // receives the dY fragments of step it + 1, `dec` holds the codes of step it + 1
-  // (decoded now), `ld` receives those of step it + 2.
-  auto step = [&](auto B2, int it, YStage &yc, YStage &yn, CodeStageB &dec, CodeStageB &ld) {
+  // Step it: weight tile and dY stage b2 = it % 2 are this step's; the other stage
+  // receives the dY slice of step it + 1, `dec` holds the codes of step it + 1
+  // (decoded now into the other weight tile), `ld` receives those of step it + 2.
+  auto step = [&](auto B2, auto CHK, int it, CodeStageB &dec, CodeStageB &ld) {
     constexpr int b2 = decltype(B2)::v;
-    const char *sw = sW + b2 * TILE_BYTES;
-    char *swn = sW + (1 - b2) * TILE_BYTES;
+    const char *sw = b2 ? sW1 : sW0;
+    char *swn = b2 ? sW0 : sW1;
+    const char *sy = sYw[b2];
+    char *syn = sYw[1 - b2];
     const int kt1 = min(it + 1, last) * TK, kt2 = min(it + 2, last) * TK;
     Planes pd;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4_t wan[8];
+      u32x4_t wan[8], ybn[2];
       if (s == 0) {
         pd = make_planes(const_value<CT>(dec.c), p.lvl);
-        issue_y(kt1, yn);
+        // the other stage was last read two sub-steps ago, and every LDS read has
+        // completed at the previous step's barrier
+        issue_y(CHK, kt1, syn);
         decode_part(dec, pd, swn, 0, 2);
       }
       if (s == 1) {
@@ -762,40 +804,48 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       }
       if (s == 2) decode_part(dec, pd, swn, 5, 8);
       if (s == 3) {
-        // every thread's part of the next weight tile is written; no wave still
-        // reads the tile that the next step overwrites
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // this wave's dY slice of step it + 1 has landed (only the code loads of
+        // sub-step 1 were issued after it); every thread's part of the next weight
+        // tile is written; no wave still reads the tile that the next step overwrites
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(CODE_LOADS) : "memory");
 #pragma unroll
-        for (int j = 0; j < 8; ++j) wan[j] = wfrag_tr_all(swn, 0, j);
+        for (int j = 0; j < 8; ++j) wan[j] = wfrag_tr_all(swn, trb, 0, j);
+        read_y(syn, 0, ybn);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) wan[j] = wfrag_tr_all(sw, s + 1, j);
+        for (int j = 0; j < 8; ++j) wan[j] = wfrag_tr_all(sw, trb, s + 1, j);
+        read_y(sy, s + 1, ybn);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma32x32x16(wa[j], yc.v[s][i], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma32x32x16(wa[j], yb[i], acc[i][j]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) wa[j] = wan[j];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) yb[i] = ybn[i];
       if (s == 0)
-        dx_schedule<16, 5, 8, 2>();
+        dx_schedule<18, 5, 8, 2>();
       else if (s == 1)
-        dx_schedule<16, 4, 5, 3>();
+        dx_schedule<18, 4, CODE_LOADS, 3>();
       else if (s == 2)
-        dx_schedule<16, 4, 0, 3>();
+        dx_schedule<18, 4, 0, 3>();
       else
-        dx_schedule<16, 1, 0, 0>();
+        dx_schedule<18, 1, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // two steps per trip (dY stages, code stages and weight tiles alternate)
+  // Two steps per trip (stages, code stages and weight tiles alternate) while the
+  // dY prefetch stays inside N; the last steps check the contraction tail.
   int it = 0;
-  for (; it + 2 <= nk; it += 2) {
-    step(Ic<0>{}, it, Y0, Y1, S1, S0);
-    step(Ic<1>{}, it + 1, Y1, Y0, S0, S1);
+  for (; it + 4 <= nk; it += 2) {
+    step(Ic<0>{}, Ic<0>{}, it, S1, S0);
+    step(Ic<1>{}, Ic<0>{}, it + 1, S0, S1);
   }
-  if (it < nk) step(Ic<0>{}, it, Y0, Y1, S1, S0);
+  if (it < nk) step(Ic<0>{}, Ic<1>{}, it, S1, S0);
+  if (it + 1 < nk) step(Ic<1>{}, Ic<1>{}, it + 1, S0, S1);
+  if (it + 2 < nk) step(Ic<0>{}, Ic<1>{}, it + 2, S1, S0);
   __builtin_amdgcn_s_waitcnt(0);
   if (p.r > 0) lora_steps_tok(p, m0, k0, acc);
   store_out_tok(p, m0, k0, acc);
