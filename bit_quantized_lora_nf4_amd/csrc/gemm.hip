@@ -426,9 +426,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // Weight tile for contraction rows [kt, kt + 64) and output columns [k0, k0 + 256),
 // natural layout: 64 rows of 512 bytes, 16-byte chunk c of row n at slot c ^ g(n).
 // Thread t decodes row kt + (t % 64), columns k0 + 64 (t / 64) .. + 64: one block
-// constant, 32 bytes of codes, eight 16-byte LDS stores (16 consecutive rows per
-// store instruction land on distinct banks).
-__device__ __forceinline__ int gswz(int n) { return ((n & 3) << 2) | ((n >> 2) & 3); }
+// constant, 32 bytes of codes, eight 16-byte LDS stores.  With n = (n3 n2 n1 n0) in
+// binary, g(n) = (n1, n0, n1 ^ n3, n2): the 8 (16) consecutive rows of one store
+// hit 8 (16) distinct 16-byte bank groups of a 128-byte (256-byte) bank cycle, and
+// the 4 rows x 2 (4) chunks of a transposing read's 16 (32) lanes do too.
+__device__ __forceinline__ int gswz(int n) {
+  return ((n & 3) << 2) | ((((n >> 1) ^ (n >> 3)) & 1) << 1) | ((n >> 2) & 1);
+}
 __device__ __forceinline__ int wtile_off(int n, int col) {
   return n * 512 + ((((col >> 3) ^ gswz(n)) & 31) << 4) + (col & 7) * 2;
 }
