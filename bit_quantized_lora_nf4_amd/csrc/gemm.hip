@@ -553,14 +553,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
 // Pipelined dX for dY rows of whole 16-byte chunks (N % 8 == 0).
 //
-// Layout: wave w owns tokens m0 + 64 w .. + 64 (two 32-token MFMA tiles) and all 256
-// output columns of the block (eight 32-column tiles), acc[i][j].  Its dY rows are
-// private: each step's 64 x 64 slice is fetched one step ahead by direct buffer ->
-// LDS loads into the wave's own 8 KB region of one of two stages (whole 128-byte row
-// segments per load, in the swizzled row layout of tile_off), and the MFMA fragments
-// are read back with ds_read_b128 (lane l: token 32 i + l % 32, 8 contraction rows
-// at 16 s + 8 (l / 32)).  No barrier guards these regions: a wave waits only for its
-// own loads.  The decoded weight tile (64 rows x 256 columns) is shared by the four waves
+// Layout: 2 x 2 waves; wave w owns tokens m0 + 128 (w / 2) .. + 128 (four 32-token
+// MFMA tiles) and output columns k0 + 128 (w % 2) .. + 128 (four 32-column tiles),
+// acc[i][j], so per sub-step it reads 4 weight and 4 dY fragments for 16 MFMAs.  Each
+// step's 256 x 64 dY slice is fetched one step ahead by direct buffer -> LDS loads
+// into one of two stages, wave w loading rows 64 w .. + 64 (whole 128-byte row
+// segments per load, in the swizzled row layout of tile_off); the MFMA fragments are
+// read back with ds_read_b128 (lane l: token 32 i + l % 32, 8 contraction rows at
+// 16 s + 8 (l / 32)).  The step's barrier, after each wave's own load wait,
+// publishes the next stage.  The decoded weight tile (64 rows x 256 columns) is shared by the four waves
 // through LDS and read with the transposing ds_read_b64_tr_b16.  During step i
 // every thread decodes its 64 weights of step i + 1 (one block constant, eight
 // lookups) into the other of two weight tiles, spread over the first three
@@ -597,22 +598,23 @@ __device__ __forceinline__ u32x4_t wfrag_tr_all(const char *sw, const uint32_t (
   return r;
 }
 
-// Epilogue of the token-split layout: lane holds token m0 + 64 w + 32 i + l % 32 and
-// output columns c0 + 32 j + 8 g + 4 (l / 32) + 0..3 for g = 0..3.
-__device__ __forceinline__ void store_out_tok(const GemmParams &p, int m0, int c0,
-                                              const f32x16_t (&acc)[2][8]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Epilogue of the dX layout: lane holds tokens tb + 32 i + l % 32 and output columns
+// cb + 32 j + 8 g + 4 (l / 32) + 0..3 (g = 0..3) of acc[i][j].
+template <int NI, int NJ>
+__device__ __forceinline__ void store_out_dx(const GemmParams &p, int tb, int cb,
+                                             const f32x16_t (&acc)[NI][NJ]) {
+  const int lane = threadIdx.x & 63;
   const bool vec = (p.No % 4) == 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = m0 + wave * 64 + i * 32 + (lane & 31);
+  for (int i = 0; i < NI; ++i) {
+    const int m = tb + i * 32 + (lane & 31);
     if (m >= p.M) continue;
     uint16_t *row = p.C + static_cast<int64_t>(m) * p.No;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = c0 + j * 32 + g * 8 + (lane >> 5) * 4;
+        const int col = cb + j * 32 + g * 8 + (lane >> 5) * 4;
         const f32x16_t &a = acc[i][j];
         if (vec) {
           if (col < p.No) {
@@ -628,33 +630,33 @@ __device__ __forceinline__ void store_out_tok(const GemmParams &p, int m0, int c
   }
 }
 
-// LoRA steps of the token-split layout: acc[i][j] += A2 rows (tokens) x B2 rows
-// (output columns), rank in steps of 16.
-__device__ __forceinline__ void lora_steps_tok(const GemmParams &p, int m0, int c0,
-                                               f32x16_t (&acc)[2][8]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// LoRA steps of the dX layout: acc[i][j] += A2 rows (tokens tb + 32 i + ..) x B2 rows
+// (output columns cb + 32 j + ..), rank in steps of 16.
+template <int NI, int NJ>
+__device__ __forceinline__ void lora_steps_dx(const GemmParams &p, int tb, int cb, f32x16_t (&acc)[NI][NJ]) {
+  const int lane = threadIdx.x & 63;
   const int r = p.r;
   const bool vec = (r % 8) == 0;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A2, static_cast<uint32_t>(uint64_t(p.M) * r * 2));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B2, static_cast<uint32_t>(uint64_t(p.No) * r * 2));
   constexpr int RQ = LORA_RQ;  // rank steps per chunk, all loads before the MFMAs
   for (int r0 = 0; r0 < r; r0 += 16 * RQ) {
-    u32x4_t wa[RQ][8], vb[RQ][2];
+    u32x4_t wa[RQ][NJ], vb[RQ][NI];
 #pragma unroll
     for (int q = 0; q < RQ; ++q) {
       const int j0 = r0 + 16 * q + (lane >> 5) * 8;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) wa[q][j] = lora_frag(rb, vec, c0 + j * 32 + (lane & 31), p.No, r, j0, r);
+      for (int j = 0; j < NJ; ++j) wa[q][j] = lora_frag(rb, vec, cb + j * 32 + (lane & 31), p.No, r, j0, r);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) vb[q][i] = lora_frag(ra, vec, m0 + wave * 64 + i * 32 + (lane & 31), p.M, r, j0, r);
+      for (int i = 0; i < NI; ++i) vb[q][i] = lora_frag(ra, vec, tb + i * 32 + (lane & 31), p.M, r, j0, r);
     }
 #pragma unroll
     for (int q = 0; q < RQ; ++q) {
       if (r0 + 16 * q < r) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = mfma32x32x16(wa[q][j], vb[q][i], acc[i][j]);
+          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(wa[q][j], vb[q][i], acc[i][j]);
       }
     }
   }
@@ -689,6 +691,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   __shared__ __attribute__((aligned(16))) char sY1[TILE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // 2 x 2 waves: wave w computes tokens 128 (w / 2) .. + 128 and output columns
+  // 128 (w % 2) .. + 128; it loads the dY rows 64 w .. + 64 of the block
+  const int wr = wave >> 1, wc = wave & 1;
   char *const sYw[2] = {sY0 + wave * YWAVE_BYTES, sY1 + wave * YWAVE_BYTES};
   int tmi, tni;
   tile_coords((p.M + TM - 1) / TM, (p.No + TN - 1) / TN, tmi, tni);
@@ -726,17 +731,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       }
     }
   };
-  // dY fragments of sub-step s from a stage slice: swz() sees only the row's low five
-  // bits, so token tile i adds the constant 4096 to one base per sub-step
+  // dY fragments of sub-step s from a stage: token 128 wr + 32 i + l % 32 is row
+  // 32 (i % 2) + l % 32 of the slice loaded by wave 2 wr + i / 2; swz() sees only the
+  // row's low five bits, so token tile i adds the constant 4096 i to one base per
+  // sub-step
   uint32_t yrb[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) yrb[s] = tile_off(lane & 31, 2 * s + (lane >> 5));
-  auto read_y = [&](const char *sy, int s, u32x4_t (&yb)[2]) {
+  for (int s = 0; s < 4; ++s) yrb[s] = wr * 2 * YWAVE_BYTES + tile_off(lane & 31, 2 * s + (lane >> 5));
+  auto read_y = [&](const char *sy, int s, u32x4_t (&yb)[4]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) yb[i] = *reinterpret_cast<const u32x4_t *>(sy + yrb[s] + 4096 * i);
+    for (int i = 0; i < 4; ++i) yb[i] = *reinterpret_cast<const u32x4_t *>(sy + yrb[s] + 4096 * i);
   };
+  // weight fragments of this wave's column tiles j = 0..3 (block tiles 4 wc + j)
   uint32_t trb[2][4];
   wfrag_bases(trb);
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) trb[e][j] += 256 * wc;
   // Weight decode: thread t owns tile row t % 64 and columns 64 (t / 64) .. + 64.
   const int dn = tid & 63, dc = (tid >> 6) * 64;
   const bool col_ok = k0 + dc < K;
@@ -757,11 +769,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       *reinterpret_cast<u32x4_t *>(sw + wtile_off(dn, dc + q * 8)) = lookup8(cs.code[q >> 2][q & 3], pd);
   };
 
-  f32x16_t acc[2][8];
+  f32x16_t acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
@@ -776,10 +788,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  u32x4_t wa[8], yb[2];
+  u32x4_t wa[4], yb[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) wa[j] = wfrag_tr_all(sW0, trb, 0, j);
-  read_y(sYw[0], 0, yb);
+  for (int j = 0; j < 4; ++j) wa[j] = wfrag_tr_all(sW0, trb, 0, j);
+  read_y(sY0, 0, yb);
 
   // Step it: weight tile and dY stage b2 = it % 2 are this step's; the other stage
   // receives the dY slice of step it + 1, `dec` holds the codes of step it + 1
@@ -788,18 +800,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     constexpr int b2 = decltype(B2)::v;
     const char *sw = b2 ? sW1 : sW0;
     char *swn = b2 ? sW0 : sW1;
-    const char *sy = sYw[b2];
-    char *syn = sYw[1 - b2];
+    const char *sy = b2 ? sY1 : sY0;
+    const char *syn = b2 ? sY0 : sY1;
     const int kt1 = min(it + 1, last) * TK, kt2 = min(it + 2, last) * TK;
     Planes pd;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4_t wan[8], ybn[2];
+      u32x4_t wan[4], ybn[4];
       if (s == 0) {
         pd = make_planes(const_value<CT>(dec.c), p.lvl);
         // the other stage was last read two sub-steps ago, and every LDS read has
         // completed at the previous step's barrier
-        issue_y(CHK, kt1, syn);
+        issue_y(CHK, kt1, sYw[1 - b2]);
         decode_part(dec, pd, swn, 0, 2);
       }
       if (s == 1) {
@@ -809,33 +821,34 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       if (s == 2) decode_part(dec, pd, swn, 5, 8);
       if (s == 3) {
         // this wave's dY slice of step it + 1 has landed (only the code loads of
-        // sub-step 1 were issued after it); every thread's part of the next weight
-        // tile is written; no wave still reads the tile that the next step overwrites
+        // sub-step 1 were issued after it), and after the barrier every wave's has;
+        // every thread's part of the next weight tile is written; no wave still
+        // reads the tile or stage that the next step overwrites
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(CODE_LOADS) : "memory");
 #pragma unroll
-        for (int j = 0; j < 8; ++j) wan[j] = wfrag_tr_all(swn, trb, 0, j);
+        for (int j = 0; j < 4; ++j) wan[j] = wfrag_tr_all(swn, trb, 0, j);
         read_y(syn, 0, ybn);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) wan[j] = wfrag_tr_all(sw, trb, s + 1, j);
+        for (int j = 0; j < 4; ++j) wan[j] = wfrag_tr_all(sw, trb, s + 1, j);
         read_y(sy, s + 1, ybn);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma32x32x16(wa[j], yb[i], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(wa[j], yb[i], acc[i][j]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) wa[j] = wan[j];
+      for (int j = 0; j < 4; ++j) wa[j] = wan[j];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) yb[i] = ybn[i];
+      for (int i = 0; i < 4; ++i) yb[i] = ybn[i];
       if (s == 0)
-        dx_schedule<18, 5, 8, 2>();
+        dx_schedule<12, 5, 8, 2>();
       else if (s == 1)
-        dx_schedule<18, 4, CODE_LOADS, 3>();
+        dx_schedule<12, 4, CODE_LOADS, 3>();
       else if (s == 2)
-        dx_schedule<18, 4, 0, 3>();
+        dx_schedule<12, 4, 0, 3>();
       else
-        dx_schedule<18, 1, 0, 0>();
+        dx_schedule<12, 1, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -851,8 +864,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   if (it + 1 < nk) step(Ic<1>{}, Ic<1>{}, it + 1, S0, S1);
   if (it + 2 < nk) step(Ic<0>{}, Ic<1>{}, it + 2, S1, S0);
   __builtin_amdgcn_s_waitcnt(0);
-  if (p.r > 0) lora_steps_tok(p, m0, k0, acc);
-  store_out_tok(p, m0, k0, acc);
+  if (p.r > 0) lora_steps_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
+  store_out_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
 }
 
 bool fits_32bit(int64_t M, int64_t N, int64_t K, int r) {
