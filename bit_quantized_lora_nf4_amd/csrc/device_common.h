@@ -176,6 +176,19 @@ __device__ __forceinline__ Planes make_planes(float c, const LevelTable &lv) {
   return P;
 }
 
+// Half h of make_planes: the byte planes of T[8h .. 8h + 7] (L[2h], L[2h + 1], H[2h],
+// H[2h + 1]), so that the work of one block constant can be spread over two places.
+__device__ __forceinline__ void make_planes_half(float c, const LevelTable &lv, int h, Planes &P) {
+  uint32_t t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = pack_bf16x2(lv.q[8 * h + 2 * i] * c, lv.q[8 * h + 2 * i + 1] * c);
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    P.L[2 * h + pp] = __builtin_amdgcn_perm(t[2 * pp + 1], t[2 * pp], 0x06040200u);
+    P.H[2 * h + pp] = __builtin_amdgcn_perm(t[2 * pp + 1], t[2 * pp], 0x07050301u);
+  }
+}
+
 __device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t a, uint32_t b) {
   return (m & a) | (~m & b);  // v_bfi_b32
 }

@@ -370,10 +370,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const char *sxn = sX + ((b + 1) % NBUF) * TILE_BYTES;
     char *sxw = sX + ((b + 2) % NBUF) * TILE_BYTES;
     const int ktn = min(it + 2, last) * TK;
+    float cn0, cn1;  // block constants of the next step's two rows
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4_t wan[2], xbn[8];
       if (s < 2) issue_codes(ktn, s, nn);  // codes first: they are needed soonest
+      // the next step's planes, half a row per sub-step (row 1's last half is needed
+      // by this step's last sub-step)
+      if (s == 0) {
+        cn0 = const_value<CT>(nxt.c[0]);
+        make_planes_half(cn0, p.lvl, 0, pln[0]);
+      }
+      if (s == 1) make_planes_half(cn0, p.lvl, 1, pln[0]);
+      if (s == 2) {
+        cn1 = const_value<CT>(nxt.c[1]);
+        make_planes_half(cn1, p.lvl, 0, pln[1]);
+      }
+      if (s == 3) make_planes_half(cn1, p.lvl, 1, pln[1]);
       if (s == 2) issue_dma(ktn, 0, sxw);
       if (s == 3) {
         // tile it + 1 (issued a step ago) must have landed for every wave, and no wave
@@ -387,21 +400,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         read_xfrags_fwd(sx, s + 1, xbn);
 #pragma unroll
         for (int j = 0; j < 2; ++j) wan[j] = lookup8(cur.code[j][s + 1], pl[j]);
-        // block constants of the next step, one row per sub-step
-        if (s == 1) pln[0] = make_planes(const_value<CT>(nxt.c[0]), p.lvl);
-        if (s == 2) pln[1] = make_planes(const_value<CT>(nxt.c[1]), p.lvl);
       }
       mfmas();
 #pragma unroll
       for (int j = 0; j < 2; ++j) wa[j] = wan[j];
 #pragma unroll
       for (int i = 0; i < 8; ++i) xb[i] = xbn[i];
-      if (s == 0)
-        substep_schedule<4, 4>();
-      else if (s == 3)
-        substep_schedule<3, 4>();
-      else
-        substep_schedule<6, 4>();
+      substep_schedule<5, 4>();
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
