@@ -259,11 +259,15 @@ __device__ __forceinline__ void substep_schedule() {
   }
 }
 
-// Global loads per wave and contraction step: per weight row (2) the codes and three
-// constant pieces, then eight activation DMA loads; four per sub-step, the last four
-// after the step's barrier.  The barrier's wait leaves the 12 issued before it in
-// flight, so it waits exactly for the previous step's loads.
-constexpr int LOADS_BEFORE_BARRIER = 12;
+// Global loads per wave and contraction step: per weight row (2) the codes and the
+// constant's pieces (three, or one fp32 constant), then eight activation DMA loads,
+// the last four after the step's barrier.  The barrier's wait leaves in flight the
+// loads issued since the previous barrier except that barrier's own four DMA loads,
+// which complete the tile read right after it: the wait retires exactly those.
+template <int CT>
+constexpr int loads_before_barrier() {
+  return 2 * (1 + (CT == kConstF32 ? 1 : 3)) + 4;
+}
 
 // The forward is software-pipelined by contraction sub-step (16 of each 64-step):
 // while the 16 MFMAs of sub-step s run, the weight fragments of sub-step s + 1 are
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       if (s == 3) {
         // tile it + 1 (issued a step ago) must have landed for every wave, and no wave
         // may still read the buffer that the next step's loads will overwrite
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS_BEFORE_BARRIER) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(loads_before_barrier<CT>()) : "memory");
         issue_dma(ktn, 1, sxw);
         read_xfrags_fwd(sxn, 0, xbn);
 #pragma unroll
