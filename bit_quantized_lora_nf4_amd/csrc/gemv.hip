@@ -211,6 +211,7 @@ __global__ __launch_bounds__(GT) void gemv_stream_kernel(GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < GIT; ++i) {
       // block group i of this wave has landed: 2 (GIT - 1 - i) code loads remain
+      static_assert(GIT == 4, "the waits below count two code loads per block group of four");
       if (i == 0) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       if (i == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       if (i == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
