@@ -9,16 +9,18 @@
 // single bf16 rounding of each output.
 //
 // Tile: a 256-thread workgroup (four waves, one per SIMD) computes a 256 x 256 output
-// tile; wave w owns all 256 activation rows and output columns [64 w, 64 w + 64), i.e.
-// 8 x 2 tiles of the 32x32x16 MFMA (256 fp32 accumulators per lane).  The MFMA "A"
-// operand is the weight side (rows = output columns) and "B" the activation side
-// (columns = tokens), so each lane ends with 4 consecutive output columns of one
+// tile, 256 fp32 accumulators per lane.  In the forward, wave w owns all 256
+// activation rows and output columns [64 w, 64 w + 64), i.e. 8 x 2 tiles of the
+// 32x32x16 MFMA; in dX the waves split the tile 2 x 2 (4 x 4 MFMA tiles each).  The
+// MFMA "A" operand is the weight side (rows = output columns) and "B" the activation
+// side (columns = tokens), so each lane ends with 4 consecutive output columns of one
 // token: 8-byte stores.  The contraction advances 64 at a time.
 //
-// Activation tiles (X or dY, 256 rows x 64) are staged in LDS, double-buffered, with
-// an XOR swizzle of the eight 16-byte chunks of each 128-byte row, chunk c of row r
-// at slot c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): the 16-byte fragment reads of 16
-// consecutive rows hit distinct banks for either 32 or 64 LDS banks.
+// Activation tiles (X or dY, 256 rows x 64) are staged in LDS (a three-deep ring in
+// the forward, two stages in dX) with an XOR swizzle of the eight 16-byte chunks of
+// each 128-byte row, chunk c of row r at slot c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1):
+// the 16-byte fragment reads of 16 consecutive rows hit distinct banks for either 32
+// or 64 LDS banks.
 //
 // Decode: per block constant c a lane builds the 16 possible outputs
 // bf16_rne(q[j] * c) as byte planes in registers and looks codes up with byte
@@ -31,9 +33,10 @@
 // permuted identically on both operands (lane half h takes k in [32 h, 32 h + 32)).
 // Backward: the contraction runs over weight rows, so the 64 x 256 weight tile is
 // decoded cooperatively into LDS in its natural row-major layout (16-byte chunk c of
-// row n at slot c ^ g(n), g(n) = ((n & 3) << 2) | ((n >> 2) & 3)) and read with the
-// gfx950 transposing LDS read ds_read_b64_tr_b16, which hands each lane four
-// consecutive weight rows of one column.
+// row n at slot c ^ g(n), with g(n) = (n1, n0, n1 ^ n3, n2) in the bits of n) and read
+// with the gfx950 transposing LDS read ds_read_b64_tr_b16, which hands each lane four
+// consecutive weight rows of one column; the dY tiles come through LDS like the
+// forward's activations, and the four waves split the output tile 2 x 2.
 
 #include "device_common.h"
 #include "qlora_internal.h"
@@ -570,8 +573,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // segments per load, in the swizzled row layout of tile_off); the MFMA fragments are
 // read back with ds_read_b128 (lane l: token 32 i + l % 32, 8 contraction rows at
 // 16 s + 8 (l / 32)).  The step's barrier, after each wave's own load wait,
-// publishes the next stage.  The decoded weight tile (64 rows x 256 columns) is shared by the four waves
-// through LDS and read with the transposing ds_read_b64_tr_b16.  During step i
+// publishes the next stage.  The decoded weight tile (64 rows x 256 columns) is
+// shared through LDS (each wave reads its 128 columns) with the transposing
+// ds_read_b64_tr_b16.  During step i
 // every thread decodes its 64 weights of step i + 1 (one block constant, eight
 // lookups) into the other of two weight tiles, spread over the first three
 // sub-steps; the single barrier per step, before the last sub-step, publishes that
@@ -685,7 +689,7 @@ __device__ __forceinline__ void dx_schedule() {
   }
 }
 
-// dY slice of one wave and step: 64 tokens x 64 contraction rows (8 KB); a stage
+// dY rows that one wave loads per step: 64 tokens x 64 contraction rows (8 KB); a stage
 // holds the four waves' slices.
 constexpr int YWAVE_BYTES = 64 * TK * 2;
 
