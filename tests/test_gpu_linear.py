@@ -236,3 +236,34 @@ def test_workload5_forward_sampled_columns(lib):
     Xf, Af, Bf = (gc.f64(d[k]) for k in ("X", "A", "B"))
     ref = Xf @ Wrows.T + (wl.alpha / wl.r) * (Xf @ Af.T) @ Bf[cols].T
     _check("Y cols", gc.host_f32_from_bf16(Y)[:, cols], ref)
+
+
+def test_largest_activation_below_32bit_offsets(lib):
+    """X and dX of 131,000 x 16,384 bf16 (4,292,608,000 bytes, just under the 32-bit buffer
+    limit of 0xFFFFFFF0) with a 256 x 16,384 weight and r = 16: the last token rows load and
+    store at byte offsets near the top of the 32-bit range.  X is drawn on the device from a
+    seeded generator and only the sampled rows come back; Y and dX rows against the oracle
+    (dA and dB, sums over all 131,000 tokens, are checked at smaller sizes elsewhere)."""
+    import torch
+    M, K, N, r, alpha = 131000, 16384, 256, 16, 16.0
+    assert M * K * 2 <= 0xFFFFFFF0 < (M + 100) * K * 2  # within 100 rows of the limit
+    print(f"largest activation: M={M} K={K} N={N} r={r} ({M * K * 2} bytes)", flush=True)
+    d = synth.case(1, K, N, r, seed=4242, parts=("W", "X", "A", "B"))
+    qw = lib.quantize(gc.dev_weight(d))
+    A, B = gc.dev_bf16(d["A"]), gc.dev_bf16(d["B"])
+    g = torch.Generator(device="cuda").manual_seed(4242)
+    X = torch.randn(M, K, device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    dY = torch.randn(M, N, device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    Y, U = lib.linear_fwd(qw, X, A, B, alpha)
+    dX, _, _ = lib.linear_bwd(qw, dY, X, A, B, alpha, U)
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 1, 255, 256, 65535, 65536, M - 257, M - 256, M - 33, M - 2, M - 1], device="cuda")
+    Xs, dYs = gc.host_f32_from_bf16(X[rows]), gc.host_f32_from_bf16(dY[rows])
+    Ys, dXs = gc.host_f32_from_bf16(Y[rows]), gc.host_f32_from_bf16(dX[rows])
+    del X, dX, Y, U, dY
+    torch.cuda.empty_cache()
+    Wd = _oracle_w(d)
+    Af, Bf = gc.f64(d["A"]), gc.f64(d["B"])
+    _check("Y rows", Ys, linear.forward(Xs, Wd, Af, Bf, alpha, r))
+    rdX, _, _ = linear.backward(dYs, Xs, Wd, Af, Bf, alpha, r)
+    _check("dX rows", dXs, rdX)
