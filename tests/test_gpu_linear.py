@@ -267,3 +267,46 @@ def test_largest_activation_below_32bit_offsets(lib):
     _check("Y rows", Ys, linear.forward(Xs, Wd, Af, Bf, alpha, r))
     rdX, _, _ = linear.backward(dYs, Xs, Wd, Af, Bf, alpha, r)
     _check("dX rows", dXs, rdX)
+
+
+def test_largest_weight_below_32bit_offsets(lib):
+    """A 262,143 x 32,768 weight (8.59 G weights; 4,294,950,912 bytes of codes, one row under the
+    32-bit buffer limit), drawn on the device from a seeded generator and quantized there.
+    Each row is exactly two DQ groups, so the oracle quantizes a sampled row on its own: codes,
+    constants and the decoded row bit-exact, and the M = 1 GEMV and an M = 32 GEMM forward on
+    those output rows against the oracle."""
+    import torch
+    N, K = 262143, 32768
+    assert N * K // 2 <= 0xFFFFFFF0 < (N + 1) * K // 2 and K % 16384 == 0
+    print(f"largest weight: N={N} K={K} ({N * K // 2} bytes of codes)", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(777)
+    W = (torch.randn(N, K, device="cuda", generator=g, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    rows = torch.tensor([0, 1, 4095, N // 2, N - 65, N - 2, N - 1], device="cuda")
+    Wrows = gc.host_f32_from_bf16(W[rows]).astype(np.float32)
+    qw = lib.quantize(W)
+    del W
+    torch.cuda.empty_cache()
+    X1 = torch.randn(1, K, device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    X32 = torch.randn(32, K, device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    Y1, _ = lib.linear_fwd(qw, X1)
+    Y32, _ = lib.linear_fwd(qw, X32)
+    torch.cuda.synchronize()
+    rl = rows.tolist()
+    codes = qw.codes.view(N, K // 2)[rows].cpu().numpy()
+    c8 = qw.absmax_q.view(N, K // 64)[rows].cpu().numpy()
+    s = qw.dq_scale.view(N, 2)[rows].cpu().numpy()
+    o = qw.dq_offset.view(N, 2)[rows].cpu().numpy()
+    X1f, X32f = gc.host_f32_from_bf16(X1), gc.host_f32_from_bf16(X32)
+    Y1r, Y32r = gc.host_f32_from_bf16(Y1)[:, rl], gc.host_f32_from_bf16(Y32)[:, rl]
+    del qw, Y1, Y32
+    torch.cuda.empty_cache()
+    Wd = np.empty((len(rl), K), np.float64)
+    for i in range(len(rl)):
+        ref = nf4.quantize_nf4(Wrows[i:i + 1])
+        assert np.array_equal(codes[i], ref["codes"].reshape(-1))
+        assert np.array_equal(c8[i].view(np.uint8), ref["absmax_q"].view(np.uint8))
+        assert np.array_equal(s[i].view(np.uint32), ref["dq_scale"].view(np.uint32))
+        assert np.array_equal(o[i].view(np.uint32), ref["dq_offset"].view(np.uint32))
+        Wd[i] = nf4.dequantize_bf16(ref).reshape(-1)
+    _check("Y (M = 1) sampled rows", Y1r, X1f @ Wd.T)
+    _check("Y (M = 32) sampled rows", Y32r, X32f @ Wd.T)
