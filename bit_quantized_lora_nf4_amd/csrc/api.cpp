@@ -225,14 +225,15 @@ int fwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16
                 workspace_bytes);
   if (need_ws && !aligned16(workspace))
     return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
+  const qlora::WeightView wv = view(w);
+  if (M <= 16 ? !qlora::gemv_supported(wv, M, R) : !qlora::gemm_supported(wv, M, R))
+    return fail(QLORA_ERR_SHAPE, "%s: a tensor of %lld x %lld x %lld exceeds 32-bit buffer offsets", who,
+                (long long)M, (long long)K, (long long)N);
   s = check_device();
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const qlora::WeightView wv = view(w);
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
   if (M <= 16) {
-    if (!qlora::gemv_supported(wv, M, R))
-      return fail(QLORA_ERR_SHAPE, "%s: shape exceeds 32-bit buffer offsets", who);
     s = launched(timed_launch(st, [&] { return qlora::launch_gemv_stream(wv, X, M, A, R, workspace, st); }),
                  "gemv_stream");
     if (s != QLORA_OK) return s;
@@ -279,6 +280,9 @@ int bwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16
                 workspace_bytes);
   if (r > 0 && !aligned16(workspace))
     return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
+  if (dX && !qlora::gemm_supported(view(w), M, R))
+    return fail(QLORA_ERR_SHAPE, "%s: a tensor of %lld x %lld x %lld exceeds 32-bit buffer offsets", who,
+                (long long)M, (long long)K, (long long)N);
   s = check_device();
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -900,6 +900,10 @@ unsigned grid_size(int64_t M, int64_t No) {
 
 }  // namespace
 
+bool gemm_supported(const WeightView &w, int64_t M, int r) {
+  return M <= 0x7fffffff && fits_32bit(M, w.n_rows, w.n_cols, r);
+}
+
 hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
                            int ldu, const uint16_t *Bl, int r, int64_t part_rows, uint16_t *Y,
                            hipStream_t stream) {

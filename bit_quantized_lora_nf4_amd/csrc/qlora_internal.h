@@ -106,6 +106,9 @@ hipError_t launch_lora_unmerge(const uint16_t *Wm, int64_t n_rows, int64_t n_col
                                const uint16_t *B, int r, float scale, uint16_t *out,
                                hipStream_t stream);
 
+// Whether the fused GEMMs take this shape: X or dY, Y or dX, the codes and the LoRA
+// operands (rank or row pitch r) below 0xFFFFFFF0 bytes each (32-bit buffer offsets).
+bool gemm_supported(const WeightView &w, int64_t M, int r);
 // Y[M, N] = bf16(X . W'^T + U . Bl^T)  (U [M, r] pitch ldu, Bl [N, r]); r may be 0.
 // part_rows > 0 (a multiple of 256 dividing N): output rows of part q = n / part_rows
 // use U columns [q r, q r + r) (horizontally fused linears with stacked adapters).

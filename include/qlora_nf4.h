@@ -181,7 +181,8 @@ int qlora_dequantize(const qlora_nf4_weight *w, void *out, int out_dtype, void *
  * qlora_workspace_bytes(0, M, K, N, r) bytes of workspace: for M <= 16 the fp32
  * partial sums of the split-contraction GEMV (also when r = 0); for M > 16 the fp32
  * partial sums of the down-projection plus U_s when U_saved is NULL, and none when
- * r = 0. */
+ * r = 0.  The kernels use 32-bit buffer offsets: QLORA_ERR_SHAPE, before anything is
+ * launched, when X, Y, the codes or a LoRA operand exceed 0xFFFFFFF0 bytes. */
 int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
                      const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
                      void *workspace, size_t workspace_bytes, void *stream);
@@ -194,7 +195,9 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, co
  *   dA = bf16(V^T . X)                                [r, K]
  * U_saved is the forward's U_s; if NULL it is recomputed from X and A.  When r > 0 the
  * call needs qlora_workspace_bytes(1, M, K, N, r) bytes of workspace.
- * dY bf16 [M, N]; X bf16 [M, K] (needed for dA, and for U_s when U_saved is NULL). */
+ * dY bf16 [M, N]; X bf16 [M, K] (needed for dA, and for U_s when U_saved is NULL).
+ * QLORA_ERR_SHAPE, before anything is launched, when dX is requested and dY, dX, the
+ * codes or a LoRA operand exceed 0xFFFFFFF0 bytes (32-bit buffer offsets). */
 int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *dY, const uint16_t *X, int64_t M,
                      const uint16_t *A, const uint16_t *B, int r, float alpha,
                      const uint16_t *U_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB,

@@ -113,6 +113,24 @@ def test_forward_argument_errors():
     assert f(w, FAKE, 4, FAKE, FAKE, 8, 16.0, FAKE, None, None, 0, None) == _lib.QLORA_ERR_WORKSPACE
 
 
+def test_32bit_offset_limits_rejected_before_launch():
+    """Shapes whose activations or codes exceed 0xFFFFFFF0 bytes are refused with
+    QLORA_ERR_SHAPE before the device is touched (this container has none)."""
+    f, b = _lib.qlora_linear_fwd, _lib.qlora_linear_bwd
+    w = _w(n_rows=64, n_cols=4096)
+    M = (1 << 19) + 1                                # X = M x 4096 bf16 > 4 GiB
+    assert f(w, FAKE, M, None, None, 0, 16.0, FAKE, None, None, 0, None) == _lib.QLORA_ERR_SHAPE
+    assert b(w, FAKE, None, M, None, None, 0, 16.0, None, FAKE, None, None, None, 0, None) == _lib.QLORA_ERR_SHAPE
+    # just inside the limit the same calls get past the shape checks (and stop at the device check)
+    M_ok = 0xFFFFFFF0 // (4096 * 2)
+    assert f(w, FAKE, M_ok, None, None, 0, 16.0, FAKE, None, None, 0, None) == _lib.QLORA_ERR_DEVICE
+    assert b(w, FAKE, None, M_ok, None, None, 0, 16.0, None, FAKE, None, None, None, 0, None) == _lib.QLORA_ERR_DEVICE
+    # M <= 16: the GEMV's limit on the codes (64 x 2^28 weights: 8 GiB of codes)
+    wbig = _w(n_rows=64, n_cols=1 << 28)
+    need = _lib.qlora_workspace_bytes(0, 16, 1 << 28, 64, 0)
+    assert f(wbig, FAKE, 16, None, None, 0, 16.0, FAKE, None, FAKE, need, None) == _lib.QLORA_ERR_SHAPE
+
+
 def test_backward_argument_errors():
     b = _lib.qlora_linear_bwd
     w = _w()
