@@ -12,9 +12,11 @@ Also reported: the M = 1 forward weight stream (GB/s) on the 4096->11008 and
 11008->4096 weights (r = 16, alpha = 32), replayed from a HIP graph over more than
 512 MB of distinct weight copies so the bytes come from HBM; the roofline of the
 dominant kernel (the fused NF4 GEMM, timed per launch with HIP events recorded by
-the library on its launch stream); and the CPU oracle timed on a bounded sample.
+the library on its launch stream, on every --time-every-th step of the timed region:
+an event pair per launch costs a few microseconds of GPU time, so timing every launch
+would slow the step it measures); and the CPU oracle timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--time-every 4] [--no-cpu-baseline]
 """
 
 import argparse
@@ -494,6 +496,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--time-every", type=int, default=4,
+                    help="record the GEMM launch events on every n-th timed step (1 = every step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the M=1 and quantize legs")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -522,8 +526,12 @@ def main():
     t0 = time.perf_counter()
     s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    for _ in range(args.steps):
-        run_step(q, wl, L, ev, rec)
+    every = max(1, args.time_every)
+    for i in range(args.steps):
+        if i % every == 0:
+            run_step(q, wl, L, ev, rec)
+        else:
+            run_step(q, wl, L)
     f.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -554,7 +562,9 @@ def main():
             "avg_launch_us": round(g_ms * 1e3 / max(1, len(rec)), 2),
             "per_shape": {k: {"TFLOP/s": round(v[0] / (v[1] * 1e-3) / 1e12, 1),
                               "avg_us": round(v[1] * 1e3 / v[2], 1)} for k, v in per.items()},
-            "step_time_in_gemm": round(g_ms / args.steps / ms_step, 4)}
+            "timed_launches": len(rec),
+            "timed_steps": f"one step in {every} of the {args.steps} timed steps",
+            "step_time_in_gemm": round(g_ms / len(range(0, args.steps, every)) / ms_step, 4)}
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
