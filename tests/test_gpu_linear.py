@@ -140,6 +140,60 @@ def test_deterministic(lib):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("M", [300, 5])
+def test_backward_optional_inputs_and_outputs(lib, M):
+    """U_s not passed (the backward recomputes it) and dX not requested (only dA, dB).
+
+    At M > 16 the forward and the backward compute U_s with the same kernel, so the
+    recomputed backward is bitwise the saved one; at M <= 16 the forward's U_s comes
+    from the weight-stream path (another summation order), so there the results are
+    checked against the oracle.  Skipping dX leaves dA and dB bitwise unchanged."""
+    import torch
+    K, N, r, alpha = 1088, 520, 16, 16.0
+    print(f"optional-args case M={M} K={K} N={N} r={r}", flush=True)
+    d = synth.case(M, K, N, r, seed=M + 11)
+    qw = lib.quantize(gc.dev_weight(d))
+    X, A, B = _dev(d, r)
+    dYt = gc.dev_bf16(d["dY"])
+    _, U = lib.linear_fwd(qw, X, A, B, alpha)
+    full = lib.linear_bwd(qw, dYt, X, A, B, alpha, U)
+    recomputed = lib.linear_bwd(qw, dYt, X, A, B, alpha)
+    dX_none, dA_only, dB_only = lib.linear_bwd(qw, dYt, X, A, B, alpha, U, need_dx=False)
+    torch.cuda.synchronize()
+    assert dX_none is None
+    assert torch.equal(dA_only.view(torch.int16), full[1].view(torch.int16))
+    assert torch.equal(dB_only.view(torch.int16), full[2].view(torch.int16))
+    if M > 16:
+        for a, b in zip(full, recomputed):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    else:
+        Wd = _oracle_w(d)
+        Xf, Af, Bf, dYf = (gc.f64(d[k]) for k in ("X", "A", "B", "dY"))
+        for name, G, R in zip(("dX", "dA", "dB"), recomputed, linear.backward(dYf, Xf, Wd, Af, Bf, alpha, r)):
+            _check(name + " (U recomputed)", gc.host_f32_from_bf16(G), R)
+
+
+def test_launch_on_a_side_stream(lib):
+    """The binding launches on torch's current stream: a forward and backward issued on
+    another stream (default priority) give the default stream's results bitwise."""
+    import torch
+    M, K, N, r = 260, 512, 384, 32
+    d = synth.case(M, K, N, r, seed=5)
+    qw = lib.quantize(gc.dev_weight(d))
+    X, A, B = _dev(d, r)
+    dYt = gc.dev_bf16(d["dY"])
+    Y0, U0 = lib.linear_fwd(qw, X, A, B, 16.0)
+    g0 = lib.linear_bwd(qw, dYt, X, A, B, 16.0, U0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        Y1, U1 = lib.linear_fwd(qw, X, A, B, 16.0)
+        g1 = lib.linear_bwd(qw, dYt, X, A, B, 16.0, U1)
+    side.synchronize()
+    for a, b in zip([Y0, U0, *g0], [Y1, U1, *g1]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 @pytest.mark.parametrize("with_B", [False, True])
 def test_workload1_full(lib, with_B):
     """1024 -> 1024, M = 64, r = 8, alpha = 16, fp32 weight; B = 0 then B ~ N(0, 0.01^2)."""
