@@ -84,43 +84,39 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   const int wave = tid >> 6, lane = tid & 63;
   const int sub = lane >> 3, part = lane & 7;
 
-  // Issue every load of this lane first (8 passes of 8 blocks per wave).
-  float w[8][8];
+  // Issue every load of this lane first (8 passes of 8 blocks per wave), all in flight
+  // at once: the loads are straight-line buffer loads over this group's bytes, and the
+  // blocks past the last one (a partial final group) read as zero.
+  constexpr uint32_t kEsz = IN_BF16 ? 2u : 4u;
+  constexpr int kV = IN_BF16 ? 1 : 2;  // 16-byte loads per lane and pass
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(static_cast<const char *>(W) + b0 * kBlock * kEsz, static_cast<uint32_t>(nbg) * kBlock * kEsz);
+  u32x4_t raw[8][kV];
 #pragma unroll
   for (int pass = 0; pass < 8; ++pass) {
-    const int lb = wave * 64 + pass * 8 + sub;
-    const int64_t e0 = (b0 + lb) * kBlock + part * 8;
-    if (lb < nbg) {
-      if (IN_BF16) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
-            static_cast<const uint16_t *>(W) + e0);
+    const uint32_t off = static_cast<uint32_t>((wave * 64 + pass * 8 + sub) * kBlock + part * 8) * kEsz;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          w[pass][2 * p] = bf16_lo(v[p]);
-          w[pass][2 * p + 1] = bf16_hi(v[p]);
-        }
-      } else {
-        const f32x4_t *src = reinterpret_cast<const f32x4_t *>(static_cast<const float *>(W) + e0);
-        const f32x4_t v0 = src[0], v1 = src[1];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          w[pass][p] = v0[p];
-          w[pass][4 + p] = v1[p];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int p = 0; p < 8; ++p) w[pass][p] = 0.0f;
-    }
+    for (int v = 0; v < kV; ++v) raw[pass][v] = buf_load16(rw, off + 16u * v);
   }
   __syncthreads();  // bucket table ready
 
 #pragma unroll
   for (int pass = 0; pass < 8; ++pass) {
     const int lb = wave * 64 + pass * 8 + sub;
+    float w[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (IN_BF16) {
+        w[2 * p] = bf16_lo(raw[pass][0][p]);
+        w[2 * p + 1] = bf16_hi(raw[pass][0][p]);
+      } else {
+        w[p] = __uint_as_float(raw[pass][0][p]);
+        w[4 + p] = __uint_as_float(raw[pass][kV - 1][p]);
+      }
+    }
     float m = 0.0f;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) m = fmaxf(m, fabsf(w[pass][p]));
+    for (int p = 0; p < 8; ++p) m = fmaxf(m, fabsf(w[p]));
     m = fmaxf(m, __shfl_xor(m, 1, 64));
     m = fmaxf(m, __shfl_xor(m, 2, 64));
     m = fmaxf(m, __shfl_xor(m, 4, 64));
@@ -131,8 +127,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       word = 0;
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        const float x = w[pass][p] * inv;
-        int idx = static_cast<int>(x * 64.0f + 64.0f);
+        const float x = w[p] * inv;
+        // x * 64 is exact, so the fma rounds the same sum once
+        int idx = static_cast<int>(fmaf(x, 64.0f, 64.0f));
         idx = min(max(idx, 0), kBuckets - 1);
         const float2 t = s_tab[idx];
         const uint32_t code = static_cast<uint32_t>(__float_as_int(t.y)) + (x > t.x ? 1u : 0u);
