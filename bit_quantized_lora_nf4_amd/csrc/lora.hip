@@ -369,14 +369,33 @@ __global__ __launch_bounds__(NT) void down_reduce_partial_kernel(DownArgs d, Red
 
 // OUT = bf16(scale * sum_s P[s]) for the `count` partial sums (count % 4 == 0) laid out
 // as rows of `cols` values (cols % 4 == 0), written with row pitch ldout; fixed order.
+// Element i (of 4 floats) of the splits' partials summed in split order, P_0 + P_1 + ...
+// The loads of four splits are issued before any is used: a split index past the last
+// re-reads the last split and its value is not added, so the loads are straight-line
+// code and the compiler does not wait for each before issuing the next.
+__device__ __forceinline__ f32x4_t split_sum(const float *__restrict__ P, int splits, int64_t count,
+                                             int64_t i) {
+  const f32x4_t *P4 = reinterpret_cast<const f32x4_t *>(P);
+  const int64_t c4 = count / 4;
+  f32x4_t s = P4[i];
+  for (int k = 1; k < splits; k += 4) {
+    f32x4_t t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = P4[min(k + u, splits - 1) * c4 + i];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k + u < splits) s += t[u];
+  }
+  return s;
+}
+
 __global__ __launch_bounds__(NT) void finalize_kernel(const float *__restrict__ P, int splits,
                                                       int64_t count, int64_t cols, int64_t ldout,
                                                       float scale, uint16_t *__restrict__ OUT) {
   const int64_t n4 = count / 4;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < n4;
        i += static_cast<int64_t>(gridDim.x) * NT) {
-    f32x4_t s = reinterpret_cast<const f32x4_t *>(P)[i];
-    for (int k = 1; k < splits; ++k) s += reinterpret_cast<const f32x4_t *>(P + k * count)[i];
+    const f32x4_t s = split_sum(P, splits, count, i);
     u32x2_t o = {pack_bf16x2(s[0] * scale, s[1] * scale), pack_bf16x2(s[2] * scale, s[3] * scale)};
     const int64_t e = 4 * i, row = e / cols, col = e % cols;
     *reinterpret_cast<u32x2_t *>(OUT + row * ldout + col) = o;
@@ -392,8 +411,7 @@ struct FinJob {
   uint16_t *OUT;
 };
 __device__ __forceinline__ void finalize_one(const FinJob &j, int64_t i) {
-  f32x4_t s = reinterpret_cast<const f32x4_t *>(j.P)[i];
-  for (int k = 1; k < j.splits; ++k) s += reinterpret_cast<const f32x4_t *>(j.P + k * j.count)[i];
+  const f32x4_t s = split_sum(j.P, j.splits, j.count, i);
   u32x2_t o = {pack_bf16x2(s[0] * j.scale, s[1] * j.scale), pack_bf16x2(s[2] * j.scale, s[3] * j.scale)};
   const int64_t e = 4 * i, row = e / j.cols, col = e % j.cols;
   *reinterpret_cast<u32x2_t *>(j.OUT + row * j.ldout + col) = o;
