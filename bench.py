@@ -154,11 +154,30 @@ def measure_quantize_stress(torch, q, synth, gc, copies=12, reps=2):
     torch.cuda.synchronize()
     ms = s.elapsed_time(f) / (reps * copies)
     gbs = N * K * 2.516 / (ms * 1e-3) / 1e9
+    quant = {"value": round(gbs, 1), "unit": "GB/s", "bytes_per_weight": 2.516, "ms_per_weight": round(ms, 4),
+             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "stream_GB": round(copies * N * K * 2 / 1e9, 2),
+             "what": f"bf16 -> NF4 codes + int8 DQ constants, {N}x{K} stress weights (Student-t(3), outliers, "
+                     f"zero blocks), {copies} distinct device copies"}
+    # standalone decode of the same stream: the quantized copies -> one bf16 output buffer
+    qws = [q.quantize(W) for W in Ws]
     del Ws, W0
-    return {"value": round(gbs, 1), "unit": "GB/s", "bytes_per_weight": 2.516, "ms_per_weight": round(ms, 4),
-            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "stream_GB": round(copies * N * K * 2 / 1e9, 2),
-            "what": f"bf16 -> NF4 codes + int8 DQ constants, {N}x{K} stress weights (Student-t(3), outliers, "
-                    f"zero blocks), {copies} distinct device copies"}
+    out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    q.dequantize(qws[0], out=out)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        for qw in qws:
+            q.dequantize(qw, out=out)
+    f.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(f) / (reps * copies)
+    gbs = N * K * 2.516 / (ms * 1e-3) / 1e9
+    deq = {"value": round(gbs, 1), "unit": "GB/s", "bytes_per_weight": 2.516, "ms_per_weight": round(ms, 4),
+           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+           "what": f"NF4 codes + int8 DQ constants -> bf16 (standalone doubleDequant), the {copies} quantized "
+                   f"{N}x{K} stress weights"}
+    del qws, out
+    return quant, deq
 
 
 def measure_m1(torch, q, synth, gc, ev, min_bytes=600 << 20, calls=200):
@@ -583,7 +602,7 @@ def main():
         ev.close()
         result["quantize"] = measure_quantize(torch, q, L)
         print("bench: quantization stress stream", file=sys.stderr, flush=True)
-        result["quantize_stress"] = measure_quantize_stress(torch, q, synth, gc)
+        result["quantize_stress"], result["dequantize_stress"] = measure_quantize_stress(torch, q, synth, gc)
         result["adamw"] = measure_adamw(torch, q)
         result["lora_merge"] = measure_merge(torch, q)
         result["layer65b"] = measure_layer65b(torch, q)
