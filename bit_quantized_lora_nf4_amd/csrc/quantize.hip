@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         const float x = w[p] * inv;
-        // x * 64 is exact, so the fma rounds the same sum once
+        // x * 64 is exact, so fma(x, 64, 64) equals RN(x * 64 + 64)
         int idx = static_cast<int>(fmaf(x, 64.0f, 64.0f));
         idx = min(max(idx, 0), kBuckets - 1);
         const float2 t = s_tab[idx];
