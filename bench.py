@@ -134,14 +134,14 @@ def measure_quantize(torch, q, L, reps=5):
 
 def measure_quantize_stress(torch, q, synth, gc, copies=12, reps=2):
     """Quantization stress workload: NF4 + int8 DQ over a stream of 8192 x 22016 bf16 weights
-    (Student-t(3) x 0.02 with 0.1 % outliers at +-50 std and one zero block per row): one seeded
-    matrix, uploaded as `copies` distinct device buffers (about 4.3 GB of bf16 at 12 copies), so
-    every quantization streams its weight from HBM."""
+    (Student-t(3) x 0.02 with 0.1 % outliers at +-50 std and one zero block per row): `copies`
+    distinct seeded matrices drawn on the device (about 4.3 GB of bf16 at 12), so every
+    quantization streams a different weight from HBM."""
+    from synth.device import stress_weight_device
     wl = synth.WORKLOADS[5]
     K, N = wl.linears[0]
-    d = synth.workload_linear(5, 0, parts=("W",))
-    W0 = gc.dev_weight(d)
-    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    Ws = [stress_weight_device([5, i], N, K) for i in range(copies)]
+    W0 = Ws[0]
     for W in Ws[:2]:  # outputs come from torch's caching allocator: no allocation in the timed loop
         q.quantize(W)
     torch.cuda.synchronize()
@@ -157,7 +157,7 @@ def measure_quantize_stress(torch, q, synth, gc, copies=12, reps=2):
     quant = {"value": round(gbs, 1), "unit": "GB/s", "bytes_per_weight": 2.516, "ms_per_weight": round(ms, 4),
              "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "stream_GB": round(copies * N * K * 2 / 1e9, 2),
              "what": f"bf16 -> NF4 codes + int8 DQ constants, {N}x{K} stress weights (Student-t(3), outliers, "
-                     f"zero blocks), {copies} distinct device copies"}
+                     f"zero blocks), {copies} distinct seeded matrices"}
     # standalone decode of the same stream: the quantized copies -> one bf16 output buffer
     qws = [q.quantize(W) for W in Ws]
     del Ws, W0

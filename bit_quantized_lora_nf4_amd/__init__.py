@@ -70,14 +70,70 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _need(t, dtype, name):
+def _meta(t, dtype, name, shape=None):
+    """A torch tensor of ``dtype``, contiguous, of ``shape`` when given."""
     torch = _torch()
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _on(t, name, device=None):
+    """On a GPU, and on ``device`` when given."""
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _need(t, dtype, name, shape=None, device=None):
+    _meta(t, dtype, name, shape)
+    _on(t, name, device)
+
+
+class _Args:
+    """Argument checks of one call, done before anything is launched.  The C ABI takes
+    bare pointers and sizes its accesses from the weight's shape, M and r, so a tensor
+    that does not match would be read or written past its end.  Dtypes, shapes and
+    contiguity are checked first for every argument, then the devices."""
+
+    def __init__(self, device):
+        self.device = device
+        self.seen = []
+
+    def need(self, t, dtype, name, shape=None):
+        _meta(t, dtype, name, shape)
+        self.seen.append((t, name))
+        return t
+
+    def adapter(self, A, B, N, K, R=None, r=None):
+        """(A, B) for a weight [N, K]: A [R, K], B [N, r] (R = r for one linear, parts r
+        for fused linears).  Returns R, 0 without an adapter."""
+        if A is None and B is None:
+            return 0
+        if A is None or B is None:
+            raise ValueError("A and B must both be given or both be None")
+        R = A.shape[0] if R is None else R
+        r = R if r is None else r
+        self.need(A, _torch().bfloat16, "A", (R, K))
+        self.need(B, _torch().bfloat16, "B", (N, r))
+        return R
+
+    def workspace(self, ws, nbytes):
+        if ws is None:
+            return
+        self.need(ws, _torch().uint8, "ws")
+        if ws.numel() < nbytes:
+            raise ValueError(f"ws has {ws.numel()} bytes, {nbytes} needed")
+
+    def devices(self):
+        for t, name in self.seen:
+            _on(t, name, self.device)
 
 
 def _alloc_weight(n_rows, n_cols, quant_type, const_type, device):
@@ -100,6 +156,8 @@ def quantize(W, return_absmax=False, quant_type=QLORA_QUANT_NF4, const_type=QLOR
     torch = _torch()
     if W.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("W must be float32 or bfloat16")
+    if W.dim() != 2:
+        raise ValueError(f"W must be 2-D, got shape {tuple(W.shape)}")
     _need(W, W.dtype, "W")
     n_rows, n_cols = W.shape
     qw = _alloc_weight(n_rows, n_cols, quant_type, const_type, W.device)
@@ -117,8 +175,12 @@ def dequantize(qw, dtype=None, out=None):
     """W' [n_rows, n_cols]: bf16 (default) or the fp32 product before bf16 rounding."""
     torch = _torch()
     dtype = dtype or torch.bfloat16
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("dtype must be bfloat16 or float32")
     if out is None:
         out = torch.empty(qw.shape, dtype=dtype, device=qw.codes.device)
+    _meta(out, dtype, "out", qw.shape)
+    _on(out, "out", qw.codes.device)
     dt = QLORA_BF16 if dtype == torch.bfloat16 else QLORA_F32
     _lib.check(qlora_dequantize(qw.descriptor(), out.data_ptr(), dt, _stream(out)), "qlora_dequantize")
     return out
@@ -134,19 +196,27 @@ def workspace(op, M, K, N, r, device):
 def linear_fwd(qw, X, A=None, B=None, alpha=16.0, save_u=True, Y=None, U=None, ws=None):
     """Y = bf16(X W'^T + U_s B^T) with U_s = bf16((alpha/r) X A^T).  Returns (Y, U_s or None)."""
     torch = _torch()
-    _need(X, torch.bfloat16, "X")
-    M, K = X.shape
-    r = 0 if A is None else A.shape[0]
-    if r:
-        _need(A, torch.bfloat16, "A")
-        _need(B, torch.bfloat16, "B")
-    dev = X.device
+    chk = _Args(qw.codes.device)
+    K, N = qw.n_cols, qw.n_rows
+    if X.dim() != 2:
+        raise ValueError(f"X must be 2-D [M, {K}], got shape {tuple(X.shape)}")
+    M = X.shape[0]
+    chk.need(X, torch.bfloat16, "X", (M, K))
+    r = chk.adapter(A, B, N, K)
+    if Y is not None:
+        chk.need(Y, torch.bfloat16, "Y", (M, N))
+    if r and save_u and U is not None:
+        chk.need(U, torch.bfloat16, "U", (M, r))
+    nbytes = qlora_workspace_bytes(0, M, K, N, r)
+    chk.workspace(ws, nbytes)
+    chk.devices()
+    dev = chk.device
     if Y is None:
-        Y = torch.empty((M, qw.n_rows), dtype=torch.bfloat16, device=dev)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if r and save_u and U is None:
         U = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
-    if ws is None and qlora_workspace_bytes(0, M, K, qw.n_rows, r) > 0:
-        ws = workspace(0, M, K, qw.n_rows, r, dev)
+    if ws is None and nbytes > 0:
+        ws = workspace(0, M, K, N, r, dev)
     _lib.check(qlora_linear_fwd(qw.descriptor(), X.data_ptr(), M, _ptr(A), _ptr(B), r, float(alpha),
                                 Y.data_ptr(), _ptr(U) if save_u else None, _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(X)), "qlora_linear_fwd")
@@ -156,25 +226,59 @@ def linear_fwd(qw, X, A=None, B=None, alpha=16.0, save_u=True, Y=None, U=None, w
 def linear_bwd(qw, dY, X, A=None, B=None, alpha=16.0, U=None, need_dx=True, dX=None, dA=None,
                dB=None, ws=None):
     """(dX, dA, dB) of the QLoRA linear; no gradient for the frozen weight."""
+    return _bwd(qw, 1, dY, X, A, B, alpha, U, need_dx, dX, dA, dB, ws)
+
+
+def _bwd(qw, parts, dY, X, A, B, alpha, U, need_dx, dX, dA, dB, ws):
     torch = _torch()
-    _need(dY, torch.bfloat16, "dY")
-    M = dY.shape[0]
+    chk = _Args(qw.codes.device)
     K, N = qw.n_cols, qw.n_rows
-    r = 0 if A is None else A.shape[0]
-    dev = dY.device
+    if dY.dim() != 2:
+        raise ValueError(f"dY must be 2-D [M, {N}], got shape {tuple(dY.shape)}")
+    M = dY.shape[0]
+    chk.need(dY, torch.bfloat16, "dY", (M, N))
+    R = 0 if A is None else A.shape[0]
+    if R % parts:
+        raise ValueError(f"A has {R} rows, not a multiple of n_parts = {parts}")
+    r = R // parts
+    chk.adapter(A, B, N, K, R=R, r=r)
+    if R or X is not None:
+        if X is None:
+            raise ValueError("X is required when the layer has an adapter")
+        chk.need(X, torch.bfloat16, "X", (M, K))
+    if U is not None:
+        chk.need(U, torch.bfloat16, "U", (M, R))
+    if need_dx and dX is not None:
+        chk.need(dX, torch.bfloat16, "dX", (M, K))
+    nbytes = qlora_workspace_bytes_fused(1, M, K, N, r, parts) if R else 0
+    if R:
+        if dA is not None:
+            chk.need(dA, torch.bfloat16, "dA", (R, K))
+        if dB is not None:
+            chk.need(dB, torch.bfloat16, "dB", (N, r))
+        chk.workspace(ws, nbytes)
+    chk.devices()
+    dev = chk.device
     if need_dx and dX is None:
         dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    if r:
+    if R:
         if dA is None:
-            dA = torch.empty((r, K), dtype=torch.bfloat16, device=dev)
+            dA = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
         if dB is None:
             dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
         if ws is None:
-            ws = workspace(1, M, K, N, r, dev)
-    _lib.check(qlora_linear_bwd(qw.descriptor(), dY.data_ptr(), _ptr(X), M, _ptr(A), _ptr(B), r,
-                                float(alpha), _ptr(U), _ptr(dX) if need_dx else None, _ptr(dA),
-                                _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dY)),
-               "qlora_linear_bwd")
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    fn = qlora_linear_bwd_fused if parts > 1 else None
+    dxp = _ptr(dX) if need_dx else None
+    wsn = 0 if ws is None else ws.numel()
+    if fn is None:
+        st = qlora_linear_bwd(qw.descriptor(), dY.data_ptr(), _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha),
+                              _ptr(U), dxp, _ptr(dA), _ptr(dB), _ptr(ws), wsn, _stream(dY))
+        _lib.check(st, "qlora_linear_bwd")
+    else:
+        st = fn(qw.descriptor(), parts, dY.data_ptr(), _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(U),
+                dxp, _ptr(dA), _ptr(dB), _ptr(ws), wsn, _stream(dY))
+        _lib.check(st, "qlora_linear_bwd_fused")
     return (dX if need_dx else None), dA, dB
 
 
@@ -203,13 +307,9 @@ def adamw_step(param, grad, exp_avg, exp_avg_sq, step, lr, betas=(0.9, 0.999), e
 
 
 def _adapter(A, B, N, K):
-    torch = _torch()
-    r = 0 if A is None else A.shape[0]
-    if r:
-        _need(A, torch.bfloat16, "A")
-        _need(B, torch.bfloat16, "B")
-        if tuple(A.shape) != (r, K) or tuple(B.shape) != (N, r):
-            raise ValueError(f"A {tuple(A.shape)} / B {tuple(B.shape)} do not fit a [{N}, {K}] weight")
+    chk = _Args(None)
+    r = chk.adapter(A, B, N, K)
+    chk.devices()
     return r
 
 
@@ -220,7 +320,7 @@ def lora_merge(qw, A, B, alpha=16.0, out=None):
     r = _adapter(A, B, N, K)
     if out is None:
         out = torch.empty((N, K), dtype=torch.bfloat16, device=qw.codes.device)
-    _need(out, torch.bfloat16, "out")
+    _need(out, torch.bfloat16, "out", (N, K))
     _lib.check(qlora_lora_merge(qw.descriptor(), _ptr(A), _ptr(B), r, float(alpha), out.data_ptr(),
                                 _stream(out)), "qlora_lora_merge")
     return out
@@ -234,7 +334,7 @@ def lora_unmerge(Wm, A, B, alpha=16.0, out=None):
     r = _adapter(A, B, N, K)
     if out is None:
         out = torch.empty_like(Wm)
-    _need(out, torch.bfloat16, "out")
+    _need(out, torch.bfloat16, "out", (N, K))
     _lib.check(qlora_lora_unmerge(Wm.data_ptr(), N, K, _ptr(A), _ptr(B), r, float(alpha), out.data_ptr(),
                                   _stream(Wm)), "qlora_lora_unmerge")
     return out
@@ -257,24 +357,29 @@ def linear_fwd_fused(qw, n_parts, X, A=None, B=None, alpha=16.0, save_u=True, Y=
     """Fused forward of n_parts linears sharing X: A [n_parts r, K] and B [N, r] stack the
     parts' adapters; Y [M, N] holds the parts' outputs side by side."""
     torch = _torch()
-    _need(X, torch.bfloat16, "X")
-    M, K = X.shape
-    N = qw.n_rows
+    chk = _Args(qw.codes.device)
+    K, N = qw.n_cols, qw.n_rows
+    if X.dim() != 2:
+        raise ValueError(f"X must be 2-D [M, {K}], got shape {tuple(X.shape)}")
+    M = X.shape[0]
+    chk.need(X, torch.bfloat16, "X", (M, K))
     R = 0 if A is None else A.shape[0]
     if R % n_parts:
         raise ValueError(f"A has {R} rows, not a multiple of n_parts = {n_parts}")
     r = R // n_parts
-    if r:
-        _need(A, torch.bfloat16, "A")
-        _need(B, torch.bfloat16, "B")
-        if tuple(B.shape) != (N, r):
-            raise ValueError(f"B is {tuple(B.shape)}, expected {(N, r)}")
-    dev = X.device
+    chk.adapter(A, B, N, K, R=R, r=r)
+    if Y is not None:
+        chk.need(Y, torch.bfloat16, "Y", (M, N))
+    if r and save_u and U is not None:
+        chk.need(U, torch.bfloat16, "U", (M, R))
+    nbytes = qlora_workspace_bytes_fused(0, M, K, N, r, n_parts)
+    chk.workspace(ws, nbytes)
+    chk.devices()
+    dev = chk.device
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if r and save_u and U is None:
         U = torch.empty((M, R), dtype=torch.bfloat16, device=dev)
-    nbytes = qlora_workspace_bytes_fused(0, M, K, N, r, n_parts)
     if ws is None and nbytes > 0:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     _lib.check(qlora_linear_fwd_fused(qw.descriptor(), n_parts, X.data_ptr(), M, _ptr(A), _ptr(B), r,
@@ -287,26 +392,4 @@ def linear_fwd_fused(qw, n_parts, X, A=None, B=None, alpha=16.0, save_u=True, Y=
 def linear_bwd_fused(qw, n_parts, dY, X, A=None, B=None, alpha=16.0, U=None, need_dx=True, dX=None,
                      dA=None, dB=None, ws=None):
     """(dX, dA, dB) of the fused linears; dA and dB are stacked like A and B."""
-    torch = _torch()
-    _need(dY, torch.bfloat16, "dY")
-    M = dY.shape[0]
-    K, N = qw.n_cols, qw.n_rows
-    R = 0 if A is None else A.shape[0]
-    r = R // n_parts
-    dev = dY.device
-    if need_dx and dX is None:
-        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    if r:
-        if dA is None:
-            dA = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
-        if dB is None:
-            dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
-        if ws is None:
-            ws = torch.empty(max(qlora_workspace_bytes_fused(1, M, K, N, r, n_parts), 256),
-                             dtype=torch.uint8, device=dev)
-    _lib.check(qlora_linear_bwd_fused(qw.descriptor(), n_parts, dY.data_ptr(), _ptr(X), M, _ptr(A),
-                                      _ptr(B), r, float(alpha), _ptr(U), _ptr(dX) if need_dx else None,
-                                      _ptr(dA), _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(),
-                                      _stream(dY)),
-               "qlora_linear_bwd_fused")
-    return (dX if need_dx else None), dA, dB
+    return _bwd(qw, n_parts, dY, X, A, B, alpha, U, need_dx, dX, dA, dB, ws)

@@ -217,7 +217,9 @@ int fwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16
     return fail(QLORA_ERR_ALIGN, "%s: tensors must be 16-byte aligned", who);
   const int64_t K = w->n_cols, N = w->n_rows;
   const int R = r * parts;
-  const int64_t part_rows = parts > 1 ? N / parts : 0;
+  // per-part rank offsets only matter with an adapter; without one the fused weight is
+  // a single linear to the kernels (part heights need not be multiples of 256)
+  const int64_t part_rows = (parts > 1 && r > 0) ? N / parts : 0;
   const FwdLayout L = fwd_layout(M, K, N, R, !U_saved);
   const bool need_ws = L.total > 0;
   if (need_ws && (!workspace || workspace_bytes < L.total))

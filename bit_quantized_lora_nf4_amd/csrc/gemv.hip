@@ -24,6 +24,8 @@
 // permutation inside every 8-element group, so the contraction pairs the right
 // elements without re-interleaving the decoded weights.
 
+#include <mutex>
+
 #include "device_common.h"
 #include "qlora_internal.h"
 
@@ -353,30 +355,43 @@ bool gemv_supported(const WeightView &w, int64_t M, int r) {
 }
 
 namespace {
+// Dynamic LDS above 64 KB (M > 8) has to be allowed once per kernel instantiation
+// (and per device); the flag is per instantiation and thread-safe.
+template <int XL, bool C8W, int CT>
+hipError_t allow_lds() {
+  static std::once_flag once[64];
+  static hipError_t err[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [&] {
+    err[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_stream_kernel<XL, C8W, CT>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   static_cast<int>(gemv_lds_bytes(GMAXM, CT)));
+  });
+  return err[dev];
+}
+
+template <int XL, bool C8W, int CT>
+hipError_t go_stream(const GemvArgs &a, unsigned grid, hipStream_t stream) {
+  if (XL == 8) {
+    const hipError_t e = allow_lds<XL, C8W, CT>();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((gemv_stream_kernel<XL, C8W, CT>), dim3(grid), dim3(GT), gemv_lds_bytes(a.M, CT), stream, a);
+  return hipGetLastError();
+}
+
 template <int CT>
 hipError_t launch_stream(const GemvArgs &a, unsigned grid, bool c8w, hipStream_t stream) {
-  auto go = [&](auto kern) -> hipError_t {
-    // dynamic LDS above 64 KB (M > 8) has to be allowed once per instantiation
-    static bool allowed = false;
-    if (gemv_xl(a.M) == 8 && !allowed) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(gemv_lds_bytes(GMAXM, CT)));
-      if (e != hipSuccess) return e;
-      allowed = true;
-    }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(GT), gemv_lds_bytes(a.M, CT), stream, a);
-    return hipGetLastError();
-  };
   switch (gemv_xl(a.M) * 2 + (c8w ? 1 : 0)) {
-    case 3: return go(gemv_stream_kernel<1, true, CT>);
-    case 2: return go(gemv_stream_kernel<1, false, CT>);
-    case 5: return go(gemv_stream_kernel<2, true, CT>);
-    case 4: return go(gemv_stream_kernel<2, false, CT>);
-    case 9: return go(gemv_stream_kernel<4, true, CT>);
-    case 8: return go(gemv_stream_kernel<4, false, CT>);
-    case 17: return go(gemv_stream_kernel<8, true, CT>);
-    default: return go(gemv_stream_kernel<8, false, CT>);
+    case 3: return go_stream<1, true, CT>(a, grid, stream);
+    case 2: return go_stream<1, false, CT>(a, grid, stream);
+    case 5: return go_stream<2, true, CT>(a, grid, stream);
+    case 4: return go_stream<2, false, CT>(a, grid, stream);
+    case 9: return go_stream<4, true, CT>(a, grid, stream);
+    case 8: return go_stream<4, false, CT>(a, grid, stream);
+    case 17: return go_stream<8, true, CT>(a, grid, stream);
+    default: return go_stream<8, false, CT>(a, grid, stream);
   }
 }
 }  // namespace

@@ -80,11 +80,12 @@ def _status(fn, *args):
 def test_quantize_argument_errors():
     q = _lib.qlora_quantize_nf4
     assert q(FAKE, 1, 4, 100, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.QLORA_ERR_SHAPE
+    assert b"multiple of 64" in _lib.load().qlora_last_error()
     assert q(FAKE, 7, 4, 128, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.QLORA_ERR_DTYPE
     assert q(None, 1, 4, 128, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.QLORA_ERR_NULL
     assert q(FAKE, 1, 4, 128, FAKE, None, FAKE, FAKE, None, None) == _lib.QLORA_ERR_NULL
     assert q(FAKE + 2, 1, 4, 128, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.QLORA_ERR_ALIGN
-    assert b"multiple of 64" in _lib.load().qlora_last_error() or True
+    assert b"16-byte aligned" in _lib.load().qlora_last_error()
 
 
 def test_dequantize_argument_errors():

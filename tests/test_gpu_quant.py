@@ -147,6 +147,61 @@ def test_quantize_stress_matrix_sampled_groups(lib):
         assert np.array_equal(wb[e0:e1], nf4.dequantize_bf16_bits(ref).reshape(-1)), g
 
 
+def test_quantize_stress_stream_twelve_matrices(lib):
+    """The quantization-stress stream: 12 distinct seeded 8192 x 22016 stress weights (about
+    4.3 GB of bf16, drawn on the device), each quantized and decoded on the GPU.  Per matrix
+    the first and last DQ groups and 6 random ones are checked bit for bit against the
+    oracle (codes, int8 constants, scale, offset, decoded bf16); over all checked groups the
+    oracle's per-element decode error stays within its bound, and the error statistics per
+    kind of block (bulk Student-t, outlier, all-zero) are printed."""
+    import torch
+    from oracle import stress
+    from synth.device import stress_weight_device
+    N, K = 8192, 22016
+    n_groups = N * K // 16384
+    rng = np.random.default_rng(321)
+    std = 0.02 * 3.0 ** 0.5
+    W_all, labels_all, qws_ref = [], [], []
+    for i in range(12):
+        W = stress_weight_device([5, i], N, K)
+        qw, c = lib.quantize(W, return_absmax=True)
+        wb = lib.dequantize(qw)
+        torch.cuda.synchronize()
+        groups = sorted(set([0, n_groups - 1] + rng.choice(n_groups, 6, replace=False).tolist()))
+        flat = W.view(-1)
+        for g in groups:
+            e0, e1 = g * 16384, (g + 1) * 16384
+            Wg = gc.host_f32_from_bf16(flat[e0:e1]).astype(np.float32).reshape(1, -1)
+            ref = nf4.quantize_nf4(Wg)
+            assert np.array_equal(qw.codes[e0 // 2:e1 // 2].cpu().numpy(), ref["codes"]), (i, g)
+            assert np.array_equal(qw.absmax_q[g * 256:(g + 1) * 256].cpu().numpy(), ref["absmax_q"]), (i, g)
+            assert np.array_equal(c[g * 256:(g + 1) * 256].cpu().numpy().view(np.uint32),
+                                  ref["absmax"].view(np.uint32)), (i, g)
+            assert qw.dq_scale[g].item() == ref["dq_scale"][0] and qw.dq_offset[g].item() == ref["dq_offset"][0]
+            assert np.array_equal(gc.host_bits(wb.view(-1)[e0:e1]), nf4.dequantize_bf16_bits(ref).reshape(-1)), (i, g)
+            W_all.append(Wg)
+            labels_all.append(stress.block_kinds(Wg, outlier_abs=25 * std))
+            qws_ref.append(ref)
+        print(f"  stress matrix {i}: {len(groups)} groups bit-exact", flush=True)
+        del W, qw, c, wb
+        torch.cuda.empty_cache()
+    report = {}
+    for Wg, lab, ref in zip(W_all, labels_all, qws_ref):
+        for k, v in stress.error_report(Wg, ref, lab).items():
+            agg = report.setdefault(k, {"blocks": 0, "max_err_over_c": 0.0, "sq": 0.0, "n": 0,
+                                        "max_err_over_bound": 0.0})
+            agg["blocks"] += v["blocks"]
+            agg["max_err_over_c"] = max(agg["max_err_over_c"], v["max_err_over_c"])
+            agg["sq"] += v["rms_err_over_c"] ** 2 * v["blocks"]
+            agg["max_err_over_bound"] = max(agg["max_err_over_bound"], v["max_err_over_bound"])
+    for k, v in sorted(report.items()):
+        rms = (v["sq"] / v["blocks"]) ** 0.5
+        print(f"  {k}: {v['blocks']} blocks, |w - w'|/c max {v['max_err_over_c']:.4f} rms {rms:.4f}, "
+              f"error/bound max {v['max_err_over_bound']:.3f}", flush=True)
+        assert v["max_err_over_bound"] <= 1.0, k
+    assert set(report) == {"bulk", "outlier", "zero"}
+
+
 def test_quantize_deterministic(lib):
     d = synth.case(1, 4096, 256, 0, seed=5, parts=("W",))
     a, _ = _run(lib, d)
