@@ -263,13 +263,21 @@ __device__ __forceinline__ void substep_schedule() {
 }
 
 // Global loads per wave and contraction step: per weight row (2) the codes and the
-// constant's pieces (three, or one fp32 constant), then eight activation DMA loads,
-// the last four after the step's barrier.  The barrier's wait leaves in flight the
-// loads issued since the previous barrier except that barrier's own four DMA loads,
-// which complete the tile read right after it: the wait retires exactly those.
+// constant's pieces (three, or one fp32 constant) of the step two ahead, then eight
+// activation DMA loads, the last four after the step's barrier.  The barrier's wait
+// leaves in flight the loads issued since the previous barrier and retires everything
+// older, which includes the tile read right after it.  The last one or two steps of a
+// launch issue no code loads (nothing would read them; left in the source, the
+// compiler would delete them as dead and the count would no longer hold), so their
+// barriers leave only their own DMA loads in flight.
+constexpr int kDmaPerHalf = 4;  // DMA loads per wave and half tile (issue_dma)
 template <int CT>
+constexpr int code_loads_per_row() {
+  return 1 + (CT == kConstF32 ? 1 : 3);  // issue_codes
+}
+template <int CT, bool CODES>
 constexpr int loads_before_barrier() {
-  return 2 * (1 + (CT == kConstF32 ? 1 : 3)) + 4;
+  return (CODES ? 2 * code_loads_per_row<CT>() : 0) + kDmaPerHalf;
 }
 
 // The forward is software-pipelined by contraction sub-step (16 of each 64-step):
@@ -335,7 +343,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   auto issue_dma = [&](int kt, int h, char *buf) {
     char *dst = buf + wave * 8 * 1024;
 #pragma unroll
-    for (int i = 4 * h; i < 4 * h + 4; ++i)
+    for (int i = kDmaPerHalf * h; i < kDmaPerHalf * (h + 1); ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)(dst + i * 1024),
                                                16, xoff[i], kt * 2, 0, 0);
   };
@@ -370,9 +378,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(wa[j], xb[i], acc[i][j]);
   };
 
-  // One contraction step; B is the LDS buffer of the step's tile (it % 3).
-  auto step = [&](auto B, int it, CodeStage &cur, CodeStage &nxt, CodeStage &nn) {
+  // One contraction step; B is the LDS buffer of the step's tile (it % 3); CODES says
+  // whether the codes of step it + 2 are loaded (every step but the last one or two).
+  auto step = [&](auto B, auto CODES, int it, CodeStage &cur, CodeStage &nxt, CodeStage &nn) {
     constexpr int b = decltype(B)::v;
+    constexpr bool codes = decltype(CODES)::v != 0;
     const char *sx = sX + b * TILE_BYTES;
     const char *sxn = sX + ((b + 1) % NBUF) * TILE_BYTES;
     char *sxw = sX + ((b + 2) % NBUF) * TILE_BYTES;
@@ -381,7 +391,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4_t wan[2], xbn[8];
-      if (s < 2) issue_codes(ktn, s, nn);  // codes first: they are needed soonest
+      if (codes && s < 2) issue_codes(ktn, s, nn);  // codes first: they are needed soonest
       // the next step's planes, half a row per sub-step (row 1's last half is needed
       // by this step's last sub-step)
       if (s == 0) {
@@ -398,7 +408,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       if (s == 3) {
         // tile it + 1 (issued a step ago) must have landed for every wave, and no wave
         // may still read the buffer that the next step's loads will overwrite
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(loads_before_barrier<CT>()) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(loads_before_barrier<CT, codes>())
+                     : "memory");
         issue_dma(ktn, 1, sxw);
         read_xfrags_fwd(sxn, 0, xbn);
 #pragma unroll
@@ -422,12 +433,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
   int it = 0;
   for (; it + 3 <= nk; it += 3) {
-    step(Ic<0>{}, it, S0, S1, S2);
-    step(Ic<1>{}, it + 1, S1, S2, S0);
-    step(Ic<2>{}, it + 2, S2, S0, S1);
+    step(Ic<0>{}, Ic<1>{}, it, S0, S1, S2);
+    step(Ic<1>{}, Ic<1>{}, it + 1, S1, S2, S0);
+    step(Ic<2>{}, Ic<1>{}, it + 2, S2, S0, S1);
   }
-  if (it < nk) step(Ic<0>{}, it, S0, S1, S2);
-  if (it + 1 < nk) step(Ic<1>{}, it + 1, S1, S2, S0);
+  // the last one or two steps: the codes of steps past the end are not loaded
+  if (it < nk) step(Ic<0>{}, Ic<0>{}, it, S0, S1, S2);
+  if (it + 1 < nk) step(Ic<1>{}, Ic<0>{}, it + 1, S1, S2, S0);
   // drain the clamped prefetches of the last steps before the epilogue
   __builtin_amdgcn_s_waitcnt(0);
   if (p.r > 0) lora_steps(p, m0, n0, acc);
@@ -809,8 +821,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   // Step it: weight tile and dY stage b2 = it % 2 are this step's; the other stage
   // receives the dY slice of step it + 1, `dec` holds the codes of step it + 1
   // (decoded now into the other weight tile), `ld` receives those of step it + 2.
-  auto step = [&](auto B2, auto CHK, int it, CodeStageB &dec, CodeStageB &ld) {
+  // CODES: the codes of step it + 2 are loaded (not in the last two steps, where
+  // nothing would read them: left in the source, the compiler deletes such loads as
+  // dead on some paths, and the barrier's count of loads in flight would no longer
+  // hold); the barrier then leaves only the code loads in flight, else nothing.
+  auto step = [&](auto B2, auto CHK, auto CODES, int it, CodeStageB &dec, CodeStageB &ld) {
     constexpr int b2 = decltype(B2)::v;
+    constexpr bool codes = decltype(CODES)::v != 0;
     const char *sw = b2 ? sW1 : sW0;
     char *swn = b2 ? sW0 : sW1;
     const char *sy = b2 ? sY1 : sY0;
@@ -828,7 +845,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         decode_part(dec, pd, swn, 0, 2);
       }
       if (s == 1) {
-        issue_codes(kt2, ld);
+        if (codes) issue_codes(kt2, ld);
         decode_part(dec, pd, swn, 2, 5);
       }
       if (s == 2) decode_part(dec, pd, swn, 5, 8);
@@ -837,7 +854,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         // sub-step 1 were issued after it), and after the barrier every wave's has;
         // every thread's part of the next weight tile is written; no wave still
         // reads the tile or stage that the next step overwrites
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(CODE_LOADS) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(codes ? CODE_LOADS : 0) : "memory");
 #pragma unroll
         for (int j = 0; j < 4; ++j) wan[j] = wfrag_tr_all(swn, trb, 0, j);
         read_y(syn, 0, ybn);
@@ -857,7 +874,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       if (s == 0)
         dx_schedule<12, 5, 8, 2>();
       else if (s == 1)
-        dx_schedule<12, 4, CODE_LOADS, 3>();
+        dx_schedule<12, 4, codes ? CODE_LOADS : 0, 3>();
       else if (s == 2)
         dx_schedule<12, 4, 0, 3>();
       else
@@ -870,12 +887,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   // dY prefetch stays inside N; the last steps check the contraction tail.
   int it = 0;
   for (; it + 4 <= nk; it += 2) {
-    step(Ic<0>{}, Ic<0>{}, it, S1, S0);
-    step(Ic<1>{}, Ic<0>{}, it + 1, S0, S1);
+    step(Ic<0>{}, Ic<0>{}, Ic<1>{}, it, S1, S0);
+    step(Ic<1>{}, Ic<0>{}, Ic<1>{}, it + 1, S0, S1);
   }
-  if (it < nk) step(Ic<0>{}, Ic<1>{}, it, S1, S0);
-  if (it + 1 < nk) step(Ic<1>{}, Ic<1>{}, it + 1, S0, S1);
-  if (it + 2 < nk) step(Ic<0>{}, Ic<1>{}, it + 2, S1, S0);
+  // the last one to three steps, each sequence spelled out so that every step knows
+  // whether it loads the codes two steps ahead (only a step with two more after it)
+  const int rem = nk - it;
+  if (rem == 3) {
+    step(Ic<0>{}, Ic<1>{}, Ic<1>{}, it, S1, S0);
+    step(Ic<1>{}, Ic<1>{}, Ic<0>{}, it + 1, S0, S1);
+    step(Ic<0>{}, Ic<1>{}, Ic<0>{}, it + 2, S1, S0);
+  } else if (rem == 2) {
+    step(Ic<0>{}, Ic<1>{}, Ic<0>{}, it, S1, S0);
+    step(Ic<1>{}, Ic<1>{}, Ic<0>{}, it + 1, S0, S1);
+  } else if (rem == 1) {
+    step(Ic<0>{}, Ic<1>{}, Ic<0>{}, it, S1, S0);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   if (p.r > 0) lora_steps_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
   store_out_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
