@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import (QLORA_BF16, QLORA_CONST_DQ_FP8, QLORA_CONST_DQ_INT8, QLORA_CONST_FP32,  # noqa: F401
                    QLORA_F32, QLORA_QUANT_FP4, QLORA_QUANT_NF4, QloraError, qlora_adamw_step,
                    qlora_codebook, qlora_dequantize, qlora_linear_bwd, qlora_linear_bwd_fused,
-                   qlora_linear_fwd, qlora_linear_fwd_fused, qlora_lora_merge, qlora_lora_unmerge,
+                   qlora_linear_fwd, qlora_linear_fwd_fused, qlora_linear_fwd_noalloc, qlora_lora_merge,
+                   qlora_lora_unmerge,
                    qlora_nf4_codebook, qlora_nf4_concat_rows, qlora_nf4_sizes, qlora_quantize,
                    qlora_quantize_nf4, qlora_workspace_bytes, qlora_workspace_bytes_fused)
 
@@ -28,7 +29,7 @@ __all__ = ["NF4Weight", "quantize", "dequantize", "linear_fwd", "linear_bwd", "w
            "qlora_linear_bwd", "qlora_nf4_sizes", "qlora_nf4_codebook", "qlora_workspace_bytes",
            "qlora_adamw_step", "qlora_lora_merge", "qlora_lora_unmerge", "qlora_linear_fwd_fused",
            "qlora_linear_bwd_fused", "qlora_workspace_bytes_fused", "qlora_nf4_concat_rows",
-           "qlora_quantize", "qlora_codebook", "QLORA_QUANT_NF4", "QLORA_QUANT_FP4", "QLORA_CONST_DQ_INT8",
+           "qlora_quantize", "qlora_codebook", "qlora_linear_fwd_noalloc", "linear_fwd_noalloc", "QLORA_QUANT_NF4", "QLORA_QUANT_FP4", "QLORA_CONST_DQ_INT8",
            "QLORA_CONST_DQ_FP8", "QLORA_CONST_FP32"]
 
 
@@ -221,6 +222,27 @@ def linear_fwd(qw, X, A=None, B=None, alpha=16.0, save_u=True, Y=None, U=None, w
                                 Y.data_ptr(), _ptr(U) if save_u else None, _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(X)), "qlora_linear_fwd")
     return Y, (U if save_u else None)
+
+
+def linear_fwd_noalloc(qw, X, Y, A=None, B=None, alpha=16.0, U=None):
+    """linear_fwd into caller-given Y (and U, optional) with no workspace and no allocation:
+    the library's fixed per-GPU scratch holds the intermediate sums.  Calls that overlap on
+    one GPU race on that scratch."""
+    torch = _torch()
+    chk = _Args(qw.codes.device)
+    K, N = qw.n_cols, qw.n_rows
+    if X.dim() != 2:
+        raise ValueError(f"X must be 2-D [M, {K}], got shape {tuple(X.shape)}")
+    M = X.shape[0]
+    chk.need(X, torch.bfloat16, "X", (M, K))
+    r = chk.adapter(A, B, N, K)
+    chk.need(Y, torch.bfloat16, "Y", (M, N))
+    if U is not None:
+        chk.need(U, torch.bfloat16, "U", (M, r))
+    chk.devices()
+    _lib.check(qlora_linear_fwd_noalloc(qw.descriptor(), X.data_ptr(), M, _ptr(A), _ptr(B), r, float(alpha),
+                                        Y.data_ptr(), _ptr(U), _stream(X)), "qlora_linear_fwd_noalloc")
+    return Y, U
 
 
 def linear_bwd(qw, dY, X, A=None, B=None, alpha=16.0, U=None, need_dx=True, dX=None, dA=None,

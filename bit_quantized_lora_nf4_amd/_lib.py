@@ -36,7 +36,9 @@ EXPORTED = (
     "qlora_linear_bwd", "qlora_time_next_gemm", "qlora_adamw_step", "qlora_lora_merge",
     "qlora_lora_unmerge", "qlora_workspace_bytes_fused", "qlora_linear_fwd_fused",
     "qlora_linear_bwd_fused", "qlora_nf4_concat_rows", "qlora_quantize", "qlora_codebook",
+    "qlora_linear_fwd_noalloc",
 )
+QLORA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class qlora_nf4_weight(ctypes.Structure):
@@ -88,6 +90,8 @@ def load(path=LIB_PATH):
     lib.qlora_dequantize.restype = I32
     lib.qlora_linear_fwd.argtypes = [W, P, I64, P, P, I32, F32, P, P, P, SZ, P]
     lib.qlora_linear_fwd.restype = I32
+    lib.qlora_linear_fwd_noalloc.argtypes = [W, P, I64, P, P, I32, F32, P, P, P]
+    lib.qlora_linear_fwd_noalloc.restype = I32
     lib.qlora_linear_bwd.argtypes = [W, P, P, I64, P, P, I32, F32, P, P, P, P, P, SZ, P]
     lib.qlora_linear_bwd.restype = I32
     lib.qlora_time_next_gemm.argtypes = [P, P]
@@ -177,6 +181,10 @@ def qlora_dequantize(w, out, out_dtype, stream):
 def qlora_linear_fwd(w, X, M, A, B, r, alpha, Y, U_saved, workspace, workspace_bytes, stream):
     return load().qlora_linear_fwd(ctypes.byref(w), X, M, A, B, r, alpha, Y, U_saved, workspace,
                                    workspace_bytes, stream)
+
+
+def qlora_linear_fwd_noalloc(w, X, M, A, B, r, alpha, Y, U_saved, stream):
+    return load().qlora_linear_fwd_noalloc(ctypes.byref(w), X, M, A, B, r, alpha, Y, U_saved, stream)
 
 
 def qlora_linear_bwd(w, dY, X, M, A, B, r, alpha, U_saved, dX, dA, dB, workspace,

@@ -131,6 +131,34 @@ qlora::WeightView view(const qlora_nf4_weight *w) {
                            w->n_cols, w->absmax,   w->quant_type, w->const_type};
 }
 
+// ---- fixed scratch of qlora_linear_fwd_noalloc ------------------------------
+// One array per GPU, zero at load, kept until the process ends.  In host code the
+// name `scratch` only stands for the symbol: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr size_t kScratchBytes = QLORA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return fail(QLORA_ERR_DEVICE, "linear_fwd_noalloc: no usable current device");
+  }
+  static std::once_flag once[64];
+  static void *addr[64];
+  static hipError_t err[64];
+  std::call_once(once[dev], [dev] {
+    void *p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = p;
+  });
+  if (err[dev] != hipSuccess || !addr[dev])
+    return fail(QLORA_ERR_DEVICE, "linear_fwd_noalloc: hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorString(err[dev]));
+  *out = addr[dev];
+  return QLORA_OK;
+}
+
 // ---- workspace layouts ------------------------------------------------------
 struct FwdLayout {
   size_t u = 0, part = 0, total = 0;
@@ -440,6 +468,26 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, co
                      void *workspace, size_t workspace_bytes, void *stream) {
   return fwd_impl("linear_fwd", w, 1, X, M, A, B, r, alpha, Y, U_saved, workspace, workspace_bytes,
                   stream);
+}
+
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
+                             const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
+                             void *stream) {
+  int s = check_weight(w);
+  if (s == QLORA_OK) s = check_m(M);
+  if (s == QLORA_OK) s = check_rank(r, alpha);
+  if (s != QLORA_OK) return s;
+  const size_t need = fwd_layout(M, w->n_cols, w->n_rows, r, !U_saved).total;
+  if (need > kScratchBytes)
+    return fail(QLORA_ERR_WORKSPACE,
+                "linear_fwd_noalloc: these shapes need %zu bytes of scratch; the fixed scratch holds %zu",
+                need, kScratchBytes);
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  void *ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != QLORA_OK) return s;
+  return fwd_impl("linear_fwd_noalloc", w, 1, X, M, A, B, r, alpha, Y, U_saved, ws, kScratchBytes, stream);
 }
 
 int qlora_linear_fwd_fused(const qlora_nf4_weight *w, int n_parts, const uint16_t *X, int64_t M,

@@ -19,8 +19,9 @@
  *     [M, K], Y and dY are [M, N].  All matrices are dense row-major.
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte
- *     aligned.  The library never allocates or frees memory and keeps no
- *     device state; scratch memory comes from the caller's workspace.
+ *     aligned.  The library never allocates or frees memory; scratch memory
+ *     comes from the caller's workspace (qlora_linear_fwd_noalloc alone uses a
+ *     fixed scratch array of the library instead).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Each call checks
  *     its arguments on the host, then enqueues its kernels asynchronously on
  *     `stream` and returns.  Kernel faults surface at the caller's next
@@ -186,6 +187,21 @@ int qlora_dequantize(const qlora_nf4_weight *w, void *out, int out_dtype, void *
 int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
                      const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): qlora_linear_fwd with the workspace taken
+ * from a fixed scratch array that the library holds in device memory, 16 MiB per GPU
+ * it runs on (QLORA_NOALLOC_SCRATCH_BYTES), kept until the process ends.  Same
+ * arguments, results and kernels as qlora_linear_fwd without workspace / workspace_bytes;
+ * the call allocates nothing.  QLORA_ERR_WORKSPACE, before anything is launched, when
+ * qlora_workspace_bytes(0, M, K, N, r) (U_saved == NULL adds the M x r U_s) exceeds the
+ * scratch.  Every call on one GPU uses that GPU's one scratch array: calls that can
+ * overlap on one GPU (different streams, different host threads) race and must be
+ * serialised by the caller. */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
+                             const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
+                             void *stream);
 
 /* Backward ([Digest] "方法步骤与流程" step 4; [QLoRA note] "5. QLoRA 训练方式本身":
  * gradients flow through W' into the adapter only; no gradient for W):
