@@ -821,13 +821,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   // Step it: weight tile and dY stage b2 = it % 2 are this step's; the other stage
   // receives the dY slice of step it + 1, `dec` holds the codes of step it + 1
   // (decoded now into the other weight tile), `ld` receives those of step it + 2.
-  // CODES: the codes of step it + 2 are loaded (not in the last two steps, where
-  // nothing would read them: left in the source, the compiler deletes such loads as
-  // dead on some paths, and the barrier's count of loads in flight would no longer
-  // hold); the barrier then leaves only the code loads in flight, else nothing.
-  auto step = [&](auto B2, auto CHK, auto CODES, int it, CodeStageB &dec, CodeStageB &ld) {
+  // In the main loop (CHK = 0) the barrier leaves the code loads of step it + 2 in
+  // flight.  In the last one to three steps (CHK = 1) some of those loads feed nothing,
+  // and the compiler may delete them on some paths, so the count of loads in flight
+  // would not hold there: those steps wait for all of their loads at the barrier.
+  auto step = [&](auto B2, auto CHK, int it, CodeStageB &dec, CodeStageB &ld) {
     constexpr int b2 = decltype(B2)::v;
-    constexpr bool codes = decltype(CODES)::v != 0;
+    constexpr bool tail = decltype(CHK)::v != 0;
     const char *sw = b2 ? sW1 : sW0;
     char *swn = b2 ? sW0 : sW1;
     const char *sy = b2 ? sY1 : sY0;
@@ -845,7 +845,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         decode_part(dec, pd, swn, 0, 2);
       }
       if (s == 1) {
-        if (codes) issue_codes(kt2, ld);
+        issue_codes(kt2, ld);
         decode_part(dec, pd, swn, 2, 5);
       }
       if (s == 2) decode_part(dec, pd, swn, 5, 8);
@@ -854,7 +854,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         // sub-step 1 were issued after it), and after the barrier every wave's has;
         // every thread's part of the next weight tile is written; no wave still
         // reads the tile or stage that the next step overwrites
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(codes ? CODE_LOADS : 0) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(tail ? 0 : CODE_LOADS) : "memory");
 #pragma unroll
         for (int j = 0; j < 4; ++j) wan[j] = wfrag_tr_all(swn, trb, 0, j);
         read_y(syn, 0, ybn);
@@ -874,7 +874,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       if (s == 0)
         dx_schedule<12, 5, 8, 2>();
       else if (s == 1)
-        dx_schedule<12, 4, codes ? CODE_LOADS : 0, 3>();
+        dx_schedule<12, 4, CODE_LOADS, 3>();
       else if (s == 2)
         dx_schedule<12, 4, 0, 3>();
       else
@@ -887,22 +887,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   // dY prefetch stays inside N; the last steps check the contraction tail.
   int it = 0;
   for (; it + 4 <= nk; it += 2) {
-    step(Ic<0>{}, Ic<0>{}, Ic<1>{}, it, S1, S0);
-    step(Ic<1>{}, Ic<0>{}, Ic<1>{}, it + 1, S0, S1);
+    step(Ic<0>{}, Ic<0>{}, it, S1, S0);
+    step(Ic<1>{}, Ic<0>{}, it + 1, S0, S1);
   }
-  // the last one to three steps, each sequence spelled out so that every step knows
-  // whether it loads the codes two steps ahead (only a step with two more after it)
-  const int rem = nk - it;
-  if (rem == 3) {
-    step(Ic<0>{}, Ic<1>{}, Ic<1>{}, it, S1, S0);
-    step(Ic<1>{}, Ic<1>{}, Ic<0>{}, it + 1, S0, S1);
-    step(Ic<0>{}, Ic<1>{}, Ic<0>{}, it + 2, S1, S0);
-  } else if (rem == 2) {
-    step(Ic<0>{}, Ic<1>{}, Ic<0>{}, it, S1, S0);
-    step(Ic<1>{}, Ic<1>{}, Ic<0>{}, it + 1, S0, S1);
-  } else if (rem == 1) {
-    step(Ic<0>{}, Ic<1>{}, Ic<0>{}, it, S1, S0);
-  }
+  if (it < nk) step(Ic<0>{}, Ic<1>{}, it, S1, S0);
+  if (it + 1 < nk) step(Ic<1>{}, Ic<1>{}, it + 1, S0, S1);
+  if (it + 2 < nk) step(Ic<0>{}, Ic<1>{}, it + 2, S1, S0);
   __builtin_amdgcn_s_waitcnt(0);
   if (p.r > 0) lora_steps_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
   store_out_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);

@@ -5,7 +5,8 @@ order the source issues them; a load the compiler moves or deletes makes the wai
 weak and lets a wave read a tile before it has landed (a run-to-run race).
 
 This test compiles gemm.hip for gfx950 with the library's flags and reads the assembly
-of every instantiation: at each barrier of the forward kernel, the loads left in flight
+of every instantiation.  The kernels keep every value in registers (no scratch spills,
+which would cost them about half their speed), and: at each barrier of the forward kernel, the loads left in flight
 must all have been issued after the direct-to-LDS loads of the tile read right after it;
 at each barrier of the pipelined dX kernel, every direct-to-LDS (dY) load issued before
 the barrier must be retired.  No GPU needed (hipcc cross-compiles)."""
@@ -96,3 +97,13 @@ def test_dx_barrier_waits(gemm_asm, ct):
             continue
         after = sum(1 for x in ev[j + 1:i] if x[0] == "R")
         assert n <= after, f"barrier wait vmcnt({n}) with only {after} register loads after the last dY load"
+
+
+def test_no_register_spills(gemm_asm):
+    """Every fused-GEMM instantiation fits the register file: its private segment stays at
+    the few bytes the kernel ABI reserves (a spill adds hundreds)."""
+    sizes = dict(re.findall(r"\.name:\s+(\S*gemm_\S*kernel\S*)\s.*?\.private_segment_fixed_size:\s+(\d+)",
+                            gemm_asm, re.S))
+    assert len(sizes) >= 9, sizes
+    for name, size in sizes.items():
+        assert int(size) <= 16, f"{name}: {size} bytes of scratch"
