@@ -180,22 +180,22 @@ def measure_quantize_stress(torch, q, synth, gc, copies=12, reps=2):
     return quant, deq
 
 
-def measure_m1(torch, q, synth, gc, ev, min_bytes=600 << 20, calls=200):
-    """M = 1 forward over distinct weight copies, replayed from a HIP graph."""
+def measure_m1(torch, q, synth, gc, ev, M=1, min_bytes=600 << 20, calls=200):
+    """Small-M forward (M = 1, 4 or 16) over distinct weight copies, replayed from a HIP graph."""
     wl = synth.WORKLOADS[3]
-    out = {"per_linear": []}
+    out = {"M": M, "per_linear": []}
     tot_bytes = tot_ms = 0.0
     for i, (K, N) in enumerate(wl.linears):
-        d = synth.workload_linear(3, i, M=1, parts=("W", "X", "A", "B"))
+        d = synth.workload_linear(3, i, M=M, parts=("W", "X", "A", "B"))
         qw0 = q.quantize(gc.dev_weight(d))
         wbytes = qw0.codes.numel() + qw0.absmax_q.numel() + 8 * qw0.dq_scale.numel()
         copies = max(2, -(-min_bytes // wbytes))
         qws = [q.NF4Weight(qw0.codes.clone(), qw0.absmax_q.clone(), qw0.dq_scale.clone(),
                            qw0.dq_offset.clone(), qw0.n_rows, qw0.n_cols) for _ in range(copies)]
         X, A, B = gc.dev_bf16(d["X"]), gc.dev_bf16(d["A"]), gc.dev_bf16(d["B"])
-        Y = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
-        U = torch.empty((1, wl.r), dtype=torch.bfloat16, device="cuda")
-        wsf = q.workspace(0, 1, K, N, wl.r, "cuda")
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        U = torch.empty((M, wl.r), dtype=torch.bfloat16, device="cuda")
+        wsf = q.workspace(0, M, K, N, wl.r, "cuda")
         for c in range(copies):  # warm up, and make sure every copy works eagerly
             q.linear_fwd(qws[c], X, A, B, wl.alpha, Y=Y, U=U, ws=wsf)
         torch.cuda.synchronize()
@@ -221,7 +221,7 @@ def measure_m1(torch, q, synth, gc, ev, min_bytes=600 << 20, calls=200):
             q.linear_fwd(qws[c], X, A, B, wl.alpha, Y=Y, U=U, ws=wsf)
         torch.cuda.synchronize()
         kms = sum(ev.ms(a, b) for a, b in ev.pool[-copies:]) / copies
-        nb = stream_bytes(1, K, N, wl.r)
+        nb = stream_bytes(M, K, N, wl.r)
         out["per_linear"].append({"K": K, "N": N, "us_per_call": round(ms_call * 1e3, 3),
                                   "GB/s": round(nb / (ms_call * 1e-3) / 1e9, 1),
                                   "gemv_kernel_us": round(kms * 1e3, 3),
@@ -600,6 +600,9 @@ def main():
         print("bench: M=1 weight stream", file=sys.stderr, flush=True)
         result["weight_stream_m1"] = measure_m1(torch, q, synth, gc, ev)
         ev.close()
+        for m in (4, 16):
+            result[f"weight_stream_m{m}"] = measure_m1(torch, q, synth, gc, ev, M=m)
+            ev.close()
         result["quantize"] = measure_quantize(torch, q, L)
         print("bench: quantization stress stream", file=sys.stderr, flush=True)
         result["quantize_stress"], result["dequantize_stress"] = measure_quantize_stress(torch, q, synth, gc)

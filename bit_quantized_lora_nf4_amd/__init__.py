@@ -188,10 +188,12 @@ def dequantize(qw, dtype=None, out=None):
 
 
 def workspace(op, M, K, N, r, device):
-    """Allocate the caller workspace for op 0 (forward) or 1 (backward)."""
+    """Allocate the caller workspace for op 0 (forward) or 1 (backward), zeroed: its
+    first QLORA_WORKSPACE_HEADER_BYTES bytes are counters and flags of the small-M
+    forward that must start at zero (every call leaves them zero)."""
     torch = _torch()
     n = qlora_workspace_bytes(op, M, K, N, r)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, _lib.QLORA_WORKSPACE_HEADER_BYTES), dtype=torch.uint8, device=device)
 
 
 def linear_fwd(qw, X, A=None, B=None, alpha=16.0, save_u=True, Y=None, U=None, ws=None):
@@ -289,7 +291,7 @@ def _bwd(qw, parts, dY, X, A, B, alpha, U, need_dx, dX, dA, dB, ws):
         if dB is None:
             dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
         if ws is None:
-            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(max(nbytes, _lib.QLORA_WORKSPACE_HEADER_BYTES), dtype=torch.uint8, device=dev)
     fn = qlora_linear_bwd_fused if parts > 1 else None
     dxp = _ptr(dX) if need_dx else None
     wsn = 0 if ws is None else ws.numel()
@@ -403,7 +405,7 @@ def linear_fwd_fused(qw, n_parts, X, A=None, B=None, alpha=16.0, save_u=True, Y=
     if r and save_u and U is None:
         U = torch.empty((M, R), dtype=torch.bfloat16, device=dev)
     if ws is None and nbytes > 0:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     _lib.check(qlora_linear_fwd_fused(qw.descriptor(), n_parts, X.data_ptr(), M, _ptr(A), _ptr(B), r,
                                       float(alpha), Y.data_ptr(), _ptr(U) if save_u else None, _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(X)),

@@ -39,6 +39,7 @@ EXPORTED = (
     "qlora_linear_fwd_noalloc",
 )
 QLORA_NOALLOC_SCRATCH_BYTES = 16 << 20
+QLORA_WORKSPACE_HEADER_BYTES = 65792  # leading workspace bytes that must be zero at first use
 
 
 class qlora_nf4_weight(ctypes.Structure):

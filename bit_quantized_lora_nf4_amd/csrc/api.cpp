@@ -136,6 +136,7 @@ qlora::WeightView view(const qlora_nf4_weight *w) {
 // name `scratch` only stands for the symbol: kernels get the device address that
 // hipGetSymbolAddress returns for the current device, looked up once per device.
 constexpr size_t kScratchBytes = QLORA_NOALLOC_SCRATCH_BYTES;
+static_assert(qlora::kGemvSyncBytes == QLORA_WORKSPACE_HEADER_BYTES, "workspace header size");
 static __device__ __align__(256) char scratch[kScratchBytes];
 
 int scratch_address(void **out) {
@@ -163,17 +164,18 @@ int scratch_address(void **out) {
 struct FwdLayout {
   size_t u = 0, part = 0, total = 0;
 };
-// M <= 16: the fp32 partial sums of the GEMV (weight stream and LoRA down-projection).
-// Otherwise U_s (when the caller does not keep it) then the fp32 partial sums of
-// lora_down; nothing when r = 0.
+// Every layout starts with the kGemvSyncBytes header of the small-M forward's counters
+// and flags, which only that kernel touches (so one workspace can serve calls of any
+// shape).  Small M (gemv_shape_ok): the whole GEMV workspace.  Otherwise U_s (when the
+// caller does not keep it) then the fp32 partial sums of lora_down; nothing when r = 0.
 FwdLayout fwd_layout(int64_t M, int64_t K, int64_t N, int r, bool need_u) {
   FwdLayout L;
-  if (M <= 16) {
+  if (qlora::gemv_shape_ok(M, N)) {
     L.total = qlora::gemv_workspace(M, K, N, r);
     return L;
   }
   if (r == 0) return L;
-  size_t off = 0;
+  size_t off = qlora::kGemvSyncBytes;
   L.u = off;
   if (need_u) off += align_up(size_t(M) * r * 2);
   L.part = off;
@@ -193,7 +195,7 @@ BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N, int r, int parts) {
   if (r == 0) return L;
   const int R = r * parts;
   const int64_t Np = N / parts;
-  size_t off = 0;
+  size_t off = qlora::kGemvSyncBytes;
   L.u = off;
   off += align_up(size_t(M) * R * 2);
   L.bt = off;
@@ -256,21 +258,19 @@ int fwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16
   if (need_ws && !aligned16(workspace))
     return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
   const qlora::WeightView wv = view(w);
-  if (M <= 16 ? !qlora::gemv_supported(wv, M, R) : !qlora::gemm_supported(wv, M, R))
+  const bool small = qlora::gemv_shape_ok(M, wv.n_rows);
+  if (small ? !qlora::gemv_supported(wv, M, R) : !qlora::gemm_supported(wv, M, R))
     return fail(QLORA_ERR_SHAPE, "%s: a tensor of %lld x %lld x %lld exceeds 32-bit buffer offsets", who,
                 (long long)M, (long long)K, (long long)N);
   s = check_device();
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
-  if (M <= 16) {
-    s = launched(timed_launch(st, [&] { return qlora::launch_gemv_stream(wv, X, M, A, R, workspace, st); }),
-                 "gemv_stream");
-    if (s != QLORA_OK) return s;
-    return launched(
-        qlora::launch_gemv_finalize(wv, M, B, r, R, part_rows, scale, Y, U_saved, workspace, st),
-        "gemv_finalize");
-  }
+  if (small)
+    return launched(timed_launch(st, [&] {
+                      return qlora::launch_gemv(wv, X, M, A, R, B, r, part_rows, scale, Y, U_saved, workspace, st);
+                    }),
+                    "gemv");
   uint16_t *U = nullptr;
   if (r > 0) {
     char *ws = static_cast<char *>(workspace);

@@ -1,28 +1,52 @@
-// Small-M forward (M <= 16): a bandwidth-oriented dequant-GEMV (gfx950).
+// Small-M forward (M <= 16): a bandwidth-oriented dequant-GEMV in one launch (gfx950).
 //
-// Y[m, n] = bf16(sum_k X[m, k] W'[n, k] + sum_j U_s[m, j] Bl[n, j]),
-// U_s = bf16(scale * X . A^T)  ([Paper note] "关键设计 3"; [Repro] "LoRA 的公式和张量形状").
+// Y[m, n] = bf16(sum_k X[m, k] W'[n, k] + sum_j U_s[m, q r + j] Bl[n, j]),
+// U_s = bf16(scale * X . A^T)  ([Paper note] "关键设计 3"; [Repro] "LoRA 的公式和张量形状")
+// with q the part of row n for horizontally fused linears (0 for one linear).
 //
-// At such M the layer is bound by the weight stream (0.516 B per weight), so the work
-// is cut into many independent pieces, each of which issues all of its loads at once:
+// At such M the layer is bound by the weight stream (0.516 B per weight) and by the VALU
+// work of decoding it (about fifteen byte permutes per eight weights), so the launch is
+// shaped to keep both busy from start to end:
 //
-//   stream kernel   workgroup (row group g, contraction slice s): 64 weight rows x
-//                   1024 columns.  The slice of X (M rows, pre-permuted, see below) is
-//                   staged in LDS once; each wave owns 16 rows, and lane l decodes the
-//                   whole 64-weight blocks s * 16 + 4 i + l / 16 (i = 0..3) of row
-//                   l % 16: one block constant, 32 bytes of codes, eight register
-//                   lookups ([Digest] "数学公式与关键细节" item 3: w' = bf16(q[code] c')).
-//                   The dot products run on 16x16x32 bf16 MFMA (tokens padded to 16),
-//                   fp32 partial sums P[s][n][m] go to the workspace.  Extra workgroups
-//                   of the same launch compute the LoRA down-projection partials
-//                   UP[s][m][j] over the same slices.
-//   finalize        per weight row: U_s from UP (summed in slice order, scaled, rounded
-//                   once), then Y = bf16(sum_s P + U_s . Bl^T), one rounding.
+//   weight waves      a workgroup per 16 weight rows, covering all of K; its W weight
+//                     waves split K into contiguous block ranges of at most 4 T blocks
+//                     (T steps).  Per step a wave decodes 16 rows x 4 blocks of 64: lane
+//                     (row l % 16, group l / 16) loads the 32 bytes of codes of its block
+//                     with two 16-byte loads straight into registers, forms
+//                     c' = fma(c8, s, o) and the 16 table entries bf16(q[j] c') as byte
+//                     planes, and turns each code dword into an MFMA operand with register
+//                     byte-permute lookups ([Digest] "数学公式与关键细节" item 3).  The dot
+//                     products run on 16x16x32 bf16 MFMA with tokens as the 16 columns
+//                     (columns past M are never stored).  The workgroup first stages X and
+//                     its 16 rows of the LoRA B in LDS, then each wave issues the loads of
+//                     its first D steps (a register ring), so that decoding starts as soon
+//                     as the first step has landed and the weight stream never drains; the
+//                     compiler derives every wait from the register dependencies.  W and T
+//                     are chosen on the host so that the busiest SIMD of the launch runs as
+//                     few wave-steps as possible.  At the end the waves' partial sums are
+//                     added in a fixed order through LDS, and the LoRA up-projection is one
+//                     more MFMA per 32 ranks on the same accumulator, before the single
+//                     bf16 rounding.
+//   LoRA wave         one more wave per workgroup (R > 0) computes pieces of the
+//                     down-projection X . A^T: 16 ranks over a slice of LB blocks of K,
+//                     with X from the staged copy, and stores the piece's partial sums.
+//                     The last piece of a rank tile to finish (an agent-scope ticket) adds
+//                     the slices in order, rounds U_s and publishes it; the last rank tile
+//                     raises the "U_s complete" flag.  The pieces live in the lowest
+//                     workgroups of the grid, which are dispatched first, so that the
+//                     weight waves, which wait for the flag only in their epilogue, never
+//                     wait for a workgroup that cannot start.  Every counter and flag is
+//                     returned to zero by the last workgroup that uses it.
+//
+// Data handed between workgroups (the partial sums, U_s, the counters) is only ever
+// written and read with agent-coherent accesses (the SC1 cache policy: the L2 of one XCD
+// is not coherent with the others), and each hand-over waits for the writes to complete
+// before the counter that publishes them is bumped.
 //
 // Decoded weights come out of the byte-permute lookup as bf16 pairs (e0,e2), (e4,e6),
-// (e1,e3), (e5,e7) of each 8-element group; the X slice is staged with the same
-// permutation inside every 8-element group, so the contraction pairs the right
-// elements without re-interleaving the decoded weights.
+// (e1,e3), (e5,e7) of each 8-element group; X is used with the same permutation inside
+// every 8-element group, so the contraction pairs the right elements without
+// re-interleaving the decoded weights.
 
 #include <mutex>
 
@@ -32,41 +56,72 @@
 namespace qlora {
 namespace {
 
-constexpr int GT = 256;                  // threads per workgroup (4 waves)
-constexpr int GROWS = 64;                // weight rows per workgroup, 16 per wave
-#ifndef GEMV_GIT
-#define GEMV_GIT 4
-#endif
-constexpr int GIT = GEMV_GIT;            // 64-blocks per lane and workgroup
-constexpr int GSLICE = 4 * GIT * 64;     // contraction elements per workgroup (1024)
-constexpr int XPITCH = GSLICE * 2 + 16;  // bytes per staged token row (padded)
 constexpr int GMAXM = 16;
+constexpr int kMaxWaves = 16;
+constexpr int XBLK = 144;            // LDS bytes per 64-element block of a staged X row (128 + pad)
+constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr int kSC1 = 16;             // buffer cache policy: SC1 (agent-coherent access)
+// counter words at the start of the workspace
+constexpr int kSyncTiles = 1;        // rank tiles of U_s done
+constexpr int kSyncTile0 = 2;        // per rank tile: slices done
+constexpr int kMaxRankTiles = (kMaxRank + 15) / 16;
+// then one "U_s is complete" word per workgroup, kFlagStride bytes apart: the LoRA wave
+// that completes U_s raises all of them, and each workgroup polls its own and clears it
+// once it has seen it, so that no address takes the polls or the updates of the whole
+// grid (accesses to one address are served one after another)
+constexpr int kFlagBase = 256, kFlagStride = 16, kMaxFlagWGs = 4096;
+static_assert((kSyncTile0 + kMaxRankTiles) * 4 <= kFlagBase, "counter header");
+static_assert(kFlagBase + kMaxFlagWGs * kFlagStride <= static_cast<int>(kGemvSyncBytes), "flags");
+constexpr int kMaxUCopies = 64;
+// U_s is published in several copies too (at most this many bytes in all)
+constexpr size_t kUCopyBudget = 128 * 1024;
 
 struct GemvArgs {
   WeightView w;
-  const uint16_t *X;  // [M, K]
-  const uint16_t *A;  // [r, K] (unused when r = 0)
-  float *P;           // [S][N][M]
-  float *UP;          // [S][M][r]
-  int M, r, S;
+  const uint16_t *X;    // [M, K]
+  const uint16_t *A;    // [R, K] stacked adapters (R = 0: none)
+  const uint16_t *Bl;   // [N, r]
+  uint16_t *Y;          // [M, N]
+  uint16_t *U_saved;    // [M, R] or NULL
+  uint32_t *sync;       // counter words (see kSync*)
+  uint16_t *Uc;         // NC copies of U_s, bf16 [M][16 PT] each, UCE elements apart
+  float *PU;            // LoRA partial sums [PT][S][M][16]
+  int NC, UCE;
+  float scale;
+  int M, R, r, part_rows;
+  int W, T;             // weight waves per workgroup, steps of 4 blocks per weight wave
+  int PT, SP, LB, G;    // rank tiles, pieces per rank tile and their 64-blocks, workgroups
   LevelTable lvl;
 };
 
+__device__ __forceinline__ u32x4_t load16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1));
+}
+__device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                         r, off, 0, kSC1);
+}
+__device__ __forceinline__ void store8_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v),
+                                        r, off, 0, kSC1);
+}
+
 // Eight codes (element e in bits 4e..4e+3 of w) -> bf16 pairs (e0,e2), (e4,e6),
-// (e1,e3), (e5,e7): the lookup of lookup8 without its final re-interleave.
+// (e1,e3), (e5,e7): the lookup of lookup8 without its final re-interleave.  The two
+// eight-entry halves are merged with v_bitop3 (a full-rate operation on gfx950).
 __device__ __forceinline__ u32x4_t lookup8_pairs(uint32_t w, const Planes &P) {
   const uint32_t se = w & 0x07070707u;
   const uint32_t so = (w >> 4) & 0x07070707u;
   const uint32_t me = __builtin_amdgcn_perm(w << 12, w << 4, 0x090B080Au);
   const uint32_t mo = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
-  const uint32_t Le = bitsel(me, __builtin_amdgcn_perm(P.L[3], P.L[2], se),
-                             __builtin_amdgcn_perm(P.L[1], P.L[0], se));
-  const uint32_t He = bitsel(me, __builtin_amdgcn_perm(P.H[3], P.H[2], se),
-                             __builtin_amdgcn_perm(P.H[1], P.H[0], se));
-  const uint32_t Lo = bitsel(mo, __builtin_amdgcn_perm(P.L[3], P.L[2], so),
-                             __builtin_amdgcn_perm(P.L[1], P.L[0], so));
-  const uint32_t Ho = bitsel(mo, __builtin_amdgcn_perm(P.H[3], P.H[2], so),
-                             __builtin_amdgcn_perm(P.H[1], P.H[0], so));
+  const uint32_t Le = __builtin_amdgcn_bitop3_b32(me, __builtin_amdgcn_perm(P.L[3], P.L[2], se),
+                                                   __builtin_amdgcn_perm(P.L[1], P.L[0], se), 0xCA);
+  const uint32_t He = __builtin_amdgcn_bitop3_b32(me, __builtin_amdgcn_perm(P.H[3], P.H[2], se),
+                                                   __builtin_amdgcn_perm(P.H[1], P.H[0], se), 0xCA);
+  const uint32_t Lo = __builtin_amdgcn_bitop3_b32(mo, __builtin_amdgcn_perm(P.L[3], P.L[2], so),
+                                                   __builtin_amdgcn_perm(P.L[1], P.L[0], so), 0xCA);
+  const uint32_t Ho = __builtin_amdgcn_bitop3_b32(mo, __builtin_amdgcn_perm(P.H[3], P.H[2], so),
+                                                   __builtin_amdgcn_perm(P.H[1], P.H[0], so), 0xCA);
   u32x4_t r;
   r[0] = __builtin_amdgcn_perm(He, Le, 0x05010400u);
   r[1] = __builtin_amdgcn_perm(He, Le, 0x07030602u);
@@ -80,357 +135,588 @@ __device__ __forceinline__ u32x4_t permute8(u32x4_t d) {
   return u32x4_t{pack_lo(d[0], d[1]), pack_lo(d[2], d[3]), pack_hi(d[0], d[1]), pack_hi(d[2], d[3])};
 }
 
-// LDS of the stream kernel (one dynamic object): per wave its 16 rows x 512 bytes of
-// codes (16-byte chunk cr of row r at slot cr ^ (r & 15)), per wave 16 rows x 16
-// 8-bit block constants (or 16 fp32 constants for the type without double
-// quantization), then the staged X slice (M rows of XPITCH bytes).
-constexpr int CROW = 4 * GIT * 32;   // code bytes per row and slice (512)
-constexpr int WCODE = 16 * CROW;     // code bytes per wave (8 KB)
-constexpr int SC_BYTES = 4 * WCODE;  // 32 KB
-constexpr int sq_wave(int ct) { return ct == kConstF32 ? 1024 : 256; }  // constant bytes per wave
-int gemv_xl(int M) { return M <= 2 ? 1 : M <= 4 ? 2 : M <= 8 ? 4 : 8; }
-// staged X rows = XL * 256 * 8 / GSLICE = 2 XL (rows past M hold zeros)
-size_t gemv_lds_bytes(int M, int ct) {
-  return SC_BYTES + 4 * sq_wave(ct) + static_cast<size_t>(2 * gemv_xl(M)) * XPITCH;
+// One wave step of the weight stream: the loads of one lane's block, and its eight X
+// fragments when X is not staged in LDS.
+template <bool XLDS>
+struct StepLoads {
+  u32x4_t c0, c1;            // 32 bytes of codes
+  uint8_t q;                 // block constant: the 8-bit code (kept 8-bit: a wider type is
+                             // zero-extended where the loads are issued, waiting for them)
+  uint32_t s, o;             // group scale and offset (s: the fp32 constant of kConstF32)
+  u32x4_t x[XLDS ? 1 : 8];   // X[token][64 b + 8 u ..] (natural order)
+};
+
+// The constant loads of block b (zeros when !ok, so that the constant decodes to 0).
+template <int CT, bool XLDS>
+__device__ __forceinline__ void load_constant(const ConstRsrc &rq, uint32_t b, bool ok, StepLoads<XLDS> &st) {
+  if constexpr (CT == kConstF32) {
+    st.s = __builtin_amdgcn_raw_buffer_load_b32(rq.s, ok ? b * 4u : kOOB, 0, 0);
+    st.q = 0;
+    st.o = 0u;
+  } else {
+    st.q = __builtin_amdgcn_raw_buffer_load_b8(rq.q8, ok ? b : kOOB, 0, 0);
+    st.s = __builtin_amdgcn_raw_buffer_load_b32(rq.s, ok ? (b >> 8) * 4u : kOOB, 0, 0);
+    st.o = __builtin_amdgcn_raw_buffer_load_b32(rq.o, ok ? (b >> 8) * 4u : kOOB, 0, 0);
+  }
 }
 
-// XL: 16-byte X loads per thread (M * 128 / 256 rounded up to a power of two);
-// C8W: the rows' int8 constants are dword aligned (K % 256 == 0).
-template <int XL, bool C8W, int CT>
-__global__ __launch_bounds__(GT) void gemv_stream_kernel(GemvArgs a) {
-  constexpr int SQW = sq_wave(CT);
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  char *const sc = lds;
-  char *const sq = lds + SC_BYTES;
-  char *const sx = lds + SC_BYTES + 4 * SQW;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int N = static_cast<int>(a.w.n_rows), K = static_cast<int>(a.w.n_cols), KB = K / 64;
-  const int lora_wgs = a.r > 0 ? a.S : 0;
-  const int bid = blockIdx.x;
-  const bool lora = bid < lora_wgs;
-  const int s = lora ? bid : (bid - lora_wgs) % a.S;
-  const int rg = lora ? 0 : (bid - lora_wgs) / a.S;
-  const int k0 = s * GSLICE;
+// c' of a block from its loaded pieces: fma(c8, s, o) rounded once ([Digest]
+// "数学公式与关键细节" item 3), or the stored fp32 constant.  The int8 code is
+// sign-extended in floating point, (float)(byte ^ 0x80) - 128, which the compiler
+// cannot fold into a sign-extending load placed next to this use.
+template <int CT, bool XLDS>
+__device__ __forceinline__ float constant_of(const StepLoads<XLDS> &st) {
+  if constexpr (CT == kConstF32) return __uint_as_float(st.s);
+  if constexpr (CT == kConstDqFp8)
+    return __builtin_fmaf(e4m3_value(st.q), __uint_as_float(st.s), __uint_as_float(st.o));
+  const float c8 = static_cast<float>(static_cast<int>(st.q ^ 0x80u)) - 128.0f;
+  return __builtin_fmaf(c8, __uint_as_float(st.s), __uint_as_float(st.o));
+}
+
+// LDS layout (one dynamic object): the waves' partial sums [W][64 lanes][4] fp32, then
+// (R > 0) the workgroup's 16 rows of Bl (bf16, as stored: 16 r contiguous elements), then, when X is staged, X [M][KB][XBLK] bytes (each
+// 64-element block permuted per 8-element group, 16 bytes of padding).
+struct LdsPlan {
+  int red, bt, x, total;
+};
+__host__ __device__ inline int up16(int b) { return (b + 15) & ~15; }
+__host__ __device__ inline LdsPlan lds_plan(int W, int M, int R, int r, int KB, bool xlds) {
+  LdsPlan p;
+  p.red = 0;
+  p.bt = W * 1024;
+  p.x = p.bt + (R > 0 ? up16(32 * r) : 0);
+  p.total = p.x + (xlds ? M * KB * XBLK : 0);
+  return p;
+}
+
+// The f32x4 accumulators (this lane's) of waves 0 .. W - 1 added in wave order through
+// LDS (one barrier).  The sum is valid in wave 0 (callers let the other waves return
+// right after).
+__device__ __forceinline__ f32x4_t reduce_waves(char *red, f32x4_t acc, int W, int wave, int lane) {
+  *reinterpret_cast<f32x4_t *>(red + (wave * 64 + lane) * 16) = acc;
+  __syncthreads();
+  f32x4_t s = *reinterpret_cast<const f32x4_t *>(red + lane * 16);
+  if (wave == 0) {
+    for (int v = 1; v < W; ++v) {
+      const f32x4_t t = *reinterpret_cast<const f32x4_t *>(red + (v * 64 + lane) * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] += t[e];
+    }
+  }
+  return s;
+}
+
+// Eight bf16 of an LDS row, elements j0 .. j0 + 7 (zeros at j >= lim); `aligned`: the
+// eight sit at a 16-byte boundary.
+__device__ __forceinline__ u32x4_t lds_frag8(const uint16_t *row, int j0, int lim, bool aligned) {
+  if (aligned && j0 + 8 <= lim) return *reinterpret_cast<const u32x4_t *>(row + j0);
+  u32x4_t v;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int j = j0 + 2 * h;
+    const uint32_t lo = j < lim ? row[j] : 0u, hi = j + 1 < lim ? row[j + 1] : 0u;
+    v[h] = lo | (hi << 16);
+  }
+  return v;
+}
+
+// The LoRA wave of a workgroup: for each of its pieces p (rank tile t = p / SP, slice
+// s = p % SP of LB 64-blocks of K) the partial sums of X . A^T for ranks [16 t, 16 t + 16),
+// stored for the rank tile; the last piece of a tile to finish (an agent-scope ticket)
+// adds the SP slices in order, rounds U_s = bf16(scale * sum) and publishes it in NC
+// copies; the last tile raises every copy of the flag.  A lane (rank l % 16, group g)
+// takes block b_lo + 4 i + g of step i, as a weight wave does; X comes from the
+// workgroup's staged copy (then A is permuted like it) or from memory.
+template <bool XLDS>
+struct LoraLoads {
+  static constexpr int STEPS = XLDS ? 2 : 1;  // steps of 4 blocks per piece (LB <= 4 STEPS)
+  u32x4_t av[STEPS][8];
+  u32x4_t xv[XLDS ? 1 : STEPS][8];
+};
+
+template <bool XLDS>
+__device__ __forceinline__ LoraLoads<XLDS> lora_issue(const GemvArgs &a, int KB, int p) {
+  constexpr int STEPS = LoraLoads<XLDS>::STEPS;
+  const int lane = threadIdx.x & 63;
   const int ml = lane & 15, g = lane >> 4;
-  const int row0 = rg * GROWS + wave * 16;  // first weight row of this wave
-
-  // ---- issue every global load of the workgroup up front ----
-  // X slice, tokens < M only (16-byte chunks; columns past K read as zero)
+  const int K = KB * 64;
+  const bool tok_ok = ml < a.M;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, static_cast<uint32_t>(a.R) * K * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, static_cast<uint32_t>(a.M) * K * 2);
-  u32x4_t xs[XL];
+  const int t = p / a.SP, s = p % a.SP;
+  const int j = t * 16 + ml;  // rank (A row) of this lane's operand
+  const int b_lo = s * a.LB, b_hi = min(KB, b_lo + a.LB);
+  LoraLoads<XLDS> ll;
 #pragma unroll
-  for (int j = 0; j < XL; ++j) {
-    const int c = tid + j * GT;
-    const int m = c / (GSLICE / 8), k = k0 + (c % (GSLICE / 8)) * 8;
-    xs[j] = buf_load16(rx, (m < a.M && k < K) ? (static_cast<uint32_t>(m) * K + k) * 2 : kOOB);
-  }
-  uint32_t c8w = 0, sv[2] = {0u, 0u}, ov[2] = {0u, 0u}, cf[4] = {0u, 0u, 0u, 0u};
-  uint8_t c8b[4] = {0, 0, 0, 0};
-  int gfirst = 0;
-  {
-    // Straight-line for every workgroup (the LoRA ones read nothing: all offsets out of
-    // range), so that the compiler's waits stay exact counts.  Order: constants, then
-    // the codes block group by block group, so that decoding can follow the arrivals.
-    const int nlim = lora ? 0 : N;
-    const ConstRsrc rq = make_const_rsrc<CT>(a.w, static_cast<uint32_t>(uint64_t(N) * KB));
-    // group scale and offset: the slice of one row spans at most two groups
-    if constexpr (CT != kConstF32) {
-      const int n = row0 + ml;
-      const uint32_t bfirst = static_cast<uint32_t>(n) * KB + s * 16;
-      gfirst = static_cast<int>(bfirst >> 8);
+  for (int i = 0; i < STEPS; ++i) {
+    const int b = b_lo + 4 * i + g;
+    const bool ok = b < b_hi;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t og = n < nlim ? (bfirst / 256 + e) * 4u : kOOB;
-        sv[e] = __builtin_amdgcn_raw_buffer_load_b32(rq.s, og, 0, 0);
-        ov[e] = __builtin_amdgcn_raw_buffer_load_b32(rq.o, og, 0, 0);
-      }
+    for (int u = 0; u < 8; ++u) {
+      ll.av[i][u] = buf_load16(ra, (ok && j < a.R) ? (static_cast<uint32_t>(j) * K + b * 64 + 8 * u) * 2 : kOOB);
+      if constexpr (!XLDS)
+        ll.xv[i][u] = buf_load16(rx, (ok && tok_ok) ? (static_cast<uint32_t>(ml) * K + b * 64 + 8 * u) * 2 : kOOB);
     }
-    // 8-bit constants: lane l loads blocks s * 16 + 4 (l % 4) .. + 3 of row l / 4
-    // (fp32 constants: the same blocks, one dword each)
-    {
-      const int n = row0 + (lane >> 2);
-      const uint32_t b = static_cast<uint32_t>(n) * KB + s * 16 + 4 * (lane & 3);
-      if constexpr (CT == kConstF32) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cf[e] = __builtin_amdgcn_raw_buffer_load_b32(rq.s, n < nlim ? (b + e) * 4u : kOOB, 0, 0);
-      } else if constexpr (C8W) {
-        c8w = __builtin_amdgcn_raw_buffer_load_b32(rq.q8, n < nlim ? b : kOOB, 0, 0);
-      } else {  // rows not dword aligned: four byte loads, stored to LDS one by one
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c8b[e] = __builtin_amdgcn_raw_buffer_load_b8(rq.q8, n < nlim ? b + e : kOOB, 0, 0);
-      }
-    }
-    // codes: for block group i (blocks 4 i .. 4 i + 3 of the slice, 128 bytes per row)
-    // two 1 KB direct-to-LDS loads of 8 rows each; lane l fills slot l % 8 of row
-    // 8 h + l / 8 with the row's 16-byte chunk (l % 8) ^ f(row), f(r) = (r / 2) % 8
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.w.codes, static_cast<uint32_t>(uint64_t(N) * K / 2));
-    char *const wc = sc + wave * WCODE;
-#pragma unroll
-    for (int i = 0; i < GIT; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rl = 8 * h + (lane >> 3);
-        const int chunk = (lane & 7) ^ ((rl >> 1) & 7);
-        const int n = row0 + rl;
-        const int kbyte = s * CROW + i * 128 + chunk * 16;
-        const uint32_t off = (n < nlim && kbyte < K / 2) ? static_cast<uint32_t>(n) * (K / 2) + kbyte : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rc, (__attribute__((address_space(3))) void *)(wc + i * 2048 + h * 1024), 16, off, 0, 0, 0);
-      }
-    __builtin_amdgcn_sched_barrier(0);  // keep the issue order that the waits below count on
   }
-  // ---- stage X (permuted per 8-element group) and the int8 constants in LDS ----
-#pragma unroll
-  for (int j = 0; j < XL; ++j) {  // staged rows past M (up to the power of two) are zero
-    const int c = tid + j * GT;
-    const int m = c / (GSLICE / 8), q = c % (GSLICE / 8);
-    *reinterpret_cast<u32x4_t *>(sx + m * XPITCH + q * 16) = permute8(xs[j]);
-  }
-  if constexpr (CT == kConstF32) {
-    *reinterpret_cast<u32x4_t *>(sq + wave * SQW + lane * 16) = u32x4_t{cf[0], cf[1], cf[2], cf[3]};
-  } else if constexpr (C8W) {
-    *reinterpret_cast<uint32_t *>(sq + wave * 256 + lane * 4) = c8w;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sq[wave * 256 + lane * 4 + e] = static_cast<char>(c8b[e]);
-  }
-  // the X slice is shared by the four waves; the codes are per wave and are waited
-  // for block group by block group below
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  return ll;
+}
 
-  const int xrow = ml < a.M ? ml : a.M - 1;  // tokens past M only feed unused outputs
-  auto xfrag = [&](int kk) {  // B operand: token xrow, 8 elements at slice column kk
-    return *reinterpret_cast<const u32x4_t *>(sx + xrow * XPITCH + kk * 2);
-  };
-
-  if (!lora) {
-    // ---- weight stream: lane = (row ml of this wave's 16, lane group g) ----
-    const char *const wc = sc + wave * WCODE + ml * 128;
-    const u32x4_t q8 = *reinterpret_cast<const u32x4_t *>(sq + wave * SQW + ml * (SQW / 16));
-    const int n = row0 + ml;
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+template <bool XLDS>
+__device__ void lora_finish(const GemvArgs &a, const char *sx, int KB, int p, const LoraLoads<XLDS> &ll) {
+  constexpr int STEPS = LoraLoads<XLDS>::STEPS;
+  const int lane = threadIdx.x & 63;
+  const int ml = lane & 15, g = lane >> 4;
+  const bool tok_ok = ml < a.M;
+  const int tok = tok_ok ? ml : 0;
+  const uint32_t pu_bytes = static_cast<uint32_t>(a.PT) * a.SP * a.M * 64;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.PU, pu_bytes);
+  const int RP = 16 * a.PT;
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.Uc, static_cast<uint32_t>(a.NC) * a.UCE * 2);
+  const int t = p / a.SP, s = p % a.SP;
+  const int b_lo = s * a.LB, b_hi = min(KB, b_lo + a.LB);
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < GIT; ++i) {
-      // block group i of this wave has landed: 2 (GIT - 1 - i) code loads remain
-      static_assert(GIT == 4, "the waits below count two code loads per block group of four");
-      if (i == 0) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-      if (i == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      if (i == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-      if (i == 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      const int blk = 4 * i + g;  // block of the slice
-      u32x4_t code[2];
+  for (int i = 0; i < STEPS; ++i) {
+    const int b = b_lo + 4 * i + g;
+    const bool ok = b < b_hi;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        code[h] = *reinterpret_cast<const u32x4_t *>(wc + i * 2048 + (((2 * g + h) ^ ((ml >> 1) & 7)) << 4));
-      const int kk = blk * 64;
-      u32x4_t xb[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) xb[t] = xfrag(kk + 8 * t);
-      float cval;
-      if constexpr (CT == kConstF32) {  // fp32 constant blk of the row's 16
-        cval = *reinterpret_cast<const float *>(sq + wave * SQW + ml * 64 + blk * 4);
-      } else {  // constant of block blk: byte g of dword i of the row's 16 bytes
-        const int gi = static_cast<int>((static_cast<uint32_t>(n) * KB + s * 16 + blk) >> 8) - gfirst;
-        const ConstRaw cr{(q8[i] >> (8 * g)) & 0xFFu, gi ? sv[1] : sv[0], gi ? ov[1] : ov[0]};
-        cval = const_value<CT>(cr);
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (XLDS) {
+        // the staged X is permuted per 8-element group: permute A the same way
+        const u32x4_t x = *reinterpret_cast<const u32x4_t *>(sx + (tok * KB + (ok ? b : 0)) * XBLK + u * 16);
+        acc = mfma16x16x32(permute8(ll.av[i][u]), x, acc);
+      } else {
+        acc = mfma16x16x32(ll.av[i][u], ll.xv[i][u], acc);
       }
-      const Planes pl = make_planes(cval, a.lvl);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc = mfma16x16x32(lookup8_pairs(code[t >> 2][t & 3], pl), xb[t], acc);
     }
-    // lane holds rows 4 g + e of the wave's 16, token ml
-    if (ml < a.M) {
+  }
+  // lane: token ml, ranks 16 t + 4 g + e; the piece's partial sums, then the ticket once
+  // they have completed (agent-coherent loads of any workgroup then see them)
+  if (tok_ok) store16_sc1(rp, (((t * a.SP + s) * a.M + ml) * 16 + 4 * g) * 4, __builtin_bit_cast(u32x4_t, acc));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint32_t ticket = 0;
+  if (lane == 0)
+    ticket = __hip_atomic_fetch_add(a.sync + kSyncTile0 + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  ticket = __builtin_amdgcn_readfirstlane(ticket);
+  if (ticket != static_cast<uint32_t>(a.SP - 1)) return;
+  // the last piece of the tile: add the slices in order
+  float u4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < a.SP; s0 += 8) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[i] = load16_sc1(rp, (tok_ok && s0 + i < a.SP) ? (((t * a.SP + s0 + i) * a.M + ml) * 16 + 4 * g) * 4 : kOOB);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u4[e] += __uint_as_float(v[i][e]);
+  }
+  if (tok_ok) {
+    uint16_t ub[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ub[e] = to_bf16(a.scale * u4[e]);
+    const u32x2_t uv{ub[0] | (static_cast<uint32_t>(ub[1]) << 16), ub[2] | (static_cast<uint32_t>(ub[3]) << 16)};
+    for (int c = 0; c < a.NC; ++c) store8_sc1(ru, (c * a.UCE + ml * RP + t * 16 + 4 * g) * 2, uv);
+    if (a.U_saved) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int nn = row0 + 4 * g + e;
-        if (nn < N) a.P[(static_cast<int64_t>(s) * N + nn) * a.M + ml] = acc[e];
-      }
-    }
-  } else {
-    // ---- LoRA down-projection partials over this slice: wave w takes rank tiles w, w + 4, ...
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, static_cast<uint32_t>(a.r) * K * 2);
-    for (int jt = wave; jt * 16 < a.r; jt += 4) {
-      const int j = jt * 16 + ml;
-      const bool jok = j < a.r;
-      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-      for (int st = 0; st < GSLICE / 32; ++st) {
-        const int kk = st * 32 + 8 * g;
-        const int k = k0 + kk;
-        const u32x4_t av = buf_load16(ra, (jok && k < K) ? (static_cast<uint32_t>(j) * K + k) * 2 : kOOB);
-        acc = mfma16x16x32(permute8(av), xfrag(kk), acc);
-      }
-      if (ml < a.M) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int jj = jt * 16 + 4 * g + e;
-          if (jj < a.r) a.UP[(static_cast<int64_t>(s) * a.M + ml) * a.r + jj] = acc[e];
-        }
+        const int jj = t * 16 + 4 * g + e;
+        if (jj < a.R) a.U_saved[ml * a.R + jj] = ub[e];
       }
     }
   }
-}
-
-// Sum of x[0], x[stride], ..., x[(S - 1) stride] in that order, with the loads of
-// eight terms in flight at a time (the additions stay in slice order).
-__device__ __forceinline__ float ordered_sum(const float *__restrict__ x, int64_t stride, int S) {
-  float sum = 0.0f;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (s0 + e < S) ? x[(s0 + e) * stride] : 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (s0 + e < S) sum += v[e];
+  // count the tile done once every store of this wave (U_s, the reset counter) has
+  // completed; the last tile raises the flags
+  if (lane == 0) __hip_atomic_store(a.sync + kSyncTile0 + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint32_t tiles_done = 0;
+  if (a.PT > 1) {
+    if (lane == 0)
+      tiles_done = __hip_atomic_fetch_add(a.sync + kSyncTiles, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tiles_done = __builtin_amdgcn_readfirstlane(tiles_done);
   }
-  return sum;
+  if (tiles_done == static_cast<uint32_t>(a.PT - 1)) {
+    // every rank tile is published: raise each workgroup's flag (the counter of done
+    // tiles has no other user left in this call)
+    if (a.PT > 1 && lane == 0) __hip_atomic_store(a.sync + kSyncTiles, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int w = lane; w < static_cast<int>(gridDim.x); w += 64)
+      __hip_atomic_store(a.sync + (kFlagBase + w * kFlagStride) / 4, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
-constexpr int FT = 64;  // finalize threads per workgroup
+template <int CT, bool XLDS, bool MULTI>
+__global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int D = XLDS ? 4 : 2;  // steps whose loads are in flight (the register ring)
+  const int W = a.W;  // weight waves; wave W (R > 0) is the LoRA wave
+  const int N = static_cast<int>(a.w.n_rows), KB = static_cast<int>(a.w.n_cols / 64), K = KB * 64;
+  const LdsPlan lp = lds_plan(W, a.M, a.R, a.r, KB, XLDS);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ml = lane & 15, g = lane >> 4;
+  const int tile = blockIdx.x;
+  const int n0 = tile * 16;
+  const int n = n0 + ml;  // weight row of this lane's operand
+  const bool row_ok = n < N;
+  const int tok = ml < a.M ? ml : 0;
+  const bool tok_ok = ml < a.M;
+  const int kb0 = (KB * wave) / W, kb1 = (KB * (wave + 1)) / W;
+  const int Tw = (kb1 - kb0 + 3) / 4;  // this wave's steps (at most T)
 
-// Y[m, n] = bf16(sum_s P[s][n][m] + sum_j U_s[m, q r + j] Bl[n, j]); U_s = bf16(scale * sum_s UP)
-// over the R stacked ranks; q = n / part_rows is the part of a fused linear (0 for one).
-__global__ __launch_bounds__(FT) void gemv_finalize_kernel(const float *__restrict__ P,
-                                                           const float *__restrict__ UP, int S, int N,
-                                                           int M, const uint16_t *__restrict__ Bl,
-                                                           int r, int R, int part_rows, float scale,
-                                                           uint16_t *__restrict__ Y,
-                                                           uint16_t *__restrict__ U_saved) {
-  __shared__ float us[GMAXM * kMaxRank];
-  if (R > 0) {
-    for (int e = threadIdx.x; e < M * R; e += FT) {
-      const int m = e / R, j = e % R;
-      const uint16_t u = to_bf16(scale * ordered_sum(UP + m * R + j, static_cast<int64_t>(M) * R, S));
-      us[e] = bf16_to_f32(u);
-      if (U_saved && blockIdx.x == 0) U_saved[m * R + j] = u;
+  const uint32_t n_blocks = static_cast<uint32_t>(uint64_t(N) * KB);
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.w.codes, static_cast<uint32_t>(uint64_t(N) * K / 2));
+  const ConstRsrc rq = make_const_rsrc<CT>(a.w, n_blocks);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, static_cast<uint32_t>(a.M) * K * 2);
+  const uint32_t row_code = static_cast<uint32_t>(n) * (K / 2);
+  const uint32_t row_blk = static_cast<uint32_t>(n) * KB;
+  char *const sx = lds + lp.x;
+  uint16_t *const sb = reinterpret_cast<uint16_t *>(lds + lp.bt);
+
+  // 16-byte pieces staged into LDS: X (when staged) and the 16 rows of Bl (R > 0; a
+  // contiguous 32 r bytes; Bl is read to its last element's whole dword).  They are
+  // staged before the first weight load is issued: a load issued behind the weight
+  // stream of the whole chip would arrive only when that stream has drained.
+  if (wave == W) {
+    // The LoRA wave: it takes no part in the staging and issues the loads of its first
+    // piece at once, ahead of the weight stream.  It passes the same two barriers as the
+    // weight waves (the staging barrier and the one of the final reduction).
+    const int npieces = a.PT * a.SP;
+    LoraLoads<XLDS> ll;
+    if (static_cast<int>(blockIdx.x) < npieces) ll = lora_issue<XLDS>(a, KB, blockIdx.x);
+    __syncthreads();
+    if (static_cast<int>(blockIdx.x) < npieces) lora_finish<XLDS>(a, lds + lp.x, KB, blockIdx.x, ll);
+    if constexpr (MULTI) {
+      // more pieces than workgroups (few output rows): the later ones one after another
+      // (a separate instantiation: the loop costs the kernel about 35 registers)
+      for (int p = blockIdx.x + gridDim.x; p < npieces; p += gridDim.x) {
+        const LoraLoads<XLDS> lp2 = lora_issue<XLDS>(a, KB, p);
+        lora_finish<XLDS>(a, lds + lp.x, KB, p, lp2);
+      }
     }
     __syncthreads();
+    return;
   }
-  const int n = blockIdx.x * FT + threadIdx.x;
-  if (n >= N) return;
-  const uint16_t *brow = Bl + static_cast<int64_t>(n) * r;
-  const float *uq = us + (part_rows > 0 ? (n / part_rows) * r : 0);
-  for (int m = 0; m < M; ++m) {
-    float y = ordered_sum(P + static_cast<int64_t>(n) * M + m, static_cast<int64_t>(N) * M, S);
-    if ((r & 7) == 0) {
-      for (int j0 = 0; j0 < r; j0 += 8) {
-        const u32x4_t bv = *reinterpret_cast<const u32x4_t *>(brow + j0);
+  const int nthr = 64 * W, tid = threadIdx.x;
+  const int xpieces = XLDS ? a.M * KB * 8 : 0;
+  const int bpieces = a.R > 0 ? 2 * a.r : 0;
+  const uint32_t b_bytes = static_cast<uint32_t>((uint64_t(N) * a.r * 2 + 3) & ~uint64_t(3));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.Bl, b_bytes);
+  const uint32_t b_base = static_cast<uint32_t>(n0) * a.r * 2;
+  auto x_lds = [&](int c) { return sx + (c / (KB * 8) * KB + (c % (KB * 8)) / 8) * XBLK + (c % 8) * 16; };
+  u32x4_t xs[2], bs[2];
+  if constexpr (XLDS) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y = __builtin_fmaf(uq[m * R + j0 + 2 * e], bf16_lo(bv[e]), y);
-          y = __builtin_fmaf(uq[m * R + j0 + 2 * e + 1], bf16_hi(bv[e]), y);
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * nthr;
+      xs[i] = buf_load16(rx, c < xpieces ? static_cast<uint32_t>(c) * 16 : kOOB);
+    }
+  }
+  auto load_b = [&](int c) {
+    const uint32_t off = b_base + static_cast<uint32_t>(c) * 16;
+    if (c >= bpieces || off >= b_bytes) return u32x4_t{0u, 0u, 0u, 0u};
+    if (off + 16 <= b_bytes) return buf_load16(rb, off);
+    // the piece that runs past the end of Bl: dword by dword (each past the end reads 0)
+    u32x4_t v;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) v[h] = buf_load4(rb, off + 4 * h);
+    return v;
+  };
+  if (bpieces > 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) bs[i] = load_b(tid + i * nthr);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the loads of step t (blocks past the wave's range, or rows past N, read zeros: their
+  // constant decodes to c' = 0, so they add nothing)
+  auto load = [&](int t) {
+    StepLoads<XLDS> s;
+    const int b = kb0 + 4 * t + g;
+    const bool ok = row_ok && b < kb1;
+    const uint32_t off = ok ? row_code + b * 32 : kOOB;
+    s.c0 = buf_load16(rc, off);
+    s.c1 = buf_load16(rc, ok ? off + 16 : kOOB);
+    load_constant<CT, XLDS>(rq, row_blk + b, ok, s);
+    if constexpr (!XLDS) {
+      const uint32_t xo = (static_cast<uint32_t>(tok) * K + b * 64) * 2;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s.x[u] = buf_load16(rx, (tok_ok && b < kb1) ? xo + u * 16 : kOOB);
+    }
+    return s;
+  };
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const StepLoads<XLDS> &s, int t) {
+    const int b = kb0 + 4 * t + g;
+    const Planes pl = make_planes(constant_of<CT, XLDS>(s), a.lvl);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t cw = u < 4 ? s.c0[u] : s.c1[u - 4];
+      u32x4_t xv;
+      if constexpr (XLDS)
+        xv = *reinterpret_cast<const u32x4_t *>(sx + (tok * KB + (b < kb1 ? b : kb0)) * XBLK + u * 16);
+      else
+        xv = permute8(s.x[u]);
+      acc = mfma16x16x32(lookup8_pairs(cw, pl), xv, acc);
+    }
+  };
+
+  // Each step's loads are issued together and in step order, after the staging barrier
+  // and in the loop alike (the scheduling barriers keep the compiler from interleaving two steps'
+  // loads), so every path into the loop head has the same D steps in flight and the
+  // waits the compiler derives leave the later steps' loads in flight.
+  if constexpr (XLDS) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * nthr;
+      if (c < xpieces) *reinterpret_cast<u32x4_t *>(x_lds(c)) = permute8(xs[i]);
+    }
+    for (int c = tid + 2 * nthr; c < xpieces; c += nthr)
+      *reinterpret_cast<u32x4_t *>(x_lds(c)) = permute8(buf_load16(rx, static_cast<uint32_t>(c) * 16));
+  }
+  if (bpieces > 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * nthr;
+      if (c < bpieces) *reinterpret_cast<u32x4_t *>(sb + 8 * c) = bs[i];
+    }
+    for (int c = tid + 2 * nthr; c < bpieces; c += nthr) *reinterpret_cast<u32x4_t *>(sb + 8 * c) = load_b(c);
+  }
+  __syncthreads();
+  StepLoads<XLDS> st[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    st[j] = load(j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  int t0 = 0;
+  for (; t0 + D < Tw; t0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      compute(st[j], t0 + j);
+      __builtin_amdgcn_sched_barrier(0);
+      st[j] = load(t0 + j + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (t0 + j < Tw) compute(st[j], t0 + j);
+
+  f32x4_t y = reduce_waves(lds + lp.red, acc, W, wave, lane);
+  if (wave != 0) return;
+  // lane: token ml, weight rows n0 + 4 g + e
+
+  if (a.R > 0) {
+    // U_s from the LoRA waves: poll this workgroup's flag (and clear it for the next
+    // call), then read this workgroup's copy of U_s
+    uint32_t *flag = a.sync + (kFlagBase + blockIdx.x * kFlagStride) / 4;
+    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+      if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int RP = 16 * a.PT;
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.Uc, static_cast<uint32_t>(a.NC) * a.UCE * 2);
+    // Y += U_s[:, q r : q r + r] . Bl[rows]^T on the same accumulator: rows (the A
+    // operand) from the staged Bl tile, tokens (the B operand) from U_s
+    const int q = a.part_rows > 0 ? n0 / a.part_rows : 0;
+    const bool aligned = (a.r & 7) == 0;
+    const uint16_t *brow = sb + ml * a.r;
+    const uint32_t ubase = static_cast<uint32_t>((blockIdx.x % a.NC) * a.UCE + tok * RP + q * a.r);
+    for (int c = 0; c < a.r; c += 32) {
+      const int j0 = c + 8 * g;
+      const u32x4_t bf = lds_frag8(brow, j0, a.r, aligned);
+      u32x4_t uf = u32x4_t{0u, 0u, 0u, 0u};
+      if (tok_ok && j0 < a.r) {
+        if (aligned) {
+          uf = load16_sc1(ru, (ubase + j0) * 2);
+        } else {
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const int j = j0 + 2 * h;
+            const uint32_t lo = j < a.r ? __builtin_amdgcn_raw_buffer_load_b16(ru, (ubase + j) * 2, 0, kSC1) : 0u;
+            const uint32_t hi =
+                j + 1 < a.r ? __builtin_amdgcn_raw_buffer_load_b16(ru, (ubase + j + 1) * 2, 0, kSC1) : 0u;
+            uf[h] = lo | (hi << 16);
+          }
         }
       }
-    } else {
-      for (int j = 0; j < r; ++j) y = __builtin_fmaf(uq[m * R + j], bf16_to_f32(brow[j]), y);
+      y = mfma16x16x32(bf, uf, y);
     }
-    Y[static_cast<int64_t>(m) * N + n] = to_bf16(y);
+  }
+  if (tok_ok) {
+    const int nb = n0 + 4 * g;
+    uint16_t *yr = a.Y + static_cast<int64_t>(ml) * N;
+    if (nb + 3 < N && (N & 3) == 0) {
+      *reinterpret_cast<u32x2_t *>(yr + nb) = u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (nb + e < N) yr[nb + e] = to_bf16(y[e]);
+    }
   }
 }
 
-}  // namespace
-
-int gemv_slices(int64_t K) { return static_cast<int>((K + GSLICE - 1) / GSLICE); }
-
-namespace {
-size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
-float *gemv_p(void *ws) { return static_cast<float *>(ws); }
-float *gemv_up(void *ws, int64_t M, int64_t K, int64_t N) {
-  return reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                   up256(size_t(gemv_slices(K)) * size_t(N) * size_t(M) * 4));
+// Weight waves per workgroup (W) and steps per weight wave (T).  A launch of G tiles puts
+// at most c = ceil(G / 256) workgroups on one CU; its busiest SIMD runs ceil(c W / 4)
+// weight waves of T = ceil(ceil(KB / W) / 4) steps each, the decode time of the launch.
+// W minimises that product (a lone wave per SIMD counts 30% more: it cannot hide its own
+// dependency chains), within the waves a CU holds at once (`max_cu_waves`, counting the
+// LoRA wave of each workgroup, `extra`), preferring fewer steps.
+struct GemvShape {
+  int W, T;
+};
+GemvShape gemv_shape(int64_t N, int64_t K, int max_cu_waves, int extra) {
+  const int64_t tiles = (N + 15) / 16, KB = K / 64;
+  const int64_t c = (tiles + 255) / 256;
+  GemvShape best{1, static_cast<int>((KB + 3) / 4)};
+  double best_cost = 1e30;
+  for (int W = 1; W + extra <= kMaxWaves; ++W) {
+    if (W > 1 && (c * (W + extra) > max_cu_waves || W > KB)) break;
+    const int64_t T = ((KB + W - 1) / W + 3) / 4;
+    const int64_t per_simd = (c * W + 3) / 4;
+    const double cost = double(per_simd * T) * (per_simd == 1 ? 1.3 : 1.0);
+    if (cost < best_cost - 1e-9 || (cost < best_cost + 1e-9 && T < best.T)) {
+      best_cost = cost;
+      best = {W, static_cast<int>(T)};
+    }
+  }
+  return best;
 }
+
+// LDS bytes a main workgroup may use for staged X: a share of the 160 KB of a CU among
+// the workgroups that one round of the grid puts on it.
+int xlds_budget(int64_t N) {
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t per_cu = (tiles + 255) / 256;
+  const int64_t b = (160 * 1024) / (per_cu < 1 ? 1 : per_cu);
+  return static_cast<int>(b > 128 * 1024 ? 128 * 1024 : b);
+}
+
+// The launch configuration: shape, whether X is staged in LDS, LDS bytes, and the LoRA
+// pieces: about 16 slices of LB 64-blocks per rank tile (LB at most 8 with X staged,
+// 4 without: the blocks whose loads a LoRA wave keeps in flight at once).
+struct GemvPlan {
+  GemvShape sh;
+  bool xlds;
+  int lds_bytes;
+  int LB, SP;
+};
+// Depends on (M, K, N, R) alone, so that the workspace size is known before the call
+// (the Bl tile is taken at its largest, r = R, for the choice of staging X).
+GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int R) {
+  const int KB = static_cast<int>(K / 64);
+  const int extra = R > 0 ? 1 : 0;
+  GemvPlan p;
+  // staged X: about 100 VGPRs (5 waves per SIMD); X from memory: about 130 (4)
+  p.sh = gemv_shape(N, K, 20, extra);
+  p.xlds = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, true).total <= xlds_budget(N);
+  if (!p.xlds) p.sh = gemv_shape(N, K, 16, extra);
+  p.lds_bytes = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, p.xlds).total;
+  const int lb_max = p.xlds ? 8 : 4;
+  p.LB = (KB + 15) / 16;
+  if (p.LB > lb_max) p.LB = lb_max;
+  p.SP = (KB + p.LB - 1) / p.LB;
+  return p;
+}
+
+size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Copies of U_s [M][16 PT] bf16 published by the LoRA waves.
+int gemv_u_copies(int64_t M, int R) {
+  const size_t ub = static_cast<size_t>(M) * ((R + 15) / 16) * 32;
+  if (ub == 0) return 1;
+  const size_t c = kUCopyBudget / ub;
+  return static_cast<int>(c < 1 ? 1 : c > kMaxUCopies ? kMaxUCopies : c);
+}
+
 }  // namespace
 
+// Layout: the counter / flag header, the NC copies of U_s, the LoRA partial sums.
 size_t gemv_workspace(int64_t M, int64_t K, int64_t N, int r) {
-  const size_t S = static_cast<size_t>(gemv_slices(K));
-  return up256(S * size_t(N) * size_t(M) * 4) + up256(S * size_t(M) * size_t(r) * 4);
+  const size_t PT = static_cast<size_t>((r + 15) / 16);
+  const size_t SP = static_cast<size_t>(gemv_plan(M, K, N, r).SP);
+  const size_t NC = static_cast<size_t>(gemv_u_copies(M, r));
+  return kGemvSyncBytes + NC * up256(static_cast<size_t>(M) * PT * 16 * 2) + up256(PT * SP * M * 16 * 4);
 }
 
 bool gemv_supported(const WeightView &w, int64_t M, int r) {
   const int64_t N = w.n_rows, K = w.n_cols;
-  return M >= 1 && M <= GMAXM && r >= 0 && r <= kMaxRank && N <= 0x7fffffff &&
+  return gemv_shape_ok(M, N) && M <= GMAXM && r >= 0 && r <= kMaxRank && (N + 15) / 16 <= kMaxFlagWGs &&
          uint64_t(N) * K / 2 <= 0xFFFFFFF0ull && uint64_t(M) * K * 2 <= 0xFFFFFFF0ull &&
-         uint64_t(r) * K * 2 <= 0xFFFFFFF0ull;
+         uint64_t(r) * K * 2 <= 0xFFFFFFF0ull && uint64_t(N) * (K / 64) <= 0xFFFFFFF0ull &&
+         uint64_t(N) * r * 2 + 4 <= 0xFFFFFFF0ull;
 }
 
 namespace {
-// Dynamic LDS above 64 KB (M > 8) has to be allowed once per kernel instantiation
-// (and per device); the flag is per instantiation and thread-safe.
-template <int XL, bool C8W, int CT>
-hipError_t allow_lds() {
-  static std::once_flag once[64];
-  static hipError_t err[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::call_once(once[dev], [&] {
-    err[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_stream_kernel<XL, C8W, CT>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   static_cast<int>(gemv_lds_bytes(GMAXM, CT)));
-  });
-  return err[dev];
-}
-
-template <int XL, bool C8W, int CT>
-hipError_t go_stream(const GemvArgs &a, unsigned grid, hipStream_t stream) {
-  if (XL == 8) {
-    const hipError_t e = allow_lds<XL, C8W, CT>();
-    if (e != hipSuccess) return e;
+template <int CT, bool XLDS, bool MULTI>
+hipError_t go_gemv1(const GemvArgs &a, int lds_bytes, hipStream_t stream) {
+  if (lds_bytes > 64 * 1024) {
+    static std::once_flag once[64];
+    static hipError_t err[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [&] {
+      err[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_kernel<CT, XLDS, MULTI>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    });
+    if (err[dev] != hipSuccess) return err[dev];
   }
-  hipLaunchKernelGGL((gemv_stream_kernel<XL, C8W, CT>), dim3(grid), dim3(GT), gemv_lds_bytes(a.M, CT), stream, a);
+  hipLaunchKernelGGL((gemv_kernel<CT, XLDS, MULTI>), dim3(static_cast<unsigned>(a.G)), dim3(64 * (a.W + (a.R > 0 ? 1 : 0))),
+                     static_cast<size_t>(lds_bytes), stream, a);
   return hipGetLastError();
 }
-
-template <int CT>
-hipError_t launch_stream(const GemvArgs &a, unsigned grid, bool c8w, hipStream_t stream) {
-  switch (gemv_xl(a.M) * 2 + (c8w ? 1 : 0)) {
-    case 3: return go_stream<1, true, CT>(a, grid, stream);
-    case 2: return go_stream<1, false, CT>(a, grid, stream);
-    case 5: return go_stream<2, true, CT>(a, grid, stream);
-    case 4: return go_stream<2, false, CT>(a, grid, stream);
-    case 9: return go_stream<4, true, CT>(a, grid, stream);
-    case 8: return go_stream<4, false, CT>(a, grid, stream);
-    case 17: return go_stream<8, true, CT>(a, grid, stream);
-    default: return go_stream<8, false, CT>(a, grid, stream);
-  }
+template <int CT, bool XLDS>
+hipError_t go_gemv(const GemvArgs &a, int lds_bytes, hipStream_t stream) {
+  return a.PT * a.SP > a.G ? go_gemv1<CT, XLDS, true>(a, lds_bytes, stream)
+                           : go_gemv1<CT, XLDS, false>(a, lds_bytes, stream);
 }
 }  // namespace
 
-hipError_t launch_gemv_stream(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *A,
-                              int r, void *ws, hipStream_t stream) {
-  if (!gemv_supported(w, M, r)) return hipErrorInvalidValue;
+hipError_t launch_gemv(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *A, int R,
+                       const uint16_t *Bl, int r, int64_t part_rows, float scale, uint16_t *Y,
+                       uint16_t *U_saved, void *ws, hipStream_t stream) {
+  if (!gemv_supported(w, M, R) || R < r || (part_rows > 0 && (w.n_rows % part_rows != 0 || part_rows % 16 != 0)))
+    return hipErrorInvalidValue;
   const int64_t N = w.n_rows, K = w.n_cols;
+  const GemvPlan p = gemv_plan(M, K, N, R);
   GemvArgs a;
   a.w = w;
   a.X = X;
   a.A = A;
+  a.Bl = Bl;
+  a.Y = Y;
+  a.U_saved = U_saved;
+  a.sync = static_cast<uint32_t *>(ws);
+  a.PT = (R + 15) / 16;
+  a.NC = gemv_u_copies(M, R);
+  a.UCE = static_cast<int>(up256(size_t(M) * a.PT * 16 * 2) / 2);
+  a.Uc = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + kGemvSyncBytes);
+  a.PU = reinterpret_cast<float *>(static_cast<char *>(ws) + kGemvSyncBytes + size_t(a.NC) * a.UCE * 2);
+  a.scale = scale;
   a.M = static_cast<int>(M);
+  a.R = R;
   a.r = r;
-  a.S = gemv_slices(K);
-  a.P = gemv_p(ws);
-  a.UP = gemv_up(ws, M, K, N);
+  a.part_rows = static_cast<int>(part_rows);
+  a.W = p.sh.W;
+  a.T = p.sh.T;
+  a.LB = p.LB;
+  a.SP = R > 0 ? p.SP : 0;
+  a.G = static_cast<int>((N + 15) / 16);
   a.lvl = level_table(w.quant_type);
-  const unsigned groups = static_cast<unsigned>((N + GROWS - 1) / GROWS);
-  const unsigned grid = groups * static_cast<unsigned>(a.S) + (r > 0 ? static_cast<unsigned>(a.S) : 0u);
-  const bool c8w = (K / 64) % 4 == 0;
   switch (w.const_type) {
-    case kConstDqInt8: return launch_stream<kConstDqInt8>(a, grid, c8w, stream);
-    case kConstDqFp8: return launch_stream<kConstDqFp8>(a, grid, c8w, stream);
-    case kConstF32: return launch_stream<kConstF32>(a, grid, c8w, stream);
+    case kConstDqInt8:
+      return p.xlds ? go_gemv<kConstDqInt8, true>(a, p.lds_bytes, stream)
+                    : go_gemv<kConstDqInt8, false>(a, p.lds_bytes, stream);
+    case kConstDqFp8:
+      return p.xlds ? go_gemv<kConstDqFp8, true>(a, p.lds_bytes, stream)
+                    : go_gemv<kConstDqFp8, false>(a, p.lds_bytes, stream);
+    case kConstF32:
+      return p.xlds ? go_gemv<kConstF32, true>(a, p.lds_bytes, stream)
+                    : go_gemv<kConstF32, false>(a, p.lds_bytes, stream);
     default: return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_gemv_finalize(const WeightView &w, int64_t M, const uint16_t *Bl, int r, int R,
-                                int64_t part_rows, float scale, uint16_t *Y, uint16_t *U_saved,
-                                void *ws, hipStream_t stream) {
-  if (!gemv_supported(w, M, R) || R < r || (part_rows > 0 && w.n_rows % part_rows != 0))
-    return hipErrorInvalidValue;
-  const int64_t N = w.n_rows, K = w.n_cols;
-  hipLaunchKernelGGL(gemv_finalize_kernel, dim3(static_cast<unsigned>((N + FT - 1) / FT)), dim3(FT), 0,
-                     stream, gemv_p(ws), gemv_up(ws, M, K, N), gemv_slices(K), static_cast<int>(N),
-                     static_cast<int>(M), Bl, r, R, static_cast<int>(part_rows), scale, Y, U_saved);
-  return hipGetLastError();
 }
 
 }  // namespace qlora

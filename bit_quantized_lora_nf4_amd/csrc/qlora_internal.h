@@ -11,6 +11,9 @@ constexpr int kBlock = 64;     // weights per first-level block
 constexpr int kGroup = 256;    // block constants per double-quantization group
 constexpr int kBuckets = 129;  // quantizer bucket table entries (x in [-1, 1])
 constexpr int kMaxRank = 256;  // largest LoRA rank
+// Bytes at the start of every workspace layout reserved for the small-M forward's
+// cross-workgroup counters; no other kernel writes them.
+constexpr size_t kGemvSyncBytes = 256 + 4096 * 16;  // QLORA_WORKSPACE_HEADER_BYTES
 
 // Level tables of the 4-bit codes and encodings of the block constants (the values
 // of the weight descriptor's quant_type and const_type).
@@ -115,21 +118,20 @@ bool gemm_supported(const WeightView &w, int64_t M, int r);
 hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *U,
                            int ldu, const uint16_t *Bl, int r, int64_t part_rows, uint16_t *Y,
                            hipStream_t stream);
-// Small-M forward (M <= 16) in two launches sharing `ws` (gemv_workspace bytes):
-// the weight stream with the LoRA down-projection partials, then the finalize that
-// forms U_s = bf16(scale X A^T) (written to U_saved if not NULL) and
-// Y = bf16(X W'^T + U_s Bl^T).
-int gemv_slices(int64_t K);
+// Small-M forward (M <= 16) in one launch: Y = bf16(X W'^T + U_s Bl^T) and
+// U_s = bf16(scale X A^T) (written to U_saved if not NULL) over the R stacked ranks of
+// A; output row n uses U_s columns [q r, q r + r), q = n / part_rows (part_rows = 0:
+// one linear, R = r).  `ws` holds gemv_workspace bytes: a kGemvSyncBytes header of
+// counters and flags that must be zero when the call starts (every call leaves it
+// zero), then copies of U_s and the partial sums of the down-projection.
+// The small-M forward runs for M <= 16 and up to 4096 tiles of 16 output rows (one flag
+// word per workgroup in the header); other shapes take the fused GEMM.
+inline bool gemv_shape_ok(int64_t M, int64_t N) { return M >= 1 && M <= 16 && (N + 15) / 16 <= 4096; }
 size_t gemv_workspace(int64_t M, int64_t K, int64_t N, int r);
 bool gemv_supported(const WeightView &w, int64_t M, int r);
-hipError_t launch_gemv_stream(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *A,
-                              int r, void *ws, hipStream_t stream);
-// The finalize of fused linears: the stream kernel ran with the stacked rank R;
-// output row n uses U_s columns [q r, q r + r), q = n / part_rows (part_rows = 0: one
-// linear, R = r).  U_saved is [M, R].
-hipError_t launch_gemv_finalize(const WeightView &w, int64_t M, const uint16_t *Bl, int r, int R,
-                                int64_t part_rows, float scale, uint16_t *Y, uint16_t *U_saved,
-                                void *ws, hipStream_t stream);
+hipError_t launch_gemv(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *A, int R,
+                       const uint16_t *Bl, int r, int64_t part_rows, float scale, uint16_t *Y,
+                       uint16_t *U_saved, void *ws, hipStream_t stream);
 // dX[M, K] = bf16(dY . W' + V . At^T)  (V [M, r], At [K, r]); r may be 0.
 hipError_t launch_gemm_dx(const WeightView &w, const uint16_t *dY, int64_t M, const uint16_t *V,
                           const uint16_t *At, int r, uint16_t *dX, hipStream_t stream);

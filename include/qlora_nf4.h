@@ -22,6 +22,12 @@
  *     aligned.  The library never allocates or frees memory; scratch memory
  *     comes from the caller's workspace (qlora_linear_fwd_noalloc alone uses a
  *     fixed scratch array of the library instead).
+ *   - Workspaces: the first QLORA_WORKSPACE_HEADER_BYTES bytes of every
+ *     workspace hold counters and flags that the small-M forward's workgroups
+ *     use to hand U_s to each other.  They must be zero when a workspace is
+ *     first used (clear it once after allocating); every call leaves them
+ *     zero, and no other call writes them, so one workspace can serve calls of
+ *     any shape.  Calls that share a workspace must not overlap.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Each call checks
  *     its arguments on the host, then enqueues its kernels asynchronously on
  *     `stream` and returns.  Kernel faults surface at the caller's next
@@ -179,8 +185,10 @@ int qlora_dequantize(const qlora_nf4_weight *w, void *out, int out_dtype, void *
  * X bf16 [M, K]; A bf16 [r, K]; B bf16 [N, r]; Y bf16 [M, N].
  * U_saved (nullable) receives U_s for the backward.  The decode of W' happens inside
  * the GEMM; no bf16 copy of the weight is written.  The call needs
- * qlora_workspace_bytes(0, M, K, N, r) bytes of workspace: for M <= 16 the fp32
- * partial sums of the split-contraction GEMV (also when r = 0); for M > 16 the fp32
+ * qlora_workspace_bytes(0, M, K, N, r) bytes of workspace: for M <= 16 and N <= 65536
+ * (the small-M path, one launch)
+ * the counter header, copies of U_s and the partial sums of the down-projection
+ * (the header alone when r = 0); otherwise the header, the fp32
  * partial sums of the down-projection plus U_s when U_saved is NULL, and none when
  * r = 0.  The kernels use 32-bit buffer offsets: QLORA_ERR_SHAPE, before anything is
  * launched, when X, Y, the codes or a LoRA operand exceed 0xFFFFFFF0 bytes. */
@@ -199,6 +207,8 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, co
  * overlap on one GPU (different streams, different host threads) race and must be
  * serialised by the caller. */
 #define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+/* Leading workspace bytes that must be zero at first use (see Conventions). */
+#define QLORA_WORKSPACE_HEADER_BYTES ((size_t)65792)
 int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
                              const uint16_t *B, int r, float alpha, uint16_t *Y, uint16_t *U_saved,
                              void *stream);

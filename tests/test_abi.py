@@ -59,10 +59,19 @@ def test_sizes_reject_bad_shapes():
 
 def test_workspace_bytes():
     assert _lib.qlora_workspace_bytes(0, 4096, 4096, 4096, 0) == 0
-    # M <= 16 runs a split-contraction GEMV: fp32 partials even without an adapter
-    assert _lib.qlora_workspace_bytes(0, 1, 4096, 11008, 0) >= 4 * 11008 * 4
-    assert _lib.qlora_workspace_bytes(0, 16, 11008, 4096, 16) >= 11 * 4096 * 16 * 4 + 11 * 16 * 16 * 4
-    assert _lib.qlora_workspace_bytes(0, 4096, 4096, 4096, 64) >= 4096 * 64 * 2
+    H = _lib.QLORA_WORKSPACE_HEADER_BYTES
+    # M <= 16 runs the one-launch GEMV: the counter / flag header, then copies of U_s
+    # [M, r] rounded up to 16 ranks and the partial sums of the down-projection; the
+    # header alone without an adapter
+    assert _lib.qlora_workspace_bytes(0, 1, 4096, 11008, 0) == H
+    assert _lib.qlora_workspace_bytes(0, 16, 11008, 4096, 16) >= H + 16 * 16 * 2 + 16 * 16 * 4
+    assert _lib.qlora_workspace_bytes(0, 3, 4096, 4096, 17) >= H + 3 * 32 * 2 + 3 * 32 * 4
+    # past 4096 tiles of 16 rows a small M takes the fused GEMM (no workspace without an
+    # adapter)
+    assert _lib.qlora_workspace_bytes(0, 1, 64, 65536, 0) == H
+    assert _lib.qlora_workspace_bytes(0, 1, 64, 65536 + 16, 0) == 0
+    # every layout keeps the header first
+    assert _lib.qlora_workspace_bytes(0, 4096, 4096, 4096, 64) >= H + 4096 * 64 * 2
     assert _lib.qlora_workspace_bytes(1, 4096, 4096, 11008, 64) > 0
     assert _lib.qlora_workspace_bytes(1, 1, 100, 4, 8) == 0       # K % 64 != 0
     assert _lib.qlora_workspace_bytes(2, 64, 64, 64, 8) == 0       # unknown op

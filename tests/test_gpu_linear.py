@@ -59,6 +59,11 @@ SMALL = [  # (M, K, N, r)
     (513, 768, 640, 128),  # rank 128
     (130, 256, 136, 256),  # the largest rank
     (2100, 1024, 512, 64), # several M-splits in the token reductions
+    (7, 512, 300, 256),    # M <= 16 with the largest rank: 16 LoRA workgroups in the launch
+    (1, 64, 33, 5),        # M <= 16 with one 64-block of contraction
+    (12, 4096, 40, 16),    # M <= 16, X too large to stage in LDS: X fragments from memory
+    (1, 64, 65552, 4),     # M = 1 past 4096 tiles of 16 rows: the fused GEMM takes it
+    (3, 256, 48, 256),     # more LoRA pieces than workgroups: a LoRA wave takes several
 ]
 
 
@@ -179,6 +184,36 @@ def test_backward_optional_inputs_and_outputs(lib, M):
         Xf, Af, Bf, dYf = (gc.f64(d[k]) for k in ("X", "A", "B", "dY"))
         for name, G, R in zip(("dX", "dA", "dB"), recomputed, linear.backward(dYf, Xf, Wd, Af, Bf, alpha, r)):
             _check(name + " (U recomputed)", gc.host_f32_from_bf16(G), R)
+
+
+def test_workspace_reuse_across_shapes(lib):
+    """One zeroed workspace serves small-M forwards (whose workgroups hand U_s to each
+    other through counters at the start of the workspace), GEMM forwards and backwards
+    in any order: the counters are back at zero after every call and no other call
+    writes them, so the small-M results stay bitwise the same and within tolerance."""
+    import torch
+    K, N, r, alpha = 1024, 520, 16, 16.0
+    d = synth.case(300, K, N, r, seed=77)
+    qw = lib.quantize(gc.dev_weight(d))
+    X, A, B = _dev(d, r)
+    X5 = gc.dev_bf16(d["X"][:5])
+    dYt = gc.dev_bf16(d["dY"])
+    nbytes = max(lib.qlora_workspace_bytes(op, M, K, N, r) for op in (0, 1) for M in (5, 300))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    Wd = _oracle_w(d)
+    ref5 = linear.forward(gc.f64(d["X"][:5]), Wd, gc.f64(d["A"]), gc.f64(d["B"]), alpha, r)
+    outs = []
+    for _ in range(3):
+        Y5, _ = lib.linear_fwd(qw, X5, A, B, alpha, ws=ws)
+        outs.append(Y5.clone())
+        assert int(ws[:lib._lib.QLORA_WORKSPACE_HEADER_BYTES].count_nonzero()) == 0
+        Y, U = lib.linear_fwd(qw, X, A, B, alpha, ws=ws)
+        lib.linear_bwd(qw, dYt, X, A, B, alpha, U, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:lib._lib.QLORA_WORKSPACE_HEADER_BYTES].count_nonzero()) == 0
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    _check("Y (M = 5, shared workspace)", gc.host_f32_from_bf16(outs[0]), ref5)
 
 
 def test_launch_on_a_side_stream(lib):

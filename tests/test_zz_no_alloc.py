@@ -85,7 +85,7 @@ def test_noalloc_refuses_oversized_scratch(q):
     """A forward whose workspace exceeds the fixed scratch is refused host-side, with a
     message, before anything is launched."""
     from bit_quantized_lora_nf4_amd import _lib
-    N, K, M, r = 16384, 65536, 8, 256
+    N, K, M, r = 256, 4096, 65536, 256  # U_s alone is 32 MiB when the caller does not keep it
     need = _lib.qlora_workspace_bytes(0, M, K, N, r)
     assert need > _lib.QLORA_NOALLOC_SCRATCH_BYTES
     w = _lib.qlora_nf4_weight(0x10000, 0x10000, 0x10000, 0x10000, N, K, None, 0, 0)
