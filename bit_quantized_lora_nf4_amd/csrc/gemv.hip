@@ -49,6 +49,7 @@
 // re-interleaving the decoded weights.
 
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "qlora_internal.h"
@@ -136,41 +137,61 @@ __device__ __forceinline__ u32x4_t permute8(u32x4_t d) {
 }
 
 // One wave step of the weight stream: the loads of one lane's block, and its eight X
-// fragments when X is not staged in LDS.
-template <bool XLDS>
+// fragments when X is not staged in LDS.  The group scale and offset of the
+// double-quantized constants are loaded once per wave (GroupConsts).
+template <int CT, bool XLDS>
 struct StepLoads {
   u32x4_t c0, c1;            // 32 bytes of codes
-  uint8_t q;                 // block constant: the 8-bit code (kept 8-bit: a wider type is
-                             // zero-extended where the loads are issued, waiting for them)
-  uint32_t s, o;             // group scale and offset (s: the fp32 constant of kConstF32)
+  // the block constant: the 8-bit code (kept 8-bit: a wider type is zero-extended where
+  // the loads are issued, waiting for them), or the fp32 constant of kConstF32
+  typename std::conditional<CT == kConstF32, uint32_t, uint8_t>::type q;
   u32x4_t x[XLDS ? 1 : 8];   // X[token][64 b + 8 u ..] (natural order)
 };
 
-// The constant loads of block b (zeros when !ok, so that the constant decodes to 0).
-template <int CT, bool XLDS>
-__device__ __forceinline__ void load_constant(const ConstRsrc &rq, uint32_t b, bool ok, StepLoads<XLDS> &st) {
-  if constexpr (CT == kConstF32) {
-    st.s = __builtin_amdgcn_raw_buffer_load_b32(rq.s, ok ? b * 4u : kOOB, 0, 0);
-    st.q = 0;
-    st.o = 0u;
-  } else {
-    st.q = __builtin_amdgcn_raw_buffer_load_b8(rq.q8, ok ? b : kOOB, 0, 0);
-    st.s = __builtin_amdgcn_raw_buffer_load_b32(rq.s, ok ? (b >> 8) * 4u : kOOB, 0, 0);
-    st.o = __builtin_amdgcn_raw_buffer_load_b32(rq.o, ok ? (b >> 8) * 4u : kOOB, 0, 0);
+// The group scale and offset of the first and of the last block of a wave's range (the
+// range is at most 64 blocks, so it spans at most two groups of 256 blocks).
+struct GroupConsts {
+  uint32_t g0;               // group of the first block
+  uint32_t s0, o0, s1, o1;
+};
+template <int CT>
+__device__ __forceinline__ GroupConsts load_groups(const ConstRsrc &rq, uint32_t first, uint32_t last, bool ok) {
+  GroupConsts gc{first >> 8, 0u, 0u, 0u, 0u};
+  if constexpr (CT != kConstF32) {
+    gc.s0 = __builtin_amdgcn_raw_buffer_load_b32(rq.s, ok ? (first >> 8) * 4u : kOOB, 0, 0);
+    gc.o0 = __builtin_amdgcn_raw_buffer_load_b32(rq.o, ok ? (first >> 8) * 4u : kOOB, 0, 0);
+    gc.s1 = __builtin_amdgcn_raw_buffer_load_b32(rq.s, ok ? (last >> 8) * 4u : kOOB, 0, 0);
+    gc.o1 = __builtin_amdgcn_raw_buffer_load_b32(rq.o, ok ? (last >> 8) * 4u : kOOB, 0, 0);
   }
+  return gc;
 }
 
-// c' of a block from its loaded pieces: fma(c8, s, o) rounded once ([Digest]
-// "数学公式与关键细节" item 3), or the stored fp32 constant.  The int8 code is
-// sign-extended in floating point, (float)(byte ^ 0x80) - 128, which the compiler
-// cannot fold into a sign-extending load placed next to this use.
+// The block-constant load of flat block b (zero when !ok).
 template <int CT, bool XLDS>
-__device__ __forceinline__ float constant_of(const StepLoads<XLDS> &st) {
-  if constexpr (CT == kConstF32) return __uint_as_float(st.s);
+__device__ __forceinline__ void load_constant(const ConstRsrc &rq, uint32_t b, bool ok, StepLoads<CT, XLDS> &st) {
+  if constexpr (CT == kConstF32)
+    st.q = __builtin_amdgcn_raw_buffer_load_b32(rq.s, ok ? b * 4u : kOOB, 0, 0);
+  else
+    st.q = __builtin_amdgcn_raw_buffer_load_b8(rq.q8, ok ? b : kOOB, 0, 0);
+}
+
+// c' of flat block b from its loaded pieces: fma(c8, s, o) rounded once ([Digest]
+// "数学公式与关键细节" item 3), or the stored fp32 constant; 0 when !ok (blocks past the
+// wave's range and rows past N add nothing).  The int8 code is sign-extended in floating
+// point, (float)(byte ^ 0x80) - 128, which the compiler cannot fold into a sign-extending
+// load placed next to this use.
+template <int CT, bool XLDS>
+__device__ __forceinline__ float constant_of(const StepLoads<CT, XLDS> &st, const GroupConsts &gc, uint32_t b,
+                                             bool ok) {
+  if constexpr (CT == kConstF32) return __uint_as_float(st.q);
+  const bool first = (b >> 8) == gc.g0;
+  const float s = __uint_as_float(first ? gc.s0 : gc.s1), o = __uint_as_float(first ? gc.o0 : gc.o1);
+  float c8;
   if constexpr (CT == kConstDqFp8)
-    return __builtin_fmaf(e4m3_value(st.q), __uint_as_float(st.s), __uint_as_float(st.o));
-  const float c8 = static_cast<float>(static_cast<int>(st.q ^ 0x80u)) - 128.0f;
-  return __builtin_fmaf(c8, __uint_as_float(st.s), __uint_as_float(st.o));
+    c8 = e4m3_value(st.q);
+  else
+    c8 = static_cast<float>(static_cast<int>(st.q ^ 0x80u)) - 128.0f;
+  return ok ? __builtin_fmaf(c8, s, o) : 0.0f;
 }
 
 // LDS layout (one dynamic object): the waves' partial sums [W][64 lanes][4] fp32, then
@@ -424,12 +445,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) bs[i] = load_b(tid + i * nthr);
   }
+  const GroupConsts gc = load_groups<CT>(rq, row_blk + kb0, row_blk + kb1 - 1, row_ok);
   __builtin_amdgcn_sched_barrier(0);
 
   // the loads of step t (blocks past the wave's range, or rows past N, read zeros: their
   // constant decodes to c' = 0, so they add nothing)
   auto load = [&](int t) {
-    StepLoads<XLDS> s;
+    StepLoads<CT, XLDS> s;
     const int b = kb0 + 4 * t + g;
     const bool ok = row_ok && b < kb1;
     const uint32_t off = ok ? row_code + b * 32 : kOOB;
@@ -444,9 +466,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
     return s;
   };
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto compute = [&](const StepLoads<XLDS> &s, int t) {
+  auto compute = [&](const StepLoads<CT, XLDS> &s, int t) {
     const int b = kb0 + 4 * t + g;
-    const Planes pl = make_planes(constant_of<CT, XLDS>(s), a.lvl);
+    const Planes pl = make_planes(constant_of<CT, XLDS>(s, gc, row_blk + b, row_ok && b < kb1), a.lvl);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const uint32_t cw = u < 4 ? s.c0[u] : s.c1[u - 4];
@@ -481,7 +503,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
     for (int c = tid + 2 * nthr; c < bpieces; c += nthr) *reinterpret_cast<u32x4_t *>(sb + 8 * c) = load_b(c);
   }
   __syncthreads();
-  StepLoads<XLDS> st[D];
+  StepLoads<CT, XLDS> st[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     st[j] = load(j);
