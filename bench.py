@@ -160,6 +160,7 @@ def measure_quantize_stress(torch, q, synth, gc, copies=12, reps=2):
                      f"zero blocks), {copies} distinct seeded matrices"}
     # standalone decode of the same stream: the quantized copies -> one bf16 output buffer
     qws = [q.quantize(W) for W in Ws]
+    quant["error"] = stress_error(torch, q, W0, qws[0])
     del Ws, W0
     out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     q.dequantize(qws[0], out=out)
@@ -178,6 +179,131 @@ def measure_quantize_stress(torch, q, synth, gc, copies=12, reps=2):
                    f"{N}x{K} stress weights"}
     del qws, out
     return quant, deq
+
+
+def stress_error(torch, q, W, qw, outlier_abs=0.5):
+    """Decode error of one stress weight, from the library's own dequantize: per 64-block
+    absmax c of W, the max and RMS of |w - w'| / c over three kinds of blocks (all-zero,
+    blocks holding an outlier |w| >= outlier_abs, the rest), and the max absolute error in
+    the zero blocks (it must be 0)."""
+    Wd = q.dequantize(qw).float().view(-1, 64)
+    Wf = W.float().view(-1, 64)
+    c = Wf.abs().amax(dim=1)
+    err = (Wf - Wd).abs()
+    zero = c == 0
+    outl = (~zero) & (Wf.abs() >= outlier_abs).any(dim=1)
+    bulk = (~zero) & (~outl)
+    out = {"blocks": int(c.numel()), "zero_blocks": int(zero.sum()), "outlier_blocks": int(outl.sum()),
+           "max_abs_err_zero_blocks": float(err[zero].max()) if bool(zero.any()) else 0.0}
+    for name, sel in (("bulk", bulk), ("outlier", outl)):
+        if bool(sel.any()):
+            rel = err[sel] / c[sel].unsqueeze(1)
+            out[name] = {"max_err_over_c": round(float(rel.max()), 6),
+                         "rms_err_over_c": round(float(rel.pow(2).mean().sqrt()), 6)}
+    out["what"] = ("|w - w'| / c per 64-block (c = block absmax), first stress matrix: NF4's half-gap between "
+                   "adjacent levels (at most 0.16) plus |q| |c - c'| / c from the int8 double quantization of c, "
+                   "which is large for blocks of small c in groups of 256 blocks that also hold outlier blocks")
+    return out
+
+
+def step_percentiles(ms):
+    v = sorted(ms)
+    pick = lambda f: v[min(len(v) - 1, max(0, int(round(f * (len(v) - 1)))))]  # noqa: E731
+    return {"p10": round(pick(0.1), 4), "p50": round(pick(0.5), 4), "p90": round(pick(0.9), 4),
+            "min": round(v[0], 4), "max": round(v[-1], 4), "n": len(v)}
+
+
+def measure_config1(torch, q, synth, gc, calls=200):
+    """Workload 1 (one 1024 -> 1024 linear, M = 64, r = 8, W drawn fp32): device time of one
+    forward + backward (dX, dA, dB), replayed from a HIP graph, with B = 0 and with
+    B ~ N(0, 0.01^2)."""
+    wl = synth.WORKLOADS[1]
+    K, N = wl.linears[0]
+    M = wl.M[0]
+    d = synth.workload_linear(1, 0)
+    qw = q.quantize(gc.dev_weight(d))
+    X, A, Bn, dY = gc.dev_bf16(d["X"]), gc.dev_bf16(d["A"]), gc.dev_bf16(d["B"]), gc.dev_bf16(d["dY"])
+    out = {"what": "1024->1024, M=64, r=8, alpha=16: one forward + backward per call, graph-replayed"}
+    for name, B in (("B_zero", torch.zeros_like(Bn)), ("B_normal", Bn)):
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        U = torch.empty((M, wl.r), dtype=torch.bfloat16, device="cuda")
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        dA = torch.empty((wl.r, K), dtype=torch.bfloat16, device="cuda")
+        dB = torch.empty((N, wl.r), dtype=torch.bfloat16, device="cuda")
+        wsf, wsb = q.workspace(0, M, K, N, wl.r, "cuda"), q.workspace(1, M, K, N, wl.r, "cuda")
+
+        def one():
+            q.linear_fwd(qw, X, A, B, wl.alpha, Y=Y, U=U, ws=wsf)
+            q.linear_bwd(qw, dY, X, A, B, wl.alpha, U, dX=dX, dA=dA, dB=dB, ws=wsb)
+        one()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                one()
+        g.replay()
+        torch.cuda.synchronize()
+        s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(3):
+            g.replay()
+        f.record()
+        torch.cuda.synchronize()
+        us = s.elapsed_time(f) * 1e3 / (3 * calls)
+        out[name] = {"us_per_fwd_bwd": round(us, 2),
+                     "TFLOP/s": round(linear_flops(M, K, N, wl.r) / (us * 1e-6) / 1e12, 3)}
+    return out
+
+
+def measure_ceilings(torch, M=4096, shapes=((4096, 4096), (4096, 11008), (11008, 4096)), reps=10):
+    """Practical ceilings on this GPU: a plain device copy (read + write bytes per second) and
+    torch's bf16 GEMM (hipBLASLt) on the workload's dense shapes X [M, K] . W^T [K, N]."""
+    n = 512 << 20  # bf16 elements (1 GiB)
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    f.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(f) / reps
+    out = {"copy_GB/s": round(4 * n / (ms * 1e-3) / 1e9, 1),
+           "copy_what": "1 GiB bf16 device copy, read + write bytes"}
+    del src, dst
+    mm = {}
+    for K, N in shapes:
+        X = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        Wt = torch.randn(K, N, device="cuda").to(torch.bfloat16).contiguous()
+        torch.matmul(X, Wt)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            torch.matmul(X, Wt)
+        f.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(f) / reps
+        mm[f"{K}->{N}"] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        del X, Wt
+    out["torch_matmul_bf16_M4096"] = mm
+    return out
+
+
+def environment(torch):
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    return {"gpu": torch.cuda.get_device_name(0), "compute_units": props.multi_processor_count,
+            "hbm_GB": round(props.total_memory / 1e9, 1), "gcn_arch": getattr(props, "gcnArchName", None),
+            "rocm": rocm, "torch": torch.__version__, "hip": torch.version.hip,
+            "python": sys.version.split()[0], "host_cores": os.cpu_count(),
+            "seeds": "synth: numpy default_rng([workload - 1, linear, M]) per linear, drawing W, X, A, B, dY "
+                     "in that order; stress matrices: torch.Generator seeded from [5, i]"}
 
 
 def measure_m1(torch, q, synth, gc, ev, M=1, min_bytes=600 << 20, calls=200):
@@ -437,21 +563,33 @@ def cpu_baseline(synth, sample_m=4096, min_seconds=10.0, max_passes=20):
     from oracle import linear, nf4
     wl = synth.WORKLOADS[2]
     cases = []
+    tq = nq = 0.0
     for i, (K, N) in enumerate(wl.linears):
         d = synth.workload_linear(2, i)
-        qw = nf4.quantize_nf4(synth.bf16_bits_to_f32(d["W"]))
+        Wf = synth.bf16_bits_to_f32(d["W"])
+        t0 = time.perf_counter()
+        qw = nf4.quantize_nf4(Wf)
+        tq += time.perf_counter() - t0
+        nq += Wf.size
         f = lambda k: synth.bf16_bits_to_f32(d[k]).astype(np.float64)  # noqa: E731
         cases.append((K, N, qw, f("X")[:sample_m], f("A"), f("B"), f("dY")[:sample_m]))
-        del d
+        del d, Wf
     dt = fl = 0.0
+    per = {"dequantize": 0.0, "forward": 0.0, "backward": 0.0}
     passes = 0
     while passes < max_passes and (passes == 0 or dt < min_seconds):
         for K, N, qw, X, A, B, dY in cases:
             t0 = time.perf_counter()
             Wd = nf4.dequantize_bf16(qw)
+            t1 = time.perf_counter()
             linear.forward(X, Wd, A, B, wl.alpha, wl.r)
+            t2 = time.perf_counter()
             linear.backward(dY, X, Wd, A, B, wl.alpha, wl.r)
-            dt += time.perf_counter() - t0
+            t3 = time.perf_counter()
+            per["dequantize"] += t1 - t0
+            per["forward"] += t2 - t1
+            per["backward"] += t3 - t2
+            dt += t3 - t0
             fl += linear_flops(sample_m, K, N, wl.r)
         passes += 1
     try:
@@ -461,6 +599,10 @@ def cpu_baseline(synth, sample_m=4096, min_seconds=10.0, max_passes=20):
         cores = os.cpu_count()
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 2), "passes": passes,
+            "per_step_ms": {k: round(v * 1e3 / passes, 1) for k, v in per.items()},
+            "quantize": {"seconds": round(tq, 2), "weights": int(nq),
+                         "Mweights_per_s": round(nq / tq / 1e6, 3) if tq > 0 else None,
+                         "what": "the oracle's NF4 + double quantization of the three weights, once"},
             "sample": f"the three linears of the workload with the first {sample_m} of 4096 tokens, "
                       f"{passes} passes: decode W' + forward + backward in float64 numpy "
                       "(quantization untimed)"}
@@ -521,6 +663,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the M=1 and quantize legs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--m1-only", action="store_true",
+                    help="only run the M=1 weight-stream leg (for profiling the small-M forward) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; --gpus must be 1 "
@@ -534,6 +678,11 @@ def main():
     import bit_quantized_lora_nf4_amd as q
     import synth
     from synth import device as gc
+    if args.m1_only:
+        ev = HipEvents()
+        print(json.dumps({"weight_stream_m1": measure_m1(torch, q, synth, gc, ev)}), flush=True)
+        ev.close()
+        return
 
     print("bench: setting up workload 2 (3 linears, M=4096)", file=sys.stderr, flush=True)
     wl, M, L = setup_workload2(torch, q, synth, gc)
@@ -543,18 +692,19 @@ def main():
     torch.cuda.synchronize()
     rec = []
     t0 = time.perf_counter()
-    s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
     every = max(1, args.time_every)
     for i in range(args.steps):
         if i % every == 0:
             run_step(q, wl, L, ev, rec)
         else:
             run_step(q, wl, L)
-    f.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = s.elapsed_time(f) / args.steps
+    ms_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     flops_step = sum(linear_flops(M, e["K"], e["N"], wl.r) for e in L)
     value = flops_step / (ms_step * 1e-3) / 1e12
     print(f"bench: {args.steps} steps, {ms_step:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr,
@@ -594,9 +744,15 @@ def main():
                    "M": M, "r": wl.r, "alpha": wl.alpha, "block": 64, "dq_group": 256,
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "step_ms": dict(step_percentiles(step_ms),
+                        note="per-step durations of the timed steps (steps with GEMM event timing included)"),
+        "environment": environment(torch),
     }
     ev.close()
     if not args.no_extras:
+        print("bench: workload 1 latency and ceilings", file=sys.stderr, flush=True)
+        result["config1_latency"] = measure_config1(torch, q, synth, gc)
+        result["ceilings"] = measure_ceilings(torch)
         print("bench: M=1 weight stream", file=sys.stderr, flush=True)
         result["weight_stream_m1"] = measure_m1(torch, q, synth, gc, ev)
         ev.close()
