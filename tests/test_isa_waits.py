@@ -9,7 +9,9 @@ of every instantiation.  The kernels keep every value in registers (no scratch s
 which would cost them about half their speed), and: at each barrier of the forward kernel, the loads left in flight
 must all have been issued after the direct-to-LDS loads of the tile read right after it;
 at each barrier of the pipelined dX kernel, every direct-to-LDS (dY) load issued before
-the barrier must be retired.  No GPU needed (hipcc cross-compiles)."""
+the barrier must be retired.  The skinny adapter kernels of lora.hip are checked the same
+way over their control-flow graph (see the section at the end).  No GPU needed (hipcc
+cross-compiles)."""
 
 import os
 import re
@@ -105,5 +107,150 @@ def test_no_register_spills(gemm_asm):
     sizes = dict(re.findall(r"\.name:\s+(\S*gemm_\S*kernel\S*)\s.*?\.private_segment_fixed_size:\s+(\d+)",
                             gemm_asm, re.S))
     assert len(sizes) >= 9, sizes
+    for name, size in sizes.items():
+        assert int(size) <= 16, f"{name}: {size} bytes of scratch"
+
+
+# ---- the skinny adapter kernels (lora.hip) --------------------------------------------
+# Each of their staging loops issues the loads of NB - 1 steps before the loop, then one
+# step's loads per iteration, and waits at the top of the iteration with vmcnt(N).  Step i
+# has landed at that wait iff N <= P - L, where P is the number of direct-to-LDS loads the
+# prologue issued and L the number issued per iteration (every load of the prologue and
+# the loop body belongs to one step, in issue order).  Any other vector memory operation
+# inside the loop would shift the count, so there must be none.
+
+@pytest.fixture(scope="module")
+def lora_asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "lora.s"
+    flags = [f for f in libbuild.FLAGS if f not in ("-fPIC",)]
+    cmd = [HIPCC] + flags + ["--cuda-device-only", "-S", os.path.join(libbuild.CSRC, "lora.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return out.read_text()
+
+
+_VMEM = re.compile(r"(buffer|global|flat|scratch)_(load|store|atomic)")
+_BR = re.compile(r"s_(c?)branch\S*\s+(\.LBB\S+)")
+
+
+def _cfg(body):
+    """Basic blocks of one function in text order: dicts with the label, its loop-header
+    comment, the instructions and the successor block indices."""
+    blocks, cur = [], {"label": None, "note": "", "lines": []}
+    for raw in body.splitlines()[1:]:
+        ln = raw.strip()
+        m = re.match(r"(\.LBB\S+):\s*(;.*)?$", ln)
+        if m:
+            blocks.append(cur)
+            cur = {"label": m.group(1), "note": m.group(2) or "", "lines": []}
+            continue
+        if not ln or ln.startswith((";", ".")):
+            continue
+        cur["lines"].append(ln)
+        if _BR.match(ln) or ln.startswith("s_endpgm"):
+            blocks.append(cur)  # a branch ends the block; what follows is a block of its own
+            note = cur["note"]
+            if cur["label"] and "Loop Header" in note:
+                note = f"; in Loop: Header={cur['label'][2:]} Depth=1"
+            cur = {"label": None, "note": note, "lines": []}
+    blocks.append(cur)
+    blocks = [b for b in blocks if b["label"] or b["lines"]]
+    index = {b["label"]: i for i, b in enumerate(blocks) if b["label"]}
+    for i, b in enumerate(blocks):
+        last = b["lines"][-1] if b["lines"] else ""
+        m = _BR.match(last)
+        succ = []
+        if m:
+            succ.append(index[m.group(2)])
+        if not last.startswith("s_endpgm") and not (m and not m.group(1)) and i + 1 < len(blocks):
+            succ.append(i + 1)
+        b["succ"] = succ
+    return blocks
+
+
+def _dma(lines):
+    return sum(1 for ln in lines if _VMEM.match(ln) and ln.endswith(" lds"))
+
+
+def _staging_loops(body):
+    """(P, L, waits, other) for every innermost loop that waits before a barrier: P the set
+    of direct-to-LDS load counts on the paths from the entry to the loop, L the set of
+    counts per iteration, waits the vmcnt values before its barriers, other any other
+    vector memory operation inside it."""
+    blocks = _cfg(body)
+    out = []
+    for h, hb in enumerate(blocks):
+        m = re.match(r"; =>This Inner Loop Header: Depth=1", hb["note"])
+        if not m:
+            continue
+        hid = hb["label"][2:]  # ".LBBx_y" -> "BBx_y"
+        members = {i for i, b in enumerate(blocks) if i == h or f"Header={hid} " in b["note"] + " "}
+        loop_lines = [ln for i in sorted(members) for ln in blocks[i]["lines"]]
+        waits = [int(re.match(r"s_waitcnt vmcnt\((\d+)\)", loop_lines[k]).group(1))
+                 for k in range(len(loop_lines) - 1)
+                 if re.match(r"s_waitcnt vmcnt\(\d+\)", loop_lines[k]) and loop_lines[k + 1].startswith("s_barrier")]
+        if not waits:
+            continue
+        other = [ln for ln in loop_lines if _VMEM.match(ln) and not ln.endswith(" lds")]
+        # loads per iteration: every path from the header back to it
+        iters, stack, seen = set(), [(h, 0)], set()
+        while stack:
+            i, n = stack.pop()
+            if (i, n) in seen or n > 4096:
+                continue
+            seen.add((i, n))
+            n += _dma(blocks[i]["lines"])
+            for j in blocks[i]["succ"]:
+                if j == h:
+                    iters.add(n)
+                elif j in members:
+                    stack.append((j, n))
+        # loads on the paths from the entry to the header (earlier loops are walked once,
+        # along their exits; a full wait resets the count)
+        pro, stack, seen = set(), [(0, 0)], set()
+        while stack:
+            i, n = stack.pop()
+            if (i, n) in seen:
+                continue
+            seen.add((i, n))
+            for ln in blocks[i]["lines"]:
+                if ln.startswith("s_waitcnt vmcnt(0)"):
+                    n = 0
+                n += _VMEM.match(ln) is not None and ln.endswith(" lds")
+            for j in blocks[i]["succ"]:
+                if j == h:
+                    pro.add(n)
+                elif j not in members and j > i or (j not in members and j < i and len(seen) < 4096):
+                    stack.append((j, n))
+        out.append((pro, iters, waits, other))
+    return out
+
+
+def test_lora_staging_waits(lora_asm):
+    kernels = re.findall(r"^(_Z\S*(?:lora_down_partial|reduce_m_partial|down_reduce_partial)\S*):", lora_asm, re.M)
+    assert len(kernels) >= 24, len(kernels)
+    checked = 0
+    for name in kernels:
+        # the whole function: blocks may follow its first s_endpgm
+        body = re.search(r"^" + re.escape(name) + r":.*?^\.Lfunc_end", lora_asm, re.S | re.M).group(0)
+        loops = _staging_loops(body)
+        assert loops, f"{name}: no staging loop found"
+        for P, L, waits, other in loops:
+            assert not other, f"{name}: other vector memory operations inside the staging loop: {other[:3]}"
+            assert len(L) == 1 and min(L) > 0, (name, L)
+            assert P, (name, "the loop is not reached")
+            L = min(L)
+            for n in waits:
+                assert n <= min(P) - L, (f"{name}: vmcnt({n}) at the loop's barrier, but only {min(P) - L} loads "
+                                         f"follow a step's on some path ({sorted(P)} before the loop, {L} per step)")
+            checked += 1
+    assert checked >= 24
+
+
+def test_lora_no_register_spills(lora_asm):
+    sizes = dict(re.findall(r"\.name:\s+(\S*kernel\S*)\s.*?\.private_segment_fixed_size:\s+(\d+)", lora_asm, re.S))
+    assert len(sizes) >= 20, sizes
     for name, size in sizes.items():
         assert int(size) <= 16, f"{name}: {size} bytes of scratch"
