@@ -196,17 +196,19 @@ __device__ __forceinline__ float constant_of(const StepLoads<CT, XLDS> &st, cons
 
 // LDS layout (one dynamic object): the waves' partial sums [W][64 lanes][4] fp32, then
 // (R > 0) the workgroup's 16 rows of Bl (bf16, as stored: 16 r contiguous elements), then, when X is staged, X [M][KB][XBLK] bytes (each
-// 64-element block permuted per 8-element group, 16 bytes of padding).
+// 64-element block permuted per 8-element group, 16 bytes of padding), then (DIRECT
+// hand-over) the part's U_s [M][r] bf16.
 struct LdsPlan {
-  int red, bt, x, total;
+  int red, bt, x, u, total;
 };
 __host__ __device__ inline int up16(int b) { return (b + 15) & ~15; }
-__host__ __device__ inline LdsPlan lds_plan(int W, int M, int R, int r, int KB, bool xlds) {
+__host__ __device__ inline LdsPlan lds_plan(int W, int M, int R, int r, int KB, bool xlds, bool direct) {
   LdsPlan p;
   p.red = 0;
   p.bt = W * 1024;
   p.x = p.bt + (R > 0 ? up16(32 * r) : 0);
-  p.total = p.x + (xlds ? M * KB * XBLK : 0);
+  p.u = p.x + (xlds ? M * KB * XBLK : 0);
+  p.total = p.u + (direct ? up16(2 * M * r) : 0);
   return p;
 }
 
@@ -282,7 +284,7 @@ __device__ __forceinline__ LoraLoads<XLDS> lora_issue(const GemvArgs &a, int KB,
   return ll;
 }
 
-template <bool XLDS>
+template <bool XLDS, bool DIRECT>
 __device__ void lora_finish(const GemvArgs &a, const char *sx, int KB, int p, const LoraLoads<XLDS> &ll) {
   constexpr int STEPS = LoraLoads<XLDS>::STEPS;
   const int lane = threadIdx.x & 63;
@@ -315,6 +317,13 @@ __device__ void lora_finish(const GemvArgs &a, const char *sx, int KB, int p, co
   // they have completed (agent-coherent loads of any workgroup then see them)
   if (tok_ok) store16_sc1(rp, (((t * a.SP + s) * a.M + ml) * 16 + 4 * g) * 4, __builtin_bit_cast(u32x4_t, acc));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (DIRECT) {
+    // every workgroup's counter counts this piece once its partial sums have completed
+    for (int w = lane; w < static_cast<int>(gridDim.x); w += 64)
+      __hip_atomic_fetch_add(a.sync + (kFlagBase + w * kFlagStride) / 4, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   uint32_t ticket = 0;
   if (lane == 0)
     ticket = __hip_atomic_fetch_add(a.sync + kSyncTile0 + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -365,13 +374,57 @@ __device__ void lora_finish(const GemvArgs &a, const char *sx, int KB, int p, co
   }
 }
 
-template <int CT, bool XLDS, bool MULTI>
+// DIRECT hand-over (small M r SP): the LoRA wave of every workgroup waits until its own
+// counter has counted all PT SP pieces, clears it for the next call, and forms the U_s
+// columns of its part itself: U_s[m, j] = bf16(scale * sum over the slices, in slice
+// order, of the partial sums), the same value the ticket path publishes.  It writes them
+// to LDS ([M][r] bf16) for the epilogue, and the first workgroup of the part also stores
+// them to U_saved.
+__device__ void gather_u(const GemvArgs &a, uint16_t *su, int n0) {
+  const int lane = threadIdx.x & 63;
+  uint32_t *cnt = a.sync + (kFlagBase + blockIdx.x * kFlagStride) / 4;
+  const uint32_t want = static_cast<uint32_t>(a.PT * a.SP);
+  for (uint32_t it = 0; it < kSpinLimit; ++it) {
+    if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int q = a.part_rows > 0 ? n0 / a.part_rows : 0;
+  const bool saver = a.U_saved && (a.part_rows > 0 ? n0 % a.part_rows == 0 : blockIdx.x == 0);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.PU, static_cast<uint32_t>(a.PT) * a.SP * a.M * 64);
+  const int n = a.M * a.r;
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const int e = e0 + lane;
+    const bool ok = e < n;
+    const int m = ok ? e / a.r : 0, j = q * a.r + (ok ? e % a.r : 0);
+    const int t = j >> 4, jj = j & 15;
+    float sum = 0.0f;
+    for (int s0 = 0; s0 < a.SP; s0 += 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b32(
+            rp, (ok && s0 + i < a.SP) ? (((t * a.SP + s0 + i) * a.M + m) * 16 + jj) * 4 : kOOB, 0, kSC1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < a.SP) sum += __uint_as_float(v[i]);
+    }
+    if (ok) {
+      const uint16_t u = to_bf16(a.scale * sum);
+      su[e] = u;
+      if (saver) a.U_saved[m * a.R + j] = u;
+    }
+  }
+}
+
+template <int CT, bool XLDS, bool MULTI, bool DIRECT>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int D = XLDS ? 4 : 2;  // steps whose loads are in flight (the register ring)
   const int W = a.W;  // weight waves; wave W (R > 0) is the LoRA wave
   const int N = static_cast<int>(a.w.n_rows), KB = static_cast<int>(a.w.n_cols / 64), K = KB * 64;
-  const LdsPlan lp = lds_plan(W, a.M, a.R, a.r, KB, XLDS);
+  const LdsPlan lp = lds_plan(W, a.M, a.R, a.r, KB, XLDS, DIRECT);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ml = lane & 15, g = lane >> 4;
   const int tile = blockIdx.x;
@@ -404,15 +457,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
     LoraLoads<XLDS> ll;
     if (static_cast<int>(blockIdx.x) < npieces) ll = lora_issue<XLDS>(a, KB, blockIdx.x);
     __syncthreads();
-    if (static_cast<int>(blockIdx.x) < npieces) lora_finish<XLDS>(a, lds + lp.x, KB, blockIdx.x, ll);
+    if (static_cast<int>(blockIdx.x) < npieces) lora_finish<XLDS, DIRECT>(a, lds + lp.x, KB, blockIdx.x, ll);
     if constexpr (MULTI) {
       // more pieces than workgroups (few output rows): the later ones one after another
       // (a separate instantiation: the loop costs the kernel about 35 registers)
       for (int p = blockIdx.x + gridDim.x; p < npieces; p += gridDim.x) {
         const LoraLoads<XLDS> lp2 = lora_issue<XLDS>(a, KB, p);
-        lora_finish<XLDS>(a, lds + lp.x, KB, p, lp2);
+        lora_finish<XLDS, DIRECT>(a, lds + lp.x, KB, p, lp2);
       }
     }
+    // DIRECT: U_s for the epilogue, in LDS before the reduction barrier
+    if constexpr (DIRECT) gather_u(a, reinterpret_cast<uint16_t *>(lds + lp.u), static_cast<int>(blockIdx.x) * 16);
     __syncthreads();
     return;
   }
@@ -528,7 +583,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
   if (wave != 0) return;
   // lane: token ml, weight rows n0 + 4 g + e
 
-  if (a.R > 0) {
+  if (DIRECT && a.R > 0) {
+    // U_s of this part is in LDS (the LoRA wave put it there before the barrier)
+    const uint16_t *urow = reinterpret_cast<const uint16_t *>(lds + lp.u) + tok * a.r;
+    const uint16_t *brow = sb + ml * a.r;
+    const bool aligned = (a.r & 7) == 0;
+    for (int c = 0; c < a.r; c += 32) {
+      const int j0 = c + 8 * g;
+      const u32x4_t bf = lds_frag8(brow, j0, a.r, aligned);
+      const u32x4_t uf = tok_ok ? lds_frag8(urow, j0, a.r, aligned) : u32x4_t{0u, 0u, 0u, 0u};
+      y = mfma16x16x32(bf, uf, y);
+    }
+  } else if (a.R > 0) {
     // U_s from the LoRA waves: poll this workgroup's flag (and clear it for the next
     // call), then read this workgroup's copy of U_s
     uint32_t *flag = a.sync + (kFlagBase + blockIdx.x * kFlagStride) / 4;
@@ -622,6 +688,7 @@ int xlds_budget(int64_t N) {
 struct GemvPlan {
   GemvShape sh;
   bool xlds;
+  bool direct;  // U_s handed over through per-workgroup counters (gather_u)
   int lds_bytes;
   int LB, SP;
 };
@@ -633,13 +700,18 @@ GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int R) {
   GemvPlan p;
   // staged X: about 100 VGPRs (5 waves per SIMD); X from memory: about 130 (4)
   p.sh = gemv_shape(N, K, 20, extra);
-  p.xlds = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, true).total <= xlds_budget(N);
+  p.xlds = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, true, false).total <= xlds_budget(N);
   if (!p.xlds) p.sh = gemv_shape(N, K, 16, extra);
-  p.lds_bytes = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, p.xlds).total;
   const int lb_max = p.xlds ? 8 : 4;
   p.LB = (KB + 15) / 16;
   if (p.LB > lb_max) p.LB = lb_max;
   p.SP = (KB + p.LB - 1) / p.LB;
+  // Every workgroup reads M R SP partial sums in the DIRECT hand-over: taken while that
+  // stays small (and the U_s tile fits the LDS share); else the last piece of each rank
+  // tile publishes U_s once.
+  p.direct = R > 0 && M * R * p.SP * 4 <= 32 * 1024 &&
+             (!p.xlds || lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, true, true).total <= xlds_budget(N));
+  p.lds_bytes = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, p.xlds, p.direct).total;
   return p;
 }
 
@@ -672,7 +744,7 @@ bool gemv_supported(const WeightView &w, int64_t M, int r) {
 }
 
 namespace {
-template <int CT, bool XLDS, bool MULTI>
+template <int CT, bool XLDS, bool MULTI, bool DIRECT>
 hipError_t go_gemv1(const GemvArgs &a, int lds_bytes, hipStream_t stream) {
   if (lds_bytes > 64 * 1024) {
     static std::once_flag once[64];
@@ -680,19 +752,23 @@ hipError_t go_gemv1(const GemvArgs &a, int lds_bytes, hipStream_t stream) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::call_once(once[dev], [&] {
-      err[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_kernel<CT, XLDS, MULTI>),
+      err[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_kernel<CT, XLDS, MULTI, DIRECT>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     });
     if (err[dev] != hipSuccess) return err[dev];
   }
-  hipLaunchKernelGGL((gemv_kernel<CT, XLDS, MULTI>), dim3(static_cast<unsigned>(a.G)), dim3(64 * (a.W + (a.R > 0 ? 1 : 0))),
+  hipLaunchKernelGGL((gemv_kernel<CT, XLDS, MULTI, DIRECT>), dim3(static_cast<unsigned>(a.G)), dim3(64 * (a.W + (a.R > 0 ? 1 : 0))),
                      static_cast<size_t>(lds_bytes), stream, a);
   return hipGetLastError();
 }
 template <int CT, bool XLDS>
-hipError_t go_gemv(const GemvArgs &a, int lds_bytes, hipStream_t stream) {
-  return a.PT * a.SP > a.G ? go_gemv1<CT, XLDS, true>(a, lds_bytes, stream)
-                           : go_gemv1<CT, XLDS, false>(a, lds_bytes, stream);
+hipError_t go_gemv(const GemvArgs &a, bool direct, int lds_bytes, hipStream_t stream) {
+  const bool multi = a.PT * a.SP > a.G;
+  if (direct)
+    return multi ? go_gemv1<CT, XLDS, true, true>(a, lds_bytes, stream)
+                 : go_gemv1<CT, XLDS, false, true>(a, lds_bytes, stream);
+  return multi ? go_gemv1<CT, XLDS, true, false>(a, lds_bytes, stream)
+               : go_gemv1<CT, XLDS, false, false>(a, lds_bytes, stream);
 }
 }  // namespace
 
@@ -729,14 +805,14 @@ hipError_t launch_gemv(const WeightView &w, const uint16_t *X, int64_t M, const 
   a.lvl = level_table(w.quant_type);
   switch (w.const_type) {
     case kConstDqInt8:
-      return p.xlds ? go_gemv<kConstDqInt8, true>(a, p.lds_bytes, stream)
-                    : go_gemv<kConstDqInt8, false>(a, p.lds_bytes, stream);
+      return p.xlds ? go_gemv<kConstDqInt8, true>(a, p.direct, p.lds_bytes, stream)
+                    : go_gemv<kConstDqInt8, false>(a, p.direct, p.lds_bytes, stream);
     case kConstDqFp8:
-      return p.xlds ? go_gemv<kConstDqFp8, true>(a, p.lds_bytes, stream)
-                    : go_gemv<kConstDqFp8, false>(a, p.lds_bytes, stream);
+      return p.xlds ? go_gemv<kConstDqFp8, true>(a, p.direct, p.lds_bytes, stream)
+                    : go_gemv<kConstDqFp8, false>(a, p.direct, p.lds_bytes, stream);
     case kConstF32:
-      return p.xlds ? go_gemv<kConstF32, true>(a, p.lds_bytes, stream)
-                    : go_gemv<kConstF32, false>(a, p.lds_bytes, stream);
+      return p.xlds ? go_gemv<kConstF32, true>(a, p.direct, p.lds_bytes, stream)
+                    : go_gemv<kConstF32, false>(a, p.direct, p.lds_bytes, stream);
     default: return hipErrorInvalidValue;
   }
 }
