@@ -74,6 +74,9 @@ constexpr int kFlagBase = 256, kFlagStride = 16, kMaxFlagWGs = 4096;
 static_assert((kSyncTile0 + kMaxRankTiles) * 4 <= kFlagBase, "counter header");
 static_assert(kFlagBase + kMaxFlagWGs * kFlagStride <= static_cast<int>(kGemvSyncBytes), "flags");
 constexpr int kMaxUCopies = 64;
+// DIRECT hand-over: slices of partial sums a LoRA wave loads at once, and the most
+// memory round trips (element passes of 64 lanes x slice chunks) it may take
+constexpr int kGatherChunk = 16, kGatherTrips = 2;
 // U_s is published in several copies too (at most this many bytes in all)
 constexpr size_t kUCopyBudget = 128 * 1024;
 
@@ -195,9 +198,11 @@ __device__ __forceinline__ float constant_of(const StepLoads<CT, XLDS> &st, cons
 }
 
 // LDS layout (one dynamic object): the waves' partial sums [W][64 lanes][4] fp32, then
-// (R > 0) the workgroup's 16 rows of Bl (bf16, as stored: 16 r contiguous elements), then, when X is staged, X [M][KB][XBLK] bytes (each
-// 64-element block permuted per 8-element group, 16 bytes of padding), then (DIRECT
-// hand-over) the part's U_s [M][r] bf16.
+// (R > 0) the workgroup's 16 rows of Bl (bf16, row pitch r8 = r rounded up to 8, zeros
+// past r), then, when X is staged, X [M][KB][XBLK] bytes (each 64-element block permuted
+// per 8-element group, 16 bytes of padding), then (DIRECT hand-over) the part's U_s
+// [M][r8] bf16 (zeros past r).  The padded rows let every LoRA operand of the epilogue be
+// one 16-byte read (a lane whose 8 ranks start past r reads nothing).
 struct LdsPlan {
   int red, bt, x, u, total;
 };
@@ -205,10 +210,11 @@ __host__ __device__ inline int up16(int b) { return (b + 15) & ~15; }
 __host__ __device__ inline LdsPlan lds_plan(int W, int M, int R, int r, int KB, bool xlds, bool direct) {
   LdsPlan p;
   p.red = 0;
+  const int r8 = (r + 7) & ~7;
   p.bt = W * 1024;
-  p.x = p.bt + (R > 0 ? up16(32 * r) : 0);
+  p.x = p.bt + (R > 0 ? 32 * r8 : 0);
   p.u = p.x + (xlds ? M * KB * XBLK : 0);
-  p.total = p.u + (direct ? up16(2 * M * r) : 0);
+  p.total = p.u + (direct ? up16(2 * M * r8) : 0);
   return p;
 }
 
@@ -227,20 +233,6 @@ __device__ __forceinline__ f32x4_t reduce_waves(char *red, f32x4_t acc, int W, i
     }
   }
   return s;
-}
-
-// Eight bf16 of an LDS row, elements j0 .. j0 + 7 (zeros at j >= lim); `aligned`: the
-// eight sit at a 16-byte boundary.
-__device__ __forceinline__ u32x4_t lds_frag8(const uint16_t *row, int j0, int lim, bool aligned) {
-  if (aligned && j0 + 8 <= lim) return *reinterpret_cast<const u32x4_t *>(row + j0);
-  u32x4_t v;
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int j = j0 + 2 * h;
-    const uint32_t lo = j < lim ? row[j] : 0u, hi = j + 1 < lim ? row[j + 1] : 0u;
-    v[h] = lo | (hi << 16);
-  }
-  return v;
 }
 
 // The LoRA wave of a workgroup: for each of its pieces p (rank tile t = p / SP, slice
@@ -378,8 +370,8 @@ __device__ void lora_finish(const GemvArgs &a, const char *sx, int KB, int p, co
 // counter has counted all PT SP pieces, clears it for the next call, and forms the U_s
 // columns of its part itself: U_s[m, j] = bf16(scale * sum over the slices, in slice
 // order, of the partial sums), the same value the ticket path publishes.  It writes them
-// to LDS ([M][r] bf16) for the epilogue, and the first workgroup of the part also stores
-// them to U_saved.
+// to LDS ([M][r8] bf16, zeros past r) for the epilogue, and the first workgroup of the
+// part also stores them to U_saved.
 __device__ void gather_u(const GemvArgs &a, uint16_t *su, int n0) {
   const int lane = threadIdx.x & 63;
   uint32_t *cnt = a.sync + (kFlagBase + blockIdx.x * kFlagStride) / 4;
@@ -393,28 +385,28 @@ __device__ void gather_u(const GemvArgs &a, uint16_t *su, int n0) {
   const int q = a.part_rows > 0 ? n0 / a.part_rows : 0;
   const bool saver = a.U_saved && (a.part_rows > 0 ? n0 % a.part_rows == 0 : blockIdx.x == 0);
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.PU, static_cast<uint32_t>(a.PT) * a.SP * a.M * 64);
-  const int n = a.M * a.r;
+  const int r8 = (a.r + 7) & ~7;
+  const int n = a.M * r8;
   for (int e0 = 0; e0 < n; e0 += 64) {
     const int e = e0 + lane;
-    const bool ok = e < n;
-    const int m = ok ? e / a.r : 0, j = q * a.r + (ok ? e % a.r : 0);
+    const int m = e / r8, jr = e % r8;
+    const bool ok = e < n && jr < a.r;
+    const int j = q * a.r + (ok ? jr : 0);
     const int t = j >> 4, jj = j & 15;
+    // the loads of up to kGatherChunk slices at once: one memory round trip per chunk
     float sum = 0.0f;
-    for (int s0 = 0; s0 < a.SP; s0 += 8) {
-      uint32_t v[8];
+    for (int s0 = 0; s0 < a.SP; s0 += kGatherChunk) {
+      uint32_t v[kGatherChunk];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kGatherChunk; ++i)
         v[i] = __builtin_amdgcn_raw_buffer_load_b32(
             rp, (ok && s0 + i < a.SP) ? (((t * a.SP + s0 + i) * a.M + m) * 16 + jj) * 4 : kOOB, 0, kSC1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kGatherChunk; ++i)
         if (s0 + i < a.SP) sum += __uint_as_float(v[i]);
     }
-    if (ok) {
-      const uint16_t u = to_bf16(a.scale * sum);
-      su[e] = u;
-      if (saver) a.U_saved[m * a.R + j] = u;
-    }
+    if (e < n) su[e] = ok ? to_bf16(a.scale * sum) : static_cast<uint16_t>(0);
+    if (ok && saver) a.U_saved[m * a.R + j] = su[e];
   }
 }
 
@@ -473,7 +465,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
   }
   const int nthr = 64 * W, tid = threadIdx.x;
   const int xpieces = XLDS ? a.M * KB * 8 : 0;
-  const int bpieces = a.R > 0 ? 2 * a.r : 0;
+  // Bl rows: 16-byte pieces when the rows are (r a multiple of 8), else element by element
+  // into rows padded to r8
+  const int r8 = (a.r + 7) & ~7;
+  const int bpieces = (a.R > 0 && r8 == a.r) ? 2 * a.r : 0;
   const uint32_t b_bytes = static_cast<uint32_t>((uint64_t(N) * a.r * 2 + 3) & ~uint64_t(3));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.Bl, b_bytes);
   const uint32_t b_base = static_cast<uint32_t>(n0) * a.r * 2;
@@ -556,6 +551,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
       if (c < bpieces) *reinterpret_cast<u32x4_t *>(sb + 8 * c) = bs[i];
     }
     for (int c = tid + 2 * nthr; c < bpieces; c += nthr) *reinterpret_cast<u32x4_t *>(sb + 8 * c) = load_b(c);
+  } else if (a.R > 0) {
+    for (int e = tid; e < 16 * r8; e += nthr) {
+      const int row = e / r8, j = e % r8;
+      const bool ok = j < a.r && n0 + row < N;
+      sb[e] = ok ? static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(
+                       rb, static_cast<uint32_t>((n0 + row) * a.r + j) * 2, 0, 0))
+                 : static_cast<uint16_t>(0);
+    }
   }
   __syncthreads();
   StepLoads<CT, XLDS> st[D];
@@ -585,13 +588,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
 
   if (DIRECT && a.R > 0) {
     // U_s of this part is in LDS (the LoRA wave put it there before the barrier)
-    const uint16_t *urow = reinterpret_cast<const uint16_t *>(lds + lp.u) + tok * a.r;
-    const uint16_t *brow = sb + ml * a.r;
-    const bool aligned = (a.r & 7) == 0;
+    const uint16_t *urow = reinterpret_cast<const uint16_t *>(lds + lp.u) + tok * r8;
+    const uint16_t *brow = sb + ml * r8;
     for (int c = 0; c < a.r; c += 32) {
       const int j0 = c + 8 * g;
-      const u32x4_t bf = lds_frag8(brow, j0, a.r, aligned);
-      const u32x4_t uf = tok_ok ? lds_frag8(urow, j0, a.r, aligned) : u32x4_t{0u, 0u, 0u, 0u};
+      const bool in = j0 < a.r;
+      u32x4_t bf = *reinterpret_cast<const u32x4_t *>(brow + (in ? j0 : 0));
+      u32x4_t uf = *reinterpret_cast<const u32x4_t *>(urow + (in ? j0 : 0));
+      if (!in) bf = u32x4_t{0u, 0u, 0u, 0u};
+      if (!(in && tok_ok)) uf = u32x4_t{0u, 0u, 0u, 0u};
       y = mfma16x16x32(bf, uf, y);
     }
   } else if (a.R > 0) {
@@ -610,11 +615,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
     // operand) from the staged Bl tile, tokens (the B operand) from U_s
     const int q = a.part_rows > 0 ? n0 / a.part_rows : 0;
     const bool aligned = (a.r & 7) == 0;
-    const uint16_t *brow = sb + ml * a.r;
+    const uint16_t *brow = sb + ml * r8;
     const uint32_t ubase = static_cast<uint32_t>((blockIdx.x % a.NC) * a.UCE + tok * RP + q * a.r);
     for (int c = 0; c < a.r; c += 32) {
       const int j0 = c + 8 * g;
-      const u32x4_t bf = lds_frag8(brow, j0, a.r, aligned);
+      u32x4_t bf = *reinterpret_cast<const u32x4_t *>(brow + (j0 < a.r ? j0 : 0));
+      if (j0 >= a.r) bf = u32x4_t{0u, 0u, 0u, 0u};
       u32x4_t uf = u32x4_t{0u, 0u, 0u, 0u};
       if (tok_ok && j0 < a.r) {
         if (aligned) {
@@ -706,10 +712,12 @@ GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int R) {
   p.LB = (KB + 15) / 16;
   if (p.LB > lb_max) p.LB = lb_max;
   p.SP = (KB + p.LB - 1) / p.LB;
-  // Every workgroup reads M R SP partial sums in the DIRECT hand-over: taken while that
-  // stays small (and the U_s tile fits the LDS share); else the last piece of each rank
-  // tile publishes U_s once.
-  p.direct = R > 0 && M * R * p.SP * 4 <= 32 * 1024 &&
+  // In the DIRECT hand-over the LoRA wave of every workgroup loads its part's M r SP
+  // partial sums (r <= R): taken when that costs at most kGatherTrips memory round trips
+  // (and the U_s tile fits the LDS share); else the last piece of each rank tile
+  // publishes U_s once.
+  const int64_t passes = (M * ((R + 7) & ~7) + 63) / 64, chunks = (p.SP + kGatherChunk - 1) / kGatherChunk;
+  p.direct = R > 0 && passes * chunks <= kGatherTrips &&
              (!p.xlds || lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, true, true).total <= xlds_budget(N));
   p.lds_bytes = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, p.xlds, p.direct).total;
   return p;

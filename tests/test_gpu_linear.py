@@ -64,6 +64,8 @@ SMALL = [  # (M, K, N, r)
     (12, 4096, 40, 16),    # M <= 16, X too large to stage in LDS: X fragments from memory
     (1, 64, 65552, 4),     # M = 1 past 4096 tiles of 16 rows: the fused GEMM takes it
     (3, 256, 48, 256),     # more LoRA pieces than workgroups: a LoRA wave takes several
+    (1, 1024, 48, 64),     # the same with the U_s hand-over through per-workgroup counters
+    (16, 1024, 520, 8),    # M = 16 with that hand-over (M r within its bound)
 ]
 
 
