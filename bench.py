@@ -656,7 +656,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--time-every", type=int, default=4,
                     help="record the GEMM launch events on every n-th timed step (1 = every step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
