@@ -135,12 +135,14 @@ def test_identity_input_gives_weight_bitwise(lib, M, K, N):
 def test_deterministic(lib, N, const_type):
     """Repeated calls are bitwise equal, for every block-constant type and both dX kernels
     (N % 8 == 0 takes the pipelined one, N = 644 the plain one), forward at M > 16 and
-    M <= 16.  A wait that does not cover its loads would show as a run-to-run difference."""
+    M <= 16 (M = 5 hands U_s over through the ticket path, M = 1 through the per-workgroup
+    counters).  A wait that does not cover its loads would show as a run-to-run difference."""
     import torch
     M, K, r = 700, 1024, 64
     d = synth.case(M, K, N, r, seed=3)
     qw = lib.quantize(gc.dev_weight(d), const_type=const_type)
     X5 = gc.dev_bf16(d["X"][:5])
+    X1 = gc.dev_bf16(d["X"][:1])
     X, A, B = _dev(d, r)
     dYt = gc.dev_bf16(d["dY"])
     outs = []
@@ -148,7 +150,8 @@ def test_deterministic(lib, N, const_type):
         Y, U = lib.linear_fwd(qw, X, A, B, 16.0)
         g = lib.linear_bwd(qw, dYt, X, A, B, 16.0, U)
         Y5, U5 = lib.linear_fwd(qw, X5, A, B, 16.0)
-        outs.append([Y.clone(), U.clone(), *[t.clone() for t in g], Y5.clone(), U5.clone()])
+        Y1, U1 = lib.linear_fwd(qw, X1, A, B, 16.0)
+        outs.append([Y.clone(), U.clone(), *[t.clone() for t in g], Y5.clone(), U5.clone(), Y1.clone(), U1.clone()])
     torch.cuda.synchronize()
     for later in outs[1:]:
         for a, b in zip(outs[0], later):
