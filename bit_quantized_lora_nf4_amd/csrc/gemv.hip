@@ -59,7 +59,10 @@ namespace {
 
 constexpr int GMAXM = 16;
 constexpr int kMaxWaves = 16;
-constexpr int XBLK = 144;            // LDS bytes per 64-element block of a staged X row (128 + pad)
+// LDS bytes of one token's staged X row: 128 per 64-element block plus 16 of padding, so
+// that the rows of consecutive tokens start 16 bytes apart modulo 256 and the 16-byte
+// reads of the sixteen token lanes fall in distinct banks
+__host__ __device__ constexpr int xrow_bytes(int KB) { return KB * 128 + 16; }
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr int kSC1 = 16;             // buffer cache policy: SC1 (agent-coherent access)
 // counter words at the start of the workspace
@@ -199,8 +202,8 @@ __device__ __forceinline__ float constant_of(const StepLoads<CT, XLDS> &st, cons
 
 // LDS layout (one dynamic object): the waves' partial sums [W][64 lanes][4] fp32, then
 // (R > 0) the workgroup's 16 rows of Bl (bf16, row pitch r8 = r rounded up to 8, zeros
-// past r), then, when X is staged, X [M][KB][XBLK] bytes (each 64-element block permuted
-// per 8-element group, 16 bytes of padding), then (DIRECT hand-over) the part's U_s
+// past r), then, when X is staged, X [M] rows of xrow_bytes(KB) (each 64-element block
+// permuted per 8-element group), then (DIRECT hand-over) the part's U_s
 // [M][r8] bf16 (zeros past r).  The padded rows let every LoRA operand of the epilogue be
 // one 16-byte read (a lane whose 8 ranks start past r reads nothing).
 struct LdsPlan {
@@ -213,7 +216,7 @@ __host__ __device__ inline LdsPlan lds_plan(int W, int M, int R, int r, int KB, 
   const int r8 = (r + 7) & ~7;
   p.bt = W * 1024;
   p.x = p.bt + (R > 0 ? 32 * r8 : 0);
-  p.u = p.x + (xlds ? M * KB * XBLK : 0);
+  p.u = p.x + (xlds ? M * xrow_bytes(KB) : 0);
   p.total = p.u + (direct ? up16(2 * M * r8) : 0);
   return p;
 }
@@ -298,7 +301,7 @@ __device__ void lora_finish(const GemvArgs &a, const char *sx, int KB, int p, co
     for (int u = 0; u < 8; ++u) {
       if constexpr (XLDS) {
         // the staged X is permuted per 8-element group: permute A the same way
-        const u32x4_t x = *reinterpret_cast<const u32x4_t *>(sx + (tok * KB + (ok ? b : 0)) * XBLK + u * 16);
+        const u32x4_t x = *reinterpret_cast<const u32x4_t *>(sx + tok * xrow_bytes(KB) + (ok ? b : 0) * 128 + u * 16);
         acc = mfma16x16x32(permute8(ll.av[i][u]), x, acc);
       } else {
         acc = mfma16x16x32(ll.av[i][u], ll.xv[i][u], acc);
@@ -472,7 +475,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
   const uint32_t b_bytes = static_cast<uint32_t>((uint64_t(N) * a.r * 2 + 3) & ~uint64_t(3));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.Bl, b_bytes);
   const uint32_t b_base = static_cast<uint32_t>(n0) * a.r * 2;
-  auto x_lds = [&](int c) { return sx + (c / (KB * 8) * KB + (c % (KB * 8)) / 8) * XBLK + (c % 8) * 16; };
+  auto x_lds = [&](int c) { return sx + (c / (KB * 8)) * xrow_bytes(KB) + (c % (KB * 8)) * 16; };
   u32x4_t xs[2], bs[2];
   if constexpr (XLDS) {
 #pragma unroll
@@ -524,7 +527,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
       const uint32_t cw = u < 4 ? s.c0[u] : s.c1[u - 4];
       u32x4_t xv;
       if constexpr (XLDS)
-        xv = *reinterpret_cast<const u32x4_t *>(sx + (tok * KB + (b < kb1 ? b : kb0)) * XBLK + u * 16);
+        xv = *reinterpret_cast<const u32x4_t *>(sx + tok * xrow_bytes(KB) + (b < kb1 ? b : kb0) * 128 + u * 16);
       else
         xv = permute8(s.x[u]);
       acc = mfma16x16x32(lookup8_pairs(cw, pl), xv, acc);
