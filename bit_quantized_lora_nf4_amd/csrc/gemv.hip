@@ -48,6 +48,7 @@
 // every 8-element group, so the contraction pairs the right elements without
 // re-interleaving the decoded weights.
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -80,6 +81,8 @@ constexpr int kMaxUCopies = 64;
 // DIRECT hand-over: slices of partial sums a LoRA wave loads at once, and the most
 // memory round trips (element passes of 64 lanes x slice chunks) it may take
 constexpr int kGatherChunk = 16, kGatherTrips = 2;
+// with several row groups per workgroup a call runs longer, and the gather may take more
+constexpr int kGatherTripsRG = 4;
 // U_s is published in several copies too (at most this many bytes in all)
 constexpr size_t kUCopyBudget = 128 * 1024;
 
@@ -96,7 +99,8 @@ struct GemvArgs {
   int NC, UCE;
   float scale;
   int M, R, r, part_rows;
-  int W, T;             // weight waves per workgroup, steps of 4 blocks per weight wave
+  int W, T;             // weight waves per row group, steps of 4 blocks per weight wave
+  int RG;               // row groups (16-row tiles) per workgroup, sharing the staged X
   int PT, SP, LB, G;    // rank tiles, pieces per rank tile and their 64-blocks, workgroups
   LevelTable lvl;
 };
@@ -200,9 +204,9 @@ __device__ __forceinline__ float constant_of(const StepLoads<CT, XLDS> &st, cons
   return ok ? __builtin_fmaf(c8, s, o) : 0.0f;
 }
 
-// LDS layout (one dynamic object): the waves' partial sums [W][64 lanes][4] fp32, then
-// (R > 0) the workgroup's 16 rows of Bl (bf16, row pitch r8 = r rounded up to 8, zeros
-// past r), then, when X is staged, X [M] rows of xrow_bytes(KB) (each 64-element block
+// LDS layout (one dynamic object): the weight waves' partial sums [RG W][64 lanes][4]
+// fp32, then (R > 0) the workgroup's 16 RG rows of Bl (bf16, row pitch r8 = r rounded up
+// to 8, zeros past r), then, when X is staged, X [M] rows of xrow_bytes(KB) (each 64-element block
 // permuted per 8-element group), then (DIRECT hand-over) the part's U_s
 // [M][r8] bf16 (zeros past r).  The padded rows let every LoRA operand of the epilogue be
 // one 16-byte read (a lane whose 8 ranks start past r reads nothing).
@@ -210,12 +214,12 @@ struct LdsPlan {
   int red, bt, x, u, total;
 };
 __host__ __device__ inline int up16(int b) { return (b + 15) & ~15; }
-__host__ __device__ inline LdsPlan lds_plan(int W, int M, int R, int r, int KB, bool xlds, bool direct) {
+__host__ __device__ inline LdsPlan lds_plan(int nW, int M, int R, int r, int KB, bool xlds, bool direct, int RG) {
   LdsPlan p;
   p.red = 0;
   const int r8 = (r + 7) & ~7;
-  p.bt = W * 1024;
-  p.x = p.bt + (R > 0 ? 32 * r8 : 0);
+  p.bt = nW * 1024;
+  p.x = p.bt + (R > 0 ? 32 * r8 * RG : 0);
   p.u = p.x + (xlds ? M * xrow_bytes(KB) : 0);
   p.total = p.u + (direct ? up16(2 * M * r8) : 0);
   return p;
@@ -417,18 +421,20 @@ template <int CT, bool XLDS, bool MULTI, bool DIRECT>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int D = XLDS ? 4 : 2;  // steps whose loads are in flight (the register ring)
-  const int W = a.W;  // weight waves; wave W (R > 0) is the LoRA wave
+  // RG row groups of W weight waves each; wave RG W (R > 0) is the LoRA wave
+  const int W = a.W, RG = a.RG, nW = RG * W;
   const int N = static_cast<int>(a.w.n_rows), KB = static_cast<int>(a.w.n_cols / 64), K = KB * 64;
-  const LdsPlan lp = lds_plan(W, a.M, a.R, a.r, KB, XLDS, DIRECT);
+  const LdsPlan lp = lds_plan(nW, a.M, a.R, a.r, KB, XLDS, DIRECT, RG);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ml = lane & 15, g = lane >> 4;
-  const int tile = blockIdx.x;
-  const int n0 = tile * 16;
+  const int grp = wave / W, wv = wave - grp * W;  // row group and wave within it
+  const int n0w = static_cast<int>(blockIdx.x) * RG * 16;  // first row of the workgroup
+  const int n0 = n0w + grp * 16;
   const int n = n0 + ml;  // weight row of this lane's operand
   const bool row_ok = n < N;
   const int tok = ml < a.M ? ml : 0;
   const bool tok_ok = ml < a.M;
-  const int kb0 = (KB * wave) / W, kb1 = (KB * (wave + 1)) / W;
+  const int kb0 = (KB * wv) / W, kb1 = (KB * (wv + 1)) / W;
   const int Tw = (kb1 - kb0 + 3) / 4;  // this wave's steps (at most T)
 
   const uint32_t n_blocks = static_cast<uint32_t>(uint64_t(N) * KB);
@@ -444,7 +450,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
   // contiguous 32 r bytes; Bl is read to its last element's whole dword).  They are
   // staged before the first weight load is issued: a load issued behind the weight
   // stream of the whole chip would arrive only when that stream has drained.
-  if (wave == W) {
+  if (wave == nW) {
     // The LoRA wave: it takes no part in the staging and issues the loads of its first
     // piece at once, ahead of the weight stream.  It passes the same two barriers as the
     // weight waves (the staging barrier and the one of the final reduction).
@@ -462,19 +468,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
       }
     }
     // DIRECT: U_s for the epilogue, in LDS before the reduction barrier
-    if constexpr (DIRECT) gather_u(a, reinterpret_cast<uint16_t *>(lds + lp.u), static_cast<int>(blockIdx.x) * 16);
+    if constexpr (DIRECT) gather_u(a, reinterpret_cast<uint16_t *>(lds + lp.u), n0w);
     __syncthreads();
     return;
   }
-  const int nthr = 64 * W, tid = threadIdx.x;
+  const int nthr = 64 * nW, tid = threadIdx.x;
   const int xpieces = XLDS ? a.M * KB * 8 : 0;
   // Bl rows: 16-byte pieces when the rows are (r a multiple of 8), else element by element
   // into rows padded to r8
   const int r8 = (a.r + 7) & ~7;
-  const int bpieces = (a.R > 0 && r8 == a.r) ? 2 * a.r : 0;
+  const int bpieces = (a.R > 0 && r8 == a.r) ? 2 * a.r * RG : 0;
   const uint32_t b_bytes = static_cast<uint32_t>((uint64_t(N) * a.r * 2 + 3) & ~uint64_t(3));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.Bl, b_bytes);
-  const uint32_t b_base = static_cast<uint32_t>(n0) * a.r * 2;
+  const uint32_t b_base = static_cast<uint32_t>(n0w) * a.r * 2;
   auto x_lds = [&](int c) { return sx + (c / (KB * 8)) * xrow_bytes(KB) + (c % (KB * 8)) * 16; };
   u32x4_t xs[2], bs[2];
   if constexpr (XLDS) {
@@ -555,11 +561,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
     }
     for (int c = tid + 2 * nthr; c < bpieces; c += nthr) *reinterpret_cast<u32x4_t *>(sb + 8 * c) = load_b(c);
   } else if (a.R > 0) {
-    for (int e = tid; e < 16 * r8; e += nthr) {
+    for (int e = tid; e < 16 * RG * r8; e += nthr) {
       const int row = e / r8, j = e % r8;
-      const bool ok = j < a.r && n0 + row < N;
+      const bool ok = j < a.r && n0w + row < N;
       sb[e] = ok ? static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(
-                       rb, static_cast<uint32_t>((n0 + row) * a.r + j) * 2, 0, 0))
+                       rb, static_cast<uint32_t>((n0w + row) * a.r + j) * 2, 0, 0))
                  : static_cast<uint16_t>(0);
     }
   }
@@ -585,14 +591,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
   for (int j = 0; j < D; ++j)
     if (t0 + j < Tw) compute(st[j], t0 + j);
 
-  f32x4_t y = reduce_waves(lds + lp.red, acc, W, wave, lane);
-  if (wave != 0) return;
+  f32x4_t y = reduce_waves(lds + lp.red + grp * W * 1024, acc, W, wv, lane);
+  if (wv != 0) return;
   // lane: token ml, weight rows n0 + 4 g + e
 
   if (DIRECT && a.R > 0) {
     // U_s of this part is in LDS (the LoRA wave put it there before the barrier)
     const uint16_t *urow = reinterpret_cast<const uint16_t *>(lds + lp.u) + tok * r8;
-    const uint16_t *brow = sb + ml * r8;
+    const uint16_t *brow = sb + (grp * 16 + ml) * r8;
     for (int c = 0; c < a.r; c += 32) {
       const int j0 = c + 8 * g;
       const bool in = j0 < a.r;
@@ -604,7 +610,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
     }
   } else if (a.R > 0) {
     // U_s from the LoRA waves: poll this workgroup's flag (and clear it for the next
-    // call), then read this workgroup's copy of U_s
+    // call), then read this workgroup's copy of U_s (one row group per workgroup on this
+    // path: the host takes several only with the DIRECT hand-over)
     uint32_t *flag = a.sync + (kFlagBase + blockIdx.x * kFlagStride) / 4;
     for (uint32_t it = 0; it < kSpinLimit; ++it) {
       if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
@@ -618,7 +625,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
     // operand) from the staged Bl tile, tokens (the B operand) from U_s
     const int q = a.part_rows > 0 ? n0 / a.part_rows : 0;
     const bool aligned = (a.r & 7) == 0;
-    const uint16_t *brow = sb + ml * r8;
+    const uint16_t *brow = sb + (grp * 16 + ml) * r8;
     const uint32_t ubase = static_cast<uint32_t>((blockIdx.x % a.NC) * a.UCE + tok * RP + q * a.r);
     for (int c = 0; c < a.r; c += 32) {
       const int j0 = c + 8 * g;
@@ -682,13 +689,29 @@ GemvShape gemv_shape(int64_t N, int64_t K, int max_cu_waves, int extra) {
   return best;
 }
 
-// LDS bytes a main workgroup may use for staged X: a share of the 160 KB of a CU among
-// the workgroups that one round of the grid puts on it.
-int xlds_budget(int64_t N) {
-  const int64_t tiles = (N + 15) / 16;
-  const int64_t per_cu = (tiles + 255) / 256;
-  const int64_t b = (160 * 1024) / (per_cu < 1 ? 1 : per_cu);
-  return static_cast<int>(b > 128 * 1024 ? 128 * 1024 : b);
+// Row groups of W weight waves in workgroups of RG tiles, one workgroup per CU: W
+// minimises the busiest SIMD's wave-steps within the 16 waves of a workgroup.
+GemvShape gemv_shape_rg(int64_t K, int RG, int extra) {
+  const int64_t KB = K / 64;
+  GemvShape best{1, static_cast<int>((KB + 3) / 4)};
+  double best_cost = 1e30;
+  for (int W = 1; RG * W + extra <= kMaxWaves && W <= KB; ++W) {
+    const int64_t T = ((KB + W - 1) / W + 3) / 4;
+    const int64_t per_simd = (RG * W + 3) / 4;
+    const double cost = double(per_simd * T) * (per_simd == 1 ? 1.3 : 1.0);
+    if (cost < best_cost - 1e-9 || (cost < best_cost + 1e-9 && T < best.T)) {
+      best_cost = cost;
+      best = {W, static_cast<int>(T)};
+    }
+  }
+  return best;
+}
+
+// LDS bytes a workgroup may use: the 160 KB of a CU shared among the workgroups that one
+// round of the grid (of `wgs` workgroups) puts on it.
+int lds_budget(int64_t wgs) {
+  const int64_t per_cu = (wgs + 255) / 256;
+  return static_cast<int>((160 * 1024) / (per_cu < 1 ? 1 : per_cu));
 }
 
 // The launch configuration: shape, whether X is staged in LDS, LDS bytes, and the LoRA
@@ -696,33 +719,56 @@ int xlds_budget(int64_t N) {
 // 4 without: the blocks whose loads a LoRA wave keeps in flight at once).
 struct GemvPlan {
   GemvShape sh;
+  int RG;       // row groups per workgroup
   bool xlds;
   bool direct;  // U_s handed over through per-workgroup counters (gather_u)
   int lds_bytes;
   int LB, SP;
 };
-// Depends on (M, K, N, R) alone, so that the workspace size is known before the call
-// (the Bl tile is taken at its largest, r = R, for the choice of staging X).
-GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int R) {
-  const int KB = static_cast<int>(K / 64);
-  const int extra = R > 0 ? 1 : 0;
-  GemvPlan p;
-  // staged X: about 100 VGPRs (5 waves per SIMD); X from memory: about 130 (4)
-  p.sh = gemv_shape(N, K, 20, extra);
-  p.xlds = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, true, false).total <= xlds_budget(N);
-  if (!p.xlds) p.sh = gemv_shape(N, K, 16, extra);
+// LoRA pieces: about 16 slices of LB 64-blocks per rank tile.
+void lora_slices(GemvPlan &p, int KB) {
   const int lb_max = p.xlds ? 8 : 4;
   p.LB = (KB + 15) / 16;
   if (p.LB > lb_max) p.LB = lb_max;
   p.SP = (KB + p.LB - 1) / p.LB;
-  // In the DIRECT hand-over the LoRA wave of every workgroup loads its part's M r SP
-  // partial sums (r <= R): taken when that costs at most kGatherTrips memory round trips
-  // (and the U_s tile fits the LDS share); else the last piece of each rank tile
-  // publishes U_s once.
-  const int64_t passes = (M * ((R + 7) & ~7) + 63) / 64, chunks = (p.SP + kGatherChunk - 1) / kGatherChunk;
-  p.direct = R > 0 && passes * chunks <= kGatherTrips &&
-             (!p.xlds || lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, true, true).total <= xlds_budget(N));
-  p.lds_bytes = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, p.xlds, p.direct).total;
+}
+// In the DIRECT hand-over the LoRA wave of every workgroup loads its part's M r SP
+// partial sums (r <= R): taken when that costs at most `trips` memory round trips; else
+// the last piece of each rank tile publishes U_s once.
+bool gather_ok(int64_t M, int R, int SP, int trips) {
+  const int64_t passes = (M * ((R + 7) & ~7) + 63) / 64, chunks = (SP + kGatherChunk - 1) / kGatherChunk;
+  return R > 0 && passes * chunks <= trips;
+}
+// Depends on (M, K, N, R) alone (and on whether several row groups may share a
+// workgroup), so that the workspace size is known before the call (the Bl tile is taken
+// at its largest, r = R, for the choice of staging X).
+GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int R, bool allow_rg = true) {
+  const int KB = static_cast<int>(K / 64);
+  const int extra = R > 0 ? 1 : 0;
+  const int64_t tiles = (N + 15) / 16;
+  GemvPlan p;
+  p.RG = 1;
+  // staged X: about 100 VGPRs (5 waves per SIMD); X from memory: about 130 (4)
+  p.sh = gemv_shape(N, K, 20, extra);
+  p.xlds = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, true, true, 1).total <= lds_budget(tiles);
+  // X too large to stage beside several workgroups per CU: workgroups of RG tiles, one
+  // per CU, share one staged copy (they need the DIRECT hand-over: the ticket path polls
+  // a flag per workgroup from each row group's leader)
+  const int rg = static_cast<int>((tiles + 255) / 256);
+  if (!p.xlds && allow_rg && rg > 1 && rg <= 4) {
+    GemvPlan q = p;
+    q.RG = rg;
+    q.sh = gemv_shape_rg(K, rg, extra);
+    q.xlds = true;
+    lora_slices(q, KB);
+    if (lds_plan(rg * q.sh.W, static_cast<int>(M), R, R, KB, true, true, rg).total <= 160 * 1024 &&
+        (R == 0 || gather_ok(M, R, q.SP, kGatherTripsRG)))
+      p = q;
+  }
+  if (!p.xlds) p.sh = gemv_shape(N, K, 16, extra);
+  lora_slices(p, KB);
+  p.direct = gather_ok(M, R, p.SP, p.RG > 1 ? kGatherTripsRG : kGatherTrips);
+  p.lds_bytes = lds_plan(p.RG * p.sh.W, static_cast<int>(M), R, R, KB, p.xlds, p.direct, p.RG).total;
   return p;
 }
 
@@ -741,7 +787,8 @@ int gemv_u_copies(int64_t M, int R) {
 // Layout: the counter / flag header, the NC copies of U_s, the LoRA partial sums.
 size_t gemv_workspace(int64_t M, int64_t K, int64_t N, int r) {
   const size_t PT = static_cast<size_t>((r + 15) / 16);
-  const size_t SP = static_cast<size_t>(gemv_plan(M, K, N, r).SP);
+  // a fused call whose parts do not align with the row groups falls back to one group
+  const size_t SP = static_cast<size_t>(std::max(gemv_plan(M, K, N, r).SP, gemv_plan(M, K, N, r, false).SP));
   const size_t NC = static_cast<size_t>(gemv_u_copies(M, r));
   return kGemvSyncBytes + NC * up256(static_cast<size_t>(M) * PT * 16 * 2) + up256(PT * SP * M * 16 * 4);
 }
@@ -768,7 +815,8 @@ hipError_t go_gemv1(const GemvArgs &a, int lds_bytes, hipStream_t stream) {
     });
     if (err[dev] != hipSuccess) return err[dev];
   }
-  hipLaunchKernelGGL((gemv_kernel<CT, XLDS, MULTI, DIRECT>), dim3(static_cast<unsigned>(a.G)), dim3(64 * (a.W + (a.R > 0 ? 1 : 0))),
+  hipLaunchKernelGGL((gemv_kernel<CT, XLDS, MULTI, DIRECT>), dim3(static_cast<unsigned>(a.G)),
+                     dim3(64 * (a.RG * a.W + (a.R > 0 ? 1 : 0))),
                      static_cast<size_t>(lds_bytes), stream, a);
   return hipGetLastError();
 }
@@ -789,7 +837,9 @@ hipError_t launch_gemv(const WeightView &w, const uint16_t *X, int64_t M, const 
   if (!gemv_supported(w, M, R) || R < r || (part_rows > 0 && (w.n_rows % part_rows != 0 || part_rows % 16 != 0)))
     return hipErrorInvalidValue;
   const int64_t N = w.n_rows, K = w.n_cols;
-  const GemvPlan p = gemv_plan(M, K, N, R);
+  GemvPlan p = gemv_plan(M, K, N, R);
+  // the row groups of a workgroup must lie in one part (they share its U_s)
+  if (p.RG > 1 && part_rows > 0 && part_rows % (16 * p.RG) != 0) p = gemv_plan(M, K, N, R, false);
   GemvArgs a;
   a.w = w;
   a.X = X;
@@ -809,10 +859,11 @@ hipError_t launch_gemv(const WeightView &w, const uint16_t *X, int64_t M, const 
   a.r = r;
   a.part_rows = static_cast<int>(part_rows);
   a.W = p.sh.W;
+  a.RG = p.RG;
   a.T = p.sh.T;
   a.LB = p.LB;
   a.SP = R > 0 ? p.SP : 0;
-  a.G = static_cast<int>((N + 15) / 16);
+  a.G = static_cast<int>(((N + 15) / 16 + p.RG - 1) / p.RG);
   a.lvl = level_table(w.quant_type);
   switch (w.const_type) {
     case kConstDqInt8:

@@ -66,6 +66,9 @@ SMALL = [  # (M, K, N, r)
     (3, 256, 48, 256),     # more LoRA pieces than workgroups: a LoRA wave takes several
     (1, 1024, 48, 64),     # the same with the U_s hand-over through per-workgroup counters
     (16, 1024, 520, 8),    # M = 16 with that hand-over (M r within its bound)
+    (16, 4096, 7990, 16),  # X staged once for 2 row groups per workgroup (one per CU), ragged last tile
+    (16, 4096, 11008, 16), # 3 row groups per workgroup; the last workgroup holds one
+    (12, 4096, 5000, 0),   # row groups without an adapter
 ]
 
 
