@@ -67,7 +67,10 @@ def test_concat_rows_is_the_stacked_quantization(q):
 # (P, part rows, K, r, M): GEMV path (M <= 16) and GEMM path, ragged K and M, the
 # q/k/v (3 parts) and gate/up (2 parts) layouts, and no adapter.
 CASES = [(3, 256, 320, 8, 5), (3, 256, 320, 16, 300), (2, 512, 1024, 32, 1), (2, 256, 512, 64, 257),
-         (3, 256, 256, 0, 70), (4, 256, 192, 8, 33)]
+         (3, 256, 256, 0, 70), (4, 256, 192, 8, 33),
+         # M = 16 with X shared by 2 row groups per workgroup (parts of 160 tiles align with
+         # the groups), and with parts that do not (161 tiles: one row group per workgroup)
+         (2, 2560, 4096, 8, 16), (2, 2576, 4096, 8, 16)]
 
 
 @pytest.mark.parametrize("P,Np,K,r,M", CASES)
