@@ -69,8 +69,9 @@ def test_concat_rows_is_the_stacked_quantization(q):
 CASES = [(3, 256, 320, 8, 5), (3, 256, 320, 16, 300), (2, 512, 1024, 32, 1), (2, 256, 512, 64, 257),
          (3, 256, 256, 0, 70), (4, 256, 192, 8, 33),
          # M = 16 with X shared by 2 row groups per workgroup (parts of 160 tiles align with
-         # the groups), and with parts that do not (161 tiles: one row group per workgroup)
-         (2, 2560, 4096, 8, 16), (2, 2576, 4096, 8, 16)]
+         # the groups), and with parts of 272 tiles, which workgroups of 3 row groups would
+         # straddle (one row group per workgroup then)
+         (2, 2560, 4096, 8, 16), (2, 4352, 4096, 8, 16)]
 
 
 @pytest.mark.parametrize("P,Np,K,r,M", CASES)
@@ -90,7 +91,10 @@ def test_fused_matches_parts_and_oracle(q, P, Np, K, r, M):
         Ai = A[i * r:(i + 1) * r].contiguous() if r else None
         Bi = B[i * Np:(i + 1) * Np].contiguous() if r else None
         Yi, Ui = q.linear_fwd(qws[i], X, Ai, Bi, alpha)
-        dXi, dAi, dBi = q.linear_bwd(qws[i], dY[:, i * Np:(i + 1) * Np].contiguous(), X, Ai, Bi, alpha, Ui)
+        # the backward of a part from the fused call's U_s columns: at M <= 16 the parts'
+        # own U_s may round differently (see below)
+        Uf = U[:, i * r:(i + 1) * r].contiguous() if r else None
+        dXi, dAi, dBi = q.linear_bwd(qws[i], dY[:, i * Np:(i + 1) * Np].contiguous(), X, Ai, Bi, alpha, Uf)
         Ys.append(gc.host_bits(Yi))
         dXs.append(gc.host_f32_from_bf16(dXi))
         if r:
@@ -98,9 +102,19 @@ def test_fused_matches_parts_and_oracle(q, P, Np, K, r, M):
             dAs.append(gc.host_bits(dAi))
             dBs.append(gc.host_bits(dBi))
     torch.cuda.synchronize()
-    assert np.array_equal(gc.host_bits(Y), np.concatenate(Ys, axis=1))
+    if M > 16:
+        assert np.array_equal(gc.host_bits(Y), np.concatenate(Ys, axis=1))
+        if r:
+            assert np.array_equal(gc.host_bits(U), np.concatenate(Us, axis=1))
+    else:
+        # the small-M forward splits K over a number of waves (and U_s over slices) chosen
+        # for the launch's shape, so the fused call and its parts may round their fp32 sums
+        # differently
+        f32 = lambda bits: synth.bf16_bits_to_f32(bits).astype(np.float64)  # noqa: E731
+        _check("Y vs the parts", gc.host_f32_from_bf16(Y), f32(np.concatenate(Ys, axis=1)))
+        if r:
+            _check("U vs the parts", gc.host_f32_from_bf16(U), f32(np.concatenate(Us, axis=1)))
     if r:
-        assert np.array_equal(gc.host_bits(U), np.concatenate(Us, axis=1))
         assert np.array_equal(gc.host_bits(dA), np.concatenate(dAs))
         assert np.array_equal(gc.host_bits(dB), np.concatenate(dBs))
     # oracle
@@ -141,7 +155,10 @@ def test_fused_full_size(q, layer):
     for i in range(P):
         Ai, Bi = A[i * r:(i + 1) * r].contiguous(), B[i * Np:(i + 1) * Np].contiguous()
         Yi, Ui = q.linear_fwd(qws[i], X, Ai, Bi, alpha)
-        dXi, dAi, dBi = q.linear_bwd(qws[i], dY[:, i * Np:(i + 1) * Np].contiguous(), X, Ai, Bi, alpha, Ui)
+        # the backward of a part from the fused call's U_s columns: at M <= 16 the parts'
+        # own U_s may round differently (see below)
+        Uf = U[:, i * r:(i + 1) * r].contiguous() if r else None
+        dXi, dAi, dBi = q.linear_bwd(qws[i], dY[:, i * Np:(i + 1) * Np].contiguous(), X, Ai, Bi, alpha, Uf)
         assert torch.equal(Y[:, i * Np:(i + 1) * Np], Yi)
         assert torch.equal(U[:, i * r:(i + 1) * r], Ui)
         assert torch.equal(dA[i * r:(i + 1) * r], dAi)
