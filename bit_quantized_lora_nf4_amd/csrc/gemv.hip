@@ -8,7 +8,7 @@
 // work of decoding it (about fifteen byte permutes per eight weights), so the launch is
 // shaped to keep both busy from start to end:
 //
-//   weight waves      a workgroup per 16 weight rows, covering all of K; its W weight
+//   weight waves      a row group per 16 weight rows, covering all of K; its W weight
 //                     waves split K into contiguous block ranges of at most 4 T blocks
 //                     (T steps).  Per step a wave decodes 16 rows x 4 blocks of 64: lane
 //                     (row l % 16, group l / 16) loads the 32 bytes of codes of its block
@@ -17,26 +17,33 @@
 //                     planes, and turns each code dword into an MFMA operand with register
 //                     byte-permute lookups ([Digest] "数学公式与关键细节" item 3).  The dot
 //                     products run on 16x16x32 bf16 MFMA with tokens as the 16 columns
-//                     (columns past M are never stored).  The workgroup first stages X and
-//                     its 16 rows of the LoRA B in LDS, then each wave issues the loads of
-//                     its first D steps (a register ring), so that decoding starts as soon
-//                     as the first step has landed and the weight stream never drains; the
-//                     compiler derives every wait from the register dependencies.  W and T
-//                     are chosen on the host so that the busiest SIMD of the launch runs as
-//                     few wave-steps as possible.  At the end the waves' partial sums are
-//                     added in a fixed order through LDS, and the LoRA up-projection is one
-//                     more MFMA per 32 ranks on the same accumulator, before the single
-//                     bf16 rounding.
+//                     (columns past M are never stored).  A workgroup holds one row group,
+//                     or RG of them (one workgroup per CU) when X would not fit in LDS
+//                     beside several workgroups.  It first stages X and its rows of the
+//                     LoRA B in LDS, then each wave issues the loads of its first D steps
+//                     (a register ring), so that decoding starts as soon as the first step
+//                     has landed and the weight stream never drains; the compiler derives
+//                     every wait from the register dependencies.  W, T and RG are chosen on
+//                     the host so that the busiest SIMD of the launch runs as few
+//                     wave-steps as possible.  At the end each group adds its waves'
+//                     partial sums in a fixed order through LDS, and the LoRA up-projection
+//                     is one more MFMA per 32 ranks on the same accumulator, before the
+//                     single bf16 rounding.
 //   LoRA wave         one more wave per workgroup (R > 0) computes pieces of the
 //                     down-projection X . A^T: 16 ranks over a slice of LB blocks of K,
 //                     with X from the staged copy, and stores the piece's partial sums.
-//                     The last piece of a rank tile to finish (an agent-scope ticket) adds
-//                     the slices in order, rounds U_s and publishes it; the last rank tile
-//                     raises the "U_s complete" flag.  The pieces live in the lowest
-//                     workgroups of the grid, which are dispatched first, so that the
-//                     weight waves, which wait for the flag only in their epilogue, never
-//                     wait for a workgroup that cannot start.  Every counter and flag is
-//                     returned to zero by the last workgroup that uses it.
+//                     U_s then reaches the weight waves one of two ways.  Counter
+//                     hand-over (few partial sums): each piece counts itself on every
+//                     workgroup's counter, and the LoRA wave of each workgroup waits for
+//                     its own counter, adds the slices in order, rounds its part's U_s
+//                     and puts it in LDS before the reduction barrier.  Ticket hand-over:
+//                     the last piece of a rank tile to finish (an agent-scope ticket) adds
+//                     the slices in order, rounds U_s and publishes it in copies; the last
+//                     rank tile raises a flag per workgroup, which the weight waves poll
+//                     in their epilogue.  The pieces live in the lowest workgroups of the
+//                     grid, which are dispatched first, so that no wait is for a workgroup
+//                     that cannot start.  Every counter and flag is returned to zero by
+//                     its last user.
 //
 // Data handed between workgroups (the partial sums, U_s, the counters) is only ever
 // written and read with agent-coherent accesses (the SC1 cache policy: the L2 of one XCD
