@@ -16,7 +16,7 @@ the library on its launch stream, on every --time-every-th step of the timed reg
 an event pair per launch costs a few microseconds of GPU time, so timing every launch
 would slow the step it measures); and the CPU oracle timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--time-every 4] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 15] [--time-every 4] [--no-cpu-baseline]
 """
 
 import argparse
