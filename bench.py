@@ -369,7 +369,7 @@ def weight_bytes(qw):
                                                       qw.absmax) if a is not None)
 
 
-def measure_variants(torch, q, synth, gc, wl, L, ev, steps=5, min_bytes=600 << 20, calls=20):
+def measure_variants(torch, q, synth, gc, wl, L, ev, steps=10, warmup=10, min_bytes=600 << 20, calls=20):
     """The data-type variants (level table x block-constant type) on the same work: the
     M = 4096 training step of the three workload-2 linears, and the M = 1 forward
     kernel on the 4096 -> 11008 weight streamed over distinct copies (bytes as stored)."""
@@ -388,7 +388,7 @@ def measure_variants(torch, q, synth, gc, wl, L, ev, steps=5, min_bytes=600 << 2
     ws1 = q.workspace(0, 1, K1, N1, r1, "cuda")
     for (qt, ct), name in names.items():
         Lv = [dict(e, qw=q.quantize(e["W"], quant_type=qt, const_type=ct)) for e in L]
-        for _ in range(2):
+        for _ in range(warmup):
             run_step(q, wl, Lv)
         torch.cuda.synchronize()
         s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -485,7 +485,7 @@ def measure_merge(torch, q, reps=10):
     return res
 
 
-def measure_layer65b(torch, q, reps=5):
+def measure_layer65b(torch, q, reps=5, warmup=4):
     """LLaMA-65B decoder layer (M = 2048, r = 64, all seven linears, fwd + bwd): the
     linears one by one, and with q/k/v and gate/up horizontally fused (one weight stream
     and one GEMM each for the shared X)."""
@@ -537,7 +537,9 @@ def measure_layer65b(torch, q, reps=5):
 
     res = {}
     for name, fn in (("separate", separate), ("fused", fused)):
-        fn()
+        # the step time settles over a few tens of milliseconds of work after an idle gap
+        for _ in range(warmup):
+            fn()
         torch.cuda.synchronize()
         s, f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
