@@ -332,17 +332,21 @@ int bwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16
     uint16_t *Bt = reinterpret_cast<uint16_t *>(ws + L.bt);
     uint16_t *Vw = reinterpret_cast<uint16_t *>(ws + L.v);
     uint16_t *Atw = reinterpret_cast<uint16_t *>(ws + L.at);
-    // B^T for the V products and, when dX is wanted, A^T for the dX GEMM's rank steps
-    s = launched(qlora::launch_transpose2_bf16(B, N, r, Bt, dX ? A : nullptr, R, K, Atw, st), "transpose(B, A)");
     // part q: V[:, q r ..] = bf16(scale dY_q B_q) and dB_q = bf16(dY_q^T U_q), where dY_q is
-    // columns [q Np, (q + 1) Np) of dY and U_q columns [q r, (q + 1) r) of U_s; both
-    // products in one launch (and one finalize launch) where the shapes allow
+    // columns [q Np, (q + 1) Np) of dY, B_q rows [q Np, (q + 1) Np) of B and U_q columns
+    // [q r, (q + 1) r) of U_s; both products in one launch (and one finalize launch)
+    // where the shapes allow, which reads B as it is and also writes A^T for the dX
+    // GEMM's rank steps (when dX is wanted).  Otherwise B^T and A^T come from a
+    // transpose launch first.
     const bool vdb = qlora::vdb_fast(M, Np, N, R, r);
+    if (!vdb)
+      s = launched(qlora::launch_transpose2_bf16(B, N, r, Bt, dX ? A : nullptr, R, K, Atw, st), "transpose(B, A)");
     float *part2 = reinterpret_cast<float *>(ws + L.part2);
     for (int q = 0; q < parts && s == QLORA_OK; ++q) {
       if (vdb) {
-        s = launched(qlora::launch_vdb(dY + q * Np, M, Np, N, Bt + q * Np, U + q * r, R, r, scale, Vw + q * r,
-                                       dB + q * Np * r, part, part2, st),
+        const bool at = dX && q == 0;
+        s = launched(qlora::launch_vdb(dY + q * Np, M, Np, N, B + q * Np * r, U + q * r, R, r, scale, Vw + q * r,
+                                       dB + q * Np * r, part, part2, at ? A : nullptr, R, K, at ? Atw : nullptr, st),
                      "lora(V, dB)");
         continue;
       }

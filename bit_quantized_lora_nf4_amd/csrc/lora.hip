@@ -55,7 +55,41 @@ constexpr int staged_bytes() {
   return staged_nb<RT>() * (64 + 32 * RT) * 128;
 }
 
-template <int RT, int NB>
+// Row-major tiles of 64 rows x 32 RT bf16 columns (64 RT bytes per row, the 16-byte
+// chunks swizzled within the row when there are a power of two of them): the S tile of
+// reduce_m and the B tile of lora_down over B [Kc, r].
+template <int RT>
+__device__ __forceinline__ int s_swz(int row) {
+  // the S tile's rows hold 4 RT chunks; swizzle within the row when that is a power of two
+  return ((4 * RT) & (4 * RT - 1)) == 0 ? (((row & 7) ^ ((row >> 3) & 1)) & (4 * RT - 1)) : 0;
+}
+// MFMA operand fragment of such a tile read with the transposing LDS read: column
+// cb + (lane % 32) of rows 16 s + 8 (lane / 32) .. + 7 (within a 16-lane group, lane i
+// reads 8 bytes of row base + i / 4 at column 4 (i % 4) of its 16-column half and
+// receives column i of those four rows).
+template <int RT>
+__device__ __forceinline__ u32x4_t frag_rows(const char *tile, int s, int cb) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, gq = lane >> 4;
+  const int col = cb + (gq & 1) * 16 + 4 * (i & 3);
+  u32x4_t v;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int row = 16 * s + 8 * (gq >> 1) + 4 * e + (i >> 2);
+    const int off = row * (64 * RT) + (((col >> 3) ^ s_swz<RT>(row)) << 4) + (col & 7) * 2;
+    const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)(tile + off));
+    const u32x2_t w = __builtin_bit_cast(u32x2_t, t);
+    v[2 * e] = w[0];
+    v[2 * e + 1] = w[1];
+  }
+  return v;
+}
+
+// BK: the adapter operand is given as B [Kc, r] (rows of the contraction, row pitch
+// ldwt) instead of WT [r, Kc]; its step tile (64 contraction rows of r ranks) is staged
+// row-major like reduce_m's S tile and read with the transposing LDS read, so the
+// product V = dY B needs no transposed copy of B.
+template <int RT, int NB, bool BK = false>
 __device__ __forceinline__ void lora_down_dma_body(
     char *sbuf, int bx, int by, const uint16_t *__restrict__ IN, int M, int Kc, int ldin,
     const uint16_t *__restrict__ WT, int ldwt, int r, int KR, float *__restrict__ P) {
@@ -70,10 +104,12 @@ __device__ __forceinline__ void lora_down_dma_body(
   const int kbeg = by * KR, kend = min(Kc, kbeg + KR);
   const int nsteps = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(IN, static_cast<uint32_t>(uint64_t(M) * ldin * 2));
-  const __amdgpu_buffer_rsrc_t rwt = make_rsrc(WT, static_cast<uint32_t>(uint64_t(r) * ldwt * 2));
+  const __amdgpu_buffer_rsrc_t rwt =
+      make_rsrc(WT, static_cast<uint32_t>(uint64_t(BK ? Kc : r) * ldwt * 2));
 
   // per-lane row byte offsets of this wave's loads (kOOB for rows past M or r) and the
-  // 16-byte chunk each lane fetches
+  // 16-byte chunk each lane fetches; BK, loads of the B tile: the lane's tile row (a
+  // contraction offset) in chk and its column's byte offset (kOOB past r) in roff
   uint32_t roff[LPW];
   int chk[LPW];
 #pragma unroll
@@ -81,10 +117,16 @@ __device__ __forceinline__ void lora_down_dma_body(
     const int g = wave + 4 * u;            // load index: rows 8 g .. 8 g + 7 of the step tile
     const int x = 8 * g + (lane >> 3);     // staged row
     chk[u] = (lane & 7) ^ ((x & 7) ^ ((x >> 3) & 1));
-    if (x < 64)
+    if (x < 64) {
       roff[u] = m0 + x < M ? static_cast<uint32_t>(m0 + x) * ldin * 2 : kOOB;
-    else
+    } else if (!BK) {
       roff[u] = x - 64 < r ? static_cast<uint32_t>(x - 64) * ldwt * 2 : kOOB;
+    } else {
+      const int byte = (g - 8) * 1024 + lane * 16;
+      const int bx = byte / (64 * RT), c = ((byte % (64 * RT)) / 16) ^ s_swz<RT>(bx);
+      chk[u] = bx;
+      roff[u] = c * 8 < r ? static_cast<uint32_t>(c) * 16 : kOOB;
+    }
   }
   auto dma = [&](int step) {
     char *dst = sbuf + (step % NB) * BUF;
@@ -92,8 +134,14 @@ __device__ __forceinline__ void lora_down_dma_body(
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int g = wave + 4 * u;
-      const int k = kt + chk[u] * 8;
-      const uint32_t off = (roff[u] != kOOB && k < kend) ? roff[u] + k * 2 : kOOB;
+      uint32_t off;
+      if (BK && 8 * g >= 64) {
+        const int k = kt + chk[u];
+        off = (roff[u] != kOOB && k < kend) ? static_cast<uint32_t>(k) * ldwt * 2 + roff[u] : kOOB;
+      } else {
+        const int k = kt + chk[u] * 8;
+        off = (roff[u] != kOOB && k < kend) ? roff[u] + k * 2 : kOOB;
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(8 * g < 64 ? rin : rwt,
                                                (__attribute__((address_space(3))) void *)(dst + g * 1024), 16,
                                                off, 0, 0, 0);
@@ -123,7 +171,10 @@ __device__ __forceinline__ void lora_down_dma_body(
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int c = 2 * s + (lane >> 5);
-        fa[u][s] = *reinterpret_cast<const u32x4_t *>(sb + stile_off(64 + 32 * tt + (lane & 31), c));
+        if constexpr (BK)
+          fa[u][s] = frag_rows<RT>(sb + 64 * 128, s, 32 * tt);
+        else
+          fa[u][s] = *reinterpret_cast<const u32x4_t *>(sb + stile_off(64 + 32 * tt + (lane & 31), c));
         fb[u][s] = *reinterpret_cast<const u32x4_t *>(sb + stile_off(32 * ti + (lane & 31), c));
       }
     }
@@ -177,11 +228,6 @@ __global__ __launch_bounds__(NT) void lora_down_partial_kernel(
 // bytes of row base + i / 4 at column 4 (i % 4) of its 16-column half and receives
 // column i of those four rows.  NB buffers, one barrier per 64-row step; wave w owns
 // output tiles w, w + 4, ... of the 2 x RT tiles of 32 x 32.
-template <int RT>
-__device__ __forceinline__ int s_swz(int row) {
-  // the S tile's rows hold 4 RT chunks; swizzle within the row when that is a power of two
-  return ((4 * RT) & (4 * RT - 1)) == 0 ? (((row & 7) ^ ((row >> 3) & 1)) & (4 * RT - 1)) : 0;
-}
 
 template <int RT, bool JMAJOR, int NB>
 __device__ __forceinline__ void reduce_m_dma_body(
@@ -251,21 +297,7 @@ __device__ __forceinline__ void reduce_m_dma_body(
     }
     return v;
   };
-  auto frag_s = [&](const char *sb, int s, int cb) {
-    const int i = lane & 15, gq = lane >> 4;
-    const int col = cb + (gq & 1) * 16 + 4 * (i & 3);
-    u32x4_t v;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int row = 16 * s + 8 * (gq >> 1) + 4 * e + (i >> 2);
-      const int off = INB + row * SROW + (((col >> 3) ^ s_swz<RT>(row)) << 4) + (col & 7) * 2;
-      const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)(sb + off));
-      const u32x2_t w = __builtin_bit_cast(u32x2_t, t);
-      v[2 * e] = w[0];
-      v[2 * e + 1] = w[1];
-    }
-    return v;
-  };
+  auto frag_s = [&](const char *sb, int s, int cb) { return frag_rows<RT>(sb + INB, s, cb); };
 
   f32x16_t acc[TPW];
 #pragma unroll
@@ -333,10 +365,74 @@ __global__ __launch_bounds__(NT) void reduce_m_partial_kernel(
   reduce_m_dma_body<RT, JMAJOR, staged_nb<RT>()>(sbuf, blockIdx.x, blockIdx.y, IN, M, No, ldin, S, lds, r, MR, P);
 }
 
+// Transposes of bf16 matrices: OUT[C, R] = IN[R, C]^T.  A workgroup moves one 64 x 64
+// tile through LDS: 16-byte row loads when C % 8 == 0 and 16-byte stores when R % 8 == 0,
+// element accesses otherwise.
+struct TransposeJob {
+  const uint16_t *in;
+  uint16_t *out;
+  int64_t R, C;
+  int64_t tiles_c;  // ceil(C / 64)
+};
+
+// Tile b (row-major over the 64 x 64 tiles of IN) of job jb, through `tile` (64 rows of
+// 72 elements in LDS: 16-byte aligned rows).
+__device__ __forceinline__ void transpose_tile(const TransposeJob &jb, int64_t b, uint16_t (*tile)[72]) {
+  const int64_t r0 = (b / jb.tiles_c) * 64, c0 = (b % jb.tiles_c) * 64;
+  const int tid = threadIdx.x, ch = tid & 7;
+  const bool vin = jb.C % 8 == 0, vout = jb.R % 8 == 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = (tid >> 3) + 32 * i;
+    const int64_t row = r0 + rr, col = c0 + ch * 8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (row < jb.R && col < jb.C) {
+      const uint16_t *src = jb.in + row * jb.C + col;
+      if (vin) {
+        v = *reinterpret_cast<const u32x4_t *>(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t lo = col + e < jb.C ? src[e] : 0u;
+          const uint32_t hi = col + e + 1 < jb.C ? src[e + 1] : 0u;
+          v[e / 2] = lo | (hi << 16);
+        }
+      }
+    }
+    *reinterpret_cast<u32x4_t *>(&tile[rr][ch * 8]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int cc = (tid >> 3) + 32 * i;  // output row = input column c0 + cc
+    const int64_t orow = c0 + cc, ocol = r0 + ch * 8;
+    if (orow >= jb.C || ocol >= jb.R) continue;
+    uint16_t *dst = jb.out + orow * jb.R + ocol;
+    u32x4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = uint32_t(tile[ch * 8 + 2 * e][cc]) | (uint32_t(tile[ch * 8 + 2 * e + 1][cc]) << 16);
+    if (vout) {
+      *reinterpret_cast<u32x4_t *>(dst) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ocol + e < jb.R) dst[e] = static_cast<uint16_t>(v[e / 2] >> (16 * (e & 1)));
+    }
+  }
+}
+
+// Two transposes in one launch (workgroups [0, n0) take matrix 0).
+__global__ __launch_bounds__(NT) void transpose2_kernel(TransposeJob j0, TransposeJob j1, int64_t n0) {
+  __shared__ uint16_t tile[64][72];
+  const bool second = blockIdx.x >= n0;
+  transpose_tile(second ? j1 : j0, second ? blockIdx.x - n0 : blockIdx.x, tile);
+}
+
 // The two products of the backward that read only dY, in one launch: workgroups
-// [0, nd) compute the V partials (lora_down over dY and B^T), the rest the dB partials
-// (reduce over tokens of dY and U_s).  Same bodies, same partial sums as the separate
-// kernels.
+// [0, nd) compute the V partials (lora_down over dY and B, read untransposed), the next
+// nq the dB partials (reduce over tokens of dY and U_s); the rest transpose A into the
+// A^T that the dX GEMM reads afterwards.  Same partial sums as the separate kernels.
 struct DownArgs {
   const uint16_t *IN;
   int M, Kc, ldin;
@@ -354,16 +450,20 @@ struct ReduceArgs {
   int gx;
 };
 template <int RT>
-__global__ __launch_bounds__(NT) void down_reduce_partial_kernel(DownArgs d, ReduceArgs q, int nd) {
-  __shared__ __attribute__((aligned(16))) char sbuf[staged_bytes<RT>()];  // used by either body
+__global__ __launch_bounds__(NT) void down_reduce_partial_kernel(DownArgs d, ReduceArgs q, int nd, int nq,
+                                                                 TransposeJob tj) {
+  __shared__ __attribute__((aligned(16))) char sbuf[staged_bytes<RT>()];  // used by every body
+  static_assert(staged_bytes<RT>() >= 64 * 72 * 2, "transpose tile");
   const int b = blockIdx.x;
   if (b < nd) {
-    lora_down_dma_body<RT, staged_nb<RT>()>(sbuf, b % d.gx, b / d.gx, d.IN, d.M, d.Kc, d.ldin, d.WT, d.ldwt, d.r,
-                                             d.KR, d.P);
-  } else {
+    lora_down_dma_body<RT, staged_nb<RT>(), true>(sbuf, b % d.gx, b / d.gx, d.IN, d.M, d.Kc, d.ldin, d.WT, d.ldwt,
+                                                   d.r, d.KR, d.P);
+  } else if (b < nd + nq) {
     const int c = b - nd;
     reduce_m_dma_body<RT, false, staged_nb<RT>()>(sbuf, c % q.gx, c / q.gx, q.IN, q.M, q.No, q.ldin, q.S, q.lds,
                                                    q.r, q.MR, q.P);
+  } else {
+    transpose_tile(tj, b - nd - nq, reinterpret_cast<uint16_t(*)[72]>(sbuf));
   }
 }
 
@@ -552,66 +652,6 @@ __global__ __launch_bounds__(NT) void reduce_m_generic_final_kernel(
   }
 }
 
-// Transposes of two bf16 matrices in one launch: OUT_q[C_q, R_q] = IN_q[R_q, C_q]^T for
-// q = 0, 1 (workgroups [0, n0) take matrix 0).  A workgroup moves one 64 x 64 tile
-// through LDS: 16-byte row loads when C % 8 == 0 and 16-byte stores when R % 8 == 0,
-// element accesses otherwise.
-struct TransposeJob {
-  const uint16_t *in;
-  uint16_t *out;
-  int64_t R, C;
-  int64_t tiles_c;  // ceil(C / 64)
-};
-
-__global__ __launch_bounds__(NT) void transpose2_kernel(TransposeJob j0, TransposeJob j1, int64_t n0) {
-  __shared__ uint16_t tile[64][72];  // row pitch 144 B: 16-byte aligned rows
-  const bool second = blockIdx.x >= n0;
-  const TransposeJob &jb = second ? j1 : j0;
-  const int64_t b = second ? blockIdx.x - n0 : blockIdx.x;
-  const int64_t r0 = (b / jb.tiles_c) * 64, c0 = (b % jb.tiles_c) * 64;
-  const int tid = threadIdx.x, ch = tid & 7;
-  const bool vin = jb.C % 8 == 0, vout = jb.R % 8 == 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rr = (tid >> 3) + 32 * i;
-    const int64_t row = r0 + rr, col = c0 + ch * 8;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (row < jb.R && col < jb.C) {
-      const uint16_t *src = jb.in + row * jb.C + col;
-      if (vin) {
-        v = *reinterpret_cast<const u32x4_t *>(src);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const uint32_t lo = col + e < jb.C ? src[e] : 0u;
-          const uint32_t hi = col + e + 1 < jb.C ? src[e + 1] : 0u;
-          v[e / 2] = lo | (hi << 16);
-        }
-      }
-    }
-    *reinterpret_cast<u32x4_t *>(&tile[rr][ch * 8]) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int cc = (tid >> 3) + 32 * i;  // output row = input column c0 + cc
-    const int64_t orow = c0 + cc, ocol = r0 + ch * 8;
-    if (orow >= jb.C || ocol >= jb.R) continue;
-    uint16_t *dst = jb.out + orow * jb.R + ocol;
-    u32x4_t v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = uint32_t(tile[ch * 8 + 2 * e][cc]) | (uint32_t(tile[ch * 8 + 2 * e + 1][cc]) << 16);
-    if (vout) {
-      *reinterpret_cast<u32x4_t *>(dst) = v;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (ocol + e < jb.R) dst[e] = static_cast<uint16_t>(v[e / 2] >> (16 * (e & 1)));
-    }
-  }
-}
-
 // ---- split selection (shared by the workspace queries and the launches) -----------
 struct DownSplit {
   int ksplit, KR;
@@ -777,7 +817,8 @@ hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, int64_t ld
 }
 
 bool vdb_fast(int64_t M, int64_t Np, int64_t ldy, int64_t ldu, int r) {
-  return down_fast(M, Np, ldy, ldy, r, ldu) && reduce_fast(M, Np, ldy, ldu, r);
+  // B [Np, r] is read with row pitch r (its part of a stacked B)
+  return down_fast(M, Np, ldy, r, r, ldu) && reduce_fast(M, Np, ldy, ldu, r) && uint64_t(Np) * r * 2 <= k4G;
 }
 
 size_t vdb_workspace_v(int64_t M, int64_t Np, int r) {
@@ -787,24 +828,27 @@ size_t vdb_workspace_db(int64_t M, int64_t Np, int r) {
   return static_cast<size_t>(m_split(M, Np).splits) * Np * r * sizeof(float);
 }
 
-hipError_t launch_vdb(const uint16_t *dY, int64_t M, int64_t Np, int64_t ldy, const uint16_t *Bt, const uint16_t *U,
+hipError_t launch_vdb(const uint16_t *dY, int64_t M, int64_t Np, int64_t ldy, const uint16_t *B, const uint16_t *U,
                       int64_t ldu, int r, float scale, uint16_t *V, uint16_t *dB, float *ws_v, float *ws_db,
-                      hipStream_t stream) {
+                      const uint16_t *A, int64_t RA, int64_t KA, uint16_t *At, hipStream_t stream) {
   const int rt = (r + 31) / 32;
   if (rt < 1 || rt > 8 || !vdb_fast(M, Np, ldy, ldu, r)) return hipErrorInvalidValue;
   const DownSplit sd = down_split(M, Np);
   const MSplit sq = m_split(M, Np);
-  DownArgs d{dY, static_cast<int>(M), static_cast<int>(Np), static_cast<int>(ldy), Bt, static_cast<int>(ldy), r,
+  DownArgs d{dY, static_cast<int>(M), static_cast<int>(Np), static_cast<int>(ldy), B, r, r,
              sd.KR, ws_v, static_cast<int>((M + 63) / 64)};
   ReduceArgs q{dY, static_cast<int>(M), static_cast<int>(Np), static_cast<int>(ldy), U, static_cast<int>(ldu), r,
                sq.MR, ws_db, static_cast<int>((Np + 63) / 64)};
+  const TransposeJob tj{A, At, RA, KA, (KA + 63) / 64};
   const int64_t nd = int64_t(d.gx) * sd.ksplit, nq = int64_t(q.gx) * sq.splits;
-  if (nd + nq > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(nd + nq)), block(NT);
+  const int64_t nt = (A && At) ? ((RA + 63) / 64) * tj.tiles_c : 0;
+  if (nd + nq + nt > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(nd + nq + nt)), block(NT);
   switch (rt) {
-#define QLORA_CASE(T)                                                                                  \
-  case T:                                                                                              \
-    hipLaunchKernelGGL(down_reduce_partial_kernel<T>, grid, block, 0, stream, d, q, static_cast<int>(nd)); \
+#define QLORA_CASE(T)                                                                          \
+  case T:                                                                                      \
+    hipLaunchKernelGGL(down_reduce_partial_kernel<T>, grid, block, 0, stream, d, q, static_cast<int>(nd), \
+                       static_cast<int>(nq), tj);                                              \
     break;
     QLORA_CASE(1) QLORA_CASE(2) QLORA_CASE(3) QLORA_CASE(4)
     QLORA_CASE(5) QLORA_CASE(6) QLORA_CASE(7) QLORA_CASE(8)

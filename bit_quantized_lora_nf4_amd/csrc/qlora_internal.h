@@ -83,16 +83,17 @@ hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, int64_t ld
                            hipStream_t stream);
 
 // The backward's two products over dY in one launch plus one finalize launch:
-// V[M, r] (row pitch ldu) = bf16(scale dY Bt^T) and dB[Np, r] = bf16(dY^T U), where dY
-// has row pitch ldy (a column slice of width Np), Bt is [r, Np] with row pitch ldy and U
-// [M, r] with row pitch ldu.  Needs the fast-path shapes (vdb_fast) and the two fp32
-// partial regions sized by vdb_workspace_v / vdb_workspace_db.
+// V[M, r] (row pitch ldu) = bf16(scale dY B) and dB[Np, r] = bf16(dY^T U), where dY has
+// row pitch ldy (a column slice of width Np), B is [Np, r] (dense rows) and U [M, r]
+// with row pitch ldu.  If A and At are given, the same launch also writes At[KA, RA] =
+// A[RA, KA]^T.  Needs the fast-path shapes (vdb_fast) and the two fp32 partial regions
+// sized by vdb_workspace_v / vdb_workspace_db.
 bool vdb_fast(int64_t M, int64_t Np, int64_t ldy, int64_t ldu, int r);
 size_t vdb_workspace_v(int64_t M, int64_t Np, int r);
 size_t vdb_workspace_db(int64_t M, int64_t Np, int r);
-hipError_t launch_vdb(const uint16_t *dY, int64_t M, int64_t Np, int64_t ldy, const uint16_t *Bt, const uint16_t *U,
+hipError_t launch_vdb(const uint16_t *dY, int64_t M, int64_t Np, int64_t ldy, const uint16_t *B, const uint16_t *U,
                       int64_t ldu, int r, float scale, uint16_t *V, uint16_t *dB, float *ws_v, float *ws_db,
-                      hipStream_t stream);
+                      const uint16_t *A, int64_t RA, int64_t KA, uint16_t *At, hipStream_t stream);
 
 // AdamW step (fp32 parameter and moments, bf16 gradient, optional bf16 parameter copy).
 struct AdamConsts {
