@@ -5,8 +5,8 @@
 // constants and decode them to bf16 on the fly ([Digest] "方法步骤与流程" step 3 and
 // [QLoRA note] "5. QLoRA 训练方式本身": the 4-bit weight is decoded to BF16 inside
 // the operator): w' = bf16_rne(q[code] * c'), c' = fma(c8, s, o).  The LoRA product
-// is added to the same fp32 accumulators as r extra contraction steps before the
-// single bf16 rounding of each output.
+// is added to the same fp32 accumulators as r extra contraction steps (before the
+// weight's) ahead of the single bf16 rounding of each output.
 //
 // Tile: a 256-thread workgroup (four waves, one per SIMD) computes a 256 x 256 output
 // tile, 256 fp32 accumulators per lane.  In the forward, wave w owns all 256
@@ -359,8 +359,55 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     issue_dma(0, h, sX);
     issue_dma(min(1, last) * TK, h, sX + TILE_BYTES);
   }
+  // The LoRA term first, while the first tiles' loads are in flight.  Up to 64 ranks
+  // with 16-byte aligned rows: the U_s tile of the 256 tokens (the rank columns of this
+  // tile's part, zeros past r) is staged in the third activation buffer like one
+  // contraction step of X and read with the same fragment reads, so every wave reads it
+  // from LDS and loads only its own weight rows' B fragments (sub-step s: ranks
+  // 8 s .. 8 s + 7 and 32 + 8 s .. in the two lane halves, as X's contraction order).
+  // Otherwise the rank steps load both operands' fragments from memory.
+  const bool lds_lora = p.r > 0 && p.r <= TK && (p.r % 8) == 0 && (p.lda2 % 8) == 0;
+  u32x4_t wl[4][2];
+  char *const sU = sX + 2 * TILE_BYTES;  // not written by the prologue's tile loads
+  if (lds_lora) {
+    const int qc = p.part_rows > 0 ? (n0 / p.part_rows) * p.r : 0;
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.A2, static_cast<uint32_t>(uint64_t(p.M) * p.lda2 * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B2, static_cast<uint32_t>(uint64_t(p.No) * p.r * 2));
+    char *dst = sU + wave * 8 * 1024;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = (wave * 8 + i) * 8 + (lane >> 3);
+      const int row = min(m0 + rr, p.M - 1);
+      const int c = (lane & 7) ^ swz(rr);
+      const uint32_t off = c * 8 < p.r ? (static_cast<uint32_t>(row) * p.lda2 + qc + c * 8) * 2 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (__attribute__((address_space(3))) void *)(dst + i * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        wl[s][j] = lora_frag(rb, true, n0 + wave * 64 + j * 32 + (lane & 31), p.No, p.r,
+                             32 * (lane >> 5) + 8 * s, p.r);
+  } else if (p.r > 0) {
+    lora_steps(p, m0, n0, acc);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (lds_lora) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (8 * s < p.r) {
+        u32x4_t xu[8];
+        read_xfrags_fwd(sU, s, xu);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(wl[s][j], xu[i], acc[i][j]);
+      }
+    }
+    __syncthreads();  // no wave reads the U_s tile any more when step 0 loads tile 2 there
+  }
 
   Planes pl[2], pln[2];
   u32x4_t wa[2], xb[8];
@@ -442,7 +489,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   if (it + 1 < nk) step(Ic<1>{}, Ic<0>{}, it + 1, S1, S2, S0);
   // drain the clamped prefetches of the last steps before the epilogue
   __builtin_amdgcn_s_waitcnt(0);
-  if (p.r > 0) lora_steps(p, m0, n0, acc);
   store_out(p, m0, n0, acc);
 }
 
@@ -806,6 +852,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   issue_codes(0, S0);
   issue_codes(min(1, last) * TK, S1);
   issue_y(Ic<1>{}, 0, sYw[0]);
+  // the LoRA term first, while the first tiles' loads are in flight
+  if (p.r > 0) lora_steps_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
   {
     const Planes pd = make_planes(const_value<CT>(S0.c), p.lvl);
     decode_part(S0, pd, sW0, 0, 8);
@@ -894,7 +942,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   if (it + 1 < nk) step(Ic<1>{}, Ic<1>{}, it + 1, S0, S1);
   if (it + 2 < nk) step(Ic<0>{}, Ic<1>{}, it + 2, S1, S0);
   __builtin_amdgcn_s_waitcnt(0);
-  if (p.r > 0) lora_steps_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
   store_out_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
 }
 

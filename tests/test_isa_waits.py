@@ -58,6 +58,16 @@ def _barrier_waits(ev):
     return [(i, e[1]) for i, e in enumerate(ev) if e[0] == "W" and i + 1 < len(ev) and ev[i + 1][0] == "B"]
 
 
+def _all_retired(ev, j):
+    """Whether no load is in flight at event j: a vmcnt(0) wait follows the last load before it."""
+    k = j - 1
+    while k >= 0 and ev[k] != ("W", 0):
+        if ev[k][0] in ("D", "R"):
+            return False
+        k -= 1
+    return k >= 0
+
+
 FWD = "_ZN5qlora12_GLOBAL__N_115gemm_fwd_kernelILi{}EEEvNS0_10GemmParamsE"
 DX = "_ZN5qlora12_GLOBAL__N_119gemm_dx_pipe_kernelILi{}EEEvNS0_10GemmParamsE"
 
@@ -72,8 +82,8 @@ def test_forward_barrier_waits(gemm_asm, ct):
         j = i - 1
         while j >= 0 and ev[j][0] != "B":
             j -= 1
-        if j < 0 or (j >= 1 and ev[j - 1] == ("W", 0)):
-            continue  # the prologue barrier: everything before it was retired
+        if j < 0 or _all_retired(ev, j):
+            continue  # a prologue barrier: everything issued before it was retired
         # the half-tile DMA issued right after the previous barrier must be retired here:
         # the wait may leave in flight only loads issued after it
         k, seen = j + 1, 0
