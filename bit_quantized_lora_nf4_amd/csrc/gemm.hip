@@ -852,14 +852,52 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   issue_codes(0, S0);
   issue_codes(min(1, last) * TK, S1);
   issue_y(Ic<1>{}, 0, sYw[0]);
-  // the LoRA term first, while the first tiles' loads are in flight
-  if (p.r > 0) lora_steps_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
+  // The LoRA term first, while the first tiles' loads are in flight.  Up to 64 ranks
+  // with 16-byte aligned rows: the V tile of the 256 tokens (zeros past r) is loaded
+  // into the second dY stage laid out like a dY stage and read with the same fragment
+  // reads (sub-step s: ranks 16 s .. 16 s + 15); each wave loads only its own output
+  // columns' At fragments.  Otherwise the rank steps load both operands from memory.
+  const bool lds_lora = p.r > 0 && p.r <= TK && (p.r % 8) == 0;
+  u32x4_t wl[4][4];
+  if (lds_lora) {
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.A2, static_cast<uint32_t>(uint64_t(p.M) * p.r * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B2, static_cast<uint32_t>(uint64_t(p.No) * p.r * 2));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = min(m0 + wave * 64 + 8 * q + (lane >> 3), p.M - 1);
+      const int c = ych[q & 1];
+      const uint32_t off = c * 8 < p.r ? (static_cast<uint32_t>(row) * p.r + c * 8) * 2 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void *)(sYw[1] + q * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wl[s][j] = lora_frag(rb, true, k0 + 128 * wc + j * 32 + (lane & 31), p.No, p.r, 16 * s + (lane >> 5) * 8, p.r);
+  } else if (p.r > 0) {
+    lora_steps_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
+  }
   {
     const Planes pd = make_planes(const_value<CT>(S0.c), p.lvl);
     decode_part(S0, pd, sW0, 0, 8);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (lds_lora) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (16 * s < p.r) {
+        u32x4_t vb[4];
+        read_y(sY1, s, vb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(wl[s][j], vb[i], acc[i][j]);
+      }
+    }
+    __syncthreads();  // no wave reads the V tile any more when step 0 loads dY step 1 there
+  }
 
   u32x4_t wa[4], yb[4];
 #pragma unroll
