@@ -62,6 +62,7 @@ SMALL = [  # (M, K, N, r)
     (7, 512, 300, 256),    # M <= 16 with the largest rank: 16 LoRA workgroups in the launch
     (260, 512, 392, 96),   # 96 ranks: LoRA tiles of 12 chunks per row (no swizzle), B read untransposed
     (200, 384, 264, 40),   # 40 ranks: a partly filled second rank tile
+    (1000, 128, 20380, 16),  # 320 output tiles in two rounds, ragged both ways
     (1, 64, 33, 5),        # M <= 16 with one 64-block of contraction
     (12, 4096, 40, 16),    # M <= 16, X too large to stage in LDS: X fragments from memory
     (1, 64, 65552, 4),     # M = 1 past 4096 tiles of 16 rows: the fused GEMM takes it
