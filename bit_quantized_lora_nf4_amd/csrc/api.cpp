@@ -319,6 +319,7 @@ int bwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16
   const qlora::WeightView wv = view(w);
   char *ws = static_cast<char *>(workspace);
   const uint16_t *V = nullptr, *At = nullptr;
+  qlora::FinalizeJob fin_da{nullptr, 0, 0, 0, 0, 0.0f, nullptr};
   if (r > 0) {
     const float scale = alpha / static_cast<float>(r);
     float *part = reinterpret_cast<float *>(ws + L.part);
@@ -358,14 +359,16 @@ int bwd_impl(const char *who, const qlora_nf4_weight *w, int parts, const uint16
                                             false, st),
                      "reduce(dB)");
     }
+    // dA's finalize pass rides in the dX GEMM's launch when there is one
     if (s == QLORA_OK)
-      s = launched(qlora::launch_reduce_m(X, M, K, K, Vw, R, R, part, dA, true, st), "reduce(dA)");
+      s = launched(qlora::launch_reduce_m(X, M, K, K, Vw, R, R, part, dA, true, st, dX ? &fin_da : nullptr),
+                   "reduce(dA)");
     if (s != QLORA_OK) return s;
     V = Vw;
     At = Atw;
   }
   if (dX)
-    return launched(timed_launch(st, [&] { return qlora::launch_gemm_dx(wv, dY, M, V, At, R, dX, st); }),
+    return launched(timed_launch(st, [&] { return qlora::launch_gemm_dx(wv, dY, M, V, At, R, dX, st, &fin_da); }),
                     "gemm_dx");
   return QLORA_OK;
 }

@@ -156,6 +156,38 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// ---- the last pass of a split reduction (FinalizeJob) -------------------------------
+// Element i (of four floats) of the splits' partial sums added in split order,
+// P_0 + P_1 + ...  The loads of four splits are issued before any is used: a split
+// index past the last re-reads the last split and its value is not added, so the loads
+// are straight-line code and the compiler does not wait for each before issuing the next.
+__device__ __forceinline__ f32x4_t split_sum(const float *__restrict__ P, int splits, int64_t count, int64_t i) {
+  const f32x4_t *P4 = reinterpret_cast<const f32x4_t *>(P);
+  const int64_t c4 = count / 4;
+  f32x4_t s = P4[i];
+  for (int k = 1; k < splits; k += 4) {
+    f32x4_t t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = P4[min(k + u, splits - 1) * c4 + i];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k + u < splits) s += t[u];
+  }
+  return s;
+}
+// Group i of four values of the job: bf16(scale * sum) to its place in OUT.
+__device__ __forceinline__ void finalize_one(const FinalizeJob &j, int64_t i) {
+  const f32x4_t s = split_sum(j.P, j.splits, j.count, i);
+  const u32x2_t o = {pack_bf16x2(s[0] * j.scale, s[1] * j.scale), pack_bf16x2(s[2] * j.scale, s[3] * j.scale)};
+  const int64_t e = 4 * i, row = e / j.cols, col = e % j.cols;
+  *reinterpret_cast<u32x2_t *>(j.OUT + row * j.ldout + col) = o;
+}
+// Workgroup wg of wgs (256 threads each) does groups wg 256 + t, then every wgs 256 on.
+__device__ __forceinline__ void finalize_part(const FinalizeJob &j, int64_t wg, int64_t wgs) {
+  const int64_t n4 = j.count / 4;
+  for (int64_t i = wg * 256 + threadIdx.x; i < n4; i += wgs * 256) finalize_one(j, i);
+}
+
 // ---- register-only NF4 decode -------------------------------------------------------
 // For one block constant c, the 16 possible decoded weights T[j] = bf16_rne(q[j] * c)
 // are kept as byte planes: L[p] holds the low bytes of T[4p..4p+3], H[p] the high bytes.

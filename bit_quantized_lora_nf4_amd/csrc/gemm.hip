@@ -62,6 +62,9 @@ struct GemmParams {
   int lda2;       // row pitch of A2 (r, or the stacked rank of fused linears)
   int part_rows;  // fused linears: output columns [q P, q P + P) use A2 columns
                   // [q r, q r + r); 0 = one linear (tiles never straddle parts)
+  int tiles;         // dX: workgroups [0, tiles) compute output tiles; the fin_wgs after
+  int fin_wgs;       // them do the finalize job `fin` (the dA pass of the same backward)
+  FinalizeJob fin;
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -566,6 +569,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     GemmParams p) {
   __shared__ __attribute__((aligned(16))) char sX[2][TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sW[2][TILE_BYTES];
+  if (static_cast<int>(blockIdx.x) >= p.tiles) {
+    finalize_part(p.fin, blockIdx.x - p.tiles, p.fin_wgs);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   int tmi, tni;
   tile_coords((p.M + TM - 1) / TM, (p.No + TN - 1) / TN, tmi, tni);
@@ -760,6 +767,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   __shared__ __attribute__((aligned(16))) char sW1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sY0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sY1[TILE_BYTES];
+  // the workgroups after the tiles (dispatched last, so in CUs the tiles have left) do
+  // the finalize job that rides in this launch
+  if (static_cast<int>(blockIdx.x) >= p.tiles) {
+    finalize_part(p.fin, blockIdx.x - p.tiles, p.fin_wgs);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // 2 x 2 waves: wave w computes tokens 128 (w / 2) .. + 128 and output columns
@@ -993,6 +1006,9 @@ GemmParams make_params(const uint16_t *A, const WeightView &w, const uint16_t *A
                        const uint16_t *B2, uint16_t *C, int64_t M, int64_t No, int64_t Kc, int r) {
   GemmParams p{A, w, A2, B2, C, static_cast<int>(M), static_cast<int>(No), static_cast<int>(Kc), r, {}, r, 0};
   p.lvl = level_table(w.quant_type);
+  p.tiles = static_cast<int>(((M + TM - 1) / TM) * ((No + TN - 1) / TN));
+  p.fin_wgs = 0;
+  p.fin = FinalizeJob{nullptr, 0, 0, 0, 0, 0.0f, nullptr};
   return p;
 }
 
@@ -1025,10 +1041,15 @@ hipError_t launch_gemm_fwd(const WeightView &w, const uint16_t *X, int64_t M, co
 }
 
 hipError_t launch_gemm_dx(const WeightView &w, const uint16_t *dY, int64_t M, const uint16_t *V,
-                          const uint16_t *At, int r, uint16_t *dX, hipStream_t stream) {
+                          const uint16_t *At, int r, uint16_t *dX, hipStream_t stream, const FinalizeJob *fin) {
   if (!fits_32bit(M, w.n_rows, w.n_cols, r) || M > 0x7fffffff) return hipErrorInvalidValue;
-  const GemmParams p = make_params(dY, w, V, At, dX, M, w.n_cols, w.n_rows, r);
-  const dim3 grid(grid_size(M, w.n_cols));
+  GemmParams p = make_params(dY, w, V, At, dX, M, w.n_cols, w.n_rows, r);
+  if (fin && fin->splits > 0) {
+    p.fin = *fin;
+    p.fin_wgs = static_cast<int>(finalize_workgroups(*fin));
+  }
+  if (int64_t(p.tiles) + p.fin_wgs > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(p.tiles + p.fin_wgs));
   const bool pipe = w.n_rows % 8 == 0;
   auto go = [&](auto pipe_kern, auto plain_kern) {
     if (pipe)

@@ -468,27 +468,8 @@ __global__ __launch_bounds__(NT) void down_reduce_partial_kernel(DownArgs d, Red
 }
 
 // OUT = bf16(scale * sum_s P[s]) for the `count` partial sums (count % 4 == 0) laid out
-// as rows of `cols` values (cols % 4 == 0), written with row pitch ldout; fixed order.
-// Element i (of 4 floats) of the splits' partials summed in split order, P_0 + P_1 + ...
-// The loads of four splits are issued before any is used: a split index past the last
-// re-reads the last split and its value is not added, so the loads are straight-line
-// code and the compiler does not wait for each before issuing the next.
-__device__ __forceinline__ f32x4_t split_sum(const float *__restrict__ P, int splits, int64_t count,
-                                             int64_t i) {
-  const f32x4_t *P4 = reinterpret_cast<const f32x4_t *>(P);
-  const int64_t c4 = count / 4;
-  f32x4_t s = P4[i];
-  for (int k = 1; k < splits; k += 4) {
-    f32x4_t t[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) t[u] = P4[min(k + u, splits - 1) * c4 + i];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (k + u < splits) s += t[u];
-  }
-  return s;
-}
-
+// as rows of `cols` values (cols % 4 == 0), written with row pitch ldout; fixed order
+// (split_sum in device_common.h).
 __global__ __launch_bounds__(NT) void finalize_kernel(const float *__restrict__ P, int splits,
                                                       int64_t count, int64_t cols, int64_t ldout,
                                                       float scale, uint16_t *__restrict__ OUT) {
@@ -503,19 +484,7 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const float *__restrict__ 
 }
 
 // Two finalize passes in one launch (the same fixed order and rounding as finalize_kernel).
-struct FinJob {
-  const float *P;
-  int splits;
-  int64_t count, cols, ldout;
-  float scale;
-  uint16_t *OUT;
-};
-__device__ __forceinline__ void finalize_one(const FinJob &j, int64_t i) {
-  const f32x4_t s = split_sum(j.P, j.splits, j.count, i);
-  u32x2_t o = {pack_bf16x2(s[0] * j.scale, s[1] * j.scale), pack_bf16x2(s[2] * j.scale, s[3] * j.scale)};
-  const int64_t e = 4 * i, row = e / j.cols, col = e % j.cols;
-  *reinterpret_cast<u32x2_t *>(j.OUT + row * j.ldout + col) = o;
-}
+using FinJob = FinalizeJob;
 __global__ __launch_bounds__(NT) void finalize2_kernel(FinJob a, FinJob b) {
   const int64_t na = a.count / 4, n = na + b.count / 4;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < n;
@@ -768,7 +737,8 @@ size_t reduce_m_workspace(int64_t M, int64_t No, int r) {
 
 hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, int64_t ldin, const uint16_t *S,
                            int64_t lds, int r, float *partials, uint16_t *OUT, bool trans_out,
-                           hipStream_t stream) {
+                           hipStream_t stream, FinalizeJob *defer) {
+  if (defer) defer->splits = 0;
   const int rt = (r + 31) / 32;
   if (rt < 1 || rt > 8) return hipErrorInvalidValue;
   if (reduce_fast(M, No, ldin, lds, r)) {
@@ -793,6 +763,10 @@ hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, int64_t ld
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // [No, r] (or [r, No] for trans_out) dense rows
+    if (defer) {
+      *defer = FinalizeJob{partials, sp.splits, No * r, No * r, No * r, 1.0f, OUT};
+      return hipSuccess;
+    }
     return launch_finalize(partials, sp.splits, No * r, No * r, No * r, 1.0f, OUT, stream);
   }
   const int64_t splits = (M + GMS - 1) / GMS;

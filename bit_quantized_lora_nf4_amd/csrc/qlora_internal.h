@@ -74,13 +74,33 @@ hipError_t launch_lora_down(const uint16_t *IN, int64_t M, int64_t Kc, int64_t l
 // launch; IN1 may be NULL (one transpose).
 hipError_t launch_transpose2_bf16(const uint16_t *IN0, int64_t R0, int64_t C0, uint16_t *OUT0, const uint16_t *IN1,
                                   int64_t R1, int64_t C1, uint16_t *OUT1, hipStream_t stream);
+// The last pass of a split reduction: OUT = bf16(scale * (P_0 + P_1 + ...)) for the
+// `count` partial sums of each of `splits` splits (count % 4 == 0), laid out as rows of
+// `cols` values written with row pitch ldout.  splits == 0: nothing to do.
+struct FinalizeJob {
+  const float *P;
+  int splits;
+  int64_t count, cols, ldout;
+  float scale;
+  uint16_t *OUT;
+};
+// Workgroups of 256 threads a finalize job is spread over when it rides in another
+// launch (the dX GEMM's); finalize_part (device_common.h) does one workgroup's share.
+inline int64_t finalize_workgroups(const FinalizeJob &j) {
+  if (j.splits <= 0) return 0;
+  const int64_t w = (j.count / 4 + 4 * 256 - 1) / (4 * 256);  // four groups of four values per thread
+  return w < 1 ? 1 : w;
+}
+
 // P[s][No][r] fp32 partials of sum over m in split s of IN[m][no] * S[m][j]; then
 // OUT = bf16(sum_s P) written as [No, r] (trans_out = false) or [r, No] (true).
-// IN rows have pitch ldin, S rows pitch lds.
+// IN rows have pitch ldin, S rows pitch lds.  If `defer` is not NULL and the fast path
+// runs, the finalize pass is not launched but described in *defer (else defer->splits
+// is 0), for a later launch to do.
 size_t reduce_m_workspace(int64_t M, int64_t No, int r);
 hipError_t launch_reduce_m(const uint16_t *IN, int64_t M, int64_t No, int64_t ldin, const uint16_t *S,
                            int64_t lds, int r, float *partials, uint16_t *OUT, bool trans_out,
-                           hipStream_t stream);
+                           hipStream_t stream, FinalizeJob *defer = nullptr);
 
 // The backward's two products over dY in one launch plus one finalize launch:
 // V[M, r] (row pitch ldu) = bf16(scale dY B) and dB[Np, r] = bf16(dY^T U), where dY has
@@ -133,8 +153,10 @@ bool gemv_supported(const WeightView &w, int64_t M, int r);
 hipError_t launch_gemv(const WeightView &w, const uint16_t *X, int64_t M, const uint16_t *A, int R,
                        const uint16_t *Bl, int r, int64_t part_rows, float scale, uint16_t *Y,
                        uint16_t *U_saved, void *ws, hipStream_t stream);
-// dX[M, K] = bf16(dY . W' + V . At^T)  (V [M, r], At [K, r]); r may be 0.
+// dX[M, K] = bf16(dY . W' + V . At^T)  (V [M, r], At [K, r]); r may be 0.  A finalize
+// job (NULL or splits == 0: none) runs in extra workgroups after the GEMM's tiles.
 hipError_t launch_gemm_dx(const WeightView &w, const uint16_t *dY, int64_t M, const uint16_t *V,
-                          const uint16_t *At, int r, uint16_t *dX, hipStream_t stream);
+                          const uint16_t *At, int r, uint16_t *dX, hipStream_t stream,
+                          const FinalizeJob *fin = nullptr);
 
 }  // namespace qlora
