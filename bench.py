@@ -728,7 +728,7 @@ def main():
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
             "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "kernel": "fused NF4-decode GEMM (forward and dX launches)",
+            "kernel": "fused NF4-decode GEMM (forward and dX launches; a dX launch also carries dA's finalize pass)",
             "per_launch_flops": "fwd 2MNK + 2MNr; dX 2MNK + 2MKr",
             "avg_launch_us": round(g_ms * 1e3 / max(1, len(rec)), 2),
             "per_shape": {k: {"TFLOP/s": round(v[0] / (v[1] * 1e-3) / 1e12, 1),
