@@ -2,10 +2,12 @@
 //
 // out = RN(q[code] * c') (fp32) or bf16_rne of it, with c' = fma(c8, s, o)
 // ([Digest] "数学公式与关键细节" item 3, doubleDequant equation), or the stored fp32
-// constant c' = c for the constant type without double quantization.  Each thread
-// decodes 32 weights (16 bytes of codes, half a block, one constant) per
-// iteration; a wave therefore reads 1 KB of codes and writes 4 KB of bf16.
-// HBM-bound: reads 0.516 B and writes 2 (bf16) or 4 (fp32) bytes per weight.
+// constant c' = c for the constant type without double quantization.
+// HBM-bound: reads 0.516 B and writes 2 (bf16) or 4 (fp32) bytes per weight, so the
+// writes set the pace.  A wave takes a span of 256 code dwords (2048 weights); in pass
+// u = 0..3 lane l decodes dword 64 u + l of it (eight weights of one block) and
+// writes them next to its neighbours' (bf16: one 16-byte store per lane, so every
+// store instruction covers 1 KB of output contiguously).
 
 #include "device_common.h"
 #include "qlora_internal.h"
@@ -14,35 +16,42 @@ namespace qlora {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kSpanDwords = 4 * 64;  // four passes of the wave's 64 lanes
 
 template <bool OUT_BF16, int CT>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(WeightView wv, int64_t n_chunks,
+__global__ __launch_bounds__(kThreads) void dequant_kernel(WeightView wv, int64_t n_dwords,
                                                            void *__restrict__ out, LevelTable lv) {
-  const u32x4_t *__restrict__ codes = reinterpret_cast<const u32x4_t *>(wv.codes);
+  const uint32_t *__restrict__ codes = reinterpret_cast<const uint32_t *>(wv.codes);
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = lv.q[threadIdx.x];
   __syncthreads();
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t ch = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; ch < n_chunks;
-       ch += stride) {
-    const u32x4_t w = codes[ch];
-    const float c = decode_constant<CT>(wv, ch >> 1);  // 2 chunks per block
-    if (OUT_BF16) {
-      u32x4_t *dst = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(out) + ch * 32);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n_spans = (n_dwords + kSpanDwords - 1) / kSpanDwords;
+  const int64_t wstride = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  for (int64_t sp = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave; sp < n_spans; sp += wstride) {
+    uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = decode8(w[i], c, lut);
-    } else {
-      f32x4_t *dst = reinterpret_cast<f32x4_t *>(static_cast<float *>(out) + ch * 32);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t d = sp * kSpanDwords + 64 * u + lane;
+      w[u] = d < n_dwords ? codes[d] : 0u;
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+    for (int u = 0; u < 4; ++u) {
+      const int64_t d = sp * kSpanDwords + 64 * u + lane;  // weights 8 d .. 8 d + 7, block d / 8
+      if (d >= n_dwords) continue;
+      const float c = decode_constant<CT>(wv, d >> 3);
+      if (OUT_BF16) {
+        reinterpret_cast<u32x4_t *>(out)[d] = decode8(w[u], c, lut);
+      } else {
         f32x4_t a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = lut[(w[i] >> (4 * e)) & 15u] * c;
-          b[e] = lut[(w[i] >> (4 * e + 16)) & 15u] * c;
+          a[e] = lut[(w[u] >> (4 * e)) & 15u] * c;
+          b[e] = lut[(w[u] >> (4 * e + 16)) & 15u] * c;
         }
-        dst[2 * i] = a;
-        dst[2 * i + 1] = b;
+        f32x4_t *dst = reinterpret_cast<f32x4_t *>(out) + 2 * d;
+        dst[0] = a;
+        dst[1] = b;
       }
     }
   }
@@ -52,12 +61,13 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(WeightView wv, int64_
 
 hipError_t launch_dequantize(const WeightView &w, void *out, bool out_bf16, hipStream_t stream) {
   const LevelTable lv = level_table(w.quant_type);
-  const int64_t n_chunks = w.n_rows * w.n_cols / 32;
-  int64_t blocks = (n_chunks + kThreads - 1) / kThreads;
+  const int64_t n_dwords = w.n_rows * w.n_cols / 8;
+  const int64_t spans = (n_dwords + kSpanDwords - 1) / kSpanDwords;
+  int64_t blocks = (spans + kThreads / 64 - 1) / (kThreads / 64);
   if (blocks > 256 * 16) blocks = 256 * 16;
   dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, stream, w, n_chunks, out, lv);
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, w, n_dwords, out, lv);
     return hipGetLastError();
   };
   switch (w.const_type * 2 + (out_bf16 ? 1 : 0)) {
