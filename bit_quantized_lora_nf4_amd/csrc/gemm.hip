@@ -211,6 +211,44 @@ __device__ __forceinline__ void store_out(const GemmParams &p, int m0, int c0,
   }
 }
 
+// The same epilogue through LDS, for outputs with 16-byte aligned rows (No % 8 == 0):
+// each wave stages its 256 x 64 output block in two halves of 128 tokens (rows of 136
+// bytes, so that the 32 token rows of a lane half's 8-byte writes fall in distinct
+// banks) and writes it back 8 rows x 128 bytes per store instruction, where the
+// register layout would give 32 pieces of 16 bytes.  `lds` holds 4 x 128 x 136 bytes
+// that no wave reads any more.
+constexpr int kOutPitch = 136;
+__device__ __forceinline__ void store_out_lds(const GemmParams &p, int m0, int c0, const f32x16_t (&acc)[8][2],
+                                              char *lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  char *const reg = lds + wave * (128 * kOutPitch);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t &a = acc[4 * h + ii][j];
+          const int tok = ii * 32 + (lane & 31), col = j * 32 + g * 8 + (lane >> 5) * 4;
+          const u32x2_t o = {pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+          *reinterpret_cast<u32x2_t *>(reg + tok * kOutPitch + col * 2) = o;
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's writes have landed
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int tok = 8 * q + (lane >> 3), ch = lane & 7;
+      const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(reg + tok * kOutPitch + ch * 16);
+      const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(reg + tok * kOutPitch + ch * 16 + 8);
+      const int m = m0 + 128 * h + tok, col = c0 + wave * 64 + ch * 8;
+      if (m < p.M && col < p.No)
+        *reinterpret_cast<u32x4_t *>(p.C + static_cast<int64_t>(m) * p.No + col) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the next half overwrites it
+  }
+}
+
 // Map the linear workgroup id to (token tile, output tile): workgroups are dispatched
 // round-robin over the 8 XCDs, so consecutive tiles of the grouped raster order are
 // given to the same XCD (sharing its L2); groups of 4 token tiles sweep the outputs.
@@ -492,7 +530,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   if (it + 1 < nk) step(Ic<1>{}, Ic<0>{}, it + 1, S1, S2, S0);
   // drain the clamped prefetches of the last steps before the epilogue
   __builtin_amdgcn_s_waitcnt(0);
-  store_out(p, m0, n0, acc);
+  if (p.No % 8 == 0) {
+    static_assert(4 * 128 * kOutPitch <= NBUF * TILE_BYTES, "output staging");
+    __syncthreads();  // every wave is done reading the activation buffers
+    store_out_lds(p, m0, n0, acc, sX);
+  } else {
+    store_out(p, m0, n0, acc);
+  }
 }
 
 // ===================================== backward ====================================
