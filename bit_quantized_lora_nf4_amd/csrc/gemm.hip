@@ -752,6 +752,41 @@ __device__ __forceinline__ void store_out_dx(const GemmParams &p, int tb, int cb
   }
 }
 
+// The dX epilogue through LDS, for 16-byte aligned output rows (No % 8 == 0): each
+// wave stages its 128 x 128 output block in its own 32 KB buffer `reg`, in two halves
+// of 64 tokens (rows of 264 bytes, so that a lane half's 32 token rows fall in
+// distinct banks), and writes it back 4 rows x 256 bytes per store instruction.
+constexpr int kOutPitchDx = 264;
+__device__ __forceinline__ void store_out_dx_lds(const GemmParams &p, int tb, int cb, const f32x16_t (&acc)[4][4],
+                                                 char *reg) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t &a = acc[2 * h + ii][j];
+          const int tok = ii * 32 + (lane & 31), col = j * 32 + g * 8 + (lane >> 5) * 4;
+          const u32x2_t o = {pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+          *reinterpret_cast<u32x2_t *>(reg + tok * kOutPitchDx + col * 2) = o;
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's writes have landed
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int tok = 4 * q + (lane >> 4), ch = lane & 15;
+      const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(reg + tok * kOutPitchDx + ch * 16);
+      const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(reg + tok * kOutPitchDx + ch * 16 + 8);
+      const int m = tb + 64 * h + tok, col = cb + ch * 8;
+      if (m < p.M && col < p.No)
+        *reinterpret_cast<u32x4_t *>(p.C + static_cast<int64_t>(m) * p.No + col) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the next half overwrites it
+  }
+}
+
 // LoRA steps of the dX layout: acc[i][j] += A2 rows (tokens tb + 32 i + ..) x B2 rows
 // (output columns cb + 32 j + ..), rank in steps of 16.
 template <int NI, int NJ>
@@ -1037,7 +1072,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   if (it + 1 < nk) step(Ic<1>{}, Ic<1>{}, it + 1, S0, S1);
   if (it + 2 < nk) step(Ic<0>{}, Ic<1>{}, it + 2, S1, S0);
   __builtin_amdgcn_s_waitcnt(0);
-  store_out_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
+  if (p.No % 8 == 0) {
+    static_assert(64 * kOutPitchDx <= TILE_BYTES, "output staging");
+    __syncthreads();  // every wave is done reading the weight tiles and dY stages
+    char *const reg = wave == 0 ? sW0 : wave == 1 ? sW1 : wave == 2 ? sY0 : sY1;
+    store_out_dx_lds(p, m0 + 128 * wr, k0 + 128 * wc, acc, reg);
+  } else {
+    store_out_dx(p, m0 + 128 * wr, k0 + 128 * wc, acc);
+  }
 }
 
 bool fits_32bit(int64_t M, int64_t N, int64_t K, int r) {
