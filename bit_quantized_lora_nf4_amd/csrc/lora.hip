@@ -85,6 +85,42 @@ __device__ __forceinline__ u32x4_t frag_rows(const char *tile, int s, int cb) {
   return v;
 }
 
+// The workgroup's AEXT x BEXT tile of fp32 partial sums, element (a, b) going to
+// P[a pitch + b] for a < a_lim, b < b_lim.  Each wave holds tiles w, w + 4, ... of
+// 32 x 32 in the MFMA accumulator layout (lane l: a = a0 + l % 32, four consecutive
+// b from b0 + 8 g + 4 (l / 32)); tile_ab(t, a0, b0) gives tile t's corner.  The tile
+// is staged through LDS (rows of BEXT floats plus 16 bytes) and written back row by
+// row, BEXT / 4 lanes per row segment, so that a store instruction covers whole row
+// segments instead of 32 pieces of 32 bytes.
+template <int AEXT, int BEXT, int TPW, int TILES, typename TileAB>
+__device__ __forceinline__ void store_partials(char *sbuf, const f32x16_t (&acc)[TPW], TileAB tile_ab, float *P,
+                                               int64_t pitch, int a_lim, int b_lim) {
+  constexpr int PB = BEXT * 4 + 16;
+  constexpr int LPR = BEXT / 4;  // 16-byte pieces per row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();  // no wave reads the staging buffers any more
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = wave + 4 * u;
+    if (TILES % 4 != 0 && tile >= TILES) continue;
+    int a0, b0;
+    tile_ab(tile, a0, b0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int a = a0 + (lane & 31), b = b0 + 8 * g + 4 * (lane >> 5);
+      *reinterpret_cast<f32x4_t *>(sbuf + a * PB + b * 4) =
+          f32x4_t{acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = static_cast<int>(threadIdx.x); q < AEXT * LPR; q += NT) {
+    const int a = q / LPR, b = (q % LPR) * 4;
+    if (a < a_lim && b < b_lim)
+      *reinterpret_cast<f32x4_t *>(P + a * pitch + b) = *reinterpret_cast<const f32x4_t *>(sbuf + a * PB + b * 4);
+  }
+}
+
 // BK: the adapter operand is given as B [Kc, r] (rows of the contraction, row pitch
 // ldwt) instead of WT [r, Kc]; its step tile (64 contraction rows of r ranks) is staged
 // row-major like reduce_m's S tile and read with the transposing LDS read, so the
@@ -190,22 +226,11 @@ __device__ __forceinline__ void lora_down_dma_body(
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land after the kernel ends
 
-  float *dst = P + static_cast<size_t>(by) * M * r;
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int tile = wave + 4 * u;
-    if (TILES % 4 != 0 && tile >= TILES) continue;
-    const int ti = tile & 1, tt = tile >> 1;
-    const int m = m0 + 32 * ti + (lane & 31);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int j0 = tt * 32 + g * 8 + (lane >> 5) * 4;
-      if (m < M && j0 < r) {
-        f32x4_t o = {acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
-        *reinterpret_cast<f32x4_t *>(dst + static_cast<size_t>(m) * r + j0) = o;
-      }
-    }
-  }
+  // partial sums [m][j] of rows m0 .. m0 + 63 (tile t: rows 32 (t & 1), ranks 32 (t >> 1))
+  static_assert(64 * (32 * RT * 4 + 16) <= NB * BUF, "partial-sum staging");
+  store_partials<64, 32 * RT, TPW, TILES>(
+      sbuf, acc, [](int t, int &a0, int &b0) { a0 = 32 * (t & 1); b0 = 32 * (t >> 1); },
+      P + static_cast<size_t>(by) * M * r + static_cast<size_t>(m0) * r, r, M - m0, r);
 }
 
 template <int RT>
@@ -336,24 +361,18 @@ __device__ __forceinline__ void reduce_m_dma_body(
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land after the kernel ends
 
+  // tile t: columns 32 (t & 1) of the 64 no, ranks 32 (t >> 1)
   float *dst = P + static_cast<size_t>(by) * No * r;
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int tile = wave + 4 * u;
-    if (TILES % 4 != 0 && tile >= TILES) continue;
-    const int tn = tile & 1, tj = tile >> 1;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4_t o = {acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
-      const int rq = g * 8 + (lane >> 5) * 4;  // first of 4 consecutive rows
-      if (!JMAJOR) {
-        const int no = nb0 + tn * 32 + (lane & 31), j0 = tj * 32 + rq;
-        if (no < No && j0 < r) *reinterpret_cast<f32x4_t *>(dst + static_cast<size_t>(no) * r + j0) = o;
-      } else {
-        const int j = tj * 32 + (lane & 31), no0 = nb0 + tn * 32 + rq;
-        if (j < r && no0 < No) *reinterpret_cast<f32x4_t *>(dst + static_cast<size_t>(j) * No + no0) = o;
-      }
-    }
+  if constexpr (!JMAJOR) {  // partial sums [no][j]
+    static_assert(64 * (32 * RT * 4 + 16) <= NB * BUF, "partial-sum staging");
+    store_partials<64, 32 * RT, TPW, TILES>(
+        sbuf, acc, [](int t, int &a0, int &b0) { a0 = 32 * (t & 1); b0 = 32 * (t >> 1); },
+        dst + static_cast<size_t>(nb0) * r, r, No - nb0, r);
+  } else {  // partial sums [j][no]
+    static_assert(32 * RT * (64 * 4 + 16) <= NB * BUF, "partial-sum staging");
+    store_partials<32 * RT, 64, TPW, TILES>(
+        sbuf, acc, [](int t, int &a0, int &b0) { a0 = 32 * (t >> 1); b0 = 32 * (t & 1); }, dst + nb0, No, r,
+        No - nb0);
   }
 }
 
