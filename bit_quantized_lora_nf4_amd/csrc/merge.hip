@@ -26,6 +26,8 @@
 // the data read as zero and drop stores), so the wait counts stay exact and two
 // tiles of loads and of stores stay in flight per wave.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "qlora_internal.h"
 
@@ -191,6 +193,46 @@ __device__ __forceinline__ float stage_constant(const BaseStage &st, int p, int 
   return __builtin_fmaf(c8, __uint_as_float(st.s[p]), __uint_as_float(st.o[p]));
 }
 
+// The merge's base operands of one tile for this lane: row lane / 2, the 32 columns
+// c0 + 32 (lane % 2) .. + 31 (c0 = 64 wave + strip start), half of one 64-weight block:
+// one 16-byte code load and one constant per lane and tile (four passes of the per-pass
+// layout would take sixteen small loads, and the loads' issue limited the kernel).
+struct MergeStage {
+  u32x4_t code;
+  uint32_t c8w, s, o;
+};
+template <int CT>
+__device__ __forceinline__ void issue_merge_base(const MergeArgs &a, const TileRsrc &t, int tile, uint32_t code16,
+                                                 uint32_t blk16, bool col_ok, MergeStage &st) {
+  st.code = buf_load16(t.codes, code16);
+  if constexpr (CT == kConstF32) {
+    st.s = __builtin_amdgcn_raw_buffer_load_b32(t.s, col_ok ? blk16 * 4u : kOOB, 0, 0);
+    return;
+  }
+  // as in issue_base: the aligned dword holding the 8-bit constant, clamped to the array
+  const int64_t total = a.N * a.K / 64;
+  const int64_t b0 = (static_cast<int64_t>(tile) * TR * a.K) >> 6;
+  const bool live = b0 < total;
+  const int8_t *cbase = a.absmax_q + (live ? b0 : 0);
+  const uint32_t last = live ? static_cast<uint32_t>((total - 1 - b0) & ~int64_t(3)) : 0u;
+  const uint32_t g = (static_cast<uint32_t>(b0 & 255) + blk16) >> 8;
+  st.c8w = *reinterpret_cast<const uint32_t *>(cbase + min(blk16 & ~3u, last));
+  st.s = __builtin_amdgcn_raw_buffer_load_b32(t.s, col_ok ? g * 4 : kOOB, 0, 0);
+  st.o = __builtin_amdgcn_raw_buffer_load_b32(t.o, col_ok ? g * 4 : kOOB, 0, 0);
+}
+template <int CT>
+__device__ __forceinline__ float merge_constant(const MergeStage &st, int byte) {
+  if constexpr (CT == kConstF32) return __uint_as_float(st.s);
+  float c8;
+  if constexpr (CT == kConstDqFp8)
+    c8 = e4m3_value(st.c8w >> (8 * byte));
+  else
+    c8 = static_cast<float>(static_cast<int>(st.c8w << (24 - 8 * byte)) >> 24);
+  return __builtin_fmaf(c8, __uint_as_float(st.s), __uint_as_float(st.o));
+}
+constexpr int PO = 64 * 2 + 16;  // per-wave bf16 output tile pitch (bytes), in the D region
+static_assert(TR * PO <= SD_WAVE, "output tile in the D region");
+
 // B fragments of one tile: sub-step s (ranks 16 s .. 16 s + 15) of lane l holds
 // B[n0 + l % 32][16 s + 8 (l / 32) .. + 7]; ranks past r read as zero.
 template <int NCH, bool RVEC>
@@ -279,7 +321,19 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   auto tile_of = [&](int i) { return first + i * a.per_strip; };  // >= tiles: empty
 
   const LaneOffsets lo = lane_offsets(a, col, col_ok);
-  BaseStage st0, st1;
+  // the merge's base layout: row lane / 2, columns colm .. colm + 31
+  const int64_t colm = k0 + 64 * wave + 32 * (lane & 1);
+  const int64_t em = static_cast<int64_t>(lane >> 1) * a.K + colm;
+  const uint32_t code16 = col_ok ? static_cast<uint32_t>(em / 2) : kOOB;
+  const uint32_t blk16 = static_cast<uint32_t>(em >> 6);
+  using Stage = std::conditional_t<UNMERGE, BaseStage, MergeStage>;
+  auto load_base = [&](const TileRsrc &t, int tile, Stage &st) {
+    if constexpr (UNMERGE)
+      issue_base<true, CT>(a, t, tile, lo, col_ok, st);
+    else
+      issue_merge_base<CT>(a, t, tile, code16, blk16, col_ok, st);
+  };
+  Stage st0, st1;
   u32x4_t bf0[4 * NCH], bf1[4 * NCH];
   {
     const TileRsrc t0 = tile_rsrc<CT>(a, tile_of(0), UNMERGE);
@@ -288,11 +342,11 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
     // compiler derives for the loop entry match the steady state
     issue_b<NCH, RVEC>(a, t0, bf0);
     issue_fence();
-    issue_base<UNMERGE, CT>(a, t0, tile_of(0), lo, col_ok, st0);
+    load_base(t0, tile_of(0), st0);
     issue_fence();
     issue_b<NCH, RVEC>(a, t1, bf1);
     issue_fence();
-    issue_base<UNMERGE, CT>(a, t1, tile_of(1), lo, col_ok, st1);
+    load_base(t1, tile_of(1), st1);
     issue_fence();
   }
 
@@ -301,7 +355,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   // also waits for every store issued before it: the loads of tile i + 2 therefore go
   // out before the stores of tile i, which leaves two tiles of stores in flight per
   // wave.  The fences keep each group where it is issued.
-  auto step = [&](int i, BaseStage &st, u32x4_t (&bf)[4 * NCH]) {
+  auto step = [&](int i, Stage &st, u32x4_t (&bf)[4 * NCH]) {
     f32x16_t acc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -325,24 +379,50 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
         *reinterpret_cast<f32x4_t *>(sd + (lane & 31) * PD + c * 4) = v;
       }
     u32x4_t o[PASSES];
+    if constexpr (UNMERGE) {
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = 8 * p + (lane >> 3);
-      const f32x4_t d0 = *reinterpret_cast<const f32x4_t *>(sd + row * PD + (lane & 7) * 32);
-      const f32x4_t d1 = *reinterpret_cast<const f32x4_t *>(sd + row * PD + (lane & 7) * 32 + 16);
-      const float d[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-      const int byte = static_cast<int>(lo.blk[p] & 3u);
-      const u32x4_t base =
-          UNMERGE ? st.wm[p] : lookup8(st.code[p], make_planes(stage_constant<CT>(st, p, byte), a.lvl));
+      for (int p = 0; p < PASSES; ++p) {
+        const int row = 8 * p + (lane >> 3);
+        const f32x4_t d0 = *reinterpret_cast<const f32x4_t *>(sd + row * PD + (lane & 7) * 32);
+        const f32x4_t d1 = *reinterpret_cast<const f32x4_t *>(sd + row * PD + (lane & 7) * 32 + 16);
+        const float d[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float t0 = a.scale * d[2 * h], t1 = a.scale * d[2 * h + 1];
-        const float w0 = bf16_lo(base[h]), w1 = bf16_hi(base[h]);
-        o[p][h] = UNMERGE ? pack_bf16x2(w0 - t0, w1 - t1) : pack_bf16x2(w0 + t0, w1 + t1);
+        for (int h = 0; h < 4; ++h) {
+          const float t0 = a.scale * d[2 * h], t1 = a.scale * d[2 * h + 1];
+          const float w0 = bf16_lo(st.wm[p][h]), w1 = bf16_hi(st.wm[p][h]);
+          o[p][h] = pack_bf16x2(w0 - t0, w1 - t1);
+        }
       }
+    } else {
+      // this lane's 32 columns of row lane / 2: the base from one plane table, D from
+      // the D region; the bf16 results go back to the region (rows of PO bytes) and are
+      // read out in the per-pass layout of the stores (8 rows x 128 bytes a pass)
+      const int row = lane >> 1, half = lane & 1;
+      const Planes pl = make_planes(merge_constant<CT>(st, static_cast<int>(blk16 & 3u)), a.lvl);
+      u32x4_t r4[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x4_t d0 = *reinterpret_cast<const f32x4_t *>(sd + row * PD + (32 * half + 8 * w) * 4);
+        const f32x4_t d1 = *reinterpret_cast<const f32x4_t *>(sd + row * PD + (32 * half + 8 * w) * 4 + 16);
+        const float d[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        const u32x4_t base = lookup8(st.code[w], pl);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float t0 = a.scale * d[2 * h], t1 = a.scale * d[2 * h + 1];
+          r4[w][h] = pack_bf16x2(bf16_lo(base[h]) + t0, bf16_hi(base[h]) + t1);
+        }
+      }
+      // the results overwrite D rows that other lanes read above: keep every read first
+      // (one wave's LDS accesses complete in issue order)
+      issue_fence();
+#pragma unroll
+      for (int w = 0; w < 4; ++w) *reinterpret_cast<u32x4_t *>(sd + row * PO + 64 * half + 16 * w) = r4[w];
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p)
+        o[p] = *reinterpret_cast<const u32x4_t *>(sd + (8 * p + (lane >> 3)) * PO + 16 * (lane & 7));
     }
     issue_fence();
-    issue_base<UNMERGE, CT>(a, tn, tile_of(i + 2), lo, col_ok, st);
+    load_base(tn, tile_of(i + 2), st);
     issue_fence();
     const TileRsrc tc = tile_rsrc<CT>(a, tile_of(i), UNMERGE);
 #pragma unroll
