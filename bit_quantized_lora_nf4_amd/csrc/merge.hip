@@ -25,6 +25,15 @@
 // Every load and store is a buffer access at a straight-line position (offsets past
 // the data read as zero and drop stores), so the wait counts stay exact and two
 // tiles of loads and of stores stay in flight per wave.
+//
+// With r <= 64 and r % 8 == 0 (one rank chunk, 16-byte aligned B rows) the operands
+// that every wave of a workgroup shares go through a shared stage instead: the tile's
+// B rows, its block constants and (merge) the strip's codes are fetched by the whole
+// workgroup in whole rows, one 16-byte piece per thread two tiles ahead, written to
+// LDS at the start of the tile, and read back as MFMA fragments and per-lane codes
+// after a barrier; a second barrier frees the stage for the next tile.  Per wave
+// these loads had touched 32 rows each, and B and the constants were fetched by all
+// four waves.
 
 #include <type_traits>
 
@@ -44,6 +53,17 @@ constexpr int PD = 64 * 4 + 16;        // per-wave D pitch (fp32 row of 64 colum
 constexpr int SD_WAVE = TR * PD;       // 8704
 constexpr int SMEM = SA_BYTES > 4 * SD_WAVE ? SA_BYTES : 4 * SD_WAVE;
 constexpr int PASSES = 4;              // 32 x 64 outputs per wave = 4 passes of 8 per lane
+// Shared stage (r <= 64, r % 8 == 0): the tile's B rows (32 rows of 128 bytes, 16-byte
+// chunks swizzled per row), its block constants (one word per row and wave) and, for
+// the merge, the codes of the strip (32 rows of 128 bytes), loaded once per workgroup
+// in whole rows after the four D regions
+constexpr int SB_OFF = 4 * SD_WAVE;
+constexpr int SB_BYTES = TR * 128;
+constexpr int SC_OFF = SB_OFF + SB_BYTES;
+constexpr int SC_BYTES = NT * 4;
+constexpr int SK_OFF = SC_OFF + SC_BYTES;
+constexpr int SK_BYTES = TR * 128;
+constexpr int SMEM_LB = SA_BYTES > SK_OFF + SK_BYTES ? SA_BYTES : SK_OFF + SK_BYTES;
 
 
 // Keeps the memory operations on each side where they are: the empty asm with a
@@ -201,12 +221,21 @@ struct MergeStage {
   u32x4_t code;
   uint32_t c8w, s, o;
 };
-template <int CT>
+// LB: the codes and the block constant come from the workgroup's shared stage
+// (issue_shared), so only the group scale and offset (double quantization) are loaded here.
+template <int CT, bool LB>
 __device__ __forceinline__ void issue_merge_base(const MergeArgs &a, const TileRsrc &t, int tile, uint32_t code16,
                                                  uint32_t blk16, bool col_ok, MergeStage &st) {
-  st.code = buf_load16(t.codes, code16);
+  if constexpr (!LB) st.code = buf_load16(t.codes, code16);
   if constexpr (CT == kConstF32) {
-    st.s = __builtin_amdgcn_raw_buffer_load_b32(t.s, col_ok ? blk16 * 4u : kOOB, 0, 0);
+    if constexpr (!LB) st.s = __builtin_amdgcn_raw_buffer_load_b32(t.s, col_ok ? blk16 * 4u : kOOB, 0, 0);
+    return;
+  }
+  if constexpr (LB) {
+    const int64_t b0 = (static_cast<int64_t>(tile) * TR * a.K) >> 6;
+    const uint32_t g = (static_cast<uint32_t>(b0 & 255) + blk16) >> 8;
+    st.s = __builtin_amdgcn_raw_buffer_load_b32(t.s, col_ok ? g * 4 : kOOB, 0, 0);
+    st.o = __builtin_amdgcn_raw_buffer_load_b32(t.o, col_ok ? g * 4 : kOOB, 0, 0);
     return;
   }
   // as in issue_base: the aligned dword holding the 8-bit constant, clamped to the array
@@ -219,6 +248,13 @@ __device__ __forceinline__ void issue_merge_base(const MergeArgs &a, const TileR
   st.c8w = *reinterpret_cast<const uint32_t *>(cbase + min(blk16 & ~3u, last));
   st.s = __builtin_amdgcn_raw_buffer_load_b32(t.s, col_ok ? g * 4 : kOOB, 0, 0);
   st.o = __builtin_amdgcn_raw_buffer_load_b32(t.o, col_ok ? g * 4 : kOOB, 0, 0);
+}
+// The block constant c' from the shared stage's word w (the fp32 constant, or the
+// zero-extended 8-bit code) and the lane's group scale and offset.
+template <int CT>
+__device__ __forceinline__ float shared_constant(const MergeStage &st, uint32_t w) {
+  if constexpr (CT == kConstF32) return __uint_as_float(w);
+  return __builtin_fmaf(c8_value<CT>(w), __uint_as_float(st.s), __uint_as_float(st.o));
 }
 template <int CT>
 __device__ __forceinline__ float merge_constant(const MergeStage &st, int byte) {
@@ -255,6 +291,39 @@ __device__ __forceinline__ void issue_b(const MergeArgs &a, const TileRsrc &t, u
   }
 }
 
+// Shared stage of one tile, one piece per thread: 16 bytes of the tile's B rows (chunk
+// `tid` of the contiguous 32 r bf16, zero past the weight's last row or the tile) and,
+// for the merge, the block constant of (row tid / 4, wave tid % 4), the 8-bit code or
+// the fp32 constant (zero for tid >= 128 or columns past K), and 16 bytes of the strip's
+// codes (row tid / 8, columns k0 + 32 (tid % 8) ..).  Every wave of the workgroup needs
+// all of B's rows and all its rows' constants; loading them per wave took four times the
+// loads, each touching 32 rows, where these touch whole rows; the codes, which each
+// wave loaded as 32 rows x 32 bytes, now come in rows of 128 bytes.
+template <int CT>
+struct SharedStage {
+  u32x4_t b, code;
+  typename std::conditional<CT == kConstF32, uint32_t, uint8_t>::type c;  // 8-bit code kept 8-bit
+};
+template <bool UNMERGE, int CT>
+__device__ __forceinline__ void issue_shared(const MergeArgs &a, const TileRsrc &t, int tile, int64_t k0,
+                                             SharedStage<CT> &sh) {
+  const int tid = threadIdx.x;
+  sh.b = buf_load16(t.b, static_cast<uint32_t>(tid) * 16u);
+  if constexpr (!UNMERGE) {
+    const int64_t kc = k0 + 32 * (tid & 7);
+    sh.code = buf_load16(t.codes, kc < a.K ? static_cast<uint32_t>(((tid >> 3) * a.K + kc) / 2) : kOOB);
+    const int wv = tid & 3;
+    const bool ok = tid < 4 * TR && k0 + 64 * wv < a.K;
+    // the block relative to the tile's first block
+    const uint32_t blk = static_cast<uint32_t>((static_cast<int64_t>(tid >> 2) * a.K + k0) >> 6) + wv;
+    if constexpr (CT == kConstF32)
+      sh.c = __builtin_amdgcn_raw_buffer_load_b32(t.s, ok ? blk * 4u : kOOB, 0, 0);
+    else
+      sh.c = __builtin_amdgcn_raw_buffer_load_b8(t.c8, ok ? blk : kOOB, 0, 0);
+  }
+  (void)tile;
+}
+
 // A fragment of sub-step s for the 32 columns starting at `cb` of a staged chunk:
 // lane l receives column cb + l % 32 of rank rows 16 s + 8 (l / 32) .. + 7.  Within a
 // 16-lane group, lane i reads row base + i / 4 at column 4 (i % 4) of its 16-column
@@ -278,7 +347,10 @@ __device__ __forceinline__ u32x4_t afrag(const char *sa, int s, int cb) {
 
 template <bool UNMERGE, bool RVEC, int NCH, int CT>
 __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  // B rows of 16-byte aligned length and one rank chunk: B and the block constants go
+  // through the workgroup's shared stage
+  constexpr bool LB = RVEC && NCH == 1;
+  __shared__ __attribute__((aligned(16))) char smem[LB ? SMEM_LB : SMEM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int strip = blockIdx.x % a.strips;
   const int first = blockIdx.x / a.strips;  // this workgroup's tiles: first + i * per_strip
@@ -331,20 +403,34 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
     if constexpr (UNMERGE)
       issue_base<true, CT>(a, t, tile, lo, col_ok, st);
     else
-      issue_merge_base<CT>(a, t, tile, code16, blk16, col_ok, st);
+      issue_merge_base<CT, LB>(a, t, tile, code16, blk16, col_ok, st);
   };
   Stage st0, st1;
   u32x4_t bf0[4 * NCH], bf1[4 * NCH];
+  SharedStage<CT> sh0, sh1;
+  // the shared stage: this thread's slot in the swizzled B tile (row x at x * 128,
+  // chunk c at slot c ^ (x % 8), so that the 16-byte fragment reads of eight
+  // consecutive rows fall in distinct banks); threads past the 4 r chunks write none
+  const int rpc = a.r / 8;  // 16-byte chunks per B row
+  const bool b_writer = LB && rpc > 0 && tid < 4 * a.r;
+  const int bx = rpc > 0 ? tid / rpc : 0, bc = rpc > 0 ? tid - bx * rpc : 0;
+  const int b_slot = SB_OFF + bx * 128 + ((bc ^ (bx & 7)) << 4);
+  auto issue_stage = [&](const TileRsrc &t, int tile, u32x4_t (&bf)[4 * NCH], SharedStage<CT> &sh) {
+    if constexpr (LB)
+      issue_shared<UNMERGE, CT>(a, t, tile, k0, sh);
+    else
+      issue_b<NCH, RVEC>(a, t, bf);
+  };
   {
     const TileRsrc t0 = tile_rsrc<CT>(a, tile_of(0), UNMERGE);
     const TileRsrc t1 = tile_rsrc<CT>(a, tile_of(1), UNMERGE);
     // same order as inside the loop (B, then base), so that the wait counts the
     // compiler derives for the loop entry match the steady state
-    issue_b<NCH, RVEC>(a, t0, bf0);
+    issue_stage(t0, tile_of(0), bf0, sh0);
     issue_fence();
     load_base(t0, tile_of(0), st0);
     issue_fence();
-    issue_b<NCH, RVEC>(a, t1, bf1);
+    issue_stage(t1, tile_of(1), bf1, sh1);
     issue_fence();
     load_base(t1, tile_of(1), st1);
     issue_fence();
@@ -355,7 +441,45 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   // also waits for every store issued before it: the loads of tile i + 2 therefore go
   // out before the stores of tile i, which leaves two tiles of stores in flight per
   // wave.  The fences keep each group where it is issued.
-  auto step = [&](int i, Stage &st, u32x4_t (&bf)[4 * NCH]) {
+  auto step = [&](int i, Stage &st, u32x4_t (&bf)[4 * NCH], SharedStage<CT> &sh) {
+    uint32_t cword = 0;  // the lane's block constant from the shared stage (merge)
+    if constexpr (LB) {
+      // Publish the shared stage of tile i (fetched two tiles earlier); every wave has
+      // read the previous tile's out of LDS (second barrier of the previous tile).
+      if (b_writer) *reinterpret_cast<u32x4_t *>(smem + b_slot) = sh.b;
+      if constexpr (!UNMERGE) {
+        if constexpr (CT == kConstF32)
+          *reinterpret_cast<uint32_t *>(smem + SC_OFF + 4 * tid) = sh.c;
+        else
+          *reinterpret_cast<uint8_t *>(smem + SC_OFF + tid) = sh.c;
+        // row x = tid / 8 at x * 128, chunk c at slot c ^ (x & 6): the readers' eight
+        // lanes (four rows, two chunks each) fall in distinct banks
+        *reinterpret_cast<u32x4_t *>(smem + SK_OFF + (tid >> 3) * 128 + (((tid & 7) ^ ((tid >> 3) & 6)) << 4)) =
+            sh.code;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // B fragments: row l % 32, chunk 2 s + l / 32 (ranks 16 s + 8 (l / 32) ..); chunks
+      // at or past r / 8 are zero
+      const int x = lane & 31;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 2 * q + (lane >> 5);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + SB_OFF + x * 128 + ((c ^ (x & 7)) << 4));
+        bf[q] = c < rpc ? v : u32x4_t{0u, 0u, 0u, 0u};
+      }
+      if constexpr (!UNMERGE) {
+        const int ci = 4 * (lane >> 1) + wave;  // (row lane / 2, this wave's block)
+        if constexpr (CT == kConstF32)
+          cword = *reinterpret_cast<const uint32_t *>(smem + SC_OFF + 4 * ci);
+        else
+          cword = *reinterpret_cast<const uint8_t *>(smem + SC_OFF + ci);
+        // this lane's 32 codes: row lane / 2, chunk 2 wave + lane % 2
+        const int kx = lane >> 1, kcn = 2 * wave + (lane & 1);
+        st.code = *reinterpret_cast<const u32x4_t *>(smem + SK_OFF + kx * 128 + ((kcn ^ (kx & 6)) << 4));
+      }
+      // every wave holds its fragments and constant before the stage is replaced
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     f32x16_t acc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -367,7 +491,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
       for (int t = 0; t < 2; ++t) acc[t] = mfma32x32x16(af[s][t], bf[s], acc[t]);
     issue_fence();
     const TileRsrc tn = tile_rsrc<CT>(a, tile_of(i + 2), UNMERGE);
-    issue_b<NCH, RVEC>(a, tn, bf);
+    issue_stage(tn, tile_of(i + 2), bf, sh);
     issue_fence();
     // acc[t][4 q + e]: row l % 32, wave column 32 t + 8 q + 4 (l / 32) + e
 #pragma unroll
@@ -398,7 +522,9 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
       // the D region; the bf16 results go back to the region (rows of PO bytes) and are
       // read out in the per-pass layout of the stores (8 rows x 128 bytes a pass)
       const int row = lane >> 1, half = lane & 1;
-      const Planes pl = make_planes(merge_constant<CT>(st, static_cast<int>(blk16 & 3u)), a.lvl);
+      const float cc =
+          LB ? shared_constant<CT>(st, cword) : merge_constant<CT>(st, static_cast<int>(blk16 & 3u));
+      const Planes pl = make_planes(cc, a.lvl);
       u32x4_t r4[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -431,8 +557,8 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   };
 
   for (int i = 0; i < count; i += 2) {
-    step(i, st0, bf0);
-    step(i + 1, st1, bf1);  // past the last tile: zero loads, dropped stores
+    step(i, st0, bf0, sh0);
+    step(i + 1, st1, bf1, sh1);  // past the last tile: zero loads, dropped stores
   }
 }
 
