@@ -17,6 +17,7 @@ an event pair per launch costs a few microseconds of GPU time, so timing every l
 would slow the step it measures); and the CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 15] [--time-every 4] [--no-cpu-baseline]
+                    [--no-extras] [--m1-only | --merge-only | --calibrate-copy]
 """
 
 import argparse
@@ -667,6 +668,8 @@ def main():
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--m1-only", action="store_true",
                     help="only run the M=1 weight-stream leg (for profiling the small-M forward) and exit")
+    ap.add_argument("--merge-only", action="store_true",
+                    help="only run the LoRA merge / unmerge leg (for profiling it) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; --gpus must be 1 "
@@ -680,6 +683,9 @@ def main():
     import bit_quantized_lora_nf4_amd as q
     import synth
     from synth import device as gc
+    if args.merge_only:
+        print(json.dumps({"lora_merge": measure_merge(torch, q)}), flush=True)
+        return
     if args.m1_only:
         ev = HipEvents()
         print(json.dumps({"weight_stream_m1": measure_m1(torch, q, synth, gc, ev)}), flush=True)
