@@ -148,3 +148,21 @@ def test_merge_full_size_sampled_rows(q, N, K):
     Wd = oracle_rows(Wf, rows)
     want = merge.merge(bf16_bits(Wd.astype(np.float32)), d["A"], d["B"][rows], alpha, r)
     check_merge(got[rows], want, Wd, d["A"], d["B"][rows], alpha, r, +1.0, f"merge {N}x{K} rows")
+
+
+# Block-constant types and level tables other than NF4 + int8 double quantization, with
+# ranks that take the workgroup-shared stage of B, the constants and the codes (r <= 64,
+# r % 8 == 0): K / 64 odd (a row's blocks not aligned to 4), ragged rows, r below 64.
+@pytest.mark.parametrize("qt,ct", [(0, 1), (0, 2), (1, 0), (1, 2)], ids=["nf4-dqfp8", "nf4-f32", "fp4-dq8", "fp4-f32"])
+@pytest.mark.parametrize("N,K,r", [(100, 320, 16), (77, 1088, 64), (64, 256, 8)])
+def test_merge_variants_with_rank(q, qt, ct, N, K, r):
+    from oracle import variants as v
+    print(f"merge variant qt={qt} ct={ct} N={N} K={K} r={r}", flush=True)
+    d = _weight_case(N, K, r, seed=3 * N + K + r + 10 * ct + qt)
+    alpha = 16.0
+    Wf = synth.bf16_bits_to_f32(d["W"])
+    Wd = v.dequantize_bf16_bits(v.quantize(Wf, qt, ct))
+    want = merge.merge(Wd, d["A"], d["B"], alpha, r)
+    qw = q.quantize(dev_bf16(d["W"]), quant_type=qt, const_type=ct)
+    got = host_bits(q.lora_merge(qw, dev_bf16(d["A"]), dev_bf16(d["B"]), alpha))
+    check_merge(got, want, f64(Wd), d["A"], d["B"], alpha, r, +1.0, f"merge qt={qt} ct={ct} {N}x{K} r={r}")
