@@ -67,6 +67,11 @@ namespace {
 
 constexpr int GMAXM = 16;
 constexpr int kMaxWaves = 16;
+// X from memory with one workgroup per CU (XDMA): each weight wave stages its own steps'
+// X slices (M tokens x the step's 4 blocks, at most 8 KB) in two LDS stages of its own,
+// loaded in whole 128-byte rows; at most kXdmaWaves weight waves per workgroup
+constexpr int kXdmaWaves = 8;
+constexpr int kXdmaStage = GMAXM * 4 * 128;
 // LDS bytes of one token's staged X row: 128 per 64-element block plus 16 of padding, so
 // that the rows of consecutive tokens start 16 bytes apart modulo 256 and the 16-byte
 // reads of the sixteen token lanes fall in distinct banks
@@ -424,10 +429,24 @@ __device__ void gather_u(const GemvArgs &a, uint16_t *su, int n0) {
   }
 }
 
-template <int CT, bool XLDS, bool MULTI, bool DIRECT>
+// One 16-byte piece per lane from a buffer straight into LDS (lane l at dst + 16 l).  A
+// named function: called from a lambda of the kernel template, the builtin kept the host
+// compilation from emitting those instantiations' launch stubs.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
+}
+
+template <int CT, bool XLDS, bool MULTI, bool DIRECT, bool XDMA = false>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  // XDMA: the two X stages of every weight wave, separate objects so that the waits the
+  // compiler derives for a stage's reads cover only that stage's loads
+  __shared__ __attribute__((aligned(16))) char xst0[XDMA ? kXdmaWaves * kXdmaStage : 16];
+  __shared__ __attribute__((aligned(16))) char xst1[XDMA ? kXdmaWaves * kXdmaStage : 16];
+  static_assert(!(XLDS && XDMA), "X is staged for the workgroup or per wave, not both");
   constexpr int D = XLDS ? 4 : 2;  // steps whose loads are in flight (the register ring)
+  constexpr bool XREG = !XLDS && !XDMA;  // X fragments loaded into registers with every step
+  using Loads = StepLoads<CT, !XREG>;
   // RG row groups of W weight waves each; wave RG W (R > 0) is the LoRA wave
   const int W = a.W, RG = a.RG, nW = RG * W;
   const int N = static_cast<int>(a.w.n_rows), KB = static_cast<int>(a.w.n_cols / 64), K = KB * 64;
@@ -517,30 +536,61 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
   // the loads of step t (blocks past the wave's range, or rows past N, read zeros: their
   // constant decodes to c' = 0, so they add nothing)
   auto load = [&](int t) {
-    StepLoads<CT, XLDS> s;
+    Loads s;
     const int b = kb0 + 4 * t + g;
     const bool ok = row_ok && b < kb1;
     const uint32_t off = ok ? row_code + b * 32 : kOOB;
     s.c0 = buf_load16(rc, off);
     s.c1 = buf_load16(rc, ok ? off + 16 : kOOB);
-    load_constant<CT, XLDS>(rq, row_blk + b, ok, s);
-    if constexpr (!XLDS) {
+    load_constant<CT, !XREG>(rq, row_blk + b, ok, s);
+    if constexpr (XREG) {
       const uint32_t xo = (static_cast<uint32_t>(tok) * K + b * 64) * 2;
 #pragma unroll
       for (int u = 0; u < 8; ++u) s.x[u] = buf_load16(rx, (tok_ok && b < kb1) ? xo + u * 16 : kOOB);
     }
     return s;
   };
+  // XDMA: the wave's X slice of step t goes to its stage as rows (blk M + tok) of 128
+  // bytes, the 16-byte chunk c of a row at slot c ^ (tok % 8) (the eight token lanes of a
+  // read then fall in distinct banks); load q of the eight writes rows 8 q .. 8 q + 7,
+  // lane l row 8 q + l / 8 and slot l % 8, so each covers eight whole 128-byte rows of X
+  // (rows past 4 M and blocks past the wave's range read zero)
+  uint32_t xq_off[XDMA ? 8 : 1];
+  int xq_blk[XDMA ? 8 : 1];
+  uint32_t xr_off[XDMA ? 8 : 1];
+  if constexpr (XDMA) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 8 * q + (lane >> 3);
+      const int tk = row % a.M, c = (lane & 7) ^ (tk & 7);
+      xq_off[q] = row < 4 * a.M ? (static_cast<uint32_t>(tk) * K + c * 8) * 2 : kOOB;
+      xq_blk[q] = row / a.M;
+    }
+    // this lane's reads: token tok, block g of the step, chunk u
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      xr_off[u] = static_cast<uint32_t>(wave * kXdmaStage + (g * a.M + tok) * 128 + ((u ^ (tok & 7)) << 4));
+  }
+  auto issue_x = [&](int t, char *stage) {
+    const int bp = kb0 + 4 * t;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool ok = xq_off[q] != kOOB && bp + xq_blk[q] < kb1;
+      dma16(rx, stage + wave * kXdmaStage + q * 1024, ok ? xq_off[q] + static_cast<uint32_t>(bp + xq_blk[q]) * 128 : kOOB);
+    }
+  };
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto compute = [&](const StepLoads<CT, XLDS> &s, int t) {
+  auto compute = [&](const Loads &s, int t, const char *stage) {
     const int b = kb0 + 4 * t + g;
-    const Planes pl = make_planes(constant_of<CT, XLDS>(s, gc, row_blk + b, row_ok && b < kb1), a.lvl);
+    const Planes pl = make_planes(constant_of<CT, !XREG>(s, gc, row_blk + b, row_ok && b < kb1), a.lvl);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const uint32_t cw = u < 4 ? s.c0[u] : s.c1[u - 4];
       u32x4_t xv;
       if constexpr (XLDS)
         xv = *reinterpret_cast<const u32x4_t *>(sx + tok * xrow_bytes(KB) + (b < kb1 ? b : kb0) * 128 + u * 16);
+      else if constexpr (XDMA)
+        xv = permute8(*reinterpret_cast<const u32x4_t *>(stage + xr_off[u]));
       else
         xv = permute8(s.x[u]);
       acc = mfma16x16x32(lookup8_pairs(cw, pl), xv, acc);
@@ -577,10 +627,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
     }
   }
   __syncthreads();
-  StepLoads<CT, XLDS> st[D];
+  Loads st[D];
+  // XDMA: ring slot j's X stage (D = 2 there; j is a constant once the loops are unrolled)
+  auto stage_of = [&](int j) -> char * { return j == 0 ? xst0 : xst1; };
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     st[j] = load(j);
+    if constexpr (XDMA) issue_x(j, stage_of(j));
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -588,15 +641,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvArgs a) {
   for (; t0 + D < Tw; t0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-      compute(st[j], t0 + j);
+      compute(st[j], t0 + j, stage_of(j));
       __builtin_amdgcn_sched_barrier(0);
       st[j] = load(t0 + j + D);
+      if constexpr (XDMA) issue_x(t0 + j + D, stage_of(j));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    if (t0 + j < Tw) compute(st[j], t0 + j);
+    if (t0 + j < Tw) compute(st[j], t0 + j, stage_of(j));
 
   f32x4_t y = reduce_waves(lds + lp.red + grp * W * 1024, acc, W, wv, lane);
   if (wv != 0) return;
@@ -728,6 +782,7 @@ struct GemvPlan {
   GemvShape sh;
   int RG;       // row groups per workgroup
   bool xlds;
+  bool xdma;    // X not staged for the workgroup: each weight wave stages its own steps' X
   bool direct;  // U_s handed over through per-workgroup counters (gather_u)
   int lds_bytes;
   int LB, SP;
@@ -755,6 +810,7 @@ GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int R, bool allow_rg = true)
   const int64_t tiles = (N + 15) / 16;
   GemvPlan p;
   p.RG = 1;
+  p.xdma = false;
   // staged X: about 100 VGPRs (5 waves per SIMD); X from memory: about 130 (4)
   p.sh = gemv_shape(N, K, 20, extra);
   p.xlds = lds_plan(p.sh.W, static_cast<int>(M), R, R, KB, true, true, 1).total <= lds_budget(tiles);
@@ -772,7 +828,11 @@ GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int R, bool allow_rg = true)
         (R == 0 || gather_ok(M, R, q.SP, kGatherTripsRG)))
       p = q;
   }
-  if (!p.xlds) p.sh = gemv_shape(N, K, 16, extra);
+  // X from memory: with one workgroup per CU (at most 256 tiles) and two or more tokens,
+  // each of at most kXdmaWaves weight waves stages its own X slices in LDS (the X
+  // fragment loads of the other layout touch 64 rows of X each)
+  p.xdma = !p.xlds && tiles <= 256 && M >= 2;
+  if (!p.xlds) p.sh = gemv_shape(N, K, p.xdma ? kXdmaWaves + extra : 16, extra);
   lora_slices(p, KB);
   p.direct = gather_ok(M, R, p.SP, p.RG > 1 ? kGatherTripsRG : kGatherTrips);
   p.lds_bytes = lds_plan(p.RG * p.sh.W, static_cast<int>(M), R, R, KB, p.xlds, p.direct, p.RG).total;
@@ -809,7 +869,7 @@ bool gemv_supported(const WeightView &w, int64_t M, int r) {
 }
 
 namespace {
-template <int CT, bool XLDS, bool MULTI, bool DIRECT>
+template <int CT, bool XLDS, bool MULTI, bool DIRECT, bool XDMA = false>
 hipError_t go_gemv1(const GemvArgs &a, int lds_bytes, hipStream_t stream) {
   if (lds_bytes > 64 * 1024) {
     static std::once_flag once[64];
@@ -817,19 +877,29 @@ hipError_t go_gemv1(const GemvArgs &a, int lds_bytes, hipStream_t stream) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::call_once(once[dev], [&] {
-      err[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_kernel<CT, XLDS, MULTI, DIRECT>),
+      err[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_kernel<CT, XLDS, MULTI, DIRECT, XDMA>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     });
     if (err[dev] != hipSuccess) return err[dev];
   }
-  hipLaunchKernelGGL((gemv_kernel<CT, XLDS, MULTI, DIRECT>), dim3(static_cast<unsigned>(a.G)),
+  hipLaunchKernelGGL((gemv_kernel<CT, XLDS, MULTI, DIRECT, XDMA>), dim3(static_cast<unsigned>(a.G)),
                      dim3(64 * (a.RG * a.W + (a.R > 0 ? 1 : 0))),
                      static_cast<size_t>(lds_bytes), stream, a);
   return hipGetLastError();
 }
 template <int CT, bool XLDS>
-hipError_t go_gemv(const GemvArgs &a, bool direct, int lds_bytes, hipStream_t stream) {
+hipError_t go_gemv(const GemvArgs &a, bool direct, bool xdma, int lds_bytes, hipStream_t stream) {
   const bool multi = a.PT * a.SP > a.G;
+  if constexpr (!XLDS) {
+    // the XDMA layout with one row group and at most kXdmaWaves weight waves
+    if (xdma && a.RG == 1 && a.W <= kXdmaWaves) {
+      if (direct)
+        return multi ? go_gemv1<CT, false, true, true, true>(a, lds_bytes, stream)
+                     : go_gemv1<CT, false, false, true, true>(a, lds_bytes, stream);
+      return multi ? go_gemv1<CT, false, true, false, true>(a, lds_bytes, stream)
+                   : go_gemv1<CT, false, false, false, true>(a, lds_bytes, stream);
+    }
+  }
   if (direct)
     return multi ? go_gemv1<CT, XLDS, true, true>(a, lds_bytes, stream)
                  : go_gemv1<CT, XLDS, false, true>(a, lds_bytes, stream);
@@ -874,14 +944,14 @@ hipError_t launch_gemv(const WeightView &w, const uint16_t *X, int64_t M, const 
   a.lvl = level_table(w.quant_type);
   switch (w.const_type) {
     case kConstDqInt8:
-      return p.xlds ? go_gemv<kConstDqInt8, true>(a, p.direct, p.lds_bytes, stream)
-                    : go_gemv<kConstDqInt8, false>(a, p.direct, p.lds_bytes, stream);
+      return p.xlds ? go_gemv<kConstDqInt8, true>(a, p.direct, false, p.lds_bytes, stream)
+                    : go_gemv<kConstDqInt8, false>(a, p.direct, p.xdma, p.lds_bytes, stream);
     case kConstDqFp8:
-      return p.xlds ? go_gemv<kConstDqFp8, true>(a, p.direct, p.lds_bytes, stream)
-                    : go_gemv<kConstDqFp8, false>(a, p.direct, p.lds_bytes, stream);
+      return p.xlds ? go_gemv<kConstDqFp8, true>(a, p.direct, false, p.lds_bytes, stream)
+                    : go_gemv<kConstDqFp8, false>(a, p.direct, p.xdma, p.lds_bytes, stream);
     case kConstF32:
-      return p.xlds ? go_gemv<kConstF32, true>(a, p.direct, p.lds_bytes, stream)
-                    : go_gemv<kConstF32, false>(a, p.direct, p.lds_bytes, stream);
+      return p.xlds ? go_gemv<kConstF32, true>(a, p.direct, false, p.lds_bytes, stream)
+                    : go_gemv<kConstF32, false>(a, p.direct, p.xdma, p.lds_bytes, stream);
     default: return hipErrorInvalidValue;
   }
 }

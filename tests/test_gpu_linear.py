@@ -72,6 +72,9 @@ SMALL = [  # (M, K, N, r)
     (16, 4096, 7990, 16),  # X staged once for 2 row groups per workgroup (one per CU), ragged last tile
     (16, 4096, 11008, 16), # 3 row groups per workgroup; the last workgroup holds one
     (12, 4096, 5000, 0),   # row groups without an adapter
+    (16, 8256, 200, 16),   # X too large to stage for the workgroup: each weight wave stages its own slices (odd K/64)
+    (9, 10240, 72, 0),     # the same with an odd M and no adapter
+    (16, 9216, 4096, 24),  # the same at 256 tiles (one workgroup per CU)
 ]
 
 
@@ -162,6 +165,26 @@ def test_deterministic(lib, N, const_type):
     for later in outs[1:]:
         for a, b in zip(outs[0], later):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("const_type", [0, 1, 2])
+def test_deterministic_per_wave_x_staging(lib, const_type):
+    """The small-M forward whose weight waves stage their own X slices (X too large to
+    stage for the workgroup): repeated calls are bitwise equal.  A wait that did not cover
+    a stage's loads would show as a run-to-run difference."""
+    import torch
+    M, K, N, r = 16, 8256, 328, 16
+    d = synth.case(M, K, N, r, seed=29)
+    qw = lib.quantize(gc.dev_weight(d), const_type=const_type)
+    X, A, B = _dev(d, r)
+    outs = []
+    for _ in range(4):
+        Y, U = lib.linear_fwd(qw, X, A, B, 16.0)
+        outs.append((Y.clone(), U.clone()))
+    torch.cuda.synchronize()
+    for Y, U in outs[1:]:
+        assert torch.equal(Y.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(U.view(torch.int16), outs[0][1].view(torch.int16))
 
 
 @pytest.mark.parametrize("M", [300, 5])
