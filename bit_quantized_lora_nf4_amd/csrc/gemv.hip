@@ -19,11 +19,15 @@
 //                     products run on 16x16x32 bf16 MFMA with tokens as the 16 columns
 //                     (columns past M are never stored).  A workgroup holds one row group,
 //                     or RG of them (one workgroup per CU) when X would not fit in LDS
-//                     beside several workgroups.  It first stages X and its rows of the
+//                     beside several workgroups; when X fits neither way and the grid
+//                     is one workgroup per CU, each weight wave stages its own steps' X
+//                     slices (two LDS stages per wave, loaded in whole 128-byte rows).
+//                     It first stages X and its rows of the
 //                     LoRA B in LDS, then each wave issues the loads of its first D steps
 //                     (a register ring), so that decoding starts as soon as the first step
 //                     has landed and the weight stream never drains; the compiler derives
-//                     every wait from the register dependencies.  W, T and RG are chosen on
+//                     every wait from the register dependencies (for the per-wave X stages,
+//                     from the LDS object each stage is).  W, T and RG are chosen on
 //                     the host so that the busiest SIMD of the launch runs as few
 //                     wave-steps as possible.  At the end each group adds its waves'
 //                     partial sums in a fixed order through LDS, and the LoRA up-projection
