@@ -264,3 +264,55 @@ def test_lora_no_register_spills(lora_asm):
     assert len(sizes) >= 20, sizes
     for name, size in sizes.items():
         assert int(size) <= 16, f"{name}: {size} bytes of scratch"
+
+
+# The small-M forward's per-wave X stages: each weight wave loads a step's X slice straight
+# into one of its two LDS stages (two LDS objects) and reads it back as MFMA fragments two
+# ring slots later; the waits before those reads are the compiler's.  In the main loop
+# (two steps per iteration, each issuing the same loads), the wait ahead of each step's
+# first LDS read must leave in flight at most the other step's loads, so that the step's
+# own direct-to-LDS loads have landed.
+
+@pytest.fixture(scope="module")
+def gemv_asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "gemv.s"
+    flags = [f for f in libbuild.FLAGS if f not in ("-fPIC",)]
+    cmd = [HIPCC] + flags + ["--cuda-device-only", "-S", os.path.join(libbuild.CSRC, "gemv.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return out.read_text()
+
+
+def test_gemv_x_stage_waits(gemv_asm):
+    # gemv_kernel<CT, XLDS = false, MULTI, DIRECT, XDMA = true>
+    kernels = re.findall(r"^(_Z\S*gemv_kernelILi\dELb0ELb\dELb\dELb1E\S*):", gemv_asm, re.M)
+    assert len(kernels) == 12, kernels
+    for name in kernels:
+        body = re.search(r"^" + re.escape(name) + r":.*?^\.Lfunc_end", gemv_asm, re.S | re.M).group(0)
+        lines = [l.strip() for l in body.splitlines()]
+        labels = {m.group(1): i for i, l in enumerate(lines) if (m := re.match(r"^(\.LBB\S+):", l))}
+        loops = [(labels[m.group(2)], i) for i, l in enumerate(lines)
+                 if (m := _BR.search(l)) and m.group(2) in labels and labels[m.group(2)] < i]
+        a, b = max(loops, key=lambda x: x[1] - x[0])  # the main loop: the longest back edge
+        loop = lines[a:b + 1]
+        dma = sum(1 for l in loop if l.startswith("buffer_load") and l.endswith(" lds"))
+        vmem = sum(1 for l in loop if _VMEM.match(l))
+        assert dma == 16 and vmem % 2 == 0, (name, dma, vmem)
+        per_step = vmem // 2
+        # the last vmcnt wait before each run of LDS reads that follows vector memory issue
+        waits, last, seen_vmem = [], None, True
+        for l in loop:
+            w = re.match(r"s_waitcnt vmcnt\((\d+)\)", l)
+            if w:
+                last = int(w.group(1))
+            elif _VMEM.match(l):
+                seen_vmem, last = True, None
+            elif l.startswith("ds_read") and seen_vmem:
+                waits.append(last)
+                seen_vmem = False
+        assert len(waits) == 2, (name, waits)
+        for n in waits:
+            assert n is not None and n <= per_step, \
+                f"{name}: LDS reads of a stage after vmcnt({n}), but a step issues {per_step} loads"
