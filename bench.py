@@ -17,7 +17,7 @@ an event pair per launch costs a few microseconds of GPU time, so timing every l
 would slow the step it measures); and the CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 15] [--time-every 4] [--no-cpu-baseline]
-                    [--no-extras] [--m1-only | --merge-only | --calibrate-copy]
+                    [--no-extras] [--m1-only [--small-m 1|4|16] | --merge-only | --calibrate-copy]
 """
 
 import argparse
@@ -678,6 +678,8 @@ def main():
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--m1-only", action="store_true",
                     help="only run the M=1 weight-stream leg (for profiling the small-M forward) and exit")
+    ap.add_argument("--small-m", type=int, default=1, choices=(1, 4, 16),
+                    help="token count of the --m1-only leg (default 1)")
     ap.add_argument("--merge-only", action="store_true",
                     help="only run the LoRA merge / unmerge leg (for profiling it) and exit")
     args = ap.parse_args()
@@ -698,7 +700,8 @@ def main():
         return
     if args.m1_only:
         ev = HipEvents()
-        print(json.dumps({"weight_stream_m1": measure_m1(torch, q, synth, gc, ev)}), flush=True)
+        key = "weight_stream_m%d" % args.small_m
+        print(json.dumps({key: measure_m1(torch, q, synth, gc, ev, M=args.small_m)}), flush=True)
         ev.close()
         return
 
